@@ -1,0 +1,16 @@
+"""CPU oracle for speculative-sampling verification — test infrastructure only.
+
+Imported by the test suite, the smoke check and the benchmark's CPU-baseline leg;
+never by the product library or its binding.
+"""
+from .specverify_oracle import (  # noqa: F401
+    FLAG_WINDOW,
+    temperature_softmax,
+    acceptance_probability,
+    residual_weights,
+    inverse_cdf,
+    verify_chain,
+    node_depths,
+    verify_tree_greedy,
+    tree_mask,
+)

@@ -1,0 +1,22 @@
+"""Seeded synthetic inputs for speculative-sampling verification.
+
+This package draws random logits, draft tokens, temperatures, uniforms and
+candidate trees. It holds none of the verification arithmetic (no softmax, no
+acceptance test, no residual, no argmax over a verified distribution): both the
+HIP path and the CPU oracle consume what it produces, and neither is imported
+here.
+"""
+from .synth import (  # noqa: F401
+    SEED_BASE,
+    ChainConfig,
+    TreeConfig,
+    CHAIN_CONFIGS,
+    TREE_CONFIGS,
+    MC_CONFIG,
+    seed_stream,
+    chain_inputs,
+    mc_chain_inputs,
+    tree_parents_ranked,
+    tree_inputs,
+    sample_draft_tokens_gumbel,
+)
