@@ -1,0 +1,211 @@
+/*
+ * specverify — the verification step of speculative sampling on AMD Instinct
+ * MI355X (gfx950), as a C ABI.
+ *
+ * A speculative-decoding iteration has a small draft model propose K tokens,
+ * the target model score all of them in one pass, and a verification step
+ * decide which proposals to keep. This library is that verification step:
+ *
+ *   sv_verify_chain        modified rejection sampling over a chain of K
+ *                          proposals, with the residual resample at the first
+ *                          rejection or a bonus token when all K are kept;
+ *   sv_verify_tree_greedy  greedy (argmax-matching) verification of a
+ *                          candidate tree given as a parent array;
+ *   sv_build_tree_mask     the tree's ancestor ("2D tree attention") mask.
+ *
+ * Sources, cited by page title and section:
+ *   [Topologies]       "Speculative Decoding & Draft Model Topologies: Slashing
+ *                      Enterprise LLM Latency by 3.5x in 2026" — section 2
+ *                      (acceptance probability, residual distribution, timeline
+ *                      figure) and section 4 (EAGLE-2 tree figure).
+ *   [Draft-and-Verify] "Speculative Decoding for LLM Inference: How
+ *                      Draft-and-Verify Accelerates Token Generation" — "The
+ *                      draft-and-verify loop", "The correctness guarantee".
+ *   [At Scale]         "Speculative Decoding at Scale: Latency Reduction in
+ *                      Distributed LLM Serving" — sequence diagram, section 1.
+ *   [In Production]    "Speculative Decoding in Production: How Small Draft
+ *                      Models & Medusa Heads Deliver 2x–3x LLM Speedups Without
+ *                      Accuracy Loss" — section 2 (acceptance rules) and
+ *                      section 4 (tree verification, custom 2D masks).
+ *
+ * Conventions shared by every call:
+ *   - Every array argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or keeps them.
+ *   - Calls are stream-ordered and asynchronous: they enqueue kernels on
+ *     `stream` and return; outputs are valid once the caller has synchronised
+ *     that stream. No call synchronises the host.
+ *   - Argument errors (sizes, NULL pointers, dtype, workspace too small,
+ *     misaligned logits) are returned synchronously and nothing is launched.
+ *     A failed launch returns SV_ERR_HIP.
+ *   - Data errors can only be seen on the device. They are OR-ed into
+ *     `*err_flags` (when it is not NULL; the caller clears it) as SV_ERRF_*
+ *     bits, and the affected sequence reports accept_len = -1 with every
+ *     output token -1.
+ *   - Logit tensors are dense row-major with rows of V elements; bf16 is the
+ *     upper half of an IEEE binary32 (the PyTorch bfloat16 layout). NaN logits
+ *     are outside the contract.
+ *   - A workspace belongs to one call at a time: two calls that overlap in
+ *     time (different streams, or different host threads) need two workspaces.
+ */
+#ifndef SPECVERIFY_H_
+#define SPECVERIFY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP runtime's stream handle (identical to its own declaration). */
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum sv_status {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARGUMENT = 1, /* a size, pointer or alignment is invalid      */
+  SV_ERR_UNSUPPORTED = 2,      /* valid but beyond this build's limits         */
+  SV_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than required      */
+  SV_ERR_HIP = 4               /* the HIP runtime refused the launch           */
+} sv_status;
+
+typedef enum sv_dtype {
+  SV_DTYPE_F32 = 0, /* IEEE binary32 logits                                 */
+  SV_DTYPE_BF16 = 1 /* bfloat16 logits (16 high bits of a binary32)          */
+} sv_dtype;
+
+/* Data-error bits written to *err_flags. */
+#define SV_ERRF_TOKEN 0x1u       /* a draft / node token outside [0, V)          */
+#define SV_ERRF_TEMPERATURE 0x2u /* a temperature <= 0, NaN or infinite          */
+#define SV_ERRF_PARENT 0x4u      /* parents[i] is neither -1 nor in [0, i)       */
+#define SV_ERRF_NONFINITE 0x8u   /* a row's maximum is +inf, or its normaliser    \
+                                    is 0 / not finite                            */
+#define SV_ERRF_INTERNAL 0x10u   /* a partial result never became visible to the  \
+                                    block combining them (should not happen)     */
+
+#define SV_MAX_K 63           /* drafted tokens per sequence (K+1 fits a wave64) */
+#define SV_MAX_TREE_NODES 1024 /* candidate-tree nodes per call                  */
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* sv_status_string(sv_status status);
+
+/* ------------------------------------------------------------------------
+ * Chain verification.
+ *
+ * Bytes of device workspace sv_verify_chain needs for (B, K, V, dtype); 0 for
+ * invalid sizes. The workspace must be zero-filled once before its first use
+ * (e.g. hipMemset or torch.zeros). Every call that returns SV_OK leaves the
+ * whole workspace zero again once its kernels have run, so one workspace can
+ * serve any sequence of calls (of any shape, chain or tree) on one stream.
+ * After a call that returned an error, zero-fill it again.
+ */
+size_t sv_chain_workspace_bytes(int32_t B, int32_t K, int32_t V, sv_dtype dtype);
+
+/*
+ * One verification step of chain speculative sampling for B independent
+ * sequences. For sequence b, with T = temperature[b]:
+ *
+ *   p_k = softmax(target_logits[b,k,:] / T),  k = 0..K      ([Draft-and-Verify]
+ *   q_k = softmax(draft_logits[b,k,:] / T),   k = 0..K-1     "draft-and-verify loop")
+ *   x_k = draft_tokens[b,k];  alpha_k = min(1, p_k(x_k) / q_k(x_k))
+ *       (alpha_k = 0 if p_k(x_k) = 0; = 1 if q_k(x_k) = 0 < p_k(x_k))
+ *   proposal k is kept iff uniforms[b,k] < alpha_k, checked in order; the
+ *   first rejected k is j (j = K when all are kept)  ([Topologies] section 2;
+ *                                                      [In Production] section 2)
+ *   if j < K: one token drawn from max(0, p_j - q_j) / sum(max(0, p_j - q_j))
+ *             ([Topologies] residual equation; [At Scale] section 1);
+ *             if that sum is 0 in the device's arithmetic, from p_j;
+ *   if j = K: one bonus token drawn from p_K ([Draft-and-Verify] loop);
+ *   the draw uses uniforms[b,K] and the inverse CDF in ascending token id:
+ *   the first t whose cumulative weight exceeds uniforms[b,K] * total.
+ *
+ * Arguments (device pointers unless noted):
+ *   target_logits  [B, K+1, V] dtype, row-major, element-aligned (read only)
+ *   draft_logits   [B, K, V] dtype, same V (draft and target share one
+ *                  vocabulary); may be NULL when K = 0 (read only)
+ *   dtype          SV_DTYPE_F32 or SV_DTYPE_BF16, for both logit tensors
+ *   draft_tokens   [B, K] int32, each in [0, V); may be NULL when K = 0
+ *   temperature    [B] float32, each > 0 and finite; NULL means 1.0 for all
+ *   uniforms       [B, K+1] float32 in [0, 1): columns 0..K-1 for the accept
+ *                  tests, column K for the replacement / bonus draw
+ *   B, K, V        host ints: 0 <= B, 0 <= K <= SV_MAX_K, 1 <= V
+ *   accept_len     [B] int32 out: j (0..K), or -1 on a data error
+ *   out_tokens     [B, K+1] int32 out: x_0..x_{j-1}, then the drawn token,
+ *                  then -1 up to column K (1..K+1 tokens per sequence)
+ *   p_draft        [B, K] float32 out or NULL: p_k(x_k) for every k < K
+ *   q_draft        [B, K] float32 out or NULL: q_k(x_k) for every k < K
+ *   residual_mass  [B] float32 out or NULL: sum max(0, p_j - q_j) when j < K,
+ *                  -1 when all K were kept
+ *   err_flags      [1] int32 in/out or NULL: SV_ERRF_* bits are OR-ed in
+ *   workspace      device buffer of at least sv_chain_workspace_bytes() bytes
+ *   stream         HIP stream the kernels are enqueued on (NULL = default)
+ */
+sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                          const int32_t* draft_tokens, const float* temperature,
+                          const float* uniforms, int32_t B, int32_t K, int32_t V,
+                          int32_t* accept_len, int32_t* out_tokens, float* p_draft,
+                          float* q_draft, float* residual_mass, int32_t* err_flags,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Greedy tree verification.
+ *
+ * Bytes of device workspace sv_verify_tree_greedy needs; 0 for invalid sizes.
+ * Same zero-fill contract as the chain workspace (a call leaves it all zero).
+ */
+size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype);
+
+/*
+ * Greedy verification of one candidate tree per sequence ([Topologies]
+ * section 4 figure: all nodes checked in one target pass, the longest
+ * accepted path kept; [In Production] section 4; [At Scale] sequence diagram:
+ * matching proposals are kept and the target adds its own next token).
+ *
+ *   g[b,n] = argmax_v target_logits[b,n,v] (raw logits, lowest v on ties)
+ *   node i is accepted iff node_tokens[b,i] == g[b, pos(parents[i])] and its
+ *   parent is accepted (or is the root); pos(-1) = 0, pos(i) = i + 1.
+ *   The deepest accepted node (lowest index on ties) ends the accepted path;
+ *   the next token is g at that node's position (g[b,0] if none is accepted).
+ *
+ * Arguments (device pointers unless noted):
+ *   target_logits  [B, N+1, V] dtype: position 0 = after the root (the last
+ *                  accepted token), position i+1 = after node i (read only)
+ *   node_tokens    [B, N] int32 in [0, V)
+ *   parents        [N] int32, shared by all sequences: -1 for a child of the
+ *                  root, else an earlier node's index (< i)
+ *   B, N, V        host ints: 0 <= B, 1 <= N <= SV_MAX_TREE_NODES, 1 <= V
+ *   accept_len     [B] int32 out: depth of the deepest accepted node (0 if
+ *                  none), -1 on a data error
+ *   path_nodes     [B, N] int32 out: accepted node ids from the root side,
+ *                  -1 padded
+ *   next_token     [B] int32 out: the target's token after the accepted path
+ *   err_flags      [1] int32 in/out or NULL
+ *   workspace      device buffer of at least sv_tree_workspace_bytes() bytes
+ *   stream         HIP stream (NULL = default)
+ */
+sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype,
+                                const int32_t* node_tokens, const int32_t* parents, int32_t B,
+                                int32_t N, int32_t V, int32_t* accept_len, int32_t* path_nodes,
+                                int32_t* next_token, int32_t* err_flags, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Ancestor mask of a candidate tree ([Topologies] section 4 figure: all nodes
+ * verified through one 2D tree-masked attention; [In Production] section 4:
+ * a custom 2D causal mask): mask[i*N + j] = 1 iff j == i or j is an ancestor
+ * of i, else 0. Nodes only (the root is not a row or column).
+ *
+ *   parents    [N] int32 (device): -1 or an earlier node's index
+ *   N          host int, 1 <= N <= SV_MAX_TREE_NODES
+ *   mask       [N, N] uint8 out (device)
+ *   err_flags  [1] int32 in/out or NULL: SV_ERRF_PARENT on a bad parent, in
+ *              which case the mask contents are unspecified
+ *   stream     HIP stream (NULL = default)
+ */
+sv_status sv_build_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H_ */

@@ -1,0 +1,25 @@
+"""specverify for AMD MI355X: speculative-sampling verification in HIP.
+
+The compute lives in ``libspecverify.so`` (HIP kernels for gfx950 behind a C
+ABI declared in ``include/specverify.h``); :mod:`.specverify` is its thin
+ctypes binding. Build with ``python -m rejection_sampling_verification_sv_amd.build``.
+"""
+from .specverify import (  # noqa: F401
+    PreparedChainCall,
+    SpecVerifyError,
+    SV_DTYPE_BF16,
+    SV_DTYPE_F32,
+    SV_ERRF_NONFINITE,
+    SV_ERRF_PARENT,
+    SV_ERRF_TEMPERATURE,
+    SV_ERRF_TOKEN,
+    SV_MAX_K,
+    SV_MAX_TREE_NODES,
+    library,
+    sv_build_tree_mask,
+    sv_chain_workspace_bytes,
+    sv_status_string,
+    sv_tree_workspace_bytes,
+    sv_verify_chain,
+    sv_verify_tree_greedy,
+)

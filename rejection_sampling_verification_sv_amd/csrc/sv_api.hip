@@ -1,0 +1,203 @@
+// C-ABI entry points of libspecverify: argument validation, workspace
+// carve-up and kernel launches on the caller's stream. The contract of every
+// function is documented in include/specverify.h.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sv_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool dtype_ok(sv_dtype d) { return d == SV_DTYPE_F32 || d == SV_DTYPE_BF16; }
+int dtype_bytes(sv_dtype d) { return d == SV_DTYPE_BF16 ? 2 : 4; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Statistics segments per row for a row of V elements.
+int32_t stats_segments(int32_t V, sv_dtype d) {
+  const int64_t vec = 16 / dtype_bytes(d);
+  const int64_t nvec = ceil_div(V, vec);
+  const int64_t n = ceil_div(nvec, sv::kStatsSegVecs);
+  return static_cast<int32_t>(n < 1 ? 1 : n);
+}
+
+struct ChainLayout {
+  int32_t nseg, ntiles, tiles_per_block, nblk_b;
+  size_t off_part_m, off_part_s, off_cnt_a, off_cnt_b, off_plan, off_tiles, total;
+};
+
+ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
+  ChainLayout L{};
+  const int64_t R = 2 * static_cast<int64_t>(K) + 1;
+  L.nseg = stats_segments(V, d);
+  L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
+  L.tiles_per_block = sv::kSampleTilesPerBlock;
+  L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
+  const int64_t parts = static_cast<int64_t>(B) * R * L.nseg;
+  size_t off = 0;
+  L.off_part_m = off;
+  off = align_up(off + sizeof(uint64_t) * parts);
+  L.off_part_s = off;
+  off = align_up(off + sizeof(uint64_t) * parts);
+  L.off_cnt_a = off;
+  off = align_up(off + sizeof(uint32_t) * B);
+  L.off_cnt_b = off;
+  off = align_up(off + sizeof(uint32_t) * B);
+  L.off_plan = off;
+  off = align_up(off + sizeof(sv::SeqPlan) * B);
+  L.off_tiles = off;
+  off = align_up(off + sizeof(uint64_t) * static_cast<int64_t>(B) * L.ntiles);
+  L.total = off;
+  return L;
+}
+
+struct TreeLayout {
+  int32_t nseg;
+  size_t off_part, off_cnt, total;
+};
+
+TreeLayout tree_layout(int32_t B, int32_t N, int32_t V, sv_dtype d) {
+  TreeLayout L{};
+  L.nseg = stats_segments(V, d);
+  const int64_t parts = static_cast<int64_t>(B) * (N + 1) * L.nseg;
+  size_t off = 0;
+  L.off_part = off;
+  off = align_up(off + sizeof(uint64_t) * parts);
+  L.off_cnt = off;
+  off = align_up(off + sizeof(uint32_t) * B);
+  L.total = off;
+  return L;
+}
+
+bool chain_sizes_ok(int32_t B, int32_t K, int32_t V) { return B >= 0 && K >= 0 && K <= SV_MAX_K && V >= 1; }
+bool tree_sizes_ok(int32_t B, int32_t N, int32_t V) {
+  return B >= 0 && N >= 1 && N <= SV_MAX_TREE_NODES && V >= 1;
+}
+
+bool aligned_to(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+sv_status from_hip(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sv_status_string(sv_status status) {
+  switch (status) {
+    case SV_OK:
+      return "SV_OK";
+    case SV_ERR_INVALID_ARGUMENT:
+      return "SV_ERR_INVALID_ARGUMENT";
+    case SV_ERR_UNSUPPORTED:
+      return "SV_ERR_UNSUPPORTED";
+    case SV_ERR_WORKSPACE:
+      return "SV_ERR_WORKSPACE";
+    case SV_ERR_HIP:
+      return "SV_ERR_HIP";
+  }
+  return "SV_ERR_UNKNOWN";
+}
+
+size_t sv_chain_workspace_bytes(int32_t B, int32_t K, int32_t V, sv_dtype dtype) {
+  if (!chain_sizes_ok(B, K, V) || !dtype_ok(dtype)) return 0;
+  return chain_layout(B, K, V, dtype).total;
+}
+
+sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                          const int32_t* draft_tokens, const float* temperature, const float* uniforms,
+                          int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
+                          float* p_draft, float* q_draft, float* residual_mass, int32_t* err_flags,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return SV_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SV_OK;
+  if (target_logits == nullptr || uniforms == nullptr || accept_len == nullptr || out_tokens == nullptr)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (K > 0 && (draft_logits == nullptr || draft_tokens == nullptr)) return SV_ERR_INVALID_ARGUMENT;
+  const int eb = dtype_bytes(dtype);
+  if (!aligned_to(target_logits, eb) || (draft_logits != nullptr && !aligned_to(draft_logits, eb)))
+    return SV_ERR_INVALID_ARGUMENT;
+  const ChainLayout L = chain_layout(B, K, V, dtype);
+  if (workspace == nullptr || workspace_bytes < L.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
+  const int64_t R = 2 * static_cast<int64_t>(K) + 1;
+  if (static_cast<int64_t>(B) * R * L.nseg > INT32_MAX || static_cast<int64_t>(B) * L.nblk_b > INT32_MAX)
+    return SV_ERR_UNSUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  sv::ChainParams p{};
+  p.target = target_logits;
+  p.draft = draft_logits;
+  p.tokens = draft_tokens;
+  p.temperature = temperature;
+  p.uniforms = uniforms;
+  p.B = B;
+  p.K = K;
+  p.V = V;
+  p.nseg = L.nseg;
+  p.seg_vecs = sv::kStatsSegVecs;
+  p.ntiles = L.ntiles;
+  p.tiles_per_block = L.tiles_per_block;
+  p.nblk_b = L.nblk_b;
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  p.p_draft = p_draft;
+  p.q_draft = q_draft;
+  p.residual_mass = residual_mass;
+  p.err_flags = err_flags;
+  p.part_m = reinterpret_cast<uint64_t*>(ws + L.off_part_m);
+  p.part_s = reinterpret_cast<uint64_t*>(ws + L.off_part_s);
+  p.cnt_a = reinterpret_cast<uint32_t*>(ws + L.off_cnt_a);
+  p.cnt_b = reinterpret_cast<uint32_t*>(ws + L.off_cnt_b);
+  p.plan = reinterpret_cast<sv::SeqPlan*>(ws + L.off_plan);
+  p.tile_sum = reinterpret_cast<uint64_t*>(ws + L.off_tiles);
+  return from_hip(sv::launch_chain(p, dtype, stream));
+}
+
+size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype) {
+  if (!tree_sizes_ok(B, N, V) || !dtype_ok(dtype)) return 0;
+  return tree_layout(B, N, V, dtype).total;
+}
+
+sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const int32_t* node_tokens,
+                                const int32_t* parents, int32_t B, int32_t N, int32_t V, int32_t* accept_len,
+                                int32_t* path_nodes, int32_t* next_token, int32_t* err_flags, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype) || !tree_sizes_ok(B, N, V)) return SV_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SV_OK;
+  if (target_logits == nullptr || node_tokens == nullptr || parents == nullptr || accept_len == nullptr ||
+      path_nodes == nullptr || next_token == nullptr)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (!aligned_to(target_logits, dtype_bytes(dtype))) return SV_ERR_INVALID_ARGUMENT;
+  const TreeLayout L = tree_layout(B, N, V, dtype);
+  if (workspace == nullptr || workspace_bytes < L.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
+  if (static_cast<int64_t>(B) * (N + 1) * L.nseg > INT32_MAX) return SV_ERR_UNSUPPORTED;
+
+  char* ws = static_cast<char*>(workspace);
+  sv::TreeParams p{};
+  p.target = target_logits;
+  p.tokens = node_tokens;
+  p.parents = parents;
+  p.B = B;
+  p.N = N;
+  p.V = V;
+  p.nseg = L.nseg;
+  p.seg_vecs = sv::kStatsSegVecs;
+  p.accept_len = accept_len;
+  p.path_nodes = path_nodes;
+  p.next_token = next_token;
+  p.err_flags = err_flags;
+  p.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
+  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+  return from_hip(sv::launch_tree(p, dtype, stream));
+}
+
+sv_status sv_build_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
+                             hipStream_t stream) {
+  if (N < 1 || N > SV_MAX_TREE_NODES || parents == nullptr || mask == nullptr) return SV_ERR_INVALID_ARGUMENT;
+  return from_hip(sv::launch_tree_mask(parents, N, mask, err_flags, stream));
+}
+
+}  // extern "C"

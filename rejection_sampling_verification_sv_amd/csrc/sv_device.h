@@ -1,0 +1,228 @@
+// Device-side building blocks shared by the specverify kernels (gfx950, wave64).
+//
+// - 16-byte vector loads of logits and their conversion to fp32 (bf16 is the
+//   upper half of a binary32, so widening is a shift or a mask);
+// - wave64 reductions through cross-lane shuffles and block (256-thread)
+//   reductions / exclusive scans through LDS, in a fixed order so that the
+//   same inputs always give bit-identical results;
+// - the "last workgroup to arrive" hand-off: every workgroup of a sequence
+//   publishes its partial result, bumps the sequence's counter, and the one
+//   that brings the counter to its total finishes the sequence (atomic
+//   slots, see below: no fences, so no L2 write-back per workgroup).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;             // threads per workgroup (4 wave64s)
+constexpr int kWave = 64;
+constexpr int kWaves = kThreads / kWave;
+
+// Logit element types. kVec = elements per 16-byte load.
+struct BF16 {
+  static constexpr int kVec = 8;
+  static constexpr int kBytes = 2;
+};
+struct F32 {
+  static constexpr int kVec = 4;
+  static constexpr int kBytes = 4;
+};
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+template <class T>
+__device__ __forceinline__ float load_elem(const void* row, int64_t i);
+
+template <>
+__device__ __forceinline__ float load_elem<BF16>(const void* row, int64_t i) {
+  return bf16_bits_to_float(static_cast<const uint16_t*>(row)[i]);
+}
+template <>
+__device__ __forceinline__ float load_elem<F32>(const void* row, int64_t i) {
+  return static_cast<const float*>(row)[i];
+}
+
+// Widen one 16-byte vector into T::kVec floats, in ascending element order.
+template <class T>
+__device__ __forceinline__ void unpack(const uint4& v, float* out);
+
+template <>
+__device__ __forceinline__ void unpack<BF16>(const uint4& v, float* out) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void unpack<F32>(const uint4& v, float* out) {
+  out[0] = __uint_as_float(v.x);
+  out[1] = __uint_as_float(v.y);
+  out[2] = __uint_as_float(v.z);
+  out[3] = __uint_as_float(v.w);
+}
+
+__device__ __forceinline__ uint4 load_vec(const void* p) { return *static_cast<const uint4*>(p); }
+
+// v_exp_f32: 2^x (about 1 ulp; inputs below -126 give 0 or a denormal).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- wave64 reductions
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// ---------------------------------------------------------------- block (256) reductions
+// `scratch` must hold kWaves elements; every thread of the block must call.
+
+__device__ __forceinline__ float block_max(float v, float* scratch) {
+  v = wave_max(v);
+  if (lane_id() == 0) scratch[wave_id()] = v;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, scratch[w]);
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ double block_sum(double v, double* scratch) {
+  v = wave_sum(v);
+  if (lane_id() == 0) scratch[wave_id()] = v;
+  __syncthreads();
+  double r = scratch[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r += scratch[w];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int block_max_int(int v, int* scratch) {
+  v = wave_max_int(v);
+  if (lane_id() == 0) scratch[wave_id()] = v;
+  __syncthreads();
+  int r = scratch[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) r = max(r, scratch[w]);
+  __syncthreads();
+  return r;
+}
+
+// Exclusive prefix sum over the block in thread order (fp64). Returns the
+// exclusive prefix of this thread; *total gets the block total, computed as
+// (exclusive prefix of the last thread) + (its value) so that a caller can
+// reproduce it exactly from the same inputs.
+__device__ __forceinline__ double block_exclusive_scan(double v, double* scratch, double* total) {
+  const int lane = lane_id();
+  double inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double n = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += n;
+  }
+  double excl_in_wave = __shfl_up(inc, 1, kWave);
+  if (lane == 0) excl_in_wave = 0.0;
+  if (lane == kWave - 1) scratch[wave_id()] = inc;
+  __syncthreads();
+  double wave_prefix = 0.0;
+  for (int w = 0; w < wave_id(); ++w) wave_prefix += scratch[w];
+  const double excl = wave_prefix + excl_in_wave;
+  __syncthreads();
+  // The last thread publishes the total in the same terms a caller uses:
+  // its exclusive prefix plus its own value.
+  if (threadIdx.x == kThreads - 1) scratch[0] = excl + v;
+  __syncthreads();
+  *total = scratch[0];
+  __syncthreads();
+  return excl;
+}
+
+// ---------------------------------------------------------------- last-arriver hand-off
+//
+// Blocks of one sequence publish partial results into 64-bit slots of the
+// workspace and bump the sequence's counter; the block whose increment brings
+// the counter to its total combines the slots. No cache write-back or
+// invalidate is needed (an agent-scope fence costs an L2 write-back per block
+// on this part): each slot is written by ONE agent-scope atomic store whose
+// value is never all-zero bits, and the last block reads each slot with
+// agent-scope atomic loads until it is non-zero. Every store it waits for has
+// already been issued by a block that has arrived, so the wait ends; it is
+// still bounded (kSpinLimit polls) and reports SV_ERRF_INTERNAL if it ever
+// expires. The last block sets the slots back to zero after use.
+
+constexpr int kSpinLimit = 1 << 22;
+constexpr uint32_t kErrInternal = 0x10u;  // SV_ERRF_INTERNAL
+
+__device__ __forceinline__ void publish(uint64_t* slot, uint64_t v) {
+  __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t await_slot(uint64_t* slot, uint32_t* err) {
+  uint64_t v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int it = 0; v == 0ull && it < kSpinLimit; ++it) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (v == 0ull) *err |= kErrInternal;
+  return v;
+}
+
+__device__ __forceinline__ void clear_slot(uint64_t* slot) { publish(slot, 0ull); }
+
+// Tagged encodings (a written slot is never zero).
+__device__ __forceinline__ uint64_t tag_float(float f) {
+  return (1ull << 32) | static_cast<uint64_t>(__float_as_uint(f));
+}
+__device__ __forceinline__ float untag_float(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v)); }
+// a non-negative double with its sign bit set (so 0.0 is stored as -0.0)
+__device__ __forceinline__ uint64_t tag_nonneg_double(double d) {
+  return static_cast<uint64_t>(__double_as_longlong(d)) | (1ull << 63);
+}
+__device__ __forceinline__ double untag_nonneg_double(uint64_t v) {
+  return __longlong_as_double(static_cast<long long>(v & ~(1ull << 63)));
+}
+
+// Every thread of the block calls this after thread 0 has published the
+// block's slots. Returns true in exactly one block per counter round (the
+// last to arrive), which then resets the counter for the next launch.
+__device__ __forceinline__ bool arrive_and_check_last(uint32_t* counter, uint32_t total, int* s_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_flag = (prev + 1u == total) ? 1 : 0;
+  }
+  __syncthreads();
+  return *s_flag != 0;
+}
+
+__device__ __forceinline__ void reset_counter(uint32_t* counter) {
+  if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void raise_error(int32_t* err_flags, uint32_t bits) {
+  if (err_flags != nullptr && bits != 0u)
+    __hip_atomic_fetch_or(err_flags, static_cast<int32_t>(bits), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace sv

@@ -1,0 +1,304 @@
+// Greedy tree verification and the tree ancestor mask.
+//
+// tree_argmax_kernel, one workgroup per (sequence, position, segment): streams
+// a segment of one logit row with 16-byte loads and keeps, per thread, the
+// largest value and its lowest index (a batch is scanned for its first maximum
+// only when it beats the running one). The block combines (value desc, index
+// asc) and publishes the pair. The last block of a sequence combines the
+// segments into g[n] = argmax of every position and resolves the tree:
+// node i is accepted iff its token equals g at its parent's position and its
+// parent is accepted; acceptance and depth are propagated up the parent links
+// by pointer jumping (log2(depth) rounds); the deepest accepted node (lowest
+// index on ties) ends the path, and g at its position is the next token.
+// [Topologies] "Speculative Decoding & Draft Model Topologies", section 4
+// figure (all tree nodes checked in one pass, the longest accepted path kept);
+// [In Production] "Speculative Decoding in Production", section 4;
+// [At Scale] "Speculative Decoding at Scale", sequence diagram (matching
+// proposals are kept, the target adds its own next token).
+//
+// tree_mask_kernel, one workgroup per node i: marks i and its ancestors in an
+// LDS bitmap by walking the parent links, then writes row i of the mask.
+// [Topologies] section 4 figure (2D tree-masked attention); [In Production]
+// section 4 (custom 2D causal mask).
+#include <limits.h>
+#include <math.h>
+
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+namespace {
+
+// (value, index) with "better" = larger value, then smaller index.
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(v, o, kWave);
+    const int oi = __shfl_xor(i, o, kWave);
+    if (better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+__device__ __forceinline__ void block_argmax(float& v, int& i, float* sv, int* si) {
+  wave_argmax(v, i);
+  if (lane_id() == 0) {
+    sv[wave_id()] = v;
+    si[wave_id()] = i;
+  }
+  __syncthreads();
+  v = sv[0];
+  i = si[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) {
+    if (better(sv[w], si[w], v, i)) {
+      v = sv[w];
+      i = si[w];
+    }
+  }
+  __syncthreads();
+}
+
+__device__ void tree_decide(const TreeParams& P, int b) {
+  __shared__ int s_g[SV_MAX_TREE_NODES + 1];
+  __shared__ int s_par[SV_MAX_TREE_NODES];
+  __shared__ int s_anc[2][SV_MAX_TREE_NODES];
+  __shared__ int s_dep[2][SV_MAX_TREE_NODES];
+  __shared__ unsigned char s_ok[2][SV_MAX_TREE_NODES];
+  __shared__ uint32_t s_err;
+  __shared__ int s_red[kWaves];
+  const int N = P.N;
+  const int N1 = N + 1;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_err = 0u;
+  __syncthreads();
+
+  // g[n]: combine the segment partials of every position.
+  for (int n = tid; n < N1; n += kThreads) {
+    const int64_t base = (static_cast<int64_t>(b) * N1 + n) * P.nseg;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    uint32_t err = 0u;
+    for (int s = 0; s < P.nseg; ++s) {
+      const uint64_t slot = await_slot(&P.part[base + s], &err);
+      const float v = __uint_as_float(static_cast<uint32_t>(slot >> 32));
+      const int i = static_cast<int>(static_cast<uint32_t>(slot) - 1u);
+      if (better(v, i, bv, bi)) {
+        bv = v;
+        bi = i;
+      }
+    }
+    s_g[n] = (bi == INT_MAX) ? 0 : bi;  // a row of -inf only: its first index
+    if (err != 0u) atomicOr(&s_err, err);
+  }
+  __syncthreads();
+
+  // Node i: validity, match with its parent's argmax, first jump.
+  for (int i = tid; i < N; i += kThreads) {
+    const int par = P.parents[i];
+    const int tok = P.tokens[static_cast<int64_t>(b) * N + i];
+    uint32_t err = 0u;
+    const bool par_ok = (par == -1) || (par >= 0 && par < i);
+    if (!par_ok) err |= SV_ERRF_PARENT;
+    if (tok < 0 || tok >= P.V) err |= SV_ERRF_TOKEN;
+    if (err != 0u) atomicOr(&s_err, err);
+    const int pos = (par_ok && par >= 0) ? par + 1 : 0;
+    s_par[i] = par_ok ? par : -1;
+    s_anc[0][i] = par_ok ? par : -1;
+    s_ok[0][i] = (par_ok && tok == s_g[pos]) ? 1 : 0;
+    s_dep[0][i] = 1;
+  }
+  __syncthreads();
+
+  // Pointer jumping. Invariant: the segment from i up to (not including)
+  // anc[i] has dep[i] nodes, and ok[i] is the AND of their matches. With 11
+  // rounds the jump length 2^11 exceeds any depth <= SV_MAX_TREE_NODES.
+  int cur = 0;
+  for (int round = 0; round < 11; ++round) {
+    const int nxt = cur ^ 1;
+    for (int i = tid; i < N; i += kThreads) {
+      const int a = s_anc[cur][i];
+      if (a >= 0) {
+        s_ok[nxt][i] = s_ok[cur][i] & s_ok[cur][a];
+        s_dep[nxt][i] = s_dep[cur][i] + s_dep[cur][a];
+        s_anc[nxt][i] = s_anc[cur][a];
+      } else {
+        s_ok[nxt][i] = s_ok[cur][i];
+        s_dep[nxt][i] = s_dep[cur][i];
+        s_anc[nxt][i] = -1;
+      }
+    }
+    __syncthreads();
+    cur = nxt;
+  }
+
+  // Deepest accepted node, lowest index on ties: max of (depth, 2047 - i).
+  int key = -1;
+  for (int i = tid; i < N; i += kThreads)
+    if (s_ok[cur][i]) key = max(key, (s_dep[cur][i] << 11) | (2047 - i));
+  key = block_max_int(key, s_red);
+  const int best = key < 0 ? -1 : 2047 - (key & 2047);
+  const int depth = key < 0 ? 0 : (key >> 11);
+  const bool bad = s_err != 0u;
+
+  // Path from the root side, built in LDS (reusing the jump buffer).
+  int* s_path = s_anc[cur ^ 1];
+  if (tid == 0 && !bad) {
+    int k = best;
+    for (int d = depth - 1; d >= 0 && k >= 0; --d) {
+      s_path[d] = k;
+      k = s_par[k];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += kThreads)
+    P.path_nodes[static_cast<int64_t>(b) * N + i] = (!bad && i < depth) ? s_path[i] : -1;
+  if (tid == 0) {
+    P.accept_len[b] = bad ? -1 : depth;
+    P.next_token[b] = bad ? -1 : s_g[best + 1];
+    raise_error(P.err_flags, s_err);
+  }
+}
+
+}  // namespace
+
+template <class T>
+__global__ __launch_bounds__(kThreads) void tree_argmax_kernel(TreeParams P) {
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves];
+  __shared__ int s_flag;
+  constexpr int VEC = T::kVec;
+  constexpr int U = kStatsUnroll;
+
+  const int N1 = P.N + 1;
+  const int64_t blk = blockIdx.x;
+  const int seg = static_cast<int>(blk % P.nseg);
+  const int64_t rowid = blk / P.nseg;
+  const int b = static_cast<int>(rowid / N1);
+  const int tid = threadIdx.x;
+
+  const void* row = static_cast<const char*>(P.target) + rowid * static_cast<int64_t>(P.V) * T::kBytes;
+  const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
+  const int head = min(static_cast<int>(((16u - (addr & 15u)) & 15u) / T::kBytes), P.V);
+  const int64_t nvec = (P.V - head) / VEC;
+  const int tail = static_cast<int>((P.V - head) - nvec * VEC);
+  const int64_t v0 = static_cast<int64_t>(seg) * P.seg_vecs;
+  const int64_t v1 = min(nvec, v0 + P.seg_vecs);
+  const uint4* body = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + head * T::kBytes);
+
+  // Each thread sees its elements in ascending index order, so a strict '>'
+  // keeps the first occurrence of its maximum.
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  if (seg == 0 && tid < head) {
+    const float x = load_elem<T>(row, tid);
+    if (x > bv) {
+      bv = x;
+      bi = tid;
+    }
+  }
+  for (int64_t base = v0 + tid; base < v1; base += static_cast<int64_t>(kThreads) * U) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t vi = base + static_cast<int64_t>(u) * kThreads;
+      raw[u] = (vi < v1) ? body[vi] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float x[U * VEC];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      unpack<T>(raw[u], &x[u * VEC]);
+      const int64_t vi = base + static_cast<int64_t>(u) * kThreads;
+      if (vi >= v1) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) x[u * VEC + k] = -INFINITY;
+      }
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) bm = fmaxf(bm, x[u * VEC + k]);
+    }
+    if (bm > bv) {
+      int first = -1;
+#pragma unroll
+      for (int q = U * VEC - 1; q >= 0; --q)
+        if (x[q] == bm) first = q;
+      const int u = first / VEC;
+      bv = bm;
+      bi = static_cast<int>(head + (base + static_cast<int64_t>(u) * kThreads) * VEC + (first % VEC));
+    }
+  }
+  if (seg == P.nseg - 1 && tid < tail) {
+    const int idx = static_cast<int>(head + nvec * VEC + tid);
+    const float x = load_elem<T>(row, idx);
+    if (x > bv) {
+      bv = x;
+      bi = idx;
+    }
+  }
+  block_argmax(bv, bi, s_v, s_i);
+  if (tid == 0)
+    publish(&P.part[blk], (static_cast<uint64_t>(__float_as_uint(bv)) << 32) | static_cast<uint32_t>(bi + 1));
+
+  if (!arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(N1) * P.nseg, &s_flag)) return;
+  tree_decide(P, b);
+  // Leave the workspace all zero for the next call, whatever its shape.
+  __syncthreads();
+  const int64_t base = static_cast<int64_t>(b) * N1 * P.nseg;
+  for (int64_t i = tid; i < static_cast<int64_t>(N1) * P.nseg; i += kThreads) clear_slot(&P.part[base + i]);
+  reset_counter(&P.cnt[b]);
+}
+
+__global__ __launch_bounds__(kThreads) void tree_mask_kernel(const int32_t* parents, int N, uint8_t* mask,
+                                                             int32_t* err_flags) {
+  __shared__ uint32_t s_bits[SV_MAX_TREE_NODES / 32];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  for (int w = tid; w < SV_MAX_TREE_NODES / 32; w += kThreads) s_bits[w] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    // parent indices strictly decrease along a valid chain, so the walk ends
+    int k = i;
+    uint32_t err = 0u;
+    while (k >= 0) {
+      s_bits[k >> 5] |= 1u << (k & 31);
+      const int p = parents[k];
+      if (p != -1 && (p < 0 || p >= k)) {
+        err = SV_ERRF_PARENT;
+        break;
+      }
+      k = p;
+    }
+    raise_error(err_flags, err);
+  }
+  __syncthreads();
+  uint8_t* out = mask + static_cast<int64_t>(i) * N;
+  for (int j = tid; j < N; j += kThreads) out[j] = static_cast<uint8_t>((s_bits[j >> 5] >> (j & 31)) & 1u);
+}
+
+template <class T>
+static hipError_t launch_tree_t(const TreeParams& p, hipStream_t stream) {
+  const int64_t grid = static_cast<int64_t>(p.B) * (p.N + 1) * p.nseg;
+  if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(tree_argmax_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, hipStream_t stream) {
+  return dtype == SV_DTYPE_BF16 ? launch_tree_t<BF16>(p, stream) : launch_tree_t<F32>(p, stream);
+}
+
+hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(tree_mask_kernel, dim3(static_cast<uint32_t>(N)), dim3(kThreads), 0, stream, parents, N,
+                     mask, err_flags);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,279 @@
+"""Python binding of libspecverify: argument marshalling only.
+
+Each ``sv_*`` function here has the name of the C entry point it calls. It
+checks that the tensors are contiguous device tensors of the expected dtype
+and shape, allocates outputs (and a zero-filled workspace) with PyTorch when
+the caller does not pass them, and forwards raw device pointers and the
+current HIP stream. Every step of the computation runs in the library's HIP
+kernels; there is no CPU or PyTorch fallback: a missing library or a CPU
+tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Optional
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libspecverify.so")
+
+SV_OK = 0
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+SV_ERRF_TOKEN = 0x1
+SV_ERRF_TEMPERATURE = 0x2
+SV_ERRF_PARENT = 0x4
+SV_ERRF_NONFINITE = 0x8
+SV_MAX_K = 63
+SV_MAX_TREE_NODES = 1024
+
+_DTYPES = {torch.float32: SV_DTYPE_F32, torch.bfloat16: SV_DTYPE_BF16}
+
+_c_i32 = ctypes.c_int32
+_c_ptr = ctypes.c_void_p
+_c_size = ctypes.c_size_t
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class SpecVerifyError(RuntimeError):
+    """A non-SV_OK status from the library."""
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m rejection_sampling_verification_sv_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.sv_status_string.argtypes = [ctypes.c_int]
+        lib.sv_status_string.restype = ctypes.c_char_p
+        lib.sv_chain_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int]
+        lib.sv_chain_workspace_bytes.restype = _c_size
+        lib.sv_verify_chain.argtypes = [
+            _c_ptr, _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
+        ]
+        lib.sv_verify_chain.restype = ctypes.c_int
+        lib.sv_tree_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int]
+        lib.sv_tree_workspace_bytes.restype = _c_size
+        lib.sv_verify_tree_greedy.argtypes = [
+            _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
+        ]
+        lib.sv_verify_tree_greedy.restype = ctypes.c_int
+        lib.sv_build_tree_mask.argtypes = [_c_ptr, _c_i32, _c_ptr, _c_ptr, _c_ptr]
+        lib.sv_build_tree_mask.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def library():
+    """The loaded ctypes library (loads it on first use)."""
+    return _load()
+
+
+def sv_status_string(status: int) -> str:
+    return _load().sv_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != SV_OK:
+        raise SpecVerifyError(f"{what}: {sv_status_string(status)}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None, device=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device}); the library has no CPU path")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(device, stream) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+# Zero-filled workspaces, one per (device, stream): the library returns every
+# workspace to all-zero counters at the end of each call, so a workspace can
+# be reused by the next call on the same stream.
+_workspaces: Dict[tuple, torch.Tensor] = {}
+
+
+def workspace(device, nbytes: int, stream=None) -> torch.Tensor:
+    key = (torch.device(device).index, _stream_handle(device, stream))
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def sv_chain_workspace_bytes(B: int, K: int, V: int, dtype: torch.dtype) -> int:
+    return int(_load().sv_chain_workspace_bytes(B, K, V, _DTYPES[dtype]))
+
+
+def sv_tree_workspace_bytes(B: int, N: int, V: int, dtype: torch.dtype) -> int:
+    return int(_load().sv_tree_workspace_bytes(B, N, V, _DTYPES[dtype]))
+
+
+def sv_verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
+                    temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
+                    accept_len=None, out_tokens=None, p_draft=None, q_draft=None, residual_mass=None,
+                    err_flags=None, workspace_tensor=None, stream=None, want_probs: bool = True) -> dict:
+    """Chain verification (``sv_verify_chain``). Shapes as in include/specverify.h.
+
+    Returns a dict with ``accept_len [B]``, ``out_tokens [B,K+1]``, and when
+    ``want_probs`` ``p_draft``, ``q_draft [B,K]``, ``residual_mass [B]``, plus
+    ``err_flags [1]``. Outputs are ready once the stream has been synchronised.
+    """
+    lib = _load()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, K+1, V]")
+    B, K1, V = target.shape
+    K = K1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _dev(target, "target")
+    if K > 0:
+        _dev(draft, "draft", dtype=target.dtype, shape=(B, K, V), device=dev)
+        _dev(draft_tokens, "draft_tokens", dtype=torch.int32, shape=(B, K), device=dev)
+    if temperature is not None:
+        _dev(temperature, "temperature", dtype=torch.float32, shape=(B,), device=dev)
+    _dev(uniforms, "uniforms", dtype=torch.float32, shape=(B, K1), device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    accept_len = torch.empty((B,), **i32) if accept_len is None else _dev(accept_len, "accept_len", torch.int32, (B,), dev)
+    out_tokens = torch.empty((B, K1), **i32) if out_tokens is None else _dev(out_tokens, "out_tokens", torch.int32, (B, K1), dev)
+    if want_probs:
+        p_draft = torch.empty((B, K), **f32) if p_draft is None else _dev(p_draft, "p_draft", torch.float32, (B, K), dev)
+        q_draft = torch.empty((B, K), **f32) if q_draft is None else _dev(q_draft, "q_draft", torch.float32, (B, K), dev)
+        residual_mass = torch.empty((B,), **f32) if residual_mass is None else _dev(residual_mass, "residual_mass", torch.float32, (B,), dev)
+    err_flags = torch.zeros((1,), **i32) if err_flags is None else _dev(err_flags, "err_flags", torch.int32, (1,), dev)
+    nbytes = int(lib.sv_chain_workspace_bytes(B, K, V, code))
+    ws = workspace(dev, nbytes, stream) if workspace_tensor is None else workspace_tensor
+    st = lib.sv_verify_chain(
+        _ptr(target), _ptr(draft) if K > 0 else None, code, _ptr(draft_tokens) if K > 0 else None,
+        _ptr(temperature), _ptr(uniforms), B, K, V,
+        _ptr(accept_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft), _ptr(residual_mass), _ptr(err_flags),
+        _ptr(ws), ws.numel(), _stream_handle(dev, stream))
+    _check(st, "sv_verify_chain")
+    out = {"accept_len": accept_len, "out_tokens": out_tokens, "err_flags": err_flags}
+    if want_probs:
+        out.update(p_draft=p_draft, q_draft=q_draft, residual_mass=residual_mass)
+    return out
+
+
+def sv_verify_tree_greedy(target: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor, *,
+                          accept_len=None, path_nodes=None, next_token=None, err_flags=None,
+                          workspace_tensor=None, stream=None) -> dict:
+    """Greedy tree verification (``sv_verify_tree_greedy``)."""
+    lib = _load()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, N+1, V]")
+    B, N1, V = target.shape
+    N = N1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _dev(target, "target")
+    _dev(node_tokens, "node_tokens", torch.int32, (B, N), dev)
+    _dev(parents, "parents", torch.int32, (N,), dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    accept_len = torch.empty((B,), **i32) if accept_len is None else _dev(accept_len, "accept_len", torch.int32, (B,), dev)
+    path_nodes = torch.empty((B, N), **i32) if path_nodes is None else _dev(path_nodes, "path_nodes", torch.int32, (B, N), dev)
+    next_token = torch.empty((B,), **i32) if next_token is None else _dev(next_token, "next_token", torch.int32, (B,), dev)
+    err_flags = torch.zeros((1,), **i32) if err_flags is None else _dev(err_flags, "err_flags", torch.int32, (1,), dev)
+    nbytes = int(lib.sv_tree_workspace_bytes(B, N, V, code))
+    ws = workspace(dev, nbytes, stream) if workspace_tensor is None else workspace_tensor
+    st = lib.sv_verify_tree_greedy(
+        _ptr(target), code, _ptr(node_tokens), _ptr(parents), B, N, V,
+        _ptr(accept_len), _ptr(path_nodes), _ptr(next_token), _ptr(err_flags),
+        _ptr(ws), ws.numel(), _stream_handle(dev, stream))
+    _check(st, "sv_verify_tree_greedy")
+    return {"accept_len": accept_len, "path_nodes": path_nodes, "next_token": next_token, "err_flags": err_flags}
+
+
+def sv_build_tree_mask(parents: torch.Tensor, *, mask=None, err_flags=None, stream=None) -> dict:
+    """Tree ancestor mask (``sv_build_tree_mask``): uint8 ``[N, N]``."""
+    lib = _load()
+    _dev(parents, "parents", torch.int32)
+    if parents.dim() != 1:
+        raise ValueError("parents must be 1-D")
+    N = parents.shape[0]
+    dev = parents.device
+    mask = torch.empty((N, N), dtype=torch.uint8, device=dev) if mask is None else _dev(mask, "mask", torch.uint8, (N, N), dev)
+    err_flags = torch.zeros((1,), dtype=torch.int32, device=dev) if err_flags is None else _dev(err_flags, "err_flags", torch.int32, (1,), dev)
+    st = lib.sv_build_tree_mask(_ptr(parents), N, _ptr(mask), _ptr(err_flags), _stream_handle(dev, stream))
+    _check(st, "sv_build_tree_mask")
+    return {"mask": mask, "err_flags": err_flags}
+
+
+class PreparedChainCall:
+    """``sv_verify_chain`` with every argument checked and marshalled once.
+
+    Calling the object only enqueues the kernels (one ctypes call), so a
+    launch loop is not limited by Python-side argument checking. The tensors
+    passed at construction are kept alive and reused by every call.
+    """
+
+    def __init__(self, target, draft, draft_tokens, temperature, uniforms, *, stream=None, want_probs=True):
+        B, K1, V = target.shape
+        K = K1 - 1
+        dev = target.device
+        self.out = {
+            "accept_len": torch.empty((B,), dtype=torch.int32, device=dev),
+            "out_tokens": torch.empty((B, K1), dtype=torch.int32, device=dev),
+            "err_flags": torch.zeros((1,), dtype=torch.int32, device=dev),
+        }
+        if want_probs:
+            self.out["p_draft"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+            self.out["q_draft"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+            self.out["residual_mass"] = torch.empty((B,), dtype=torch.float32, device=dev)
+        # one checked call through the regular path validates every argument
+        sv_verify_chain(target, draft, draft_tokens, temperature, uniforms, stream=stream,
+                        want_probs=want_probs, **self.out)
+        lib = _load()
+        code = _dtype_code(target)
+        self._ws = workspace(dev, int(lib.sv_chain_workspace_bytes(B, K, V, code)), stream)
+        self._keep = (target, draft, draft_tokens, temperature, uniforms)
+        o = self.out
+        self._fn = lib.sv_verify_chain
+        self._args = (
+            _ptr(target), _ptr(draft) if K > 0 else None, code, _ptr(draft_tokens) if K > 0 else None,
+            _ptr(temperature), _ptr(uniforms), B, K, V,
+            _ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o.get("p_draft")), _ptr(o.get("q_draft")),
+            _ptr(o.get("residual_mass")), _ptr(o["err_flags"]), _ptr(self._ws), self._ws.numel(),
+            _stream_handle(dev, stream))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SV_OK:
+            _check(st, "sv_verify_chain")
+        return self.out

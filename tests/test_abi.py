@@ -1,0 +1,105 @@
+"""The C ABI on the host: the library loads, exports what the header declares,
+and rejects bad arguments synchronously (no GPU needed: these paths never
+reach the HIP runtime)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from rejection_sampling_verification_sv_amd import specverify as b
+    if not os.path.exists(b.LIB_PATH):
+        from rejection_sampling_verification_sv_amd import build
+        build.build()
+    return b.library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sv_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared()
+    for n in ("sv_verify_chain", "sv_verify_tree_greedy", "sv_build_tree_mask"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(["SV_OK", "SV_ERR_INVALID_ARGUMENT", "SV_ERR_UNSUPPORTED", "SV_ERR_WORKSPACE",
+                                 "SV_ERR_HIP"]):
+        assert lib.sv_status_string(code).decode() == name
+    assert lib.sv_status_string(99).decode() == "SV_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(lib):
+    assert lib.sv_chain_workspace_bytes(64, 5, 128256, 1) > 0
+    assert lib.sv_chain_workspace_bytes(64, 64, 128256, 1) == 0   # K > 63
+    assert lib.sv_chain_workspace_bytes(64, 5, 0, 1) == 0         # V < 1
+    assert lib.sv_chain_workspace_bytes(-1, 5, 10, 1) == 0
+    assert lib.sv_chain_workspace_bytes(4, 4, 10, 7) == 0         # bad dtype
+    assert lib.sv_tree_workspace_bytes(32, 64, 128256, 1) > 0
+    assert lib.sv_tree_workspace_bytes(32, 1025, 128256, 1) == 0
+    assert lib.sv_tree_workspace_bytes(32, 0, 128256, 1) == 0
+    # grows with the batch
+    assert lib.sv_chain_workspace_bytes(128, 5, 128256, 1) > lib.sv_chain_workspace_bytes(64, 5, 128256, 1)
+
+
+FAKE = 0x10000  # a non-NULL address that is never dereferenced on these paths
+
+
+def _chain(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dt=1, x=FAKE, T=None, u=FAKE, B=4, K=4, V=100, acc=FAKE, out=FAKE,
+             p=None, q=None, s=None, err=None, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.sv_verify_chain(a["t"], a["d"], a["dt"], a["x"], a["T"], a["u"], a["B"], a["K"], a["V"],
+                               a["acc"], a["out"], a["p"], a["q"], a["s"], a["err"], a["ws"], a["wsb"],
+                               a["stream"])
+
+
+def test_chain_argument_errors(lib):
+    from rejection_sampling_verification_sv_amd import specverify as b
+    b._load()
+    INV, WS = 1, 3
+    assert _chain(lib, t=None) == INV
+    assert _chain(lib, u=None) == INV
+    assert _chain(lib, acc=None) == INV
+    assert _chain(lib, out=None) == INV
+    assert _chain(lib, d=None) == INV            # K > 0 needs draft logits
+    assert _chain(lib, x=None) == INV
+    assert _chain(lib, K=64) == INV
+    assert _chain(lib, V=0) == INV
+    assert _chain(lib, B=-1) == INV
+    assert _chain(lib, dt=5) == INV
+    assert _chain(lib, t=FAKE + 1) == INV        # misaligned bf16 logits
+    assert _chain(lib, ws=None) == WS
+    assert _chain(lib, wsb=16) == WS
+    assert _chain(lib, B=0, t=None) == 0          # empty batch: nothing to do
+
+
+def test_tree_and_mask_argument_errors(lib):
+    INV, WS = 1, 3
+    f = lib.sv_verify_tree_greedy
+    args = [FAKE, 1, FAKE, FAKE, 4, 8, 100, FAKE, FAKE, FAKE, None, FAKE, 1 << 20, None]
+    assert f(*args[:2], None, *args[3:]) == INV
+    bad_n = list(args)
+    bad_n[5] = 1025
+    assert f(*bad_n) == INV
+    small = list(args)
+    small[12] = 8
+    assert f(*small) == WS
+    assert lib.sv_build_tree_mask(None, 4, FAKE, None, None) == INV
+    assert lib.sv_build_tree_mask(FAKE, 0, FAKE, None, None) == INV
+    assert lib.sv_build_tree_mask(FAKE, 1025, FAKE, None, None) == INV
