@@ -27,8 +27,21 @@ int32_t stats_segments(int32_t V, sv_dtype d) {
 
 struct ChainLayout {
   int32_t nseg, ntiles, tiles_per_block, nblk_b;
-  size_t off_part_m, off_part_s, off_cnt_a, off_cnt_b, off_plan, off_tiles, total;
+  int32_t fl_blocks, fl_kmax;  // flattened statistics layout (when rows allow it)
+  int64_t fl_nvec, fl_per;
+  size_t off_part_m, off_part_s, off_plan, off_cnt, off_tiles, total;
 };
+
+// Flattened layout parameters for rows of whole 16-byte vectors.
+void flat_layout(int64_t rows, int64_t nvec, int32_t* blocks, int32_t* kmax, int64_t* per) {
+  const int64_t total = rows * nvec;
+  int64_t g = ceil_div(total, sv::kFlatMinVecsPerBlock);
+  if (g > sv::kFlatMaxBlocks) g = sv::kFlatMaxBlocks;
+  if (g < 1) g = 1;
+  *per = ceil_div(total, g);
+  *blocks = static_cast<int32_t>(ceil_div(total, *per));
+  *kmax = static_cast<int32_t>((*per + nvec - 2) / nvec + 1);
+}
 
 ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   ChainLayout L{};
@@ -37,18 +50,23 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
   L.tiles_per_block = sv::kSampleTilesPerBlock;
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
-  const int64_t parts = static_cast<int64_t>(B) * R * L.nseg;
+  int64_t parts = static_cast<int64_t>(B) * R * L.nseg;
+  const int64_t row_bytes = static_cast<int64_t>(V) * dtype_bytes(d);
+  if (row_bytes % 16 == 0 && B > 0) {
+    L.fl_nvec = row_bytes / 16;
+    flat_layout(static_cast<int64_t>(B) * R, L.fl_nvec, &L.fl_blocks, &L.fl_kmax, &L.fl_per);
+    const int64_t fl_parts = static_cast<int64_t>(L.fl_blocks) * L.fl_kmax;
+    if (fl_parts > parts) parts = fl_parts;
+  }
   size_t off = 0;
   L.off_part_m = off;
-  off = align_up(off + sizeof(uint64_t) * parts);
+  off = align_up(off + sizeof(float) * parts);
   L.off_part_s = off;
-  off = align_up(off + sizeof(uint64_t) * parts);
-  L.off_cnt_a = off;
-  off = align_up(off + sizeof(uint32_t) * B);
-  L.off_cnt_b = off;
-  off = align_up(off + sizeof(uint32_t) * B);
+  off = align_up(off + sizeof(double) * parts);
   L.off_plan = off;
   off = align_up(off + sizeof(sv::SeqPlan) * B);
+  L.off_cnt = off;
+  off = align_up(off + sizeof(uint32_t) * B);
   L.off_tiles = off;
   off = align_up(off + sizeof(uint64_t) * static_cast<int64_t>(B) * L.ntiles);
   L.total = off;
@@ -138,6 +156,12 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.V = V;
   p.nseg = L.nseg;
   p.seg_vecs = sv::kStatsSegVecs;
+  // The flattened statistics layout needs every row on a 16-byte boundary.
+  const bool flat = L.fl_blocks > 0 && aligned_to(target_logits, 16) && (K == 0 || aligned_to(draft_logits, 16));
+  p.fl_blocks = flat ? L.fl_blocks : 0;
+  p.fl_kmax = L.fl_kmax;
+  p.fl_nvec = L.fl_nvec;
+  p.fl_per = L.fl_per;
   p.ntiles = L.ntiles;
   p.tiles_per_block = L.tiles_per_block;
   p.nblk_b = L.nblk_b;
@@ -147,11 +171,10 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.q_draft = q_draft;
   p.residual_mass = residual_mass;
   p.err_flags = err_flags;
-  p.part_m = reinterpret_cast<uint64_t*>(ws + L.off_part_m);
-  p.part_s = reinterpret_cast<uint64_t*>(ws + L.off_part_s);
-  p.cnt_a = reinterpret_cast<uint32_t*>(ws + L.off_cnt_a);
-  p.cnt_b = reinterpret_cast<uint32_t*>(ws + L.off_cnt_b);
+  p.part_m = reinterpret_cast<float*>(ws + L.off_part_m);
+  p.part_s = reinterpret_cast<double*>(ws + L.off_part_s);
   p.plan = reinterpret_cast<sv::SeqPlan*>(ws + L.off_plan);
+  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
   p.tile_sum = reinterpret_cast<uint64_t*>(ws + L.off_tiles);
   return from_hip(sv::launch_chain(p, dtype, stream));
 }

@@ -1,28 +1,36 @@
 // Chain verification kernels (modified rejection sampling over K proposals).
 //
-// Pass 1 — chain_stats_kernel, one workgroup per (sequence, row, segment):
-//   streams a segment of one logit row (the K+1 target rows and K draft rows
-//   of each sequence) with coalesced 16-byte loads and keeps, per thread, the
-//   running maximum m of the logits and the sum of 2^(l*c - m*c), c = log2(e)/T
-//   (one-pass max/sum; the sum is rescaled only when a batch raises the max).
-//   The block combines its threads in fp64 and publishes (max*c, sum). The
-//   last block to finish a sequence combines all segments of its 2K+1 rows
-//   and makes the decision: p_k(x_k), q_k(x_k) in fp64, alpha_k = min(1, p/q),
-//   accept while u_k < alpha_k, j = first rejection (wave ballot).
-//   [Topologies] "Speculative Decoding & Draft Model Topologies", section 2
-//   (acceptance-probability equation, timeline figure steps 2-3);
-//   [In Production] "Speculative Decoding in Production", section 2.
+// Pass 1 — statistics. Streams every logit row of the call once (the K+1
+// target rows and K draft rows of each sequence) with coalesced 16-byte loads.
+// Each thread keeps the running maximum m of its logits and the sum of
+// 2^(x*c - m*c), c = log2(e)/T (one pass: a batch of 32 values is reduced to
+// its maximum first, the sum is rescaled once per batch, then the batch's
+// exponentials are added). Each block combines its threads in fp64 and stores
+// one (reference, sum) pair per row piece. Two layouts:
+//   chain_stats_flat_kernel: rows on 16-byte boundaries (the usual case); the
+//     flattened vector space of all rows is cut into equal ranges, one per
+//     block, so every block streams the same number of bytes;
+//   chain_stats_rows_kernel: any row alignment; one block per (row, segment).
 //
-// Pass 2 — chain_sample_kernel, one workgroup per (sequence, tile group):
-//   re-reads row j (target, and draft when j < K), forms the weights
-//   max(0, p_j - q_j) (or p_K for the bonus draw) tile by tile, and publishes
-//   each tile's total. The last block of a sequence scans the tile totals,
-//   finds the tile holding u_K * total, rescans that tile with a block-wide
-//   prefix sum and picks the first token whose cumulative weight exceeds it.
-//   [Topologies] section 2 (residual equation, step 4); [At Scale]
-//   "Speculative Decoding at Scale", section 1; [Draft-and-Verify]
-//   "Speculative Decoding for LLM Inference", "The draft-and-verify loop"
-//   (the bonus token when every proposal is kept).
+// Pass 2 — chain_sample_kernel, one workgroup per (sequence, tile pair):
+//   1. decision: combines the pieces of the sequence's 2K+1 rows into their
+//      log-normalisers L = log2 sum_v 2^(x_v c) (fp64), forms p_k(x_k) and
+//      q_k(x_k) in fp64, alpha_k = min(1, p/q), accepts while u_k < alpha_k
+//      and takes j = the first rejection with a wave ballot. Every block of
+//      the sequence makes the same decision; the first one writes it out.
+//      [Topologies] "Speculative Decoding & Draft Model Topologies", section 2
+//      (acceptance-probability equation, timeline figure steps 2-3);
+//      [In Production] "Speculative Decoding in Production", section 2.
+//   2. re-reads its tiles of row j (target, and draft when j < K), forms the
+//      weights max(0, p_j - q_j) (or p_K for the bonus draw) and publishes
+//      each tile's total;
+//   3. the last block of the sequence scans the tile totals, finds the tile
+//      holding u_K * total, rescans it with a block-wide prefix sum and picks
+//      the first token whose cumulative weight exceeds it.
+//      [Topologies] section 2 (residual equation, step 4); [At Scale]
+//      "Speculative Decoding at Scale", section 1; [Draft-and-Verify]
+//      "Speculative Decoding for LLM Inference", "The draft-and-verify loop"
+//      (the bonus token when every proposal is kept).
 #include <math.h>
 
 #include "sv_device.h"
@@ -91,22 +99,22 @@ __device__ __forceinline__ void running_add(Running& st, const float (&x)[N], Sc
   float bm = x[0];
 #pragma unroll
   for (int i = 1; i < N; ++i) bm = fmaxf(bm, x[i]);
-  if (bm > st.mx) {
-    st.s = (st.mx == -INFINITY) ? 0.0f : st.s * fast_exp2(st.mx * c.hi - bm * c.hi);
-    st.mx = bm;
-  }
-  const float neg_m = neg_reference(st.mx, c);
-  // pairwise within each group of 8, then sequential over the groups
-  float acc = 0.0f;
+  // Rescale the running sum to the new maximum (branch-free: a factor of 1
+  // when the maximum did not move, 0 while nothing finite had been seen).
+  const float m_new = fmaxf(st.mx, bm);
+  const float scale = (st.mx == -INFINITY) ? 0.0f : fast_exp2(st.mx * c.hi - m_new * c.hi);
+  st.mx = m_new;
+  const float neg_m = neg_reference(m_new, c);
+  // four partial sums, pairwise inside each group of 8
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int g = 0; g < N; g += 8) {
     float e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) e[i] = (g + i < N) ? fast_exp2(scaled_arg(x[g + i], c, neg_m)) : 0.0f;
-    const float e01 = e[0] + e[1], e23 = e[2] + e[3], e45 = e[4] + e[5], e67 = e[6] + e[7];
-    acc += (e01 + e23) + (e45 + e67);
+    acc[(g / 8) & 3] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
   }
-  st.s += acc;
+  st.s = st.s * scale + ((acc[0] + acc[1]) + (acc[2] + acc[3]));
 }
 
 __device__ __forceinline__ void running_add1(Running& st, float x, Scale c) {
@@ -122,114 +130,74 @@ __device__ __forceinline__ void split(double v, float& hi, float& lo) {
   lo = static_cast<float>(v - static_cast<double>(hi));
 }
 
-// ---------------------------------------------------------------- decision
+// Block-wide combine of the threads' running states into (reference, sum):
+// the largest fl(mx*c_hi), and the fp64 sum of each thread's sum rescaled to it.
+__device__ __forceinline__ void block_combine(const Running& st, Scale c, float* s_redf, double* s_redd, float* MC,
+                                              double* S) {
+  const float mc = (st.mx == -INFINITY) ? -INFINITY : st.mx * c.hi;
+  *MC = block_max(mc, s_redf);
+  double sd = 0.0;
+  if (mc != -INFINITY) sd = static_cast<double>(st.s * fast_exp2(mc - *MC));
+  *S = block_sum(sd, s_redd);
+}
+
+// 16 bytes of -inf logits (a padding vector contributes exactly 0).
+template <class T>
+__device__ __forceinline__ uint4 neg_inf_vec();
+template <>
+__device__ __forceinline__ uint4 neg_inf_vec<BF16>() {
+  return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+}
+template <>
+__device__ __forceinline__ uint4 neg_inf_vec<F32>() {
+  return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+}
 
 template <class T>
-__device__ void chain_decide(const ChainParams& P, int b, Scale c) {
-  __shared__ double s_L[2 * SV_MAX_K + 1];
-  __shared__ uint32_t s_err;
-  __shared__ int s_j;
-  const int K = P.K;
-  const int R = 2 * K + 1;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    s_err = 0u;
-    s_j = K;
-  }
-  __syncthreads();
+__device__ __forceinline__ void add_batch(Running& st, const uint4 (&raw)[kStatsUnroll], Scale c) {
+  float x[kStatsUnroll * T::kVec];
+#pragma unroll
+  for (int u = 0; u < kStatsUnroll; ++u) unpack<T>(raw[u], &x[u * T::kVec]);
+  running_add(st, x, c);
+}
 
-  // Log-normaliser of every row at scale c: L = M + log2(sum_s S_s 2^(M_s - M)).
-  for (int r = tid; r < R; r += kThreads) {
-    const int64_t base = (static_cast<int64_t>(b) * R + r) * P.nseg;
-    uint32_t err = 0u;
-    float M = -INFINITY;
-    for (int s = 0; s < P.nseg; ++s) M = fmaxf(M, untag_float(await_slot(&P.part_m[base + s], &err)));
-    double Z = 0.0;
-    for (int s = 0; s < P.nseg; ++s) {
-      const float ms = untag_float(await_slot(&P.part_m[base + s], &err));
-      const double ss = untag_nonneg_double(await_slot(&P.part_s[base + s], &err));
-      if (ms != -INFINITY) Z += ss * exp2(static_cast<double>(ms) - static_cast<double>(M));
-    }
-    s_L[r] = static_cast<double>(M) + log2(Z);
-    if (!(Z > 0.0) || !isfinite(Z) || !isfinite(M)) err |= SV_ERRF_NONFINITE;
-    if (err != 0u) atomicOr(&s_err, err);
+// One thread's share of the vectors [p0, p1) of a row: full batches of
+// kStatsUnroll vectors per thread without any masking, then one ragged batch
+// whose missing vectors are replaced by -inf.
+template <class T>
+__device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, int64_t p1, Scale c, Running& st) {
+  constexpr int U = kStatsUnroll;
+  constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
+  const int64_t nfull = (p1 - p0) / STEP;
+  const uint4* ptr = body + p0 + threadIdx.x;
+#pragma unroll 1
+  for (int64_t i = 0; i < nfull; ++i, ptr += STEP) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) raw[u] = ptr[u * kThreads];
+    add_batch<T>(st, raw, c);
   }
-  __syncthreads();
-
-  const double c64 = static_cast<double>(c.hi) + static_cast<double>(c.lo);
-  if (tid < kWave) {
-    const int k = tid;
-    uint32_t err = 0u;
-    bool reject = false;
-    const float Tv = temperature_of(P.temperature, b);
-    if (!(Tv > 0.0f) || !isfinite(Tv)) err |= SV_ERRF_TEMPERATURE;
-    if (k < K) {
-      const int x = P.tokens[static_cast<int64_t>(b) * K + k];
-      float pf = NAN, qf = NAN;
-      if (x < 0 || x >= P.V) {
-        err |= SV_ERRF_TOKEN;
-      } else {
-        const double lt = load_elem<T>(chain_row<T>(P, b, k), x);
-        const double ld = load_elem<T>(chain_row<T>(P, b, K + 1 + k), x);
-        const double p = exp2(lt * c64 - s_L[k]);
-        const double q = exp2(ld * c64 - s_L[K + 1 + k]);
-        const double alpha = (p > 0.0) ? ((q > 0.0) ? fmin(1.0, p / q) : 1.0) : 0.0;
-        const double u = static_cast<double>(P.uniforms[static_cast<int64_t>(b) * (K + 1) + k]);
-        reject = !(u < alpha);
-        pf = static_cast<float>(p);
-        qf = static_cast<float>(q);
-      }
-      if (P.p_draft != nullptr) P.p_draft[static_cast<int64_t>(b) * K + k] = pf;
-      if (P.q_draft != nullptr) P.q_draft[static_cast<int64_t>(b) * K + k] = qf;
+  const int64_t rest = (p1 - p0) - nfull * STEP;  // vectors in the ragged batch
+  if (rest > 0) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = static_cast<int64_t>(u) * kThreads + threadIdx.x;
+      raw[u] = (k < rest) ? ptr[u * kThreads] : neg_inf_vec<T>();
     }
-    if (err != 0u) atomicOr(&s_err, err);
-    const uint64_t rej = __ballot(reject);
-    if (tid == 0) s_j = (rej != 0ull) ? (__ffsll(static_cast<unsigned long long>(rej)) - 1) : K;
-  }
-  __syncthreads();
-
-  const bool bad = s_err != 0u;
-  const int j = s_j;
-  for (int i = tid; i <= K; i += kThreads) {
-    int32_t v;
-    if (bad || i > j) {
-      v = -1;
-    } else if (i < j) {
-      v = P.tokens[static_cast<int64_t>(b) * K + i];
-    } else {
-      continue;  // position j: written by the sampling pass
-    }
-    P.out_tokens[static_cast<int64_t>(b) * (K + 1) + i] = v;
-  }
-  if (tid == 0) {
-    P.accept_len[b] = bad ? -1 : j;
-    SeqPlan pl;
-    pl.j = bad ? -1 : j;
-    pl.c_hi = c.hi;
-    pl.c_lo = c.lo;
-    split(s_L[j], pl.lt_hi, pl.lt_lo);
-    if (j < K) {
-      split(s_L[K + 1 + j] - s_L[j], pl.d_hi, pl.d_lo);
-    } else {
-      pl.d_hi = 0.0f;
-      pl.d_lo = 0.0f;
-    }
-    pl.pad = 0.0f;
-    P.plan[b] = pl;
-    if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
-    raise_error(P.err_flags, s_err);
+    add_batch<T>(st, raw, c);
   }
 }
+
 
 }  // namespace
 
 // ---------------------------------------------------------------- pass 1
 
 template <class T>
-__global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainParams P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_rows_kernel(ChainParams P) {
   __shared__ float s_redf[kWaves];
   __shared__ double s_redd[kWaves];
-  __shared__ int s_flag;
   constexpr int VEC = T::kVec;
   constexpr int U = kStatsUnroll;
 
@@ -255,54 +223,247 @@ __global__ __launch_bounds__(kThreads) void chain_stats_kernel(ChainParams P) {
 
   Running st{-INFINITY, 0.0f};
   if (seg == 0 && tid < head) running_add1(st, load_elem<T>(row, tid), c);
-
   for (int64_t base = v0 + tid; base < v1; base += static_cast<int64_t>(kThreads) * U) {
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t vi = base + static_cast<int64_t>(u) * kThreads;
-      raw[u] = (vi < v1) ? body[vi] : make_uint4(0u, 0u, 0u, 0u);
+      raw[u] = (vi < v1) ? body[vi] : neg_inf_vec<T>();
     }
-    float x[U * VEC];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      unpack<T>(raw[u], &x[u * VEC]);
-      const int64_t vi = base + static_cast<int64_t>(u) * kThreads;
-      if (vi >= v1) {
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) x[u * VEC + i] = -INFINITY;
-      }
-    }
-    running_add(st, x, c);
+    add_batch<T>(st, raw, c);
   }
-
   if (seg == P.nseg - 1 && tid < tail) running_add1(st, load_elem<T>(row, head + nvec * VEC + tid), c);
 
-  // Block combine: max of the references fl(mx*c_hi), then the fp64 sum of
-  // the rescaled sums.
-  const float mc = (st.mx == -INFINITY) ? -INFINITY : st.mx * c.hi;
-  const float MC = block_max(mc, s_redf);
-  double sd = 0.0;
-  if (mc != -INFINITY) sd = static_cast<double>(st.s) * exp2(static_cast<double>(mc) - static_cast<double>(MC));
-  const double S = block_sum(sd, s_redd);
+  float MC;
+  double S;
+  block_combine(st, c, s_redf, s_redd, &MC, &S);
   if (tid == 0) {
-    publish(&P.part_m[blk], tag_float(MC));
-    publish(&P.part_s[blk], tag_nonneg_double(S));
+    P.part_m[blk] = MC;
+    P.part_s[blk] = S;
   }
+}
 
-  if (!arrive_and_check_last(&P.cnt_a[b], static_cast<uint32_t>(R) * P.nseg, &s_flag)) return;
-  chain_decide<T>(P, b, c);
-  // Leave the workspace as it was found (all zero): the partials are consumed.
-  __syncthreads();
-  const int64_t base = static_cast<int64_t>(b) * R * P.nseg;
-  for (int64_t i = tid; i < static_cast<int64_t>(R) * P.nseg; i += kThreads) {
-    clear_slot(&P.part_m[base + i]);
-    clear_slot(&P.part_s[base + i]);
+// The flattened layout: block g streams the vectors [g*per, (g+1)*per) of the
+// concatenation of all rows, as one piece per row it touches.
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_flat_kernel(ChainParams P) {
+  __shared__ float s_redf[kWaves];
+  __shared__ double s_redd[kWaves];
+  const int R = 2 * P.K + 1;
+  const int64_t nvec = P.fl_nvec;
+  const int64_t per = P.fl_per;
+  const int64_t total = static_cast<int64_t>(P.B) * R * nvec;
+  const int g = blockIdx.x;
+  const int64_t lo = static_cast<int64_t>(g) * per;
+  const int64_t hi = min(total, lo + per);
+  const int64_t row_lo = lo / nvec;
+  const int64_t row_hi = (hi - 1) / nvec;
+
+  for (int64_t row = row_lo; row <= row_hi; ++row) {
+    const int b = static_cast<int>(row / R);
+    const int r = static_cast<int>(row % R);
+    const int64_t p0 = max(lo, row * nvec) - row * nvec;
+    const int64_t p1 = min(hi, (row + 1) * nvec) - row * nvec;
+    const uint4* body = static_cast<const uint4*>(chain_row<T>(P, b, r));
+    const Scale c = exponent_scale(temperature_of(P.temperature, b));
+    Running st{-INFINITY, 0.0f};
+    flat_piece_stats<T>(body, p0, p1, c, st);
+    float MC;
+    double S;
+    block_combine(st, c, s_redf, s_redd, &MC, &S);
+    if (threadIdx.x == 0) {
+      const int64_t slot = static_cast<int64_t>(g) * P.fl_kmax + (row - row_lo);
+      P.part_m[slot] = MC;
+      P.part_s[slot] = S;
+    }
   }
-  reset_counter(&P.cnt_a[b]);
 }
 
 // ---------------------------------------------------------------- pass 2
+
+namespace {
+
+// a / b for non-negative 64-bit values, in 32-bit arithmetic when both fit
+// (a hardware-friendly path for every realistic size).
+__device__ __forceinline__ int64_t div_nonneg(int64_t a, int64_t b) {
+  if (((a | b) >> 32) == 0) return static_cast<int64_t>(static_cast<uint32_t>(a) / static_cast<uint32_t>(b));
+  return a / b;
+}
+
+// Slot index of piece `p` of global row `grow`, or -1 past its last piece.
+__device__ __forceinline__ int64_t piece_slot(const ChainParams& P, int64_t grow, int p) {
+  if (P.fl_blocks > 0) {
+    const int64_t nvec = P.fl_nvec, per = P.fl_per;
+    const int64_t gg = div_nonneg(grow * nvec, per) + p;
+    if (gg > div_nonneg((grow + 1) * nvec - 1, per)) return -1;
+    return gg * P.fl_kmax + (grow - div_nonneg(gg * per, nvec));
+  }
+  return p < P.nseg ? grow * P.nseg + p : -1;
+}
+
+// Largest number of statistics pieces of any row (host and device agree).
+__device__ __forceinline__ int max_pieces(const ChainParams& P) {
+  if (P.fl_blocks > 0) return static_cast<int>(div_nonneg(P.fl_nvec + P.fl_per - 2, P.fl_per)) + 1;
+  return P.nseg;
+}
+
+}  // namespace
+
+// The decision, one block per sequence: the rows' log-normalisers (one wave
+// per row, rows spread over the waves), the drafted tokens' logits gathered
+// by the last wave meanwhile, then p_k(x_k), q_k(x_k) in fp64, alpha_k =
+// min(1, p/q), acceptance while u_k < alpha_k and j = the first rejection
+// (wave ballot). Writes accept_len, the accepted prefix of out_tokens,
+// p_draft / q_draft, the error bits, and the sampling plan.
+template <class T>
+__global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
+  __shared__ double s_L[2 * SV_MAX_K + 1];
+  __shared__ float s_lt[kWave], s_ld[kWave], s_u[kWave];
+  __shared__ int s_x[kWave];
+  __shared__ uint32_t s_err;
+  __shared__ int s_j;
+  const int b = blockIdx.x;
+  const int K = P.K;
+  const int R = 2 * K + 1;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const Scale c = exponent_scale(temperature_of(P.temperature, b));
+  if (tid == 0) {
+    s_err = 0u;
+    s_j = K;
+  }
+  __syncthreads();
+
+  uint32_t err = 0u;
+  if (wave_id() == kWaves - 1) {  // gathers
+    const int k = lane;
+    if (k < K) {
+      const int x = P.tokens[static_cast<int64_t>(b) * K + k];
+      s_x[k] = x;
+      s_u[k] = P.uniforms[static_cast<int64_t>(b) * (K + 1) + k];
+      if (x < 0 || x >= P.V) {
+        err |= SV_ERRF_TOKEN;
+      } else {
+        s_lt[k] = load_elem<T>(chain_row<T>(P, b, k), x);
+        s_ld[k] = load_elem<T>(chain_row<T>(P, b, K + 1 + k), x);
+      }
+    }
+  }
+  // Rows' log-normalisers: a group of G lanes per row (G a power of two that
+  // covers the row's pieces, up to a wave), all pieces loaded in one round.
+  // Group max of the references M, each lane rescales its sum by 2^(m - M) in
+  // fp64, group sum Z, L = M + log2 Z. The consumed pieces are set to zero.
+  {
+    const int pmax = max_pieces(P);
+    int G = 1;
+    while (G < pmax && G < kWave) G <<= 1;
+    const int rows_per_round = kThreads / G;
+    for (int r0 = 0; r0 < R; r0 += rows_per_round) {
+      const int r = r0 + tid / G;
+      const int gl = tid % G;
+      const bool row_ok = r < R;
+      const int64_t grow = static_cast<int64_t>(b) * R + r;
+      float mf = -INFINITY;  // reference of the folded sum zf (pieces beyond four per lane)
+      double zf = 0.0;
+      float ms[4];
+      double ss[4];
+      int64_t sl[4];
+      int n = 0;
+      // pieces gl, gl+G, ... of this row (one round when G >= pieces)
+      for (int p = gl; row_ok && p < pmax; p += G) {
+        const int64_t s = piece_slot(P, grow, p);
+        if (s < 0) break;
+        if (n < 4) {
+          sl[n] = s;
+          ms[n] = P.part_m[s];
+          ss[n] = P.part_s[s];
+          ++n;
+        } else {
+          const float mm = P.part_m[s];
+          const double sv = P.part_s[s];
+          if (mm != -INFINITY) {
+            if (mm > mf) {
+              zf = (mf == -INFINITY ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(mm))) + sv;
+              mf = mm;
+            } else {
+              zf += sv * exp2(static_cast<double>(mm) - static_cast<double>(mf));
+            }
+          }
+          P.part_m[s] = 0.0f;
+          P.part_s[s] = 0.0;
+        }
+      }
+      float M = mf;
+      for (int i = 0; i < n; ++i) M = fmaxf(M, ms[i]);
+      for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+      double zl = (mf == -INFINITY) ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(M));
+      for (int i = 0; i < n; ++i) {
+        if (ms[i] != -INFINITY) zl += ss[i] * exp2(static_cast<double>(ms[i]) - static_cast<double>(M));
+        P.part_m[sl[i]] = 0.0f;  // consumed: leave the workspace zero
+        P.part_s[sl[i]] = 0.0;
+      }
+      for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
+      if (row_ok && gl == 0) {
+        if (!(zl > 0.0) || !isfinite(zl) || !isfinite(M)) err |= SV_ERRF_NONFINITE;
+        s_L[r] = static_cast<double>(M) + log2(zl);
+      }
+    }
+  }
+  if (err != 0u) atomicOr(&s_err, err);
+  __syncthreads();
+
+  const double c64 = static_cast<double>(c.hi) + static_cast<double>(c.lo);
+  if (tid < kWave) {
+    const int k = tid;
+    uint32_t e = 0u;
+    bool reject = false;
+    const float Tv = temperature_of(P.temperature, b);
+    if (!(Tv > 0.0f) || !isfinite(Tv)) e |= SV_ERRF_TEMPERATURE;
+    if (k < K) {
+      const int x = s_x[k];
+      float pf = NAN, qf = NAN;
+      if (x >= 0 && x < P.V) {
+        const double p = exp2(static_cast<double>(s_lt[k]) * c64 - s_L[k]);
+        const double q = exp2(static_cast<double>(s_ld[k]) * c64 - s_L[K + 1 + k]);
+        const double alpha = (p > 0.0) ? ((q > 0.0) ? fmin(1.0, p / q) : 1.0) : 0.0;
+        reject = !(static_cast<double>(s_u[k]) < alpha);
+        pf = static_cast<float>(p);
+        qf = static_cast<float>(q);
+      }
+      if (P.p_draft != nullptr) P.p_draft[static_cast<int64_t>(b) * K + k] = pf;
+      if (P.q_draft != nullptr) P.q_draft[static_cast<int64_t>(b) * K + k] = qf;
+    }
+    if (e != 0u) atomicOr(&s_err, e);
+    const uint64_t rej = __ballot(reject);
+    if (tid == 0) s_j = (rej != 0ull) ? (__ffsll(static_cast<unsigned long long>(rej)) - 1) : K;
+  }
+  __syncthreads();
+
+  const bool bad = s_err != 0u;
+  const int j = s_j;
+  for (int i = tid; i <= K; i += kThreads) {
+    if (i == j && !bad) continue;  // the drawn token: written by the sampling pass
+    P.out_tokens[static_cast<int64_t>(b) * (K + 1) + i] = (bad || i > j) ? -1 : s_x[i];
+  }
+  if (tid == 0) {
+    P.accept_len[b] = bad ? -1 : j;
+    if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
+    raise_error(P.err_flags, s_err);
+    SeqPlan pl;
+    pl.j = bad ? -1 : j;
+    pl.c_hi = c.hi;
+    pl.c_lo = c.lo;
+    split(s_L[j], pl.lt_hi, pl.lt_lo);
+    if (j < K) {
+      split(s_L[K + 1 + j] - s_L[j], pl.d_hi, pl.d_lo);
+    } else {
+      pl.d_hi = 0.0f;
+      pl.d_lo = 0.0f;
+    }
+    pl.pad = 0.0f;
+    P.plan[b] = pl;
+  }
+}
 
 namespace {
 
@@ -328,27 +489,35 @@ struct SampleRows {
   float neg_d_hi, neg_d_lo;    // -(L_d - L_t)
 };
 
-// Weights of this thread's kSampleEPT tokens in tile `tile`, and their running
-// fp32 sum (the same operations in the same order wherever it is called).
+// One thread's kSampleEPT logits of a tile, for the target row and (when
+// sampling from the residual) the draft row.
+struct TileData {
+  float xt[kSampleEPT];
+  float xd[kSampleEPT];
+};
+
+template <class T>
+__device__ __forceinline__ void tile_load(const SampleRows& S, int64_t tile, int V, TileData& d) {
+  const int64_t e0 = tile * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
+  load_ept<T>(S.t, e0, V, d.xt);
+  if (S.d != nullptr) load_ept<T>(S.d, e0, V, d.xd);
+}
+
+// Weights of this thread's kSampleEPT tokens, and their running fp32 sum (the
+// same operations in the same order wherever it is called).
 //   bonus / p only:  w = p_t(v) = 2^(x_t c - L_t)
 //   residual:        w = p_t(v) * max(0, 1 - 2^((x_d - x_t) c - (L_d - L_t)))
 //                      = max(0, p_t(v) - p_d(v))
 // The ratio form keeps the exponent small exactly where p_t and p_d nearly
 // cancel, and any rounding common to all weights cancels in the draw.
-template <class T>
-__device__ __forceinline__ float tile_weights(const SampleRows& S, int64_t tile, int V, float (&w)[kSampleEPT]) {
-  const int64_t e0 = tile * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
-  float xt[kSampleEPT];
-  load_ept<T>(S.t, e0, V, xt);
+__device__ __forceinline__ float tile_compute(const SampleRows& S, const TileData& d, float (&w)[kSampleEPT]) {
   float pt[kSampleEPT];
 #pragma unroll
-  for (int i = 0; i < kSampleEPT; ++i) pt[i] = fast_exp2(scaled_arg(xt[i], S.c, S.neg_lt_hi) + S.neg_lt_lo);
+  for (int i = 0; i < kSampleEPT; ++i) pt[i] = fast_exp2(scaled_arg(d.xt[i], S.c, S.neg_lt_hi) + S.neg_lt_lo);
   if (S.d != nullptr) {
-    float xd[kSampleEPT];
-    load_ept<T>(S.d, e0, V, xd);
 #pragma unroll
     for (int i = 0; i < kSampleEPT; ++i) {
-      const float dx = xd[i] - xt[i];
+      const float dx = d.xd[i] - d.xt[i];
       const float ratio = fast_exp2(scaled_arg(dx, S.c, S.neg_d_hi) + S.neg_d_lo);
       w[i] = pt[i] * fmaxf(1.0f - ratio, 0.0f);
     }
@@ -360,6 +529,13 @@ __device__ __forceinline__ float tile_weights(const SampleRows& S, int64_t tile,
 #pragma unroll
   for (int i = 0; i < kSampleEPT; ++i) run += w[i];
   return run;
+}
+
+template <class T>
+__device__ __forceinline__ float tile_weights(const SampleRows& S, int64_t tile, int V, float (&w)[kSampleEPT]) {
+  TileData d;
+  tile_load<T>(S, tile, V, d);
+  return tile_compute(S, d, w);
 }
 
 template <class T>
@@ -420,13 +596,16 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   __syncthreads();
 
   // (1) total weight and the tile holding u * total (wave 0, fp64, tile order).
+  //     With at most 64 tiles the totals stay in registers between the passes.
   if (tid < kWave) {
     uint32_t err = 0u;
+    const bool one_chunk = P.ntiles <= kWave;
+    double v0 = (one_chunk && lane < P.ntiles) ? untag_nonneg_double(await_slot(&ts[lane], &err)) : 0.0;
     double carry = 0.0;
     int last_pos = -1;
     for (int base = 0; base < P.ntiles; base += kWave) {
       const int t = base + lane;
-      const double v = (t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err)) : 0.0;
+      const double v = one_chunk ? v0 : ((t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err)) : 0.0);
       double inc = v;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -444,7 +623,7 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
     carry = 0.0;
     for (int base = 0; base < P.ntiles && found < 0; base += kWave) {
       const int t = base + lane;
-      const double v = (t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err)) : 0.0;
+      const double v = one_chunk ? v0 : ((t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err)) : 0.0);
       double inc = v;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -524,33 +703,43 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
 
 template <class T>
 __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
-  __shared__ double s_scan[kWaves];
+  constexpr int TPB = kSampleTilesPerBlock;
+  __shared__ double s_red[TPB][kWaves];
   __shared__ int s_flag;
   const int b = blockIdx.x / P.nblk_b;
   const int blk = blockIdx.x % P.nblk_b;
   const SeqPlan pl = P.plan[b];
 
-  if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are already -1
+  if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
     const SampleRows S = sample_rows<T>(P, b, pl, false);
-    const int t0 = blk * P.tiles_per_block;
-    const int t1 = min(P.ntiles, t0 + P.tiles_per_block);
-    for (int t = t0; t < t1; ++t) {
+    const int t0 = blk * TPB;
+    TileData d[TPB];
+#pragma unroll
+    for (int i = 0; i < TPB; ++i)  // every load of the block in flight at once
+      if (t0 + i < P.ntiles) tile_load<T>(S, t0 + i, P.V, d[i]);
+#pragma unroll
+    for (int i = 0; i < TPB; ++i) {
       float w[kSampleEPT];
-      const float x = tile_weights<T>(S, t, P.V, w);
-      double tot;
-      block_exclusive_scan(static_cast<double>(x), s_scan, &tot);
-      if (threadIdx.x == 0) publish(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t], tag_nonneg_double(tot));
+      const double part = (t0 + i < P.ntiles) ? wave_sum(static_cast<double>(tile_compute(S, d[i], w))) : 0.0;
+      if (lane_id() == 0) s_red[i][wave_id()] = part;
+    }
+    __syncthreads();
+    if (threadIdx.x < TPB && t0 + static_cast<int>(threadIdx.x) < P.ntiles) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tot += s_red[threadIdx.x][w];
+      publish(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t0 + threadIdx.x], tag_nonneg_double(tot));
     }
   }
 
-  if (!arrive_and_check_last(&P.cnt_b[b], static_cast<uint32_t>(P.nblk_b), &s_flag)) return;
+  if (!arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(P.nblk_b), &s_flag)) return;
   if (pl.j >= 0) chain_draw<T>(P, b, pl);
   // Leave the workspace all zero for the next call, whatever its shape.
   __syncthreads();
   if (pl.j >= 0)
     for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
   if (threadIdx.x == 0) P.plan[b] = SeqPlan{};
-  reset_counter(&P.cnt_b[b]);
+  reset_counter(&P.cnt[b]);
 }
 
 // ---------------------------------------------------------------- launcher
@@ -558,11 +747,17 @@ __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
 template <class T>
 static hipError_t launch_chain_t(const ChainParams& p, hipStream_t stream) {
   const int64_t R = 2 * static_cast<int64_t>(p.K) + 1;
-  const int64_t grid_a = static_cast<int64_t>(p.B) * R * p.nseg;
+  const int64_t grid_a = p.fl_blocks > 0 ? p.fl_blocks : static_cast<int64_t>(p.B) * R * p.nseg;
   const int64_t grid_b = static_cast<int64_t>(p.B) * p.nblk_b;
   if (grid_a > INT32_MAX || grid_b > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(chain_stats_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, p);
+  if (p.fl_blocks > 0)
+    hipLaunchKernelGGL(chain_stats_flat_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(chain_stats_rows_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(chain_decide_kernel<T>, dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, stream, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chain_sample_kernel<T>, dim3(static_cast<uint32_t>(grid_b)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();

@@ -31,8 +31,12 @@ struct ChainParams {
   const float* temperature;
   const float* uniforms;
   int32_t B, K, V;
-  int32_t nseg;            // statistics segments per logit row
+  int32_t nseg;            // statistics segments per logit row (row layout)
   int32_t seg_vecs;        // 16-byte vectors per statistics segment
+  int32_t fl_blocks;       // > 0: flattened layout with this many statistics blocks
+  int32_t fl_kmax;         //   row pieces per block (upper bound)
+  int64_t fl_nvec;         //   16-byte vectors per row
+  int64_t fl_per;          //   vectors per block
   int32_t ntiles;          // sampling tiles per row (kSampleTile elements each)
   int32_t tiles_per_block; // sampling tiles handled by one workgroup
   int32_t nblk_b;          // sampling workgroups per sequence
@@ -43,11 +47,11 @@ struct ChainParams {
   float* residual_mass;
   int32_t* err_flags;
   // workspace (all zero between calls)
-  uint64_t* part_m;   // [B, 2K+1, nseg] tagged fp32 per-segment reference max*c
-  uint64_t* part_s;   // [B, 2K+1, nseg] tagged fp64 per-segment sums of 2^(x c - m)
-  uint32_t* cnt_a;    // [B] statistics arrivals
-  uint32_t* cnt_b;    // [B] sampling arrivals
-  SeqPlan* plan;      // [B]
+  float* part_m;      // per row piece: fp32 reference fl(max * c_hi), [B, 2K+1, nseg]
+                      // (row layout) or [fl_blocks, fl_kmax] (flattened)
+  double* part_s;     // per row piece: sum of 2^(x c - reference), same shape
+  SeqPlan* plan;      // [B] decision -> sampling hand-off
+  uint32_t* cnt;      // [B] sampling arrivals
   uint64_t* tile_sum; // [B, ntiles] tagged fp64 sampling weight per tile
 };
 
@@ -73,7 +77,15 @@ constexpr int kSampleTile = 256 * kSampleEPT;      // elements per sampling tile
 constexpr int kStatsUnroll = 4;
 constexpr int kStatsBatches = 2;
 constexpr int kStatsSegVecs = 256 * kStatsUnroll * kStatsBatches;
-constexpr int kSampleTilesPerBlock = 8;
+constexpr int kSampleTilesPerBlock = 4;
+
+// Flattened statistics layout: at most this many blocks, each with at least
+// kFlatMinVecsPerBlock vectors.
+#ifndef SV_FLAT_BLOCKS
+#define SV_FLAT_BLOCKS 2048
+#endif
+constexpr int kFlatMaxBlocks = SV_FLAT_BLOCKS;
+constexpr int kFlatMinVecsPerBlock = 256 * kStatsUnroll * 2;
 
 static_assert(kErrInternal == SV_ERRF_INTERNAL, "error bit mismatch");
 
