@@ -27,20 +27,20 @@ int32_t stats_segments(int32_t V, sv_dtype d) {
 
 struct ChainLayout {
   int32_t nseg, ntiles, tiles_per_block, nblk_b;
-  int32_t fl_blocks, fl_kmax;  // flattened statistics layout (when rows allow it)
+  int32_t fl_blocks, fl_kmax;  // flattened statistics layout (rows of whole 16-byte vectors)
   int64_t fl_nvec, fl_per;
-  size_t off_part_m, off_part_s, off_plan, off_cnt, off_tiles, total;
+  size_t off_part_m, off_part_s, off_plan, off_cnt, off_tiles, off_abort, total;
 };
 
-// Flattened layout parameters for rows of whole 16-byte vectors.
-void flat_layout(int64_t rows, int64_t nvec, int32_t* blocks, int32_t* kmax, int64_t* per) {
+// Flattened layout: the concatenated rows cut into chunks of `per` vectors,
+// about kFlatChunksTarget of them, each at least kFlatMinVecsPerBlock long.
+void flat_layout(int64_t rows, int64_t nvec, int32_t* chunks, int32_t* kmax, int64_t* per) {
   const int64_t total = rows * nvec;
-  int64_t g = ceil_div(total, sv::kFlatMinVecsPerBlock);
-  if (g > sv::kFlatMaxBlocks) g = sv::kFlatMaxBlocks;
-  if (g < 1) g = 1;
-  *per = ceil_div(total, g);
-  *blocks = static_cast<int32_t>(ceil_div(total, *per));
-  *kmax = static_cast<int32_t>((*per + nvec - 2) / nvec + 1);
+  int64_t p = ceil_div(total, sv::kFlatChunksTarget);
+  if (p < sv::kFlatMinVecsPerBlock) p = sv::kFlatMinVecsPerBlock;
+  *per = p;
+  *chunks = static_cast<int32_t>(ceil_div(total, p));
+  *kmax = static_cast<int32_t>((p + nvec - 2) / nvec + 1);
 }
 
 ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
@@ -60,22 +60,24 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   }
   size_t off = 0;
   L.off_part_m = off;
-  off = align_up(off + sizeof(float) * parts);
+  off = align_up(off + sizeof(uint64_t) * parts);
   L.off_part_s = off;
-  off = align_up(off + sizeof(double) * parts);
+  off = align_up(off + sizeof(uint64_t) * parts);
   L.off_plan = off;
-  off = align_up(off + sizeof(sv::SeqPlan) * B);
+  off = align_up(off + sizeof(uint64_t) * sv::kPlanWords * static_cast<int64_t>(B));
   L.off_cnt = off;
   off = align_up(off + sizeof(uint32_t) * B);
   L.off_tiles = off;
   off = align_up(off + sizeof(uint64_t) * static_cast<int64_t>(B) * L.ntiles);
+  L.off_abort = off;
+  off = align_up(off + sizeof(uint64_t));
   L.total = off;
   return L;
 }
 
 struct TreeLayout {
   int32_t nseg;
-  size_t off_part, off_cnt, total;
+  size_t off_part, off_cnt, off_abort, total;
 };
 
 TreeLayout tree_layout(int32_t B, int32_t N, int32_t V, sv_dtype d) {
@@ -87,6 +89,8 @@ TreeLayout tree_layout(int32_t B, int32_t N, int32_t V, sv_dtype d) {
   off = align_up(off + sizeof(uint64_t) * parts);
   L.off_cnt = off;
   off = align_up(off + sizeof(uint32_t) * B);
+  L.off_abort = off;
+  off = align_up(off + sizeof(uint64_t));
   L.total = off;
   return L;
 }
@@ -171,11 +175,12 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.q_draft = q_draft;
   p.residual_mass = residual_mass;
   p.err_flags = err_flags;
-  p.part_m = reinterpret_cast<float*>(ws + L.off_part_m);
-  p.part_s = reinterpret_cast<double*>(ws + L.off_part_s);
-  p.plan = reinterpret_cast<sv::SeqPlan*>(ws + L.off_plan);
+  p.part_m = reinterpret_cast<uint64_t*>(ws + L.off_part_m);
+  p.part_s = reinterpret_cast<uint64_t*>(ws + L.off_part_s);
+  p.plan_w = reinterpret_cast<uint64_t*>(ws + L.off_plan);
   p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
   p.tile_sum = reinterpret_cast<uint64_t*>(ws + L.off_tiles);
+  p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
   return from_hip(sv::launch_chain(p, dtype, stream));
 }
 
@@ -214,6 +219,7 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
   p.err_flags = err_flags;
   p.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
   p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+  p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
   return from_hip(sv::launch_tree(p, dtype, stream));
 }
 

@@ -12,21 +12,22 @@
 //     block, so every block streams the same number of bytes;
 //   chain_stats_rows_kernel: any row alignment; one block per (row, segment).
 //
-// Pass 2 — chain_sample_kernel, one workgroup per (sequence, tile pair):
-//   1. decision: combines the pieces of the sequence's 2K+1 rows into their
-//      log-normalisers L = log2 sum_v 2^(x_v c) (fp64), forms p_k(x_k) and
-//      q_k(x_k) in fp64, alpha_k = min(1, p/q), accepts while u_k < alpha_k
-//      and takes j = the first rejection with a wave ballot. Every block of
-//      the sequence makes the same decision; the first one writes it out.
-//      [Topologies] "Speculative Decoding & Draft Model Topologies", section 2
-//      (acceptance-probability equation, timeline figure steps 2-3);
-//      [In Production] "Speculative Decoding in Production", section 2.
-//   2. re-reads its tiles of row j (target, and draft when j < K), forms the
+// Pass 2 — chain_decide_kernel, one workgroup per sequence: combines the
+// pieces of the sequence's 2K+1 rows into their log-normalisers
+// L = log2 sum_v 2^(x_v c) (fp64), forms p_k(x_k) and q_k(x_k) in fp64,
+// alpha_k = min(1, p/q), accepts while u_k < alpha_k and takes j = the first
+// rejection with a wave ballot; writes the accepted prefix and a sampling plan.
+//   [Topologies] "Speculative Decoding & Draft Model Topologies", section 2
+//   (acceptance-probability equation, timeline figure steps 2-3);
+//   [In Production] "Speculative Decoding in Production", section 2.
+//
+// Pass 3 — chain_sample_kernel, one workgroup per (sequence, group of tiles):
+//   1. re-reads its tiles of row j (target, and draft when j < K), forms the
 //      weights max(0, p_j - q_j) (or p_K for the bonus draw) and publishes
 //      each tile's total;
-//   3. the last block of the sequence scans the tile totals, finds the tile
-//      holding u_K * total, rescans it with a block-wide prefix sum and picks
-//      the first token whose cumulative weight exceeds it.
+//   2. the last workgroup of the sequence scans the tile totals, finds the
+//      tile holding u_K * total, rescans it with a block-wide prefix sum and
+//      picks the first token whose cumulative weight exceeds it.
 //      [Topologies] section 2 (residual equation, step 4); [At Scale]
 //      "Speculative Decoding at Scale", section 1; [Draft-and-Verify]
 //      "Speculative Decoding for LLM Inference", "The draft-and-verify loop"
@@ -238,27 +239,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
   double S;
   block_combine(st, c, s_redf, s_redd, &MC, &S);
   if (tid == 0) {
-    P.part_m[blk] = MC;
-    P.part_s[blk] = S;
+    publish(&P.part_m[blk], tag_float(MC));
+    publish(&P.part_s[blk], tag_nonneg_double(S));
   }
 }
 
-// The flattened layout: block g streams the vectors [g*per, (g+1)*per) of the
-// concatenation of all rows, as one piece per row it touches.
+namespace {
+
+// The flattened layout: chunk g covers the vectors [g*per, (g+1)*per) of the
+// concatenation of all rows, streamed as one piece per row it touches; each
+// piece's (reference, sum) goes to slot g * fl_kmax + (row - first row).
 template <class T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_flat_kernel(ChainParams P) {
+__device__ __forceinline__ void stats_chunk(const ChainParams& P, int64_t g) {
   __shared__ float s_redf[kWaves];
   __shared__ double s_redd[kWaves];
   const int R = 2 * P.K + 1;
   const int64_t nvec = P.fl_nvec;
   const int64_t per = P.fl_per;
   const int64_t total = static_cast<int64_t>(P.B) * R * nvec;
-  const int g = blockIdx.x;
-  const int64_t lo = static_cast<int64_t>(g) * per;
+  const int64_t lo = g * per;
   const int64_t hi = min(total, lo + per);
   const int64_t row_lo = lo / nvec;
   const int64_t row_hi = (hi - 1) / nvec;
-
   for (int64_t row = row_lo; row <= row_hi; ++row) {
     const int b = static_cast<int>(row / R);
     const int r = static_cast<int>(row % R);
@@ -272,11 +274,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     double S;
     block_combine(st, c, s_redf, s_redd, &MC, &S);
     if (threadIdx.x == 0) {
-      const int64_t slot = static_cast<int64_t>(g) * P.fl_kmax + (row - row_lo);
-      P.part_m[slot] = MC;
-      P.part_s[slot] = S;
+      const int64_t slot = g * P.fl_kmax + (row - row_lo);
+      publish(&P.part_m[slot], tag_float(MC));
+      publish(&P.part_s[slot], tag_nonneg_double(S));
     }
   }
+}
+
+}  // namespace
+
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_flat_kernel(ChainParams P) {
+  stats_chunk<T>(P, blockIdx.x);
 }
 
 // ---------------------------------------------------------------- pass 2
@@ -301,6 +310,26 @@ __device__ __forceinline__ int64_t piece_slot(const ChainParams& P, int64_t grow
   return p < P.nseg ? grow * P.nseg + p : -1;
 }
 
+// The sampling plan travels as kPlanWords tagged 32-bit payloads (each word
+// is (1 << 32) | payload, never zero), so a reader can wait for each word.
+__device__ __forceinline__ void publish_plan(const ChainParams& P, int b, const SeqPlan& pl) {
+  uint32_t w[kPlanWords];
+  static_assert(sizeof(SeqPlan) == 4 * kPlanWords, "plan layout");
+  __builtin_memcpy(w, &pl, sizeof(SeqPlan));
+  for (int i = 0; i < kPlanWords; ++i) publish(&P.plan_w[static_cast<int64_t>(b) * kPlanWords + i], (1ull << 32) | w[i]);
+}
+
+__device__ __forceinline__ SeqPlan await_plan(const ChainParams& P, int b, uint32_t* err) {
+  uint64_t v[kPlanWords];
+  await_run(P.plan_w + static_cast<int64_t>(b) * kPlanWords, v, err, P.abort);
+  uint32_t w[kPlanWords];
+#pragma unroll
+  for (int i = 0; i < kPlanWords; ++i) w[i] = static_cast<uint32_t>(v[i]);
+  SeqPlan pl;
+  __builtin_memcpy(&pl, w, sizeof(SeqPlan));
+  return pl;
+}
+
 // Largest number of statistics pieces of any row (host and device agree).
 __device__ __forceinline__ int max_pieces(const ChainParams& P) {
   if (P.fl_blocks > 0) return static_cast<int>(div_nonneg(P.fl_nvec + P.fl_per - 2, P.fl_per)) + 1;
@@ -309,20 +338,21 @@ __device__ __forceinline__ int max_pieces(const ChainParams& P) {
 
 }  // namespace
 
-// The decision, one block per sequence: the rows' log-normalisers (one wave
+// The decision of one sequence: the rows' log-normalisers (one wave
 // per row, rows spread over the waves), the drafted tokens' logits gathered
 // by the last wave meanwhile, then p_k(x_k), q_k(x_k) in fp64, alpha_k =
 // min(1, p/q), acceptance while u_k < alpha_k and j = the first rejection
 // (wave ballot). Writes accept_len, the accepted prefix of out_tokens,
 // p_draft / q_draft, the error bits, and the sampling plan.
+namespace {
+
 template <class T>
-__global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
+__device__ void decide_seq(const ChainParams& P, int b) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
   __shared__ float s_lt[kWave], s_ld[kWave], s_u[kWave];
   __shared__ int s_x[kWave];
   __shared__ uint32_t s_err;
   __shared__ int s_j;
-  const int b = blockIdx.x;
   const int K = P.K;
   const int R = 2 * K + 1;
   const int tid = threadIdx.x;
@@ -369,18 +399,21 @@ __global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
       double ss[4];
       int64_t sl[4];
       int n = 0;
-      // pieces gl, gl+G, ... of this row (one round when G >= pieces)
+      // pieces gl, gl+G, ... of this row (one round when G >= pieces): the
+      // first four of each lane are loaded together, any further ones folded
+      // in one at a time
+      uint64_t rm[4], rs[4];
       for (int p = gl; row_ok && p < pmax; p += G) {
         const int64_t s = piece_slot(P, grow, p);
         if (s < 0) break;
         if (n < 4) {
           sl[n] = s;
-          ms[n] = P.part_m[s];
-          ss[n] = P.part_s[s];
+          rm[n] = peek(&P.part_m[s]);
+          rs[n] = peek(&P.part_s[s]);
           ++n;
         } else {
-          const float mm = P.part_m[s];
-          const double sv = P.part_s[s];
+          const float mm = untag_float(await_slot(&P.part_m[s], &err, P.abort));
+          const double sv = untag_nonneg_double(await_slot(&P.part_s[s], &err, P.abort));
           if (mm != -INFINITY) {
             if (mm > mf) {
               zf = (mf == -INFINITY ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(mm))) + sv;
@@ -389,9 +422,15 @@ __global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
               zf += sv * exp2(static_cast<double>(mm) - static_cast<double>(mf));
             }
           }
-          P.part_m[s] = 0.0f;
-          P.part_s[s] = 0.0;
+          clear_slot(&P.part_m[s]);
+          clear_slot(&P.part_s[s]);
         }
+      }
+      for (int i = 0; i < n; ++i) {
+        if (rm[i] == 0ull) rm[i] = await_slot(&P.part_m[sl[i]], &err, P.abort);
+        if (rs[i] == 0ull) rs[i] = await_slot(&P.part_s[sl[i]], &err, P.abort);
+        ms[i] = untag_float(rm[i]);
+        ss[i] = untag_nonneg_double(rs[i]);
       }
       float M = mf;
       for (int i = 0; i < n; ++i) M = fmaxf(M, ms[i]);
@@ -399,8 +438,8 @@ __global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
       double zl = (mf == -INFINITY) ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(M));
       for (int i = 0; i < n; ++i) {
         if (ms[i] != -INFINITY) zl += ss[i] * exp2(static_cast<double>(ms[i]) - static_cast<double>(M));
-        P.part_m[sl[i]] = 0.0f;  // consumed: leave the workspace zero
-        P.part_s[sl[i]] = 0.0;
+        clear_slot(&P.part_m[sl[i]]);  // consumed: leave the workspace zero
+        clear_slot(&P.part_s[sl[i]]);
       }
       for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
       if (row_ok && gl == 0) {
@@ -461,8 +500,17 @@ __global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
       pl.d_lo = 0.0f;
     }
     pl.pad = 0.0f;
-    P.plan[b] = pl;
+    publish_plan(P, b, pl);
   }
+  __syncthreads();
+}
+
+}  // namespace
+
+// The decision, one block per sequence (the three-kernel schedule).
+template <class T>
+__global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
+  decide_seq<T>(P, blockIdx.x);
 }
 
 namespace {
@@ -600,12 +648,12 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   if (tid < kWave) {
     uint32_t err = 0u;
     const bool one_chunk = P.ntiles <= kWave;
-    double v0 = (one_chunk && lane < P.ntiles) ? untag_nonneg_double(await_slot(&ts[lane], &err)) : 0.0;
+    double v0 = (one_chunk && lane < P.ntiles) ? untag_nonneg_double(await_slot(&ts[lane], &err, P.abort)) : 0.0;
     double carry = 0.0;
     int last_pos = -1;
     for (int base = 0; base < P.ntiles; base += kWave) {
       const int t = base + lane;
-      const double v = one_chunk ? v0 : ((t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err)) : 0.0);
+      const double v = one_chunk ? v0 : ((t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err, P.abort)) : 0.0);
       double inc = v;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -623,7 +671,7 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
     carry = 0.0;
     for (int base = 0; base < P.ntiles && found < 0; base += kWave) {
       const int t = base + lane;
-      const double v = one_chunk ? v0 : ((t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err)) : 0.0);
+      const double v = one_chunk ? v0 : ((t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err, P.abort)) : 0.0);
       double inc = v;
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
@@ -699,23 +747,23 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   }
 }
 
-}  // namespace
-
+// One sampling work item: tiles [4 blk, 4 blk + 4) of sequence b's row pair.
 template <class T>
-__global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
+__device__ void sample_item(const ChainParams& P, int b, int blk) {
   constexpr int TPB = kSampleTilesPerBlock;
   __shared__ double s_red[TPB][kWaves];
   __shared__ int s_flag;
-  const int b = blockIdx.x / P.nblk_b;
-  const int blk = blockIdx.x % P.nblk_b;
-  const SeqPlan pl = P.plan[b];
+  __shared__ uint32_t s_perr;
+  uint32_t perr = 0u;
+  const SeqPlan pl = await_plan(P, b, &perr);
+  if (threadIdx.x == 0) s_perr = perr;
 
   if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
     const SampleRows S = sample_rows<T>(P, b, pl, false);
     const int t0 = blk * TPB;
     TileData d[TPB];
 #pragma unroll
-    for (int i = 0; i < TPB; ++i)  // every load of the block in flight at once
+    for (int i = 0; i < TPB; ++i)  // every load of the item in flight at once
       if (t0 + i < P.ntiles) tile_load<T>(S, t0 + i, P.V, d[i]);
 #pragma unroll
     for (int i = 0; i < TPB; ++i) {
@@ -738,8 +786,17 @@ __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
   __syncthreads();
   if (pl.j >= 0)
     for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
-  if (threadIdx.x == 0) P.plan[b] = SeqPlan{};
+  if (threadIdx.x < kPlanWords) clear_slot(&P.plan_w[static_cast<int64_t>(b) * kPlanWords + threadIdx.x]);
+  if (threadIdx.x == 0) raise_error(P.err_flags, s_perr);
   reset_counter(&P.cnt[b]);
+  __syncthreads();
+}
+
+}  // namespace
+
+template <class T>
+__global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
+  sample_item<T>(P, blockIdx.x / P.nblk_b, blockIdx.x % P.nblk_b);
 }
 
 // ---------------------------------------------------------------- launcher

@@ -166,26 +166,55 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* scratch
 // invalidate is needed (an agent-scope fence costs an L2 write-back per block
 // on this part): each slot is written by ONE agent-scope atomic store whose
 // value is never all-zero bits, and the last block reads each slot with
-// agent-scope atomic loads until it is non-zero. Every store it waits for has
-// already been issued by a block that has arrived, so the wait ends; it is
-// still bounded (kSpinLimit polls) and reports SV_ERRF_INTERNAL if it ever
-// expires. The last block sets the slots back to zero after use.
+// agent-scope atomic loads until it is non-zero. Every store it waits for
+// has already been issued (or belongs to work held by a running block), so
+// the wait ends; it is still bounded in wall time and reports
+// SV_ERRF_INTERNAL if it ever expires. The reader sets slots back to zero
+// after use.
 
-constexpr int kSpinLimit = 1 << 22;
-constexpr uint32_t kErrInternal = 0x10u;  // SV_ERRF_INTERNAL
+constexpr uint64_t kWaitTicks = 10000000ull;  // 100 ms of the 100 MHz real-time counter
+constexpr uint32_t kErrInternal = 0x10u;      // SV_ERRF_INTERNAL
 
 __device__ __forceinline__ void publish(uint64_t* slot, uint64_t v) {
   __hip_atomic_store(slot, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint64_t await_slot(uint64_t* slot, uint32_t* err) {
-  uint64_t v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int it = 0; v == 0ull && it < kSpinLimit; ++it) {
-    __builtin_amdgcn_s_sleep(1);
-    v = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t peek(const uint64_t* slot) {
+  return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait until *slot is non-zero and return it. Bounded: after kWaitTicks of
+// wall time, or as soon as *abort is set by another expired wait, give up,
+// set *abort, flag kErrInternal and return 0 (so a failure drains the launch
+// quickly instead of spinning).
+__device__ __forceinline__ uint64_t await_slot(uint64_t* slot, uint32_t* err, uint64_t* abort) {
+  uint64_t v = peek(slot);
+  if (v != 0ull) return v;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    __builtin_amdgcn_s_sleep(2);
+    v = peek(slot);
+    if (v != 0ull) return v;
+    if (peek(abort) != 0ull) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      publish(abort, 1ull);
+      break;
+    }
   }
-  if (v == 0ull) *err |= kErrInternal;
-  return v;
+  *err |= kErrInternal;
+  return 0ull;
+}
+
+// Wait for the N consecutive slots base[0..N): every load is issued before
+// any value is inspected, so slots that are already written cost a single
+// memory round trip together.
+template <int N>
+__device__ __forceinline__ void await_run(uint64_t* base, uint64_t (&v)[N], uint32_t* err, uint64_t* abort) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = peek(base + i);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (v[i] == 0ull) v[i] = await_slot(base + i, err, abort);
 }
 
 __device__ __forceinline__ void clear_slot(uint64_t* slot) { publish(slot, 0ull); }

@@ -11,7 +11,7 @@
 
 namespace sv {
 
-// Hand-off from the decision (stats kernel) to the sampling kernel, one per
+// Hand-off from the decision kernel to the sampling kernel, one per
 // sequence: which row pair to sample from and its normalisers.
 struct SeqPlan {
   int32_t j;     // first rejected position; K = bonus draw; -1 = invalid row
@@ -23,6 +23,8 @@ struct SeqPlan {
   float d_lo;    //   2^((x_d - x_t) c - D)    (unused for the bonus draw)
   float pad;
 };
+
+constexpr int kPlanWords = 8;  // 32-bit fields of a SeqPlan
 
 struct ChainParams {
   const void* target;
@@ -47,12 +49,13 @@ struct ChainParams {
   float* residual_mass;
   int32_t* err_flags;
   // workspace (all zero between calls)
-  float* part_m;      // per row piece: fp32 reference fl(max * c_hi), [B, 2K+1, nseg]
-                      // (row layout) or [fl_blocks, fl_kmax] (flattened)
-  double* part_s;     // per row piece: sum of 2^(x c - reference), same shape
-  SeqPlan* plan;      // [B] decision -> sampling hand-off
+  uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi),
+                      // [B, 2K+1, nseg] (row layout) or [fl_blocks, fl_kmax]
+  uint64_t* part_s;   // per row piece: tagged fp64 sum of 2^(x c - reference)
+  uint64_t* plan_w;   // [B, kPlanWords] tagged decision -> sampling hand-off
   uint32_t* cnt;      // [B] sampling arrivals
   uint64_t* tile_sum; // [B, ntiles] tagged fp64 sampling weight per tile
+  uint64_t* abort;    // [1] set when a bounded wait expires (drains the launch)
 };
 
 struct TreeParams {
@@ -68,6 +71,7 @@ struct TreeParams {
   int32_t* err_flags;
   uint64_t* part;    // [B, N+1, nseg] per-segment (max value, lowest index + 1)
   uint32_t* cnt;     // [B]
+  uint64_t* abort;   // [1] set when a bounded wait expires
 };
 
 constexpr int kSampleEPT = 8;                      // sampling elements per thread per tile
@@ -79,12 +83,12 @@ constexpr int kStatsBatches = 2;
 constexpr int kStatsSegVecs = 256 * kStatsUnroll * kStatsBatches;
 constexpr int kSampleTilesPerBlock = 4;
 
-// Flattened statistics layout: at most this many blocks, each with at least
-// kFlatMinVecsPerBlock vectors.
-#ifndef SV_FLAT_BLOCKS
-#define SV_FLAT_BLOCKS 2048
+// Flattened statistics layout: about this many chunks, each with at least
+// kFlatMinVecsPerBlock 16-byte vectors.
+#ifndef SV_FLAT_CHUNKS
+#define SV_FLAT_CHUNKS 4096
 #endif
-constexpr int kFlatMaxBlocks = SV_FLAT_BLOCKS;
+constexpr int kFlatChunksTarget = SV_FLAT_CHUNKS;
 constexpr int kFlatMinVecsPerBlock = 256 * kStatsUnroll * 2;
 
 static_assert(kErrInternal == SV_ERRF_INTERNAL, "error bit mismatch");

@@ -87,7 +87,7 @@ __device__ void tree_decide(const TreeParams& P, int b) {
     int bi = INT_MAX;
     uint32_t err = 0u;
     for (int s = 0; s < P.nseg; ++s) {
-      const uint64_t slot = await_slot(&P.part[base + s], &err);
+      const uint64_t slot = await_slot(&P.part[base + s], &err, P.abort);
       const float v = __uint_as_float(static_cast<uint32_t>(slot >> 32));
       const int i = static_cast<int>(static_cast<uint32_t>(slot) - 1u);
       if (better(v, i, bv, bi)) {
