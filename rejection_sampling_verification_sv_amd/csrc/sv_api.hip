@@ -27,20 +27,21 @@ int32_t stats_segments(int32_t V, sv_dtype d) {
 
 struct ChainLayout {
   int32_t nseg, ntiles, tiles_per_block, nblk_b;
-  int32_t fl_blocks, fl_kmax;  // flattened statistics layout (rows of whole 16-byte vectors)
-  int64_t fl_nvec, fl_per;
-  size_t off_part_m, off_part_s, off_plan, off_cnt, off_tiles, off_abort, total;
+  int32_t cps, kmax;  // chunked statistics layout (rows of whole 16-byte vectors)
+  int64_t nvec, per;
+  size_t off_part_m, off_part_s, off_plan, off_cnt, off_tiles, off_gat, off_abort, total;
 };
 
-// Flattened layout: the concatenated rows cut into chunks of `per` vectors,
-// about kFlatChunksTarget of them, each at least kFlatMinVecsPerBlock long.
-void flat_layout(int64_t rows, int64_t nvec, int32_t* chunks, int32_t* kmax, int64_t* per) {
-  const int64_t total = rows * nvec;
-  int64_t p = ceil_div(total, sv::kFlatChunksTarget);
-  if (p < sv::kFlatMinVecsPerBlock) p = sv::kFlatMinVecsPerBlock;
-  *per = p;
-  *chunks = static_cast<int32_t>(ceil_div(total, p));
-  *kmax = static_cast<int32_t>((p + nvec - 2) / nvec + 1);
+// Chunked layout: each sequence's rows cut into cps equal chunks, about
+// kChunksTarget chunks over the call, each of at least kChunkMinVecs vectors.
+void chunk_layout(int64_t B, int64_t R, int64_t nvec, ChainLayout* L) {
+  const int64_t seq_vecs = R * nvec;
+  int64_t p = ceil_div(B * seq_vecs, sv::kChunksTarget);
+  if (p < sv::kChunkMinVecs) p = sv::kChunkMinVecs;
+  L->cps = static_cast<int32_t>(ceil_div(seq_vecs, p));
+  L->per = ceil_div(seq_vecs, L->cps);
+  L->nvec = nvec;
+  L->kmax = static_cast<int32_t>((L->per + nvec - 2) / nvec + 1);
 }
 
 ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
@@ -48,15 +49,14 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   const int64_t R = 2 * static_cast<int64_t>(K) + 1;
   L.nseg = stats_segments(V, d);
   L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
-  L.tiles_per_block = sv::kSampleTilesPerBlock;
+  L.tiles_per_block = d == SV_DTYPE_BF16 ? sv::kSampleTilesBF16 : sv::kSampleTilesF32;
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
   int64_t parts = static_cast<int64_t>(B) * R * L.nseg;
   const int64_t row_bytes = static_cast<int64_t>(V) * dtype_bytes(d);
   if (row_bytes % 16 == 0 && B > 0) {
-    L.fl_nvec = row_bytes / 16;
-    flat_layout(static_cast<int64_t>(B) * R, L.fl_nvec, &L.fl_blocks, &L.fl_kmax, &L.fl_per);
-    const int64_t fl_parts = static_cast<int64_t>(L.fl_blocks) * L.fl_kmax;
-    if (fl_parts > parts) parts = fl_parts;
+    chunk_layout(B, R, row_bytes / 16, &L);
+    const int64_t ch_parts = static_cast<int64_t>(B) * L.cps * L.kmax;
+    if (ch_parts > parts) parts = ch_parts;
   }
   size_t off = 0;
   L.off_part_m = off;
@@ -64,11 +64,13 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   L.off_part_s = off;
   off = align_up(off + sizeof(uint64_t) * parts);
   L.off_plan = off;
-  off = align_up(off + sizeof(uint64_t) * sv::kPlanWords * static_cast<int64_t>(B));
+  off = align_up(off + sizeof(sv::SeqPlan) * static_cast<int64_t>(B));
   L.off_cnt = off;
   off = align_up(off + sizeof(uint32_t) * B);
   L.off_tiles = off;
   off = align_up(off + sizeof(uint64_t) * static_cast<int64_t>(B) * L.ntiles);
+  L.off_gat = off;
+  off = align_up(off + sizeof(uint64_t) * static_cast<int64_t>(B) * R);
   L.off_abort = off;
   off = align_up(off + sizeof(uint64_t));
   L.total = off;
@@ -144,10 +146,6 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
     return SV_ERR_INVALID_ARGUMENT;
   const ChainLayout L = chain_layout(B, K, V, dtype);
   if (workspace == nullptr || workspace_bytes < L.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
-  const int64_t R = 2 * static_cast<int64_t>(K) + 1;
-  if (static_cast<int64_t>(B) * R * L.nseg > INT32_MAX || static_cast<int64_t>(B) * L.nblk_b > INT32_MAX)
-    return SV_ERR_UNSUPPORTED;
-
   char* ws = static_cast<char*>(workspace);
   sv::ChainParams p{};
   p.target = target_logits;
@@ -158,14 +156,15 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.B = B;
   p.K = K;
   p.V = V;
+  // The chunked statistics layout needs every row on a 16-byte boundary;
+  // otherwise the rows layout.
+  const bool chunked = L.cps > 0 && aligned_to(target_logits, 16) && (K == 0 || aligned_to(draft_logits, 16));
+  p.cps = chunked ? L.cps : 0;
+  p.kmax = L.kmax;
+  p.nvec = L.nvec;
+  p.per = L.per;
   p.nseg = L.nseg;
   p.seg_vecs = sv::kStatsSegVecs;
-  // The flattened statistics layout needs every row on a 16-byte boundary.
-  const bool flat = L.fl_blocks > 0 && aligned_to(target_logits, 16) && (K == 0 || aligned_to(draft_logits, 16));
-  p.fl_blocks = flat ? L.fl_blocks : 0;
-  p.fl_kmax = L.fl_kmax;
-  p.fl_nvec = L.fl_nvec;
-  p.fl_per = L.fl_per;
   p.ntiles = L.ntiles;
   p.tiles_per_block = L.tiles_per_block;
   p.nblk_b = L.nblk_b;
@@ -177,10 +176,13 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.err_flags = err_flags;
   p.part_m = reinterpret_cast<uint64_t*>(ws + L.off_part_m);
   p.part_s = reinterpret_cast<uint64_t*>(ws + L.off_part_s);
-  p.plan_w = reinterpret_cast<uint64_t*>(ws + L.off_plan);
+  p.plan = reinterpret_cast<sv::SeqPlan*>(ws + L.off_plan);
   p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
   p.tile_sum = reinterpret_cast<uint64_t*>(ws + L.off_tiles);
+  p.gat = reinterpret_cast<uint64_t*>(ws + L.off_gat);
   p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
+
+  if (sv::chain_stats_items(p) > INT32_MAX || static_cast<int64_t>(B) * p.nblk_b > INT32_MAX) return SV_ERR_UNSUPPORTED;
   return from_hip(sv::launch_chain(p, dtype, stream));
 }
 

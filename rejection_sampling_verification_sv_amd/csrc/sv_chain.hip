@@ -195,19 +195,31 @@ __device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, 
 
 // ---------------------------------------------------------------- pass 1
 
+namespace {
+
+// The drafted token verified on row r of sequence b (target row k or draft
+// row K+1+k carry token k; the bonus row K carries none): -1 if none.
+__device__ __forceinline__ int row_token(const ChainParams& P, int b, int r) {
+  const int k = r < P.K ? r : r - P.K - 1;
+  return (r == P.K) ? -1 : P.tokens[static_cast<int64_t>(b) * P.K + k];
+}
+
+// Publish the logit of row r at its drafted token x (a valid id) for the
+// decision, which then needs no dependent gather of its own.
 template <class T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_rows_kernel(ChainParams P) {
+__device__ __forceinline__ void publish_gather(const ChainParams& P, int b, int r, const void* row, int x) {
+  publish(&P.gat[static_cast<int64_t>(b) * (2 * P.K + 1) + r], tag_float(load_elem<T>(row, x)));
+}
+
+// Rows layout: segment `seg` of row r of sequence b (any alignment), its
+// (reference, sum) to slot (b * (2K+1) + r) * nseg + seg.
+template <class T>
+__device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
   __shared__ float s_redf[kWaves];
   __shared__ double s_redd[kWaves];
   constexpr int VEC = T::kVec;
   constexpr int U = kStatsUnroll;
-
   const int R = 2 * P.K + 1;
-  const int64_t blk = blockIdx.x;
-  const int seg = static_cast<int>(blk % P.nseg);
-  const int64_t rowid = blk / P.nseg;
-  const int r = static_cast<int>(rowid % R);
-  const int b = static_cast<int>(rowid / R);
   const int tid = threadIdx.x;
 
   const void* row = chain_row<T>(P, b, r);
@@ -222,6 +234,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
   const int64_t v1 = min(nvec, v0 + P.seg_vecs);
   const uint4* body = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + head * T::kBytes);
 
+  const int x = (seg == 0 && tid == 0) ? row_token(P, b, r) : -1;
   Running st{-INFINITY, 0.0f};
   if (seg == 0 && tid < head) running_add1(st, load_elem<T>(row, tid), c);
   for (int64_t base = v0 + tid; base < v1; base += static_cast<int64_t>(kThreads) * U) {
@@ -239,58 +252,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
   double S;
   block_combine(st, c, s_redf, s_redd, &MC, &S);
   if (tid == 0) {
-    publish(&P.part_m[blk], tag_float(MC));
-    publish(&P.part_s[blk], tag_nonneg_double(S));
+    const int64_t slot = (static_cast<int64_t>(b) * R + r) * P.nseg + seg;
+    publish(&P.part_m[slot], tag_float(MC));
+    publish(&P.part_s[slot], tag_nonneg_double(S));
+    if (x >= 0 && x < P.V) publish_gather<T>(P, b, r, row, x);
   }
 }
 
-namespace {
-
-// The flattened layout: chunk g covers the vectors [g*per, (g+1)*per) of the
-// concatenation of all rows, streamed as one piece per row it touches; each
-// piece's (reference, sum) goes to slot g * fl_kmax + (row - first row).
+// Chunked layout: chunk `ch` of sequence b covers the vectors
+// [ch * per, (ch + 1) * per) of the sequence's 2K+1 rows laid end to end,
+// streamed as one piece per row it touches; the piece of row r goes to slot
+// (b * cps + ch) * kmax + (r - first row of the chunk).
 template <class T>
-__device__ __forceinline__ void stats_chunk(const ChainParams& P, int64_t g) {
+__device__ void stats_chunk(const ChainParams& P, int b, int ch) {
   __shared__ float s_redf[kWaves];
   __shared__ double s_redd[kWaves];
   const int R = 2 * P.K + 1;
-  const int64_t nvec = P.fl_nvec;
-  const int64_t per = P.fl_per;
-  const int64_t total = static_cast<int64_t>(P.B) * R * nvec;
-  const int64_t lo = g * per;
-  const int64_t hi = min(total, lo + per);
-  const int64_t row_lo = lo / nvec;
-  const int64_t row_hi = (hi - 1) / nvec;
-  for (int64_t row = row_lo; row <= row_hi; ++row) {
-    const int b = static_cast<int>(row / R);
-    const int r = static_cast<int>(row % R);
-    const int64_t p0 = max(lo, row * nvec) - row * nvec;
-    const int64_t p1 = min(hi, (row + 1) * nvec) - row * nvec;
+  const int64_t nvec = P.nvec;
+  const int64_t lo = static_cast<int64_t>(ch) * P.per;
+  const int64_t hi = min(static_cast<int64_t>(R) * nvec, lo + P.per);
+  const int r_lo = static_cast<int>(lo / nvec);
+  const int r_hi = static_cast<int>((hi - 1) / nvec);
+  const Scale c = exponent_scale(temperature_of(P.temperature, b));
+  for (int r = r_lo; r <= r_hi; ++r) {
+    const int64_t p0 = max(lo, r * nvec) - r * nvec;
+    const int64_t p1 = min(hi, (r + 1) * nvec) - r * nvec;
     const uint4* body = static_cast<const uint4*>(chain_row<T>(P, b, r));
-    const Scale c = exponent_scale(temperature_of(P.temperature, b));
+    const int x = threadIdx.x == 0 ? row_token(P, b, r) : -1;  // consumed after the piece
     Running st{-INFINITY, 0.0f};
     flat_piece_stats<T>(body, p0, p1, c, st);
     float MC;
     double S;
     block_combine(st, c, s_redf, s_redd, &MC, &S);
     if (threadIdx.x == 0) {
-      const int64_t slot = g * P.fl_kmax + (row - row_lo);
+      const int64_t slot = (static_cast<int64_t>(b) * P.cps + ch) * P.kmax + (r - r_lo);
       publish(&P.part_m[slot], tag_float(MC));
       publish(&P.part_s[slot], tag_nonneg_double(S));
+      // the piece holding the drafted token publishes its logit
+      if (x >= 0 && x < P.V && x / T::kVec >= p0 && x / T::kVec < p1) publish_gather<T>(P, b, r, body, x);
     }
   }
 }
 
-}  // namespace
-
-template <class T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_flat_kernel(ChainParams P) {
-  stats_chunk<T>(P, blockIdx.x);
-}
-
 // ---------------------------------------------------------------- pass 2
-
-namespace {
 
 // a / b for non-negative 64-bit values, in 32-bit arithmetic when both fit
 // (a hardware-friendly path for every realistic size).
@@ -299,53 +303,29 @@ __device__ __forceinline__ int64_t div_nonneg(int64_t a, int64_t b) {
   return a / b;
 }
 
-// Slot index of piece `p` of global row `grow`, or -1 past its last piece.
-__device__ __forceinline__ int64_t piece_slot(const ChainParams& P, int64_t grow, int p) {
-  if (P.fl_blocks > 0) {
-    const int64_t nvec = P.fl_nvec, per = P.fl_per;
-    const int64_t gg = div_nonneg(grow * nvec, per) + p;
-    if (gg > div_nonneg((grow + 1) * nvec - 1, per)) return -1;
-    return gg * P.fl_kmax + (grow - div_nonneg(gg * per, nvec));
+// Slot index of piece `p` of row r of sequence b, or -1 past its last piece.
+__device__ __forceinline__ int64_t piece_slot(const ChainParams& P, int b, int r, int p) {
+  if (P.cps > 0) {
+    const int64_t nvec = P.nvec, per = P.per;
+    const int64_t ch = div_nonneg(r * nvec, per) + p;
+    if (ch > div_nonneg((r + 1) * nvec - 1, per)) return -1;
+    return (static_cast<int64_t>(b) * P.cps + ch) * P.kmax + (r - div_nonneg(ch * per, nvec));
   }
-  return p < P.nseg ? grow * P.nseg + p : -1;
-}
-
-// The sampling plan travels as kPlanWords tagged 32-bit payloads (each word
-// is (1 << 32) | payload, never zero), so a reader can wait for each word.
-__device__ __forceinline__ void publish_plan(const ChainParams& P, int b, const SeqPlan& pl) {
-  uint32_t w[kPlanWords];
-  static_assert(sizeof(SeqPlan) == 4 * kPlanWords, "plan layout");
-  __builtin_memcpy(w, &pl, sizeof(SeqPlan));
-  for (int i = 0; i < kPlanWords; ++i) publish(&P.plan_w[static_cast<int64_t>(b) * kPlanWords + i], (1ull << 32) | w[i]);
-}
-
-__device__ __forceinline__ SeqPlan await_plan(const ChainParams& P, int b, uint32_t* err) {
-  uint64_t v[kPlanWords];
-  await_run(P.plan_w + static_cast<int64_t>(b) * kPlanWords, v, err, P.abort);
-  uint32_t w[kPlanWords];
-#pragma unroll
-  for (int i = 0; i < kPlanWords; ++i) w[i] = static_cast<uint32_t>(v[i]);
-  SeqPlan pl;
-  __builtin_memcpy(&pl, w, sizeof(SeqPlan));
-  return pl;
+  return p < P.nseg ? (static_cast<int64_t>(b) * (2 * P.K + 1) + r) * P.nseg + p : -1;
 }
 
 // Largest number of statistics pieces of any row (host and device agree).
 __device__ __forceinline__ int max_pieces(const ChainParams& P) {
-  if (P.fl_blocks > 0) return static_cast<int>(div_nonneg(P.fl_nvec + P.fl_per - 2, P.fl_per)) + 1;
+  if (P.cps > 0) return static_cast<int>(div_nonneg(P.nvec + P.per - 2, P.per)) + 1;
   return P.nseg;
 }
 
-}  // namespace
-
-// The decision of one sequence: the rows' log-normalisers (one wave
-// per row, rows spread over the waves), the drafted tokens' logits gathered
-// by the last wave meanwhile, then p_k(x_k), q_k(x_k) in fp64, alpha_k =
-// min(1, p/q), acceptance while u_k < alpha_k and j = the first rejection
-// (wave ballot). Writes accept_len, the accepted prefix of out_tokens,
-// p_draft / q_draft, the error bits, and the sampling plan.
-namespace {
-
+// The decision of sequence b (one workgroup): the rows' log-normalisers (a
+// group of lanes per row), the drafted tokens' logits published by pass 1,
+// then p_k(x_k), q_k(x_k) in fp64, alpha_k = min(1, p/q), acceptance while
+// u_k < alpha_k and j = the first rejection (wave ballot). Writes accept_len,
+// the accepted prefix of out_tokens, p_draft / q_draft, the error bits and
+// the sampling plan, and returns the pieces it consumed to zero.
 template <class T>
 __device__ void decide_seq(const ChainParams& P, int b) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
@@ -356,7 +336,6 @@ __device__ void decide_seq(const ChainParams& P, int b) {
   const int K = P.K;
   const int R = 2 * K + 1;
   const int tid = threadIdx.x;
-  const int lane = lane_id();
   const Scale c = exponent_scale(temperature_of(P.temperature, b));
   if (tid == 0) {
     s_err = 0u;
@@ -365,24 +344,30 @@ __device__ void decide_seq(const ChainParams& P, int b) {
   __syncthreads();
 
   uint32_t err = 0u;
-  if (wave_id() == kWaves - 1) {  // gathers
-    const int k = lane;
+  if (wave_id() == kWaves - 1) {  // the drafted tokens and their logits (published by pass 1)
+    const int k = lane_id();
     if (k < K) {
+      uint64_t* gt = &P.gat[static_cast<int64_t>(b) * R + k];
+      uint64_t* gd = &P.gat[static_cast<int64_t>(b) * R + K + 1 + k];
       const int x = P.tokens[static_cast<int64_t>(b) * K + k];
+      const float u = P.uniforms[static_cast<int64_t>(b) * (K + 1) + k];
+      const uint64_t vt = *gt, vd = *gd;
       s_x[k] = x;
-      s_u[k] = P.uniforms[static_cast<int64_t>(b) * (K + 1) + k];
+      s_u[k] = u;
       if (x < 0 || x >= P.V) {
         err |= SV_ERRF_TOKEN;
       } else {
-        s_lt[k] = load_elem<T>(chain_row<T>(P, b, k), x);
-        s_ld[k] = load_elem<T>(chain_row<T>(P, b, K + 1 + k), x);
+        if (vt == 0ull || vd == 0ull) err |= kErrInternal;
+        s_lt[k] = untag_float(vt);
+        s_ld[k] = untag_float(vd);
       }
     }
   }
   // Rows' log-normalisers: a group of G lanes per row (G a power of two that
-  // covers the row's pieces, up to a wave), all pieces loaded in one round.
-  // Group max of the references M, each lane rescales its sum by 2^(m - M) in
-  // fp64, group sum Z, L = M + log2 Z. The consumed pieces are set to zero.
+  // covers the row's pieces, up to a wave). Each lane loads its first piece
+  // at once and folds any further ones in one at a time; group max of the
+  // references M, each lane rescales its sum by 2^(m - M) in fp64, group sum
+  // Z, L = M + log2 Z.
   {
     const int pmax = max_pieces(P);
     int G = 1;
@@ -392,55 +377,39 @@ __device__ void decide_seq(const ChainParams& P, int b) {
       const int r = r0 + tid / G;
       const int gl = tid % G;
       const bool row_ok = r < R;
-      const int64_t grow = static_cast<int64_t>(b) * R + r;
-      float mf = -INFINITY;  // reference of the folded sum zf (pieces beyond four per lane)
+      const int64_t s_first = row_ok ? piece_slot(P, b, r, gl) : -1;
+      uint64_t rm = 0ull, rs = 0ull;
+      if (s_first >= 0) {
+        rm = P.part_m[s_first];
+        rs = P.part_s[s_first];
+      }
+      float mf = -INFINITY;  // reference of the folded sum zf
       double zf = 0.0;
-      float ms[4];
-      double ss[4];
-      int64_t sl[4];
-      int n = 0;
-      // pieces gl, gl+G, ... of this row (one round when G >= pieces): the
-      // first four of each lane are loaded together, any further ones folded
-      // in one at a time
-      uint64_t rm[4], rs[4];
-      for (int p = gl; row_ok && p < pmax; p += G) {
-        const int64_t s = piece_slot(P, grow, p);
+      for (int p = gl + G; s_first >= 0 && p < pmax; p += G) {
+        const int64_t s = piece_slot(P, b, r, p);
         if (s < 0) break;
-        if (n < 4) {
-          sl[n] = s;
-          rm[n] = peek(&P.part_m[s]);
-          rs[n] = peek(&P.part_s[s]);
-          ++n;
-        } else {
-          const float mm = untag_float(await_slot(&P.part_m[s], &err, P.abort));
-          const double sv = untag_nonneg_double(await_slot(&P.part_s[s], &err, P.abort));
-          if (mm != -INFINITY) {
-            if (mm > mf) {
-              zf = (mf == -INFINITY ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(mm))) + sv;
-              mf = mm;
-            } else {
-              zf += sv * exp2(static_cast<double>(mm) - static_cast<double>(mf));
-            }
+        const float mm = untag_float(load_ready(&P.part_m[s], &err));
+        const double sv = untag_nonneg_double(load_ready(&P.part_s[s], &err));
+        if (mm != -INFINITY) {
+          if (mm > mf) {
+            zf = (mf == -INFINITY ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(mm))) + sv;
+            mf = mm;
+          } else {
+            zf += sv * exp2(static_cast<double>(mm) - static_cast<double>(mf));
           }
-          clear_slot(&P.part_m[s]);
-          clear_slot(&P.part_s[s]);
         }
       }
-      for (int i = 0; i < n; ++i) {
-        if (rm[i] == 0ull) rm[i] = await_slot(&P.part_m[sl[i]], &err, P.abort);
-        if (rs[i] == 0ull) rs[i] = await_slot(&P.part_s[sl[i]], &err, P.abort);
-        ms[i] = untag_float(rm[i]);
-        ss[i] = untag_nonneg_double(rs[i]);
+      float m1 = -INFINITY;
+      double s1 = 0.0;
+      if (s_first >= 0) {
+        if (rm == 0ull || rs == 0ull) err |= kErrInternal;
+        m1 = untag_float(rm);
+        s1 = untag_nonneg_double(rs);
       }
-      float M = mf;
-      for (int i = 0; i < n; ++i) M = fmaxf(M, ms[i]);
+      float M = fmaxf(mf, m1);
       for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
       double zl = (mf == -INFINITY) ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(M));
-      for (int i = 0; i < n; ++i) {
-        if (ms[i] != -INFINITY) zl += ss[i] * exp2(static_cast<double>(ms[i]) - static_cast<double>(M));
-        clear_slot(&P.part_m[sl[i]]);  // consumed: leave the workspace zero
-        clear_slot(&P.part_s[sl[i]]);
-      }
+      if (m1 != -INFINITY) zl += s1 * exp2(static_cast<double>(m1) - static_cast<double>(M));
       for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
       if (row_ok && gl == 0) {
         if (!(zl > 0.0) || !isfinite(zl) || !isfinite(M)) err |= SV_ERRF_NONFINITE;
@@ -478,7 +447,8 @@ __device__ void decide_seq(const ChainParams& P, int b) {
   }
   __syncthreads();
 
-  const bool bad = s_err != 0u;
+  const uint32_t serr = s_err;
+  const bool bad = serr != 0u;
   const int j = s_j;
   for (int i = tid; i <= K; i += kThreads) {
     if (i == j && !bad) continue;  // the drawn token: written by the sampling pass
@@ -487,7 +457,7 @@ __device__ void decide_seq(const ChainParams& P, int b) {
   if (tid == 0) {
     P.accept_len[b] = bad ? -1 : j;
     if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
-    raise_error(P.err_flags, s_err);
+    raise_error(P.err_flags, serr);
     SeqPlan pl;
     pl.j = bad ? -1 : j;
     pl.c_hi = c.hi;
@@ -499,33 +469,70 @@ __device__ void decide_seq(const ChainParams& P, int b) {
       pl.d_hi = 0.0f;
       pl.d_lo = 0.0f;
     }
-    pl.pad = 0.0f;
-    publish_plan(P, b, pl);
+    pl.valid = 1u;
+    P.plan[b] = pl;
   }
-  __syncthreads();
+  // Consumed: the sequence's statistics pieces and gathered logits go back
+  // to zero for the next call.
+  const int64_t per_seq = P.cps > 0 ? static_cast<int64_t>(P.cps) * P.kmax : static_cast<int64_t>(R) * P.nseg;
+  for (int64_t s = static_cast<int64_t>(b) * per_seq + tid; s < (static_cast<int64_t>(b) + 1) * per_seq; s += kThreads) {
+    P.part_m[s] = 0ull;
+    P.part_s[s] = 0ull;
+  }
+  if (tid < R) P.gat[static_cast<int64_t>(b) * R + tid] = 0ull;
 }
 
-}  // namespace
-
-// The decision, one block per sequence (the three-kernel schedule).
 template <class T>
-__global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
-  decide_seq<T>(P, blockIdx.x);
+struct SampleTiles;
+template <>
+struct SampleTiles<BF16> {
+  static constexpr int kPerBlock = kSampleTilesBF16;
+};
+template <>
+struct SampleTiles<F32> {
+  static constexpr int kPerBlock = kSampleTilesF32;
+};
+
+// 16-byte vectors holding one thread's kSampleEPT logits of a tile.
+template <class T>
+constexpr int kEptVecs = kSampleEPT / T::kVec;
+
+// Logits [e0, e0 + T::kVec) of a row packed as one raw 16-byte vector, -inf
+// beyond V (element loads: for rows off a 16-byte boundary and the tail).
+template <class T>
+__device__ __forceinline__ uint4 pack_elems(const void* row, int64_t e0, int V);
+template <>
+__device__ __forceinline__ uint4 pack_elems<BF16>(const void* row, int64_t e0, int V) {
+  const uint16_t* p = static_cast<const uint16_t*>(row);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (e0 + 2 * i < V) ? p[e0 + 2 * i] : 0xff80u;
+    const uint32_t hi = (e0 + 2 * i + 1 < V) ? p[e0 + 2 * i + 1] : 0xff80u;
+    w[i] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ uint4 pack_elems<F32>(const void* row, int64_t e0, int V) {
+  const uint32_t* p = static_cast<const uint32_t*>(row);
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = (e0 + i < V) ? p[e0 + i] : 0xff800000u;
+  return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-namespace {
-
-// The kSampleEPT logits of one thread in a tile, -inf beyond V.
+// One thread's kSampleEPT logits of a tile starting at element e0.
 template <class T>
-__device__ __forceinline__ void load_ept(const void* row, int64_t e0, int V, float (&x)[kSampleEPT]) {
+__device__ __forceinline__ void load_raw(const void* row, int64_t e0, int V, uint4 (&r)[kEptVecs<T>]) {
   const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0u;
   if (aligned && e0 + kSampleEPT <= V) {
-    const char* p = static_cast<const char*>(row) + e0 * T::kBytes;
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + e0 * T::kBytes);
 #pragma unroll
-    for (int v = 0; v < kSampleEPT / T::kVec; ++v) unpack<T>(load_vec(p + 16 * v), &x[v * T::kVec]);
+    for (int v = 0; v < kEptVecs<T>; ++v) r[v] = p[v];
   } else {
 #pragma unroll
-    for (int i = 0; i < kSampleEPT; ++i) x[i] = (e0 + i < V) ? load_elem<T>(row, e0 + i) : -INFINITY;
+    for (int v = 0; v < kEptVecs<T>; ++v) r[v] = pack_elems<T>(row, e0 + v * T::kVec, V);
   }
 }
 
@@ -536,55 +543,6 @@ struct SampleRows {
   float neg_lt_hi, neg_lt_lo;  // -L_t
   float neg_d_hi, neg_d_lo;    // -(L_d - L_t)
 };
-
-// One thread's kSampleEPT logits of a tile, for the target row and (when
-// sampling from the residual) the draft row.
-struct TileData {
-  float xt[kSampleEPT];
-  float xd[kSampleEPT];
-};
-
-template <class T>
-__device__ __forceinline__ void tile_load(const SampleRows& S, int64_t tile, int V, TileData& d) {
-  const int64_t e0 = tile * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
-  load_ept<T>(S.t, e0, V, d.xt);
-  if (S.d != nullptr) load_ept<T>(S.d, e0, V, d.xd);
-}
-
-// Weights of this thread's kSampleEPT tokens, and their running fp32 sum (the
-// same operations in the same order wherever it is called).
-//   bonus / p only:  w = p_t(v) = 2^(x_t c - L_t)
-//   residual:        w = p_t(v) * max(0, 1 - 2^((x_d - x_t) c - (L_d - L_t)))
-//                      = max(0, p_t(v) - p_d(v))
-// The ratio form keeps the exponent small exactly where p_t and p_d nearly
-// cancel, and any rounding common to all weights cancels in the draw.
-__device__ __forceinline__ float tile_compute(const SampleRows& S, const TileData& d, float (&w)[kSampleEPT]) {
-  float pt[kSampleEPT];
-#pragma unroll
-  for (int i = 0; i < kSampleEPT; ++i) pt[i] = fast_exp2(scaled_arg(d.xt[i], S.c, S.neg_lt_hi) + S.neg_lt_lo);
-  if (S.d != nullptr) {
-#pragma unroll
-    for (int i = 0; i < kSampleEPT; ++i) {
-      const float dx = d.xd[i] - d.xt[i];
-      const float ratio = fast_exp2(scaled_arg(dx, S.c, S.neg_d_hi) + S.neg_d_lo);
-      w[i] = pt[i] * fmaxf(1.0f - ratio, 0.0f);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kSampleEPT; ++i) w[i] = pt[i];
-  }
-  float run = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kSampleEPT; ++i) run += w[i];
-  return run;
-}
-
-template <class T>
-__device__ __forceinline__ float tile_weights(const SampleRows& S, int64_t tile, int V, float (&w)[kSampleEPT]) {
-  TileData d;
-  tile_load<T>(S, tile, V, d);
-  return tile_compute(S, d, w);
-}
 
 template <class T>
 __device__ __forceinline__ SampleRows sample_rows(const ChainParams& P, int b, const SeqPlan& pl, bool p_only) {
@@ -597,6 +555,46 @@ __device__ __forceinline__ SampleRows sample_rows(const ChainParams& P, int b, c
   S.neg_d_hi = -pl.d_hi;
   S.neg_d_lo = -pl.d_lo;
   return S;
+}
+
+// Weights of this thread's kSampleEPT tokens, and their running fp32 sum (the
+// same operations in the same order wherever it is called).
+//   bonus / p only:  w = p_t(v) = 2^(x_t c - L_t)
+//   residual:        w = p_t(v) * max(0, 1 - 2^((x_d - x_t) c - (L_d - L_t)))
+//                      = max(0, p_t(v) - p_d(v))
+// The ratio form keeps the exponent small exactly where p_t and p_d nearly
+// cancel, and any rounding common to all weights cancels in the draw.
+template <class T>
+__device__ __forceinline__ float tile_compute(const SampleRows& S, const uint4 (&rt)[kEptVecs<T>],
+                                              const uint4 (&rd)[kEptVecs<T>], float (&w)[kSampleEPT]) {
+  float xt[kSampleEPT];
+#pragma unroll
+  for (int v = 0; v < kEptVecs<T>; ++v) unpack<T>(rt[v], &xt[v * T::kVec]);
+#pragma unroll
+  for (int i = 0; i < kSampleEPT; ++i) w[i] = fast_exp2(scaled_arg(xt[i], S.c, S.neg_lt_hi) + S.neg_lt_lo);
+  if (S.d != nullptr) {
+    float xd[kSampleEPT];
+#pragma unroll
+    for (int v = 0; v < kEptVecs<T>; ++v) unpack<T>(rd[v], &xd[v * T::kVec]);
+#pragma unroll
+    for (int i = 0; i < kSampleEPT; ++i) {
+      const float ratio = fast_exp2(scaled_arg(xd[i] - xt[i], S.c, S.neg_d_hi) + S.neg_d_lo);
+      w[i] = w[i] * fmaxf(1.0f - ratio, 0.0f);
+    }
+  }
+  float run = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kSampleEPT; ++i) run += w[i];
+  return run;
+}
+
+template <class T>
+__device__ __forceinline__ float tile_weights(const SampleRows& S, int64_t tile, int V, float (&w)[kSampleEPT]) {
+  const int64_t e0 = tile * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
+  uint4 rt[kEptVecs<T>], rd[kEptVecs<T>] = {};
+  load_raw<T>(S.t, e0, V, rt);
+  if (S.d != nullptr) load_raw<T>(S.d, e0, V, rd);
+  return tile_compute<T>(S, rt, rd, w);
 }
 
 // Rescan tile `tile` of the sampling row: the first token (ascending id) with
@@ -627,8 +625,8 @@ __device__ int draw_in_tile(const SampleRows& Sr, int tile, double target, int V
   return (e >= 0) ? static_cast<int>(static_cast<int64_t>(tile) * kSampleTile + e) : -1;
 }
 
-// Draw the token: called by the last sampling block of sequence b, once every
-// block of the sequence has published its tile totals.
+// Draw the token: called by the last resolving workgroup of sequence b, once
+// every workgroup of the sequence has published its tile totals.
 template <class T>
 __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   __shared__ double s_scan[kWaves];
@@ -747,28 +745,39 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   }
 }
 
-// One sampling work item: tiles [4 blk, 4 blk + 4) of sequence b's row pair.
+// Sampling work item `blk` of sequence b: the weights of tiles
+// [blk * TPB, blk * TPB + TPB) of the sampling row pair, published as
+// per-tile totals; the last item of the sequence to arrive draws the token
+// and returns the sequence's sampling workspace (tile totals, plan, counter)
+// to zero.
 template <class T>
 __device__ void sample_item(const ChainParams& P, int b, int blk) {
-  constexpr int TPB = kSampleTilesPerBlock;
+  constexpr int TPB = SampleTiles<T>::kPerBlock;
+  constexpr int NV = kEptVecs<T>;
   __shared__ double s_red[TPB][kWaves];
   __shared__ int s_flag;
-  __shared__ uint32_t s_perr;
-  uint32_t perr = 0u;
-  const SeqPlan pl = await_plan(P, b, &perr);
-  if (threadIdx.x == 0) s_perr = perr;
+  const SeqPlan pl = P.plan[b];  // written by the decision launch
+  if (pl.valid == 0u) {
+    raise_error(P.err_flags, threadIdx.x == 0 ? kErrInternal : 0u);
+    return;
+  }
 
   if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
     const SampleRows S = sample_rows<T>(P, b, pl, false);
     const int t0 = blk * TPB;
-    TileData d[TPB];
+    uint4 rt[TPB][NV], rd[TPB][NV] = {};
 #pragma unroll
-    for (int i = 0; i < TPB; ++i)  // every load of the item in flight at once
-      if (t0 + i < P.ntiles) tile_load<T>(S, t0 + i, P.V, d[i]);
+    for (int i = 0; i < TPB; ++i) {  // every load of the item in flight at once
+      if (t0 + i < P.ntiles) {
+        const int64_t e0 = static_cast<int64_t>(t0 + i) * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
+        load_raw<T>(S.t, e0, P.V, rt[i]);
+        if (S.d != nullptr) load_raw<T>(S.d, e0, P.V, rd[i]);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < TPB; ++i) {
       float w[kSampleEPT];
-      const double part = (t0 + i < P.ntiles) ? wave_sum(static_cast<double>(tile_compute(S, d[i], w))) : 0.0;
+      const double part = (t0 + i < P.ntiles) ? wave_sum(static_cast<double>(tile_compute<T>(S, rt[i], rd[i], w))) : 0.0;
       if (lane_id() == 0) s_red[i][wave_id()] = part;
     }
     __syncthreads();
@@ -782,18 +791,37 @@ __device__ void sample_item(const ChainParams& P, int b, int blk) {
 
   if (!arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(P.nblk_b), &s_flag)) return;
   if (pl.j >= 0) chain_draw<T>(P, b, pl);
-  // Leave the workspace all zero for the next call, whatever its shape.
+  // Every workgroup of the sequence has read the plan and published its
+  // totals: leave the sequence's sampling workspace all zero.
   __syncthreads();
   if (pl.j >= 0)
     for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
-  if (threadIdx.x < kPlanWords) clear_slot(&P.plan_w[static_cast<int64_t>(b) * kPlanWords + threadIdx.x]);
-  if (threadIdx.x == 0) raise_error(P.err_flags, s_perr);
+  if (threadIdx.x == 0) P.plan[b] = SeqPlan{};
   reset_counter(&P.cnt[b]);
-  __syncthreads();
 }
 
 }  // namespace
 
+// Pass 1: one workgroup per statistics item (a chunk, or a row segment).
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_kernel(ChainParams P) {
+  const int64_t per_seq = P.cps > 0 ? P.cps : static_cast<int64_t>(2 * P.K + 1) * P.nseg;
+  const int64_t k = blockIdx.x;
+  const int b = static_cast<int>(k / per_seq);
+  const int rem = static_cast<int>(k % per_seq);
+  if (P.cps > 0)
+    stats_chunk<T>(P, b, rem);
+  else
+    stats_segment<T>(P, b, rem / P.nseg, rem % P.nseg);
+}
+
+// Pass 2: one workgroup per sequence.
+template <class T>
+__global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
+  decide_seq<T>(P, blockIdx.x);
+}
+
+// Pass 3: nblk_b workgroups per sequence.
 template <class T>
 __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
   sample_item<T>(P, blockIdx.x / P.nblk_b, blockIdx.x % P.nblk_b);
@@ -801,22 +829,23 @@ __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
 
 // ---------------------------------------------------------------- launcher
 
+int64_t chain_stats_items(const ChainParams& p) {
+  const int64_t stats_per_seq = p.cps > 0 ? p.cps : static_cast<int64_t>(2 * p.K + 1) * p.nseg;
+  return static_cast<int64_t>(p.B) * stats_per_seq;
+}
+
 template <class T>
 static hipError_t launch_chain_t(const ChainParams& p, hipStream_t stream) {
-  const int64_t R = 2 * static_cast<int64_t>(p.K) + 1;
-  const int64_t grid_a = p.fl_blocks > 0 ? p.fl_blocks : static_cast<int64_t>(p.B) * R * p.nseg;
-  const int64_t grid_b = static_cast<int64_t>(p.B) * p.nblk_b;
-  if (grid_a > INT32_MAX || grid_b > INT32_MAX) return hipErrorInvalidConfiguration;
-  if (p.fl_blocks > 0)
-    hipLaunchKernelGGL(chain_stats_flat_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, p);
-  else
-    hipLaunchKernelGGL(chain_stats_rows_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, p);
+  const int64_t grid_a = chain_stats_items(p);
+  const int64_t grid_c = static_cast<int64_t>(p.B) * p.nblk_b;
+  if (grid_a > INT32_MAX || grid_c > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(chain_stats_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chain_decide_kernel<T>, dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chain_sample_kernel<T>, dim3(static_cast<uint32_t>(grid_b)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(chain_sample_kernel<T>, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -205,6 +205,15 @@ __device__ __forceinline__ uint64_t await_slot(uint64_t* slot, uint32_t* err, ui
   return 0ull;
 }
 
+// A slot written by an earlier launch on the same stream: the kernel boundary
+// makes it visible, so a plain (cacheable) load suffices. A zero means it was
+// never written, which is reported as kErrInternal.
+__device__ __forceinline__ uint64_t load_ready(const uint64_t* slot, uint32_t* err) {
+  const uint64_t v = *slot;
+  if (v == 0ull) *err |= kErrInternal;
+  return v;
+}
+
 // Wait for the N consecutive slots base[0..N): every load is issued before
 // any value is inspected, so slots that are already written cost a single
 // memory round trip together.

@@ -11,8 +11,9 @@
 
 namespace sv {
 
-// Hand-off from the decision kernel to the sampling kernel, one per
-// sequence: which row pair to sample from and its normalisers.
+// The decision of one sequence as the sampling step needs it: which row pair
+// to draw from and the rows' normalisers (written by the decision kernel,
+// read by every sampling workgroup of the sequence).
 struct SeqPlan {
   int32_t j;     // first rejected position; K = bonus draw; -1 = invalid row
   float c_hi;    // log2(e) / T as an unevaluated fp32 sum c_hi + c_lo
@@ -21,10 +22,8 @@ struct SeqPlan {
   float lt_lo;   //   c, as lt_hi + lt_lo:  p_t(v) = 2^(x_t c - L_t)
   float d_hi;    // D = L_d - L_t as d_hi + d_lo:  p_d(v) / p_t(v) =
   float d_lo;    //   2^((x_d - x_t) c - D)    (unused for the bonus draw)
-  float pad;
+  uint32_t valid;  // 1 once written (the workspace is zero otherwise)
 };
-
-constexpr int kPlanWords = 8;  // 32-bit fields of a SeqPlan
 
 struct ChainParams {
   const void* target;
@@ -33,15 +32,22 @@ struct ChainParams {
   const float* temperature;
   const float* uniforms;
   int32_t B, K, V;
-  int32_t nseg;            // statistics segments per logit row (row layout)
-  int32_t seg_vecs;        // 16-byte vectors per statistics segment
-  int32_t fl_blocks;       // > 0: flattened layout with this many statistics blocks
-  int32_t fl_kmax;         //   row pieces per block (upper bound)
-  int64_t fl_nvec;         //   16-byte vectors per row
-  int64_t fl_per;          //   vectors per block
-  int32_t ntiles;          // sampling tiles per row (kSampleTile elements each)
-  int32_t tiles_per_block; // sampling tiles handled by one workgroup
-  int32_t nblk_b;          // sampling workgroups per sequence
+  // Statistics layout, one of:
+  //  chunked (every row on a 16-byte boundary): each sequence's 2K+1 rows,
+  //    concatenated, are cut into cps chunks of `per` 16-byte vectors; a chunk
+  //    publishes one piece per row it touches (at most kmax);
+  //  rows (any alignment): nseg segments of seg_vecs vectors per row.
+  int32_t cps;             // > 0: chunked layout
+  int32_t kmax;
+  int64_t nvec;            // 16-byte vectors per row (chunked layout)
+  int64_t per;
+  int32_t nseg;
+  int32_t seg_vecs;
+  // Sampling: nblk_b workgroups per sequence, each over tiles_per_block
+  // tiles of kSampleTile tokens.
+  int32_t ntiles;
+  int32_t tiles_per_block;
+  int32_t nblk_b;
   int32_t* accept_len;
   int32_t* out_tokens;
   float* p_draft;
@@ -50,11 +56,14 @@ struct ChainParams {
   int32_t* err_flags;
   // workspace (all zero between calls)
   uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi),
-                      // [B, 2K+1, nseg] (row layout) or [fl_blocks, fl_kmax]
+                      // [B, cps, kmax] (chunked) or [B, 2K+1, nseg] (rows)
   uint64_t* part_s;   // per row piece: tagged fp64 sum of 2^(x c - reference)
-  uint64_t* plan_w;   // [B, kPlanWords] tagged decision -> sampling hand-off
+  SeqPlan* plan;      // [B] decision -> sampling hand-off
   uint32_t* cnt;      // [B] sampling arrivals
   uint64_t* tile_sum; // [B, ntiles] tagged fp64 sampling weight per tile
+  uint64_t* gat;      // [B, 2K+1] tagged fp32 logit of row r at its drafted
+                      // token (rows 0..K-1 and K+1..2K; set by the pass that
+                      // streams the piece holding it)
   uint64_t* abort;    // [1] set when a bounded wait expires (drains the launch)
 };
 
@@ -76,23 +85,27 @@ struct TreeParams {
 
 constexpr int kSampleEPT = 8;                      // sampling elements per thread per tile
 constexpr int kSampleTile = 256 * kSampleEPT;      // elements per sampling tile
+// Tiles per resolving workgroup: 16 KB of each sampled row either way.
+constexpr int kSampleTilesBF16 = 4;
+constexpr int kSampleTilesF32 = 2;
 
-// Statistics segment: kThreads * kStatsUnroll * kStatsBatches vectors.
+// Statistics segment (rows layout): kThreads * kStatsUnroll * kStatsBatches vectors.
 constexpr int kStatsUnroll = 4;
 constexpr int kStatsBatches = 2;
 constexpr int kStatsSegVecs = 256 * kStatsUnroll * kStatsBatches;
-constexpr int kSampleTilesPerBlock = 4;
 
-// Flattened statistics layout: about this many chunks, each with at least
-// kFlatMinVecsPerBlock 16-byte vectors.
-#ifndef SV_FLAT_CHUNKS
-#define SV_FLAT_CHUNKS 4096
+// Chunked statistics layout: about this many chunks per call, each with at
+// least kChunkMinVecs 16-byte vectors.
+#ifndef SV_CHUNKS
+#define SV_CHUNKS 4096
 #endif
-constexpr int kFlatChunksTarget = SV_FLAT_CHUNKS;
-constexpr int kFlatMinVecsPerBlock = 256 * kStatsUnroll * 2;
+constexpr int kChunksTarget = SV_CHUNKS;
+constexpr int kChunkMinVecs = 256 * kStatsUnroll * 2;
 
 static_assert(kErrInternal == SV_ERRF_INTERNAL, "error bit mismatch");
 
+// Statistics work items of the call, and the three launches of a chain call.
+int64_t chain_stats_items(const ChainParams& p);
 hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, hipStream_t stream);
 hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
