@@ -1,21 +1,29 @@
-"""Throughput of chain speculative-sampling verification on one MI355X.
+"""Throughput of speculative-sampling verification on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload c2]
+                    [--no-cpu-baseline] [--cpu-seconds 12]
 
-One step = one sv_verify_chain call over one batch: B=64 sequences, K=5
-drafted tokens, V=128256, bf16 logits, temperature 0.7 (synthetic, seeded:
-target N(0, 2.5^2) plus a Zipf(1.1) log-prior, draft = target + N(0, 0.8^2)).
-Three independent input sets (3 x 180.6 MB) are rotated so that the 256 MB
-last-level cache cannot serve a step from the previous one; every input is
-resident in HBM before the timed region starts.
+Default workload (the headline line): one step = one sv_verify_chain call over
+one batch of B=64 sequences, K=5 drafted tokens, V=128256, bf16 logits,
+temperature 0.7 (synthetic, seeded: target N(0, 2.5^2) plus a Zipf(1.1)
+log-prior, draft = target + N(0, 0.8^2)). Three independent input sets
+(3 x 180.6 MB) are rotated so that the 256 MB last-level cache cannot serve a
+step from the previous one; every input is resident in HBM before the timed
+region starts. Other workloads (--workload c1, c3_s0.3, c3_s1.0, c3_s3.0, c5,
+c4) print a line of the same form; c5 rotates its ten iterations (one set of
+logits, fresh uniforms each), c4 is the greedy tree call.
 
-Prints one JSON line: the metric (rows x vocab elements verified per second),
-the whole-call time, the roofline of the call against MI355X's 8 TB/s HBM
-peak, and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: rows x vocab elements verified per second over the
+whole call, the roofline of the dominant kernel (the streaming pass, timed
+with HIP events the library records around that one kernel) against MI355X's
+8 TB/s HBM peak, its HBM traffic from committed rocprofv3 counter runs (when
+the kernel sources still match the ones counted), and the CPU oracle timed on
+a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +35,12 @@ sys.path.insert(0, ROOT)
 METRIC = "verify throughput: rows·vocab/s + HBM GB/s vs peak, B=64 K=5 V=128256 bf16"
 HBM_PEAK_GBS = 8000.0
 N_SETS = 3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "rejection_sampling_verification_sv_amd", "csrc")
+KERNEL_SOURCES = {
+    "chain": ["sv_chain.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
+    "tree": ["sv_tree.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
+}
 
 
 def parse():
@@ -34,46 +48,101 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c2", help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain) or c4 (tree)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle sample's CPU time")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle sample's wall time")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run three plain device-to-device copies of MIB MiB (untimed), the known-size "
+                         "kernel that scales hardware traffic counters")
     return ap.parse_args()
 
 
-def cpu_baseline(inp_cpu: dict, cfg, budget_s: float) -> dict:
-    """The float64 numpy oracle, timed on repeated passes over the same workload.
+def sources_sha256(kind: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
-    Sequences are verified four at a time, in order, wrapping around the batch,
-    until about `budget_s` seconds of wall time have been spent.
-    """
+
+def counted_traffic(workload: str, kind: str):
+    """HBM bytes per launch of the streaming kernel from the committed counter
+    runs (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration), or
+    None when there are none or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources_sha256") != sources_sha256(kind):
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def _timed_oracle(jobs, budget_s: float):
+    """Run oracle jobs (each a (prepare, run, count) triple) in order, wrapping
+    around, until about `budget_s` seconds have been spent inside `run`; the
+    input conversion in `prepare` is not timed. Returns (items, wall, cpu)."""
+    import torch
+
+    threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        done = wall = cpu = 0.0
+        i = 0
+        while wall < budget_s:
+            prepare, run, count = jobs[i % len(jobs)]
+            args = prepare()
+            t0, c0 = time.perf_counter(), os.times()
+            run(*args)
+            t1, c1 = time.perf_counter(), os.times()
+            wall += t1 - t0
+            cpu += (c1.user - c0.user) + (c1.system - c0.system)
+            done += count
+            i += 1
+    finally:
+        torch.set_num_threads(threads)
+    return int(done), wall, cpu
+
+
+def cpu_baseline_chain(inp, cfg, budget_s: float) -> dict:
+    """The float64 numpy oracle on the same workload: sequences four at a time,
+    in order, wrapping around the batch, for about `budget_s` seconds."""
     import oracle
 
-    t = inp_cpu["target"].double().numpy()
-    d = inp_cpu["draft"].double().numpy()
-    x = inp_cpu["draft_tokens"].numpy().astype("int64")
-    T = inp_cpu["temperature"].double().numpy()
-    u = inp_cpu["uniforms"].double().numpy()
-    chunk = 4
-    done = 0
-    t0 = time.perf_counter()
-    c0 = os.times()
-    while True:
-        s0 = done % cfg.B
-        s = slice(s0, min(cfg.B, s0 + chunk))
-        oracle.verify_chain(t[s], d[s], x[s], T[s], u[s])
-        done += s.stop - s.start
-        if time.perf_counter() - t0 > budget_s:
-            break
-    wall = time.perf_counter() - t0
-    c1 = os.times()
-    cpu = (c1.user - c0.user) + (c1.system - c0.system)
-    elems = done * (2 * cfg.K + 1) * cfg.V
+    jobs = []
+    for s0 in range(0, cfg.B, 4):
+        s = slice(s0, min(cfg.B, s0 + 4))
+        jobs.append((lambda s=s: (inp["target"][s].double().numpy(), inp["draft"][s].double().numpy(),
+                                  inp["draft_tokens"][s].numpy().astype("int64"),
+                                  inp["temperature"][s].double().numpy(), inp["uniforms"][s].double().numpy()),
+                     oracle.verify_chain, s.stop - s.start))
+    done, wall, cpu = _timed_oracle(jobs, budget_s)
     return {
-        "value": elems / wall,
+        "value": done * (2 * cfg.K + 1) * cfg.V / wall,
         "unit": "rows·vocab/s",
         "cores": max(1, round(cpu / wall)),
         "kind": "oracle",
-        "sample": f"{done} sequences ({done / cfg.B:.1f} passes over the {cfg.B}-sequence batch) of the same "
-                  f"workload, float64 numpy, {wall:.1f} s wall, {cpu:.1f} s CPU",
+        "sample": f"{done} sequences ({done / cfg.B:.2f} passes over the {cfg.B}-sequence batch) of the same "
+                  f"workload, float64 numpy, {wall:.1f} s in the oracle, {cpu:.1f} s CPU",
+    }
+
+
+def cpu_baseline_tree(inp, cfg, budget_s: float) -> dict:
+    """The oracle's greedy tree verification, one sequence at a time."""
+    import oracle
+
+    parents = inp["parents"].numpy()
+    jobs = [(lambda b=b: (inp["target"][b:b + 1].float().numpy(), inp["node_tokens"][b:b + 1].numpy(), parents),
+             oracle.verify_tree_greedy, 1) for b in range(cfg.B)]
+    done, wall, cpu = _timed_oracle(jobs, budget_s)
+    return {
+        "value": done * (cfg.N + 1) * cfg.V / wall,
+        "unit": "rows·vocab/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"{done} sequences ({done / cfg.B:.2f} passes over the {cfg.B}-sequence batch) of the same "
+                  f"workload, numpy argmax, {wall:.1f} s in the oracle, {cpu:.1f} s CPU",
     }
 
 
@@ -87,52 +156,99 @@ def main():
     import torch
 
     import rejection_sampling_verification_sv_amd as sv
-    from workloads import CHAIN_CONFIGS, chain_inputs
+    from workloads import CHAIN_CONFIGS, TREE_CONFIGS, chain_inputs, chain_uniforms, tree_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     sv.library()
     dev = torch.device("cuda:0")
-    cfg = CHAIN_CONFIGS["c2"]
-    sets = []
-    for i in range(N_SETS):
-        c = cfg.with_(variant=10 + i) if i else cfg
-        sets.append(chain_inputs(c, device=dev))
-    torch.cuda.synchronize()
-
-    B, K, V = cfg.B, cfg.K, cfg.V
-    elems = B * (2 * K + 1) * V
-    alg_bytes = elems * 2 + B * K * 4 + B * (K + 1) * 4 + B * 4  # logits + tokens + uniforms + temperature
     stream = torch.cuda.current_stream(dev)
-
-    # every argument marshalled once; a step only enqueues the kernels
-    calls = [sv.PreparedChainCall(s["target"], s["draft"], s["draft_tokens"], s["temperature"], s["uniforms"],
-                                  stream=stream) for s in sets]
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    wl = args.workload
+    kind = "tree" if wl in TREE_CONFIGS else "chain"
+    if kind == "chain":
+        cfg = CHAIN_CONFIGS[wl]
+        B, K, V = cfg.B, cfg.K, cfg.V
+        rows = B * (2 * K + 1)
+        eb = 2 if cfg.dtype == "bf16" else 4
+        sets = []
+        if cfg.iterations > 1:  # one set of logits, fresh uniforms per iteration
+            base = chain_inputs(cfg, device=dev)
+            for it in range(cfg.iterations):
+                s = dict(base)
+                s["uniforms"] = chain_uniforms(cfg, iteration=it, device=dev)
+                sets.append(s)
+        else:
+            for i in range(N_SETS):
+                sets.append(chain_inputs(cfg.with_(variant=cfg.variant + 10 * i) if i else cfg, device=dev))
+        calls = [sv.PreparedChainCall(s["target"], s["draft"], s["draft_tokens"], s["temperature"], s["uniforms"],
+                                      stream=stream) for s in sets]
+        # every logit once, plus tokens (gathered by the stream), uniforms and temperatures
+        stream_bytes = rows * V * eb + B * K * 4
+        call_bytes = stream_bytes + B * (K + 1) * 4 + B * 4
+        config = {"workload": cfg.name, "B": B, "K": K, "V": V, "logits": cfg.dtype,
+                  "temperature": cfg.temperature if cfg.temperature is not None else list(cfg.temperature_range),
+                  "input_sets_rotated": len(sets)}
+        kernel_name = "chain_stats_kernel (statistics pass: every logit row once)"
+    else:
+        cfg = TREE_CONFIGS[wl]
+        B, N, V = cfg.B, cfg.N, cfg.V
+        rows = B * (N + 1)
+        eb = 2 if cfg.dtype == "bf16" else 4
+        sets = [tree_inputs(cfg.with_(variant=cfg.variant + 10 * i) if i else cfg, device=dev)
+                for i in range(N_SETS)]
+        calls = [sv.PreparedTreeCall(s["target"], s["node_tokens"], s["parents"], stream=stream) for s in sets]
+        stream_bytes = rows * V * eb
+        call_bytes = stream_bytes + B * N * 4 + N * 4
+        config = {"workload": cfg.name, "B": B, "N": N, "V": V, "logits": cfg.dtype,
+                  "branching": list(cfg.branching), "input_sets_rotated": len(sets)}
+        kernel_name = "tree_argmax_kernel (argmax pass with the path decision of the last workgroup)"
+    elems = rows * V
     torch.cuda.synchronize()
-
-    def step(i):
-        calls[i % N_SETS]()
+    nsets = len(calls)
 
     for i in range(args.warmup):
-        step(i)
+        calls[i % nsets]()
     torch.cuda.synchronize()
 
-    # per-call events on the library's stream (torch's current stream)
+    # Timed region: K steps, events around each call on the library's stream.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
-        step(i)
+        calls[i % nsets]()
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
-    per_call_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     total_ms = ev[0].elapsed_time(ev[-1])
     ms_per_step = total_ms / args.steps
-    per_call_ms.sort()
-    med_ms = per_call_ms[len(per_call_ms) // 2]
+    per_call_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
 
-    # warm reference: the same input set every call (last-level cache may serve it)
+    # Kernel region: the same K steps again, each call's streaming kernel
+    # launched with a start / stop event pair (its own dispatch timestamps).
+    # Kept apart from the timed region: an armed launch delays the next kernel
+    # by a few microseconds.
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in kev:  # create the events on the device before arming them
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        sv.sv_time_next_stream_pass(*kev[i])
+        calls[i % nsets]()
+    torch.cuda.synchronize()
+    kern_ms = [a.elapsed_time(b) for a, b in kev]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    kern_sorted = sorted(kern_ms)
+
+    # warm reference: the same input set every call (the last-level cache may serve it)
     for _ in range(5):
         calls[0]()
     w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -146,9 +262,10 @@ def main():
     flags = sum(int(c.out["err_flags"].item()) for c in calls)
     assert flags == 0, f"device error flags {flags}"
 
-    achieved = alg_bytes / (med_ms * 1e-3) / 1e9
+    achieved = stream_bytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = counted_traffic(wl, kind)
     result = {
-        "metric": METRIC,
+        "metric": METRIC if wl == "c2" else f"verify throughput: rows·vocab/s + HBM GB/s vs peak, {cfg.name}",
         "value": elems / (ms_per_step * 1e-3),
         "unit": "rows·vocab/s",
         "n_gpus": 1,
@@ -160,28 +277,32 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {
-            "workload": cfg.name,
-            "B": B, "K": K, "V": V, "logits": "bf16", "temperature": cfg.temperature,
-            "input_sets_rotated": N_SETS,
-        },
+        "config": config,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
-            "kernel": "whole sv_verify_chain call (stats + sampling kernels)",
-            "duration_us_median": med_ms * 1e3,
+            "traffic": traffic,
+            "kernel": kernel_name,
+            "algorithmic_bytes_per_launch": stream_bytes,
+            "duration_us_avg": kern_avg_ms * 1e3,
+            "duration_us_median": kern_sorted[len(kern_sorted) // 2] * 1e3,
+            "timing": "launch start/stop events of the streaming kernel over a second pass of the same steps",
         },
-        "hbm_gbs_per_step": alg_bytes / (ms_per_step * 1e-3) / 1e9,
+        "call_us_median": per_call_ms[len(per_call_ms) // 2] * 1e3,
+        "call_hbm_gbs": call_bytes / (ms_per_step * 1e-3) / 1e9,
+        "call_frac_of_peak": call_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "warm_same_inputs_us": warm_ms * 1e3,
         "wall_s_timed": t_wall,
     }
     if not args.no_cpu_baseline:
         cpu_inp = {k: v.cpu() for k, v in sets[0].items()}
-        result["cpu_baseline"] = cpu_baseline(cpu_inp, cfg, args.cpu_seconds)
+        if kind == "chain":
+            result["cpu_baseline"] = cpu_baseline_chain(cpu_inp, cfg, args.cpu_seconds)
+        else:
+            result["cpu_baseline"] = cpu_baseline_tree(cpu_inp, cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

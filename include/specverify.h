@@ -57,8 +57,9 @@
 extern "C" {
 #endif
 
-/* The HIP runtime's stream handle (identical to its own declaration). */
+/* The HIP runtime's stream and event handles (identical to its own declarations). */
 typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
 
 typedef enum sv_status {
   SV_OK = 0,
@@ -203,6 +204,25 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype,
  */
 sv_status sv_build_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Profiling hook (not part of the verification contract).
+ *
+ * Arms the calling host thread's NEXT sv_verify_chain or sv_verify_tree_greedy
+ * call to launch its streaming pass (the kernel that reads every logit once:
+ * chain statistics, tree argmax) with `before` and `after` as the launch's
+ * start and stop events (hipExtLaunchKernel), so that they carry that kernel's
+ * own start and end timestamps; the call then disarms the hook. A call that
+ * fails its argument checks records nothing and also disarms it.
+ * hipEventElapsedTime(before, after) is then that one kernel's duration.
+ *
+ *   before, after  hipEvent_t handles created by the caller (both non-NULL),
+ *                  or both NULL to disarm
+ *
+ * Returns SV_ERR_INVALID_ARGUMENT if exactly one is NULL. The armed pair is
+ * the only mutable state the library keeps, and it is per host thread.
+ */
+sv_status sv_time_next_stream_pass(hipEvent_t before, hipEvent_t after);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,7 @@ ctypes binding. Build with ``python -m rejection_sampling_verification_sv_amd.bu
 """
 from .specverify import (  # noqa: F401
     PreparedChainCall,
+    PreparedTreeCall,
     SpecVerifyError,
     SV_DTYPE_BF16,
     SV_DTYPE_F32,
@@ -19,6 +20,7 @@ from .specverify import (  # noqa: F401
     sv_build_tree_mask,
     sv_chain_workspace_bytes,
     sv_status_string,
+    sv_time_next_stream_pass,
     sv_tree_workspace_bytes,
     sv_verify_chain,
     sv_verify_tree_greedy,

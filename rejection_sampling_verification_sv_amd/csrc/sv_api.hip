@@ -106,7 +106,15 @@ bool aligned_to(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(
 
 sv_status from_hip(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
+thread_local sv::PassEvents g_pass_events{nullptr, nullptr};
+
 }  // namespace
+
+sv::PassEvents sv::take_pass_events() {
+  const PassEvents e = g_pass_events;
+  g_pass_events = PassEvents{nullptr, nullptr};
+  return e;
+}
 
 extern "C" {
 
@@ -136,6 +144,7 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
                           int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
                           float* p_draft, float* q_draft, float* residual_mass, int32_t* err_flags,
                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const sv::PassEvents ev = sv::take_pass_events();
   if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return SV_ERR_INVALID_ARGUMENT;
   if (B == 0) return SV_OK;
   if (target_logits == nullptr || uniforms == nullptr || accept_len == nullptr || out_tokens == nullptr)
@@ -183,7 +192,7 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
 
   if (sv::chain_stats_items(p) > INT32_MAX || static_cast<int64_t>(B) * p.nblk_b > INT32_MAX) return SV_ERR_UNSUPPORTED;
-  return from_hip(sv::launch_chain(p, dtype, stream));
+  return from_hip(sv::launch_chain(p, dtype, ev, stream));
 }
 
 size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype) {
@@ -195,6 +204,7 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
                                 const int32_t* parents, int32_t B, int32_t N, int32_t V, int32_t* accept_len,
                                 int32_t* path_nodes, int32_t* next_token, int32_t* err_flags, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
+  const sv::PassEvents ev = sv::take_pass_events();
   if (!dtype_ok(dtype) || !tree_sizes_ok(B, N, V)) return SV_ERR_INVALID_ARGUMENT;
   if (B == 0) return SV_OK;
   if (target_logits == nullptr || node_tokens == nullptr || parents == nullptr || accept_len == nullptr ||
@@ -222,7 +232,13 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
   p.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
   p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
   p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
-  return from_hip(sv::launch_tree(p, dtype, stream));
+  return from_hip(sv::launch_tree(p, dtype, ev, stream));
+}
+
+sv_status sv_time_next_stream_pass(hipEvent_t before, hipEvent_t after) {
+  if ((before == nullptr) != (after == nullptr)) return SV_ERR_INVALID_ARGUMENT;
+  g_pass_events = sv::PassEvents{before, after};
+  return SV_OK;
 }
 
 sv_status sv_build_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,

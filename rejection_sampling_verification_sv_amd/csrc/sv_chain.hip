@@ -32,6 +32,7 @@
 //      "Speculative Decoding at Scale", section 1; [Draft-and-Verify]
 //      "Speculative Decoding for LLM Inference", "The draft-and-verify loop"
 //      (the bonus token when every proposal is kept).
+#include <hip/hip_ext.h>
 #include <math.h>
 
 #include "sv_device.h"
@@ -835,11 +836,13 @@ int64_t chain_stats_items(const ChainParams& p) {
 }
 
 template <class T>
-static hipError_t launch_chain_t(const ChainParams& p, hipStream_t stream) {
+static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hipStream_t stream) {
   const int64_t grid_a = chain_stats_items(p);
   const int64_t grid_c = static_cast<int64_t>(p.B) * p.nblk_b;
   if (grid_a > INT32_MAX || grid_c > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(chain_stats_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, p);
+  // Armed events take the statistics kernel's own start and end timestamps.
+  hipExtLaunchKernelGGL(chain_stats_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream,
+                        ev.before, ev.after, 0u, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chain_decide_kernel<T>, dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, stream, p);
@@ -849,8 +852,8 @@ static hipError_t launch_chain_t(const ChainParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, hipStream_t stream) {
-  return dtype == SV_DTYPE_BF16 ? launch_chain_t<BF16>(p, stream) : launch_chain_t<F32>(p, stream);
+hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream) {
+  return dtype == SV_DTYPE_BF16 ? launch_chain_t<BF16>(p, ev, stream) : launch_chain_t<F32>(p, ev, stream);
 }
 
 }  // namespace sv

@@ -104,10 +104,19 @@ constexpr int kChunkMinVecs = 256 * kStatsUnroll * 2;
 
 static_assert(kErrInternal == SV_ERRF_INTERNAL, "error bit mismatch");
 
+// Events armed by sv_time_next_stream_pass for the calling thread's next
+// call; take_pass_events() returns them and disarms the hook.
+struct PassEvents {
+  hipEvent_t before;
+  hipEvent_t after;
+};
+PassEvents take_pass_events();
+
 // Statistics work items of the call, and the three launches of a chain call.
 int64_t chain_stats_items(const ChainParams& p);
-hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, hipStream_t stream);
-hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, hipStream_t stream);
+// `ev` (possibly null events) brackets the streaming pass of the call.
+hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
+hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
                             hipStream_t stream);
 

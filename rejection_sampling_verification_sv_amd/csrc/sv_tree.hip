@@ -23,6 +23,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <hip/hip_ext.h>
+
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -283,15 +285,17 @@ __global__ __launch_bounds__(kThreads) void tree_mask_kernel(const int32_t* pare
 }
 
 template <class T>
-static hipError_t launch_tree_t(const TreeParams& p, hipStream_t stream) {
+static hipError_t launch_tree_t(const TreeParams& p, const PassEvents& ev, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(p.B) * (p.N + 1) * p.nseg;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(tree_argmax_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream, p);
+  // Armed events take the kernel's own start and end timestamps.
+  hipExtLaunchKernelGGL(tree_argmax_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+                        ev.before, ev.after, 0u, p);
   return hipGetLastError();
 }
 
-hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, hipStream_t stream) {
-  return dtype == SV_DTYPE_BF16 ? launch_tree_t<BF16>(p, stream) : launch_tree_t<F32>(p, stream);
+hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream) {
+  return dtype == SV_DTYPE_BF16 ? launch_tree_t<BF16>(p, ev, stream) : launch_tree_t<F32>(p, ev, stream);
 }
 
 hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,

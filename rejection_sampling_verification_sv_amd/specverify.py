@@ -72,6 +72,8 @@ def _load():
         lib.sv_verify_tree_greedy.restype = ctypes.c_int
         lib.sv_build_tree_mask.argtypes = [_c_ptr, _c_i32, _c_ptr, _c_ptr, _c_ptr]
         lib.sv_build_tree_mask.restype = ctypes.c_int
+        lib.sv_time_next_stream_pass.argtypes = [_c_ptr, _c_ptr]
+        lib.sv_time_next_stream_pass.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -119,6 +121,25 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 def _stream_handle(device, stream) -> int:
     s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
+
+
+def sv_time_next_stream_pass(before: Optional[torch.cuda.Event], after: Optional[torch.cuda.Event]) -> None:
+    """Arm this thread's next chain / tree call to launch its streaming pass with
+    ``before`` and ``after`` as start / stop events (both None disarms).
+
+    The events must be timing events that exist on the device already (recorded
+    at least once); ``before.elapsed_time(after)`` then gives that kernel's
+    duration once the stream has run past it.
+    """
+    if (before is None) != (after is None):
+        raise ValueError("pass both events or neither")
+    handles = [None, None]
+    if before is not None:
+        for i, e in enumerate((before, after)):
+            if not e.cuda_event:
+                raise ValueError("record each event once before arming it (the handle is created lazily)")
+            handles[i] = e.cuda_event
+    _check(_load().sv_time_next_stream_pass(handles[0], handles[1]), "sv_time_next_stream_pass")
 
 
 # Zero-filled workspaces, one per (device, stream): the library returns every
@@ -276,4 +297,38 @@ class PreparedChainCall:
         st = self._fn(*self._args)
         if st != SV_OK:
             _check(st, "sv_verify_chain")
+        return self.out
+
+
+class PreparedTreeCall:
+    """``sv_verify_tree_greedy`` with every argument checked and marshalled once
+    (the tree counterpart of :class:`PreparedChainCall`)."""
+
+    def __init__(self, target, node_tokens, parents, *, stream=None):
+        B, N1, V = target.shape
+        N = N1 - 1
+        dev = target.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.out = {
+            "accept_len": torch.empty((B,), **i32),
+            "path_nodes": torch.empty((B, N), **i32),
+            "next_token": torch.empty((B,), **i32),
+            "err_flags": torch.zeros((1,), **i32),
+        }
+        sv_verify_tree_greedy(target, node_tokens, parents, stream=stream, **self.out)
+        lib = _load()
+        code = _dtype_code(target)
+        self._ws = workspace(dev, int(lib.sv_tree_workspace_bytes(B, N, V, code)), stream)
+        self._keep = (target, node_tokens, parents)
+        o = self.out
+        self._fn = lib.sv_verify_tree_greedy
+        self._args = (
+            _ptr(target), code, _ptr(node_tokens), _ptr(parents), B, N, V,
+            _ptr(o["accept_len"]), _ptr(o["path_nodes"]), _ptr(o["next_token"]), _ptr(o["err_flags"]),
+            _ptr(self._ws), self._ws.numel(), _stream_handle(dev, stream))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SV_OK:
+            _check(st, "sv_verify_tree_greedy")
         return self.out

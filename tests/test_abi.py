@@ -103,3 +103,18 @@ def test_tree_and_mask_argument_errors(lib):
     assert lib.sv_build_tree_mask(None, 4, FAKE, None, None) == INV
     assert lib.sv_build_tree_mask(FAKE, 0, FAKE, None, None) == INV
     assert lib.sv_build_tree_mask(FAKE, 1025, FAKE, None, None) == INV
+
+
+def test_stream_pass_hook_arguments(lib):
+    INV = 1
+    f = lib.sv_time_next_stream_pass
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert f(FAKE, None) == INV
+    assert f(None, FAKE) == INV
+    # arming and disarming touch no event (the handles are only used at launch)
+    assert f(FAKE, FAKE + 64) == 0
+    assert f(None, None) == 0
+    # a call that fails its argument checks also disarms the hook
+    assert f(FAKE, FAKE + 64) == 0
+    assert _chain(lib, t=None) == INV
+    assert f(None, None) == 0

@@ -15,6 +15,8 @@ from .synth import (  # noqa: F401
     MC_CONFIG,
     seed_stream,
     chain_inputs,
+    chain_uniforms,
+    chain_temperatures,
     mc_chain_inputs,
     tree_parents_ranked,
     tree_inputs,
