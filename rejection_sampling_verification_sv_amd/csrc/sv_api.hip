@@ -25,39 +25,51 @@ int32_t stats_segments(int32_t V, sv_dtype d) {
   return static_cast<int32_t>(n < 1 ? 1 : n);
 }
 
+// A streaming pass over B sequences of `rows` rows of V elements, cut into
+// work items; `chunked` (rows of whole 16-byte vectors on 16-byte
+// boundaries) selects the chunked layout: about kChunksTarget chunks over the
+// call, each of at least kChunkMinVecs vectors, the same number per sequence.
+sv::PieceLayout piece_layout(int64_t B, int32_t rows, int32_t V, sv_dtype d, bool chunked) {
+  sv::PieceLayout L{};
+  L.rows = rows;
+  L.nseg = stats_segments(V, d);
+  L.seg_vecs = sv::kStatsSegVecs;
+  if (chunked) {
+    const int64_t nvec = static_cast<int64_t>(V) * dtype_bytes(d) / 16;
+    const int64_t seq_vecs = rows * nvec;
+    int64_t p = ceil_div(B * seq_vecs, sv::kChunksTarget);
+    if (p < sv::kChunkMinVecs) p = sv::kChunkMinVecs;
+    L.cps = static_cast<int32_t>(ceil_div(seq_vecs, p));
+    L.per = ceil_div(seq_vecs, L.cps);
+    L.nvec = nvec;
+    L.kmax = static_cast<int32_t>((L.per + nvec - 2) / nvec + 1);
+  }
+  return L;
+}
+
+bool whole_vector_rows(int32_t V, sv_dtype d) { return (static_cast<int64_t>(V) * dtype_bytes(d)) % 16 == 0; }
+
+// Slots the pass needs under either layout (the workspace does not depend on
+// the alignment of the logits the call is made with).
+int64_t piece_slots(int64_t B, int32_t rows, int32_t V, sv_dtype d) {
+  const int64_t seg = B * sv::slots_per_seq(piece_layout(B, rows, V, d, false));
+  if (!whole_vector_rows(V, d) || B == 0) return seg;
+  const int64_t ch = B * sv::slots_per_seq(piece_layout(B, rows, V, d, true));
+  return ch > seg ? ch : seg;
+}
+
 struct ChainLayout {
-  int32_t nseg, ntiles, tiles_per_block, nblk_b;
-  int32_t cps, kmax;  // chunked statistics layout (rows of whole 16-byte vectors)
-  int64_t nvec, per;
+  int32_t ntiles, tiles_per_block, nblk_b;
   size_t off_part_m, off_part_s, off_plan, off_cnt, off_tiles, off_gat, off_abort, total;
 };
 
-// Chunked layout: each sequence's rows cut into cps equal chunks, about
-// kChunksTarget chunks over the call, each of at least kChunkMinVecs vectors.
-void chunk_layout(int64_t B, int64_t R, int64_t nvec, ChainLayout* L) {
-  const int64_t seq_vecs = R * nvec;
-  int64_t p = ceil_div(B * seq_vecs, sv::kChunksTarget);
-  if (p < sv::kChunkMinVecs) p = sv::kChunkMinVecs;
-  L->cps = static_cast<int32_t>(ceil_div(seq_vecs, p));
-  L->per = ceil_div(seq_vecs, L->cps);
-  L->nvec = nvec;
-  L->kmax = static_cast<int32_t>((L->per + nvec - 2) / nvec + 1);
-}
-
 ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   ChainLayout L{};
-  const int64_t R = 2 * static_cast<int64_t>(K) + 1;
-  L.nseg = stats_segments(V, d);
+  const int32_t R = 2 * K + 1;
   L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
   L.tiles_per_block = d == SV_DTYPE_BF16 ? sv::kSampleTilesBF16 : sv::kSampleTilesF32;
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
-  int64_t parts = static_cast<int64_t>(B) * R * L.nseg;
-  const int64_t row_bytes = static_cast<int64_t>(V) * dtype_bytes(d);
-  if (row_bytes % 16 == 0 && B > 0) {
-    chunk_layout(B, R, row_bytes / 16, &L);
-    const int64_t ch_parts = static_cast<int64_t>(B) * L.cps * L.kmax;
-    if (ch_parts > parts) parts = ch_parts;
-  }
+  const int64_t parts = piece_slots(B, R, V, d);
   size_t off = 0;
   L.off_part_m = off;
   off = align_up(off + sizeof(uint64_t) * parts);
@@ -78,21 +90,14 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
 }
 
 struct TreeLayout {
-  int32_t nseg;
-  size_t off_part, off_cnt, off_abort, total;
+  size_t off_part, total;
 };
 
 TreeLayout tree_layout(int32_t B, int32_t N, int32_t V, sv_dtype d) {
   TreeLayout L{};
-  L.nseg = stats_segments(V, d);
-  const int64_t parts = static_cast<int64_t>(B) * (N + 1) * L.nseg;
   size_t off = 0;
   L.off_part = off;
-  off = align_up(off + sizeof(uint64_t) * parts);
-  L.off_cnt = off;
-  off = align_up(off + sizeof(uint32_t) * B);
-  L.off_abort = off;
-  off = align_up(off + sizeof(uint64_t));
+  off = align_up(off + sizeof(uint64_t) * piece_slots(B, N + 1, V, d));
   L.total = off;
   return L;
 }
@@ -165,15 +170,10 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.B = B;
   p.K = K;
   p.V = V;
-  // The chunked statistics layout needs every row on a 16-byte boundary;
-  // otherwise the rows layout.
-  const bool chunked = L.cps > 0 && aligned_to(target_logits, 16) && (K == 0 || aligned_to(draft_logits, 16));
-  p.cps = chunked ? L.cps : 0;
-  p.kmax = L.kmax;
-  p.nvec = L.nvec;
-  p.per = L.per;
-  p.nseg = L.nseg;
-  p.seg_vecs = sv::kStatsSegVecs;
+  // The chunked layout needs every row on a 16-byte boundary.
+  const bool chunked = whole_vector_rows(V, dtype) && aligned_to(target_logits, 16) &&
+                       (K == 0 || aligned_to(draft_logits, 16));
+  p.L = piece_layout(B, 2 * K + 1, V, dtype, chunked);
   p.ntiles = L.ntiles;
   p.tiles_per_block = L.tiles_per_block;
   p.nblk_b = L.nblk_b;
@@ -191,7 +191,8 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.gat = reinterpret_cast<uint64_t*>(ws + L.off_gat);
   p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
 
-  if (sv::chain_stats_items(p) > INT32_MAX || static_cast<int64_t>(B) * p.nblk_b > INT32_MAX) return SV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(B) * sv::items_per_seq(p.L) > INT32_MAX || static_cast<int64_t>(B) * p.nblk_b > INT32_MAX)
+    return SV_ERR_UNSUPPORTED;
   return from_hip(sv::launch_chain(p, dtype, ev, stream));
 }
 
@@ -213,7 +214,6 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
   if (!aligned_to(target_logits, dtype_bytes(dtype))) return SV_ERR_INVALID_ARGUMENT;
   const TreeLayout L = tree_layout(B, N, V, dtype);
   if (workspace == nullptr || workspace_bytes < L.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
-  if (static_cast<int64_t>(B) * (N + 1) * L.nseg > INT32_MAX) return SV_ERR_UNSUPPORTED;
 
   char* ws = static_cast<char*>(workspace);
   sv::TreeParams p{};
@@ -223,15 +223,13 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
   p.B = B;
   p.N = N;
   p.V = V;
-  p.nseg = L.nseg;
-  p.seg_vecs = sv::kStatsSegVecs;
+  p.L = piece_layout(B, N + 1, V, dtype, whole_vector_rows(V, dtype) && aligned_to(target_logits, 16));
+  if (static_cast<int64_t>(B) * sv::items_per_seq(p.L) > INT32_MAX) return SV_ERR_UNSUPPORTED;
   p.accept_len = accept_len;
   p.path_nodes = path_nodes;
   p.next_token = next_token;
   p.err_flags = err_flags;
   p.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
-  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
-  p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
   return from_hip(sv::launch_tree(p, dtype, ev, stream));
 }
 

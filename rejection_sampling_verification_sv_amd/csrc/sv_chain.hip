@@ -143,18 +143,6 @@ __device__ __forceinline__ void block_combine(const Running& st, Scale c, float*
   *S = block_sum(sd, s_redd);
 }
 
-// 16 bytes of -inf logits (a padding vector contributes exactly 0).
-template <class T>
-__device__ __forceinline__ uint4 neg_inf_vec();
-template <>
-__device__ __forceinline__ uint4 neg_inf_vec<BF16>() {
-  return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-}
-template <>
-__device__ __forceinline__ uint4 neg_inf_vec<F32>() {
-  return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
-}
-
 template <class T>
 __device__ __forceinline__ void add_batch(Running& st, const uint4 (&raw)[kStatsUnroll], Scale c) {
   float x[kStatsUnroll * T::kVec];
@@ -231,8 +219,8 @@ __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
   const int head = min(static_cast<int>(((16u - (addr & 15u)) & 15u) / T::kBytes), P.V);
   const int64_t nvec = (P.V - head) / VEC;
   const int tail = static_cast<int>((P.V - head) - nvec * VEC);
-  const int64_t v0 = static_cast<int64_t>(seg) * P.seg_vecs;
-  const int64_t v1 = min(nvec, v0 + P.seg_vecs);
+  const int64_t v0 = static_cast<int64_t>(seg) * P.L.seg_vecs;
+  const int64_t v1 = min(nvec, v0 + P.L.seg_vecs);
   const uint4* body = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + head * T::kBytes);
 
   const int x = (seg == 0 && tid == 0) ? row_token(P, b, r) : -1;
@@ -247,13 +235,13 @@ __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
     }
     add_batch<T>(st, raw, c);
   }
-  if (seg == P.nseg - 1 && tid < tail) running_add1(st, load_elem<T>(row, head + nvec * VEC + tid), c);
+  if (seg == P.L.nseg - 1 && tid < tail) running_add1(st, load_elem<T>(row, head + nvec * VEC + tid), c);
 
   float MC;
   double S;
   block_combine(st, c, s_redf, s_redd, &MC, &S);
   if (tid == 0) {
-    const int64_t slot = (static_cast<int64_t>(b) * R + r) * P.nseg + seg;
+    const int64_t slot = (static_cast<int64_t>(b) * R + r) * P.L.nseg + seg;
     publish(&P.part_m[slot], tag_float(MC));
     publish(&P.part_s[slot], tag_nonneg_double(S));
     if (x >= 0 && x < P.V) publish_gather<T>(P, b, r, row, x);
@@ -269,9 +257,9 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
   __shared__ float s_redf[kWaves];
   __shared__ double s_redd[kWaves];
   const int R = 2 * P.K + 1;
-  const int64_t nvec = P.nvec;
-  const int64_t lo = static_cast<int64_t>(ch) * P.per;
-  const int64_t hi = min(static_cast<int64_t>(R) * nvec, lo + P.per);
+  const int64_t nvec = P.L.nvec;
+  const int64_t lo = static_cast<int64_t>(ch) * P.L.per;
+  const int64_t hi = min(static_cast<int64_t>(R) * nvec, lo + P.L.per);
   const int r_lo = static_cast<int>(lo / nvec);
   const int r_hi = static_cast<int>((hi - 1) / nvec);
   const Scale c = exponent_scale(temperature_of(P.temperature, b));
@@ -286,7 +274,7 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
     double S;
     block_combine(st, c, s_redf, s_redd, &MC, &S);
     if (threadIdx.x == 0) {
-      const int64_t slot = (static_cast<int64_t>(b) * P.cps + ch) * P.kmax + (r - r_lo);
+      const int64_t slot = (static_cast<int64_t>(b) * P.L.cps + ch) * P.L.kmax + (r - r_lo);
       publish(&P.part_m[slot], tag_float(MC));
       publish(&P.part_s[slot], tag_nonneg_double(S));
       // the piece holding the drafted token publishes its logit
@@ -296,30 +284,6 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
 }
 
 // ---------------------------------------------------------------- pass 2
-
-// a / b for non-negative 64-bit values, in 32-bit arithmetic when both fit
-// (a hardware-friendly path for every realistic size).
-__device__ __forceinline__ int64_t div_nonneg(int64_t a, int64_t b) {
-  if (((a | b) >> 32) == 0) return static_cast<int64_t>(static_cast<uint32_t>(a) / static_cast<uint32_t>(b));
-  return a / b;
-}
-
-// Slot index of piece `p` of row r of sequence b, or -1 past its last piece.
-__device__ __forceinline__ int64_t piece_slot(const ChainParams& P, int b, int r, int p) {
-  if (P.cps > 0) {
-    const int64_t nvec = P.nvec, per = P.per;
-    const int64_t ch = div_nonneg(r * nvec, per) + p;
-    if (ch > div_nonneg((r + 1) * nvec - 1, per)) return -1;
-    return (static_cast<int64_t>(b) * P.cps + ch) * P.kmax + (r - div_nonneg(ch * per, nvec));
-  }
-  return p < P.nseg ? (static_cast<int64_t>(b) * (2 * P.K + 1) + r) * P.nseg + p : -1;
-}
-
-// Largest number of statistics pieces of any row (host and device agree).
-__device__ __forceinline__ int max_pieces(const ChainParams& P) {
-  if (P.cps > 0) return static_cast<int>(div_nonneg(P.nvec + P.per - 2, P.per)) + 1;
-  return P.nseg;
-}
 
 // The decision of sequence b (one workgroup): the rows' log-normalisers (a
 // group of lanes per row), the drafted tokens' logits published by pass 1,
@@ -370,7 +334,7 @@ __device__ void decide_seq(const ChainParams& P, int b) {
   // references M, each lane rescales its sum by 2^(m - M) in fp64, group sum
   // Z, L = M + log2 Z.
   {
-    const int pmax = max_pieces(P);
+    const int pmax = max_pieces(P.L);
     int G = 1;
     while (G < pmax && G < kWave) G <<= 1;
     const int rows_per_round = kThreads / G;
@@ -378,7 +342,7 @@ __device__ void decide_seq(const ChainParams& P, int b) {
       const int r = r0 + tid / G;
       const int gl = tid % G;
       const bool row_ok = r < R;
-      const int64_t s_first = row_ok ? piece_slot(P, b, r, gl) : -1;
+      const int64_t s_first = row_ok ? piece_slot(P.L, b, r, gl) : -1;
       uint64_t rm = 0ull, rs = 0ull;
       if (s_first >= 0) {
         rm = P.part_m[s_first];
@@ -387,7 +351,7 @@ __device__ void decide_seq(const ChainParams& P, int b) {
       float mf = -INFINITY;  // reference of the folded sum zf
       double zf = 0.0;
       for (int p = gl + G; s_first >= 0 && p < pmax; p += G) {
-        const int64_t s = piece_slot(P, b, r, p);
+        const int64_t s = piece_slot(P.L, b, r, p);
         if (s < 0) break;
         const float mm = untag_float(load_ready(&P.part_m[s], &err));
         const double sv = untag_nonneg_double(load_ready(&P.part_s[s], &err));
@@ -475,7 +439,7 @@ __device__ void decide_seq(const ChainParams& P, int b) {
   }
   // Consumed: the sequence's statistics pieces and gathered logits go back
   // to zero for the next call.
-  const int64_t per_seq = P.cps > 0 ? static_cast<int64_t>(P.cps) * P.kmax : static_cast<int64_t>(R) * P.nseg;
+  const int64_t per_seq = slots_per_seq(P.L);
   for (int64_t s = static_cast<int64_t>(b) * per_seq + tid; s < (static_cast<int64_t>(b) + 1) * per_seq; s += kThreads) {
     P.part_m[s] = 0ull;
     P.part_s[s] = 0ull;
@@ -806,14 +770,14 @@ __device__ void sample_item(const ChainParams& P, int b, int blk) {
 // Pass 1: one workgroup per statistics item (a chunk, or a row segment).
 template <class T>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_kernel(ChainParams P) {
-  const int64_t per_seq = P.cps > 0 ? P.cps : static_cast<int64_t>(2 * P.K + 1) * P.nseg;
+  const int64_t per_seq = items_per_seq(P.L);
   const int64_t k = blockIdx.x;
   const int b = static_cast<int>(k / per_seq);
   const int rem = static_cast<int>(k % per_seq);
-  if (P.cps > 0)
+  if (P.L.cps > 0)
     stats_chunk<T>(P, b, rem);
   else
-    stats_segment<T>(P, b, rem / P.nseg, rem % P.nseg);
+    stats_segment<T>(P, b, rem / P.L.nseg, rem % P.L.nseg);
 }
 
 // Pass 2: one workgroup per sequence.
@@ -830,14 +794,9 @@ __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
 
 // ---------------------------------------------------------------- launcher
 
-int64_t chain_stats_items(const ChainParams& p) {
-  const int64_t stats_per_seq = p.cps > 0 ? p.cps : static_cast<int64_t>(2 * p.K + 1) * p.nseg;
-  return static_cast<int64_t>(p.B) * stats_per_seq;
-}
-
 template <class T>
 static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hipStream_t stream) {
-  const int64_t grid_a = chain_stats_items(p);
+  const int64_t grid_a = static_cast<int64_t>(p.B) * items_per_seq(p.L);
   const int64_t grid_c = static_cast<int64_t>(p.B) * p.nblk_b;
   if (grid_a > INT32_MAX || grid_c > INT32_MAX) return hipErrorInvalidConfiguration;
   // Armed events take the statistics kernel's own start and end timestamps.

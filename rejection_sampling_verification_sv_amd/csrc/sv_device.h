@@ -67,6 +67,18 @@ __device__ __forceinline__ void unpack<F32>(const uint4& v, float* out) {
 
 __device__ __forceinline__ uint4 load_vec(const void* p) { return *static_cast<const uint4*>(p); }
 
+// 16 bytes of -inf logits (padding that never wins a maximum and weighs 0).
+template <class T>
+__device__ __forceinline__ uint4 neg_inf_vec();
+template <>
+__device__ __forceinline__ uint4 neg_inf_vec<BF16>() {
+  return make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+}
+template <>
+__device__ __forceinline__ uint4 neg_inf_vec<F32>() {
+  return make_uint4(0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u);
+}
+
 // v_exp_f32: 2^x (about 1 ulp; inputs below -126 give 0 or a denormal).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

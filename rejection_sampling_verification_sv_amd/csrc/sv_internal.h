@@ -25,6 +25,55 @@ struct SeqPlan {
   uint32_t valid;  // 1 once written (the workspace is zero otherwise)
 };
 
+// How a streaming pass cuts the logit rows of a call into work items, and
+// where each item publishes one 64-bit slot per row piece. Two layouts:
+//  chunked (every row starts on a 16-byte boundary): the `rows` rows of a
+//    sequence, laid end to end, are cut into cps chunks of `per` 16-byte
+//    vectors; a chunk publishes one slot per row it touches (at most kmax),
+//    slot (b * cps + chunk) * kmax + (row - first row of the chunk);
+//  segments (any alignment): nseg segments of seg_vecs vectors per row, slot
+//    (b * rows + row) * nseg + segment.
+struct PieceLayout {
+  int32_t rows;      // logit rows per sequence
+  int32_t cps;       // > 0: chunked layout
+  int32_t kmax;
+  int64_t nvec;      // 16-byte vectors per row (chunked layout)
+  int64_t per;
+  int32_t nseg;      // segments layout
+  int32_t seg_vecs;
+};
+
+// Work items per sequence, and slots per sequence.
+__host__ __device__ __forceinline__ int64_t items_per_seq(const PieceLayout& L) {
+  return L.cps > 0 ? L.cps : static_cast<int64_t>(L.rows) * L.nseg;
+}
+__host__ __device__ __forceinline__ int64_t slots_per_seq(const PieceLayout& L) {
+  return L.cps > 0 ? static_cast<int64_t>(L.cps) * L.kmax : static_cast<int64_t>(L.rows) * L.nseg;
+}
+
+// a / b for non-negative 64-bit values, in 32-bit arithmetic when both fit
+// (a hardware-friendly path for every realistic size).
+__device__ __forceinline__ int64_t div_nonneg(int64_t a, int64_t b) {
+  if (((a | b) >> 32) == 0) return static_cast<int64_t>(static_cast<uint32_t>(a) / static_cast<uint32_t>(b));
+  return a / b;
+}
+
+// Slot of piece p of row r of sequence b, or -1 past the row's last piece.
+__device__ __forceinline__ int64_t piece_slot(const PieceLayout& L, int b, int r, int p) {
+  if (L.cps > 0) {
+    const int64_t ch = div_nonneg(r * L.nvec, L.per) + p;
+    if (ch > div_nonneg((r + 1) * L.nvec - 1, L.per)) return -1;
+    return (static_cast<int64_t>(b) * L.cps + ch) * L.kmax + (r - div_nonneg(ch * L.per, L.nvec));
+  }
+  return p < L.nseg ? (static_cast<int64_t>(b) * L.rows + r) * L.nseg + p : -1;
+}
+
+// Largest number of pieces of any row.
+__device__ __forceinline__ int max_pieces(const PieceLayout& L) {
+  if (L.cps > 0) return static_cast<int>(div_nonneg(L.nvec + L.per - 2, L.per)) + 1;
+  return L.nseg;
+}
+
 struct ChainParams {
   const void* target;
   const void* draft;
@@ -32,17 +81,7 @@ struct ChainParams {
   const float* temperature;
   const float* uniforms;
   int32_t B, K, V;
-  // Statistics layout, one of:
-  //  chunked (every row on a 16-byte boundary): each sequence's 2K+1 rows,
-  //    concatenated, are cut into cps chunks of `per` 16-byte vectors; a chunk
-  //    publishes one piece per row it touches (at most kmax);
-  //  rows (any alignment): nseg segments of seg_vecs vectors per row.
-  int32_t cps;             // > 0: chunked layout
-  int32_t kmax;
-  int64_t nvec;            // 16-byte vectors per row (chunked layout)
-  int64_t per;
-  int32_t nseg;
-  int32_t seg_vecs;
+  PieceLayout L;           // statistics pass; rows = 2K+1 (target 0..K, then draft)
   // Sampling: nblk_b workgroups per sequence, each over tiles_per_block
   // tiles of kSampleTile tokens.
   int32_t ntiles;
@@ -55,8 +94,7 @@ struct ChainParams {
   float* residual_mass;
   int32_t* err_flags;
   // workspace (all zero between calls)
-  uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi),
-                      // [B, cps, kmax] (chunked) or [B, 2K+1, nseg] (rows)
+  uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi)
   uint64_t* part_s;   // per row piece: tagged fp64 sum of 2^(x c - reference)
   SeqPlan* plan;      // [B] decision -> sampling hand-off
   uint32_t* cnt;      // [B] sampling arrivals
@@ -72,15 +110,12 @@ struct TreeParams {
   const int32_t* tokens;
   const int32_t* parents;
   int32_t B, N, V;
-  int32_t nseg;
-  int32_t seg_vecs;
+  PieceLayout L;      // argmax pass; rows = N+1
   int32_t* accept_len;
   int32_t* path_nodes;
   int32_t* next_token;
   int32_t* err_flags;
-  uint64_t* part;    // [B, N+1, nseg] per-segment (max value, lowest index + 1)
-  uint32_t* cnt;     // [B]
-  uint64_t* abort;   // [1] set when a bounded wait expires
+  uint64_t* part;     // per row piece: (max value bits << 32) | (lowest index + 1)
 };
 
 constexpr int kSampleEPT = 8;                      // sampling elements per thread per tile
@@ -89,13 +124,13 @@ constexpr int kSampleTile = 256 * kSampleEPT;      // elements per sampling tile
 constexpr int kSampleTilesBF16 = 4;
 constexpr int kSampleTilesF32 = 2;
 
-// Statistics segment (rows layout): kThreads * kStatsUnroll * kStatsBatches vectors.
+// Segments layout: kThreads * kStatsUnroll * kStatsBatches vectors per segment.
 constexpr int kStatsUnroll = 4;
 constexpr int kStatsBatches = 2;
 constexpr int kStatsSegVecs = 256 * kStatsUnroll * kStatsBatches;
 
-// Chunked statistics layout: about this many chunks per call, each with at
-// least kChunkMinVecs 16-byte vectors.
+// Chunked layout: about this many chunks per call, each with at least
+// kChunkMinVecs 16-byte vectors.
 #ifndef SV_CHUNKS
 #define SV_CHUNKS 4096
 #endif
@@ -112,9 +147,9 @@ struct PassEvents {
 };
 PassEvents take_pass_events();
 
-// Statistics work items of the call, and the three launches of a chain call.
-int64_t chain_stats_items(const ChainParams& p);
-// `ev` (possibly null events) brackets the streaming pass of the call.
+// The launches of a chain call (statistics, decision, sampling) and of a tree
+// call (argmax, decision); `ev` (possibly null events) become the start and
+// stop events of the streaming pass.
 hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,

@@ -1,14 +1,17 @@
 // Greedy tree verification and the tree ancestor mask.
 //
-// tree_argmax_kernel, one workgroup per (sequence, position, segment): streams
-// a segment of one logit row with 16-byte loads and keeps, per thread, the
-// largest value and its lowest index (a batch is scanned for its first maximum
-// only when it beats the running one). The block combines (value desc, index
-// asc) and publishes the pair. The last block of a sequence combines the
-// segments into g[n] = argmax of every position and resolves the tree:
-// node i is accepted iff its token equals g at its parent's position and its
-// parent is accepted; acceptance and depth are propagated up the parent links
-// by pointer jumping (log2(depth) rounds); the deepest accepted node (lowest
+// tree_argmax_kernel, one workgroup per streaming item (a chunk of a
+// sequence's N+1 rows laid end to end, or a segment of one row): streams the
+// logits with 16-byte loads and keeps, per thread, the largest value and its
+// lowest index (a batch is scanned for its first maximum only when it beats
+// the running one). The block combines (value desc, index asc) and publishes
+// one slot per row piece.
+//
+// tree_decide_kernel, one workgroup per sequence: combines the pieces into
+// g[n] = argmax of every position and resolves the tree: node i is accepted
+// iff its token equals g at its parent's position and its parent is
+// accepted; acceptance and depth are propagated up the parent links by
+// pointer jumping (log2(depth) rounds); the deepest accepted node (lowest
 // index on ties) ends the path, and g at its position is the next token.
 // [Topologies] "Speculative Decoding & Draft Model Topologies", section 4
 // figure (all tree nodes checked in one pass, the longest accepted path kept);
@@ -82,14 +85,16 @@ __device__ void tree_decide(const TreeParams& P, int b) {
   if (tid == 0) s_err = 0u;
   __syncthreads();
 
-  // g[n]: combine the segment partials of every position.
+  // g[n]: combine the pieces of every position (written by the argmax launch).
+  const int pmax = max_pieces(P.L);
   for (int n = tid; n < N1; n += kThreads) {
-    const int64_t base = (static_cast<int64_t>(b) * N1 + n) * P.nseg;
     float bv = -INFINITY;
     int bi = INT_MAX;
     uint32_t err = 0u;
-    for (int s = 0; s < P.nseg; ++s) {
-      const uint64_t slot = await_slot(&P.part[base + s], &err, P.abort);
+    for (int p = 0; p < pmax; ++p) {
+      const int64_t s = piece_slot(P.L, b, n, p);
+      if (s < 0) break;
+      const uint64_t slot = load_ready(&P.part[s], &err);
       const float v = __uint_as_float(static_cast<uint32_t>(slot >> 32));
       const int i = static_cast<int>(static_cast<uint32_t>(slot) - 1u);
       if (better(v, i, bv, bi)) {
@@ -167,36 +172,99 @@ __device__ void tree_decide(const TreeParams& P, int b) {
     P.next_token[b] = bad ? -1 : s_g[best + 1];
     raise_error(P.err_flags, s_err);
   }
+  // Consumed: the sequence's pieces go back to zero for the next call.
+  const int64_t per_seq = slots_per_seq(P.L);
+  for (int64_t s = static_cast<int64_t>(b) * per_seq + tid; s < (static_cast<int64_t>(b) + 1) * per_seq; s += kThreads)
+    P.part[s] = 0ull;
 }
 
-}  // namespace
-
+// One thread's share of the vectors [p0, p1) of a row (16-byte aligned body):
+// full batches of kStatsUnroll vectors per thread without masking, then one
+// ragged batch padded with -inf. Each thread sees its elements in ascending
+// index order, so a strict '>' keeps the first occurrence of its maximum.
 template <class T>
-__global__ __launch_bounds__(kThreads) void tree_argmax_kernel(TreeParams P) {
+__device__ __forceinline__ void piece_argmax(const uint4* body, int64_t p0, int64_t p1, float& bv, int& bi) {
+  constexpr int U = kStatsUnroll;
+  constexpr int VEC = T::kVec;
+  constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
+  const int64_t nfull = (p1 - p0) / STEP;
+  const int64_t rest = (p1 - p0) - nfull * STEP;
+  int64_t v = p0 + threadIdx.x;  // this thread's first vector of the batch
+#pragma unroll 1
+  for (int64_t i = 0; i <= nfull; ++i, v += STEP) {
+    uint4 raw[U];
+    if (i < nfull) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) raw[u] = body[v + u * kThreads];
+    } else {
+      if (rest == 0) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        raw[u] = (u * kThreads + static_cast<int64_t>(threadIdx.x) < rest) ? body[v + u * kThreads] : neg_inf_vec<T>();
+    }
+    float x[U * VEC];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      unpack<T>(raw[u], &x[u * VEC]);
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) bm = fmaxf(bm, x[u * VEC + k]);
+    }
+    if (bm > bv) {
+      int first = 0;
+#pragma unroll
+      for (int q = U * VEC - 1; q >= 0; --q)
+        if (x[q] == bm) first = q;
+      bv = bm;
+      bi = static_cast<int>((v + (first / VEC) * kThreads) * VEC + (first % VEC));
+    }
+  }
+}
+
+__device__ __forceinline__ uint64_t pack_argmax(float v, int i) {
+  return (static_cast<uint64_t>(__float_as_uint(v)) << 32) | static_cast<uint32_t>(i + 1);
+}
+
+// Chunked layout: chunk ch of sequence b, one slot per row piece.
+template <class T>
+__device__ void tree_chunk(const TreeParams& P, int b, int ch) {
   __shared__ float s_v[kWaves];
   __shared__ int s_i[kWaves];
-  __shared__ int s_flag;
+  const int64_t nvec = P.L.nvec;
+  const int64_t lo = static_cast<int64_t>(ch) * P.L.per;
+  const int64_t hi = min(static_cast<int64_t>(P.L.rows) * nvec, lo + P.L.per);
+  const int r_lo = static_cast<int>(lo / nvec);
+  const int r_hi = static_cast<int>((hi - 1) / nvec);
+  for (int r = r_lo; r <= r_hi; ++r) {
+    const int64_t p0 = max(lo, r * nvec) - r * nvec;
+    const int64_t p1 = min(hi, (r + 1) * nvec) - r * nvec;
+    const uint4* body = reinterpret_cast<const uint4*>(static_cast<const char*>(P.target) +
+                                                       (static_cast<int64_t>(b) * P.L.rows + r) * nvec * 16);
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    piece_argmax<T>(body, p0, p1, bv, bi);
+    block_argmax(bv, bi, s_v, s_i);
+    if (threadIdx.x == 0)
+      P.part[(static_cast<int64_t>(b) * P.L.cps + ch) * P.L.kmax + (r - r_lo)] = pack_argmax(bv, bi);
+  }
+}
+
+// Segments layout: segment seg of row r of sequence b (any alignment).
+template <class T>
+__device__ void tree_segment(const TreeParams& P, int b, int r, int seg) {
+  __shared__ float s_v[kWaves];
+  __shared__ int s_i[kWaves];
   constexpr int VEC = T::kVec;
-  constexpr int U = kStatsUnroll;
-
-  const int N1 = P.N + 1;
-  const int64_t blk = blockIdx.x;
-  const int seg = static_cast<int>(blk % P.nseg);
-  const int64_t rowid = blk / P.nseg;
-  const int b = static_cast<int>(rowid / N1);
   const int tid = threadIdx.x;
-
-  const void* row = static_cast<const char*>(P.target) + rowid * static_cast<int64_t>(P.V) * T::kBytes;
+  const void* row = static_cast<const char*>(P.target) + (static_cast<int64_t>(b) * P.L.rows + r) *
+                                                             static_cast<int64_t>(P.V) * T::kBytes;
   const uintptr_t addr = reinterpret_cast<uintptr_t>(row);
   const int head = min(static_cast<int>(((16u - (addr & 15u)) & 15u) / T::kBytes), P.V);
   const int64_t nvec = (P.V - head) / VEC;
   const int tail = static_cast<int>((P.V - head) - nvec * VEC);
-  const int64_t v0 = static_cast<int64_t>(seg) * P.seg_vecs;
-  const int64_t v1 = min(nvec, v0 + P.seg_vecs);
+  const int64_t v0 = static_cast<int64_t>(seg) * P.L.seg_vecs;
+  const int64_t v1 = min(nvec, v0 + P.L.seg_vecs);
   const uint4* body = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + head * T::kBytes);
-
-  // Each thread sees its elements in ascending index order, so a strict '>'
-  // keeps the first occurrence of its maximum.
   float bv = -INFINITY;
   int bi = INT_MAX;
   if (seg == 0 && tid < head) {
@@ -206,37 +274,16 @@ __global__ __launch_bounds__(kThreads) void tree_argmax_kernel(TreeParams P) {
       bi = tid;
     }
   }
-  for (int64_t base = v0 + tid; base < v1; base += static_cast<int64_t>(kThreads) * U) {
-    uint4 raw[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t vi = base + static_cast<int64_t>(u) * kThreads;
-      raw[u] = (vi < v1) ? body[vi] : make_uint4(0u, 0u, 0u, 0u);
-    }
-    float x[U * VEC];
-    float bm = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      unpack<T>(raw[u], &x[u * VEC]);
-      const int64_t vi = base + static_cast<int64_t>(u) * kThreads;
-      if (vi >= v1) {
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) x[u * VEC + k] = -INFINITY;
-      }
-#pragma unroll
-      for (int k = 0; k < VEC; ++k) bm = fmaxf(bm, x[u * VEC + k]);
-    }
-    if (bm > bv) {
-      int first = -1;
-#pragma unroll
-      for (int q = U * VEC - 1; q >= 0; --q)
-        if (x[q] == bm) first = q;
-      const int u = first / VEC;
-      bv = bm;
-      bi = static_cast<int>(head + (base + static_cast<int64_t>(u) * kThreads) * VEC + (first % VEC));
+  if (v1 > v0) {
+    float pv = -INFINITY;
+    int pi = INT_MAX;
+    piece_argmax<T>(body, v0, v1, pv, pi);
+    if (pv > bv) {  // body elements come after the head
+      bv = pv;
+      bi = head + pi;
     }
   }
-  if (seg == P.nseg - 1 && tid < tail) {
+  if (seg == P.L.nseg - 1 && tid < tail) {
     const int idx = static_cast<int>(head + nvec * VEC + tid);
     const float x = load_elem<T>(row, idx);
     if (x > bv) {
@@ -245,17 +292,24 @@ __global__ __launch_bounds__(kThreads) void tree_argmax_kernel(TreeParams P) {
     }
   }
   block_argmax(bv, bi, s_v, s_i);
-  if (tid == 0)
-    publish(&P.part[blk], (static_cast<uint64_t>(__float_as_uint(bv)) << 32) | static_cast<uint32_t>(bi + 1));
-
-  if (!arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(N1) * P.nseg, &s_flag)) return;
-  tree_decide(P, b);
-  // Leave the workspace all zero for the next call, whatever its shape.
-  __syncthreads();
-  const int64_t base = static_cast<int64_t>(b) * N1 * P.nseg;
-  for (int64_t i = tid; i < static_cast<int64_t>(N1) * P.nseg; i += kThreads) clear_slot(&P.part[base + i]);
-  reset_counter(&P.cnt[b]);
+  if (tid == 0) P.part[(static_cast<int64_t>(b) * P.L.rows + r) * P.L.nseg + seg] = pack_argmax(bv, bi);
 }
+
+}  // namespace
+
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void tree_argmax_kernel(TreeParams P) {
+  const int64_t per_seq = items_per_seq(P.L);
+  const int64_t k = blockIdx.x;
+  const int b = static_cast<int>(k / per_seq);
+  const int rem = static_cast<int>(k % per_seq);
+  if (P.L.cps > 0)
+    tree_chunk<T>(P, b, rem);
+  else
+    tree_segment<T>(P, b, rem / P.L.nseg, rem % P.L.nseg);
+}
+
+__global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) { tree_decide(P, blockIdx.x); }
 
 __global__ __launch_bounds__(kThreads) void tree_mask_kernel(const int32_t* parents, int N, uint8_t* mask,
                                                              int32_t* err_flags) {
@@ -286,11 +340,14 @@ __global__ __launch_bounds__(kThreads) void tree_mask_kernel(const int32_t* pare
 
 template <class T>
 static hipError_t launch_tree_t(const TreeParams& p, const PassEvents& ev, hipStream_t stream) {
-  const int64_t grid = static_cast<int64_t>(p.B) * (p.N + 1) * p.nseg;
+  const int64_t grid = static_cast<int64_t>(p.B) * items_per_seq(p.L);
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-  // Armed events take the kernel's own start and end timestamps.
+  // Armed events take the argmax kernel's own start and end timestamps.
   hipExtLaunchKernelGGL(tree_argmax_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
                         ev.before, ev.after, 0u, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tree_decide_kernel, dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
