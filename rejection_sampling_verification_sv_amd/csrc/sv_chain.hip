@@ -1,16 +1,17 @@
 // Chain verification kernels (modified rejection sampling over K proposals).
 //
-// Pass 1 — statistics. Streams every logit row of the call once (the K+1
-// target rows and K draft rows of each sequence) with coalesced 16-byte loads.
-// Each thread keeps the running maximum m of its logits and the sum of
-// 2^(x*c - m*c), c = log2(e)/T (one pass: a batch of 32 values is reduced to
-// its maximum first, the sum is rescaled once per batch, then the batch's
-// exponentials are added). Each block combines its threads in fp64 and stores
-// one (reference, sum) pair per row piece. Two layouts:
-//   chain_stats_flat_kernel: rows on 16-byte boundaries (the usual case); the
-//     flattened vector space of all rows is cut into equal ranges, one per
-//     block, so every block streams the same number of bytes;
-//   chain_stats_rows_kernel: any row alignment; one block per (row, segment).
+// Pass 1 — chain_stats_kernel. Streams every logit row of the call once (the
+// K+1 target rows and K draft rows of each sequence) with coalesced 16-byte
+// loads. Each thread keeps the running maximum m of its logits and the sum of
+// 2^(x*c - m*c), c = log2(e)/T (one pass: a batch of values is reduced to its
+// maximum first, the sum is rescaled once per batch, then the batch's
+// exponentials are added). Each block combines its threads in fp64 and
+// publishes one (reference, sum) pair per row piece. Work items:
+//   chunked layout (rows on 16-byte boundaries, the usual case): each
+//     sequence's rows, laid end to end, are cut into equal chunks, so every
+//     block streams the same number of bytes;
+//   segments layout (any row alignment): one item per (row, segment).
+// The piece holding a drafted token also publishes that token's logit.
 //
 // Pass 2 — chain_decide_kernel, one workgroup per sequence: combines the
 // pieces of the sequence's 2K+1 rows into their log-normalisers
@@ -143,20 +144,20 @@ __device__ __forceinline__ void block_combine(const Running& st, Scale c, float*
   *S = block_sum(sd, s_redd);
 }
 
-template <class T>
-__device__ __forceinline__ void add_batch(Running& st, const uint4 (&raw)[kStatsUnroll], Scale c) {
-  float x[kStatsUnroll * T::kVec];
+template <class T, int U = kStatsUnroll>
+__device__ __forceinline__ void add_batch(Running& st, const uint4 (&raw)[U], Scale c) {
+  float x[U * T::kVec];
 #pragma unroll
-  for (int u = 0; u < kStatsUnroll; ++u) unpack<T>(raw[u], &x[u * T::kVec]);
+  for (int u = 0; u < U; ++u) unpack<T>(raw[u], &x[u * T::kVec]);
   running_add(st, x, c);
 }
 
 // One thread's share of the vectors [p0, p1) of a row: full batches of
-// kStatsUnroll vectors per thread without any masking, then one ragged batch
+// kStreamU vectors per thread without any masking, then one ragged batch
 // whose missing vectors are replaced by -inf.
 template <class T>
 __device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, int64_t p1, Scale c, Running& st) {
-  constexpr int U = kStatsUnroll;
+  constexpr int U = kStreamU;
   constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
   const int64_t nfull = (p1 - p0) / STEP;
   const uint4* ptr = body + p0 + threadIdx.x;
@@ -165,7 +166,7 @@ __device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, 
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) raw[u] = ptr[u * kThreads];
-    add_batch<T>(st, raw, c);
+    add_batch<T, U>(st, raw, c);
   }
   const int64_t rest = (p1 - p0) - nfull * STEP;  // vectors in the ragged batch
   if (rest > 0) {
@@ -175,10 +176,9 @@ __device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, 
       const int64_t k = static_cast<int64_t>(u) * kThreads + threadIdx.x;
       raw[u] = (k < rest) ? ptr[u * kThreads] : neg_inf_vec<T>();
     }
-    add_batch<T>(st, raw, c);
+    add_batch<T, U>(st, raw, c);
   }
 }
-
 
 }  // namespace
 

@@ -129,6 +129,13 @@ constexpr int kStatsUnroll = 4;
 constexpr int kStatsBatches = 2;
 constexpr int kStatsSegVecs = 256 * kStatsUnroll * kStatsBatches;
 
+// Chunked statistics stream: 16-byte vectors per thread per batch (the
+// batch's maximum is taken before its exponentials are summed).
+#ifndef SV_STREAM_U
+#define SV_STREAM_U 2
+#endif
+constexpr int kStreamU = SV_STREAM_U;
+
 // Chunked layout: about this many chunks per call, each with at least
 // kChunkMinVecs 16-byte vectors.
 #ifndef SV_CHUNKS
