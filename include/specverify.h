@@ -81,7 +81,9 @@ typedef enum sv_dtype {
 #define SV_ERRF_NONFINITE 0x8u   /* a row's maximum is +inf, or its normaliser    \
                                     is 0 / not finite                            */
 #define SV_ERRF_INTERNAL 0x10u   /* a partial result never became visible to the  \
-                                    block combining them (should not happen)     */
+                                    block combining them within the bounded wait \
+                                    (should not happen); the workspace then has  \
+                                    to be zero-filled again                      */
 
 #define SV_MAX_K 63           /* drafted tokens per sequence (K+1 fits a wave64) */
 #define SV_MAX_TREE_NODES 1024 /* candidate-tree nodes per call                  */
@@ -97,7 +99,8 @@ const char* sv_status_string(sv_status status);
  * (e.g. hipMemset or torch.zeros). Every call that returns SV_OK leaves the
  * whole workspace zero again once its kernels have run, so one workspace can
  * serve any sequence of calls (of any shape, chain or tree) on one stream.
- * After a call that returned an error, zero-fill it again.
+ * After a call that returned an error, or whose kernels raised
+ * SV_ERRF_INTERNAL, zero-fill it again.
  */
 size_t sv_chain_workspace_bytes(int32_t B, int32_t K, int32_t V, sv_dtype dtype);
 

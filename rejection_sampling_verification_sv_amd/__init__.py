@@ -10,6 +10,7 @@ from .specverify import (  # noqa: F401
     SpecVerifyError,
     SV_DTYPE_BF16,
     SV_DTYPE_F32,
+    SV_ERRF_INTERNAL,
     SV_ERRF_NONFINITE,
     SV_ERRF_PARENT,
     SV_ERRF_TEMPERATURE,
@@ -17,6 +18,7 @@ from .specverify import (  # noqa: F401
     SV_MAX_K,
     SV_MAX_TREE_NODES,
     library,
+    reset_workspaces,
     sv_build_tree_mask,
     sv_chain_workspace_bytes,
     sv_status_string,

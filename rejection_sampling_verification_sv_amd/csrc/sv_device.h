@@ -65,8 +65,6 @@ __device__ __forceinline__ void unpack<F32>(const uint4& v, float* out) {
   out[3] = __uint_as_float(v.w);
 }
 
-__device__ __forceinline__ uint4 load_vec(const void* p) { return *static_cast<const uint4*>(p); }
-
 // 16 bytes of -inf logits (padding that never wins a maximum and weighs 0).
 template <class T>
 __device__ __forceinline__ uint4 neg_inf_vec();
@@ -224,18 +222,6 @@ __device__ __forceinline__ uint64_t load_ready(const uint64_t* slot, uint32_t* e
   const uint64_t v = *slot;
   if (v == 0ull) *err |= kErrInternal;
   return v;
-}
-
-// Wait for the N consecutive slots base[0..N): every load is issued before
-// any value is inspected, so slots that are already written cost a single
-// memory round trip together.
-template <int N>
-__device__ __forceinline__ void await_run(uint64_t* base, uint64_t (&v)[N], uint32_t* err, uint64_t* abort) {
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i] = peek(base + i);
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-    if (v[i] == 0ull) v[i] = await_slot(base + i, err, abort);
 }
 
 __device__ __forceinline__ void clear_slot(uint64_t* slot) { publish(slot, 0ull); }

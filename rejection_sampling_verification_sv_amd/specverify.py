@@ -27,6 +27,7 @@ SV_ERRF_TOKEN = 0x1
 SV_ERRF_TEMPERATURE = 0x2
 SV_ERRF_PARENT = 0x4
 SV_ERRF_NONFINITE = 0x8
+SV_ERRF_INTERNAL = 0x10
 SV_MAX_K = 63
 SV_MAX_TREE_NODES = 1024
 
@@ -144,8 +145,19 @@ def sv_time_next_stream_pass(before: Optional[torch.cuda.Event], after: Optional
 
 # Zero-filled workspaces, one per (device, stream): the library returns every
 # workspace to all-zero counters at the end of each call, so a workspace can
-# be reused by the next call on the same stream.
+# be reused by the next call on the same stream. A call whose err_flags show
+# SV_ERRF_INTERNAL leaves it dirty: reset_workspaces() zero-fills them again.
 _workspaces: Dict[tuple, torch.Tensor] = {}
+
+
+def reset_workspaces() -> None:
+    """Zero-fill every cached workspace (after a call raised SV_ERRF_INTERNAL).
+
+    Each fill is ordered on the current stream of its device; call it from the
+    stream the workspaces serve, or synchronise first.
+    """
+    for ws in _workspaces.values():
+        ws.zero_()
 
 
 def workspace(device, nbytes: int, stream=None) -> torch.Tensor:
