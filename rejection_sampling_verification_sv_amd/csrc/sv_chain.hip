@@ -13,20 +13,22 @@
 //   segments layout (any row alignment): one item per (row, segment).
 // The piece holding a drafted token also publishes that token's logit.
 //
-// Pass 2 — chain_decide_kernel, one workgroup per sequence: combines the
-// pieces of the sequence's 2K+1 rows into their log-normalisers
-// L = log2 sum_v 2^(x_v c) (fp64), forms p_k(x_k) and q_k(x_k) in fp64,
-// alpha_k = min(1, p/q), accepts while u_k < alpha_k and takes j = the first
-// rejection with a wave ballot; writes the accepted prefix and a sampling plan.
-//   [Topologies] "Speculative Decoding & Draft Model Topologies", section 2
-//   (acceptance-probability equation, timeline figure steps 2-3);
-//   [In Production] "Speculative Decoding in Production", section 2.
-//
-// Pass 3 — chain_sample_kernel, one workgroup per (sequence, group of tiles):
-//   1. re-reads its tiles of row j (target, and draft when j < K), forms the
-//      weights max(0, p_j - q_j) (or p_K for the bonus draw) and publishes
-//      each tile's total;
-//   2. the last workgroup of the sequence scans the tile totals, finds the
+// Pass 2 — chain_sample_kernel, nblk_b workgroups per sequence, which take
+// tickets from a per-sequence counter:
+//   1. ticket 0 makes the decision: combines the pieces of the sequence's
+//      2K+1 rows into their log-normalisers L = log2 sum_v 2^(x_v c) (fp64),
+//      forms p_k(x_k) and q_k(x_k) in fp64, alpha_k = min(1, p/q), accepts
+//      while u_k < alpha_k and takes j = the first rejection with a wave
+//      ballot; it writes the accepted prefix and hands a sampling plan to the
+//      other tickets, which wait for it (the holder of ticket 0 is running and
+//      waits on nothing, so every wait ends);
+//      [Topologies] "Speculative Decoding & Draft Model Topologies", section 2
+//      (acceptance-probability equation, timeline figure steps 2-3);
+//      [In Production] "Speculative Decoding in Production", section 2.
+//   2. ticket t re-reads tiles [t * TPB, t * TPB + TPB) of row j (target, and
+//      draft when j < K), forms the weights max(0, p_j - q_j) (or p_K for the
+//      bonus draw) and publishes each tile's total;
+//   3. the last workgroup of the sequence scans the tile totals, finds the
 //      tile holding u_K * total, rescans it with a block-wide prefix sum and
 //      picks the first token whose cumulative weight exceeds it.
 //      [Topologies] section 2 (residual equation, step 4); [At Scale]
@@ -285,76 +287,94 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
 
 // ---------------------------------------------------------------- pass 2
 
-// The decision of sequence b (one workgroup): the rows' log-normalisers (a
-// group of lanes per row), the drafted tokens' logits published by pass 1,
-// then p_k(x_k), q_k(x_k) in fp64, alpha_k = min(1, p/q), acceptance while
-// u_k < alpha_k and j = the first rejection (wave ballot). Writes accept_len,
-// the accepted prefix of out_tokens, p_draft / q_draft, the error bits and
-// the sampling plan, and returns the pieces it consumed to zero.
+// The sampling plan travels as kPlanWords tagged 32-bit payloads (each word
+// is (1 << 32) | payload, never zero), so a reader can wait for each word.
+__device__ __forceinline__ void publish_plan(const ChainParams& P, int b, const SeqPlan& pl) {
+  static_assert(sizeof(SeqPlan) == 4 * kPlanWords, "plan layout");
+  uint32_t w[kPlanWords];
+  __builtin_memcpy(w, &pl, sizeof(SeqPlan));
+#pragma unroll
+  for (int i = 0; i < kPlanWords; ++i) publish(&P.plan_w[static_cast<int64_t>(b) * kPlanWords + i], (1ull << 32) | w[i]);
+}
+
+// One thread waits for the plan words (all loads issued before any value is
+// inspected) and unpacks them.
+__device__ __forceinline__ SeqPlan await_plan(const ChainParams& P, int b, uint32_t* err) {
+  uint64_t* base = P.plan_w + static_cast<int64_t>(b) * kPlanWords;
+  uint64_t v[kPlanWords];
+#pragma unroll
+  for (int i = 0; i < kPlanWords; ++i) v[i] = peek(base + i);
+  uint32_t w[kPlanWords];
+#pragma unroll
+  for (int i = 0; i < kPlanWords; ++i) {
+    if (v[i] == 0ull) v[i] = await_slot<8>(base + i, err, P.abort);
+    w[i] = static_cast<uint32_t>(v[i]);
+  }
+  SeqPlan pl;
+  __builtin_memcpy(&pl, w, sizeof(SeqPlan));
+  return pl;
+}
+
+// The decision of sequence b, made by wave 0 of the sequence's ticket-0
+// workgroup alone: no block barrier, so it never waits for the other waves of
+// its workgroup to be launched. The rows' log-normalisers come from the
+// statistics pieces (G lanes per row, G the largest power of two that fits
+// all 2K+1 rows in one wave or covers a row's pieces; up to four pieces per
+// lane loaded at once, further ones folded in one at a time): group max of
+// the references M, each lane rescales its sums by 2^(m - M) in fp64, group
+// sum Z, L = M + log2 Z. Lane k < K holds drafted token k, its uniform and
+// the logits pass 1 published for it; p_k(x_k), q_k(x_k) in fp64,
+// alpha_k = min(1, p/q), acceptance while u_k < alpha_k, j = the first
+// rejection (ballot). Writes accept_len, the accepted prefix of out_tokens,
+// p_draft / q_draft and the error bits, publishes the sampling plan and
+// leaves it in *s_plan, and returns the pieces and gathered logits it
+// consumed to zero.
 template <class T>
-__device__ void decide_seq(const ChainParams& P, int b) {
+__device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
-  __shared__ float s_lt[kWave], s_ld[kWave], s_u[kWave];
-  __shared__ int s_x[kWave];
-  __shared__ uint32_t s_err;
-  __shared__ int s_j;
   const int K = P.K;
   const int R = 2 * K + 1;
-  const int tid = threadIdx.x;
+  const int lane = lane_id();
   const Scale c = exponent_scale(temperature_of(P.temperature, b));
-  if (tid == 0) {
-    s_err = 0u;
-    s_j = K;
-  }
-  __syncthreads();
-
   uint32_t err = 0u;
-  if (wave_id() == kWaves - 1) {  // the drafted tokens and their logits (published by pass 1)
-    const int k = lane_id();
-    if (k < K) {
-      uint64_t* gt = &P.gat[static_cast<int64_t>(b) * R + k];
-      uint64_t* gd = &P.gat[static_cast<int64_t>(b) * R + K + 1 + k];
-      const int x = P.tokens[static_cast<int64_t>(b) * K + k];
-      const float u = P.uniforms[static_cast<int64_t>(b) * (K + 1) + k];
-      const uint64_t vt = *gt, vd = *gd;
-      s_x[k] = x;
-      s_u[k] = u;
-      if (x < 0 || x >= P.V) {
-        err |= SV_ERRF_TOKEN;
-      } else {
-        if (vt == 0ull || vd == 0ull) err |= kErrInternal;
-        s_lt[k] = untag_float(vt);
-        s_ld[k] = untag_float(vd);
-      }
+
+  int x = -1;
+  float u = 0.0f, lt = 0.0f, ld = 0.0f;
+  if (lane < K) {
+    x = P.tokens[static_cast<int64_t>(b) * K + lane];
+    u = P.uniforms[static_cast<int64_t>(b) * (K + 1) + lane];
+    const uint64_t vt = P.gat[static_cast<int64_t>(b) * R + lane];
+    const uint64_t vd = P.gat[static_cast<int64_t>(b) * R + K + 1 + lane];
+    if (x < 0 || x >= P.V) {
+      err |= SV_ERRF_TOKEN;
+    } else {
+      if (vt == 0ull || vd == 0ull) err |= kErrInternal;
+      lt = untag_float(vt);
+      ld = untag_float(vd);
     }
   }
-  // Rows' log-normalisers: a group of G lanes per row (G a power of two that
-  // covers the row's pieces, up to a wave). Each lane loads its first piece
-  // at once and folds any further ones in one at a time; group max of the
-  // references M, each lane rescales its sum by 2^(m - M) in fp64, group sum
-  // Z, L = M + log2 Z.
-  {
-    const int pmax = max_pieces(P.L);
-    int G = 1;
-    while (G < pmax && G < kWave) G <<= 1;
-    const int rows_per_round = kThreads / G;
-    for (int r0 = 0; r0 < R; r0 += rows_per_round) {
-      const int r = r0 + tid / G;
-      const int gl = tid % G;
-      const bool row_ok = r < R;
-      const int64_t s_first = row_ok ? piece_slot(P.L, b, r, gl) : -1;
-      uint64_t rm = 0ull, rs = 0ull;
-      if (s_first >= 0) {
-        rm = P.part_m[s_first];
-        rs = P.part_s[s_first];
-      }
-      float mf = -INFINITY;  // reference of the folded sum zf
-      double zf = 0.0;
-      for (int p = gl + G; s_first >= 0 && p < pmax; p += G) {
-        const int64_t s = piece_slot(P.L, b, r, p);
-        if (s < 0) break;
-        const float mm = untag_float(load_ready(&P.part_m[s], &err));
-        const double sv = untag_nonneg_double(load_ready(&P.part_s[s], &err));
+
+  const int pmax = max_pieces(P.L);
+  int G = 1;
+  while (G < pmax && R * 2 * G <= kWave) G <<= 1;
+  for (int r0 = 0; r0 < R; r0 += kWave / G) {
+    const int r = r0 + lane / G;
+    const int gl = lane % G;
+    const bool row_ok = r < R;
+    uint64_t rm[4], rs[4];
+    int n = 0;
+    float mf = -INFINITY;  // reference of the folded sum zf
+    double zf = 0.0;
+    for (int p = gl; row_ok && p < pmax; p += G) {
+      const int64_t sl = piece_slot(P.L, b, r, p);
+      if (sl < 0) break;
+      if (n < 4) {
+        rm[n] = P.part_m[sl];
+        rs[n] = P.part_s[sl];
+        ++n;
+      } else {
+        const float mm = untag_float(load_ready(&P.part_m[sl], &err));
+        const double sv = untag_nonneg_double(load_ready(&P.part_s[sl], &err));
         if (mm != -INFINITY) {
           if (mm > mf) {
             zf = (mf == -INFINITY ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(mm))) + sv;
@@ -364,65 +384,60 @@ __device__ void decide_seq(const ChainParams& P, int b) {
           }
         }
       }
-      float m1 = -INFINITY;
-      double s1 = 0.0;
-      if (s_first >= 0) {
-        if (rm == 0ull || rs == 0ull) err |= kErrInternal;
-        m1 = untag_float(rm);
-        s1 = untag_nonneg_double(rs);
-      }
-      float M = fmaxf(mf, m1);
-      for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
-      double zl = (mf == -INFINITY) ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(M));
-      if (m1 != -INFINITY) zl += s1 * exp2(static_cast<double>(m1) - static_cast<double>(M));
-      for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
-      if (row_ok && gl == 0) {
-        if (!(zl > 0.0) || !isfinite(zl) || !isfinite(M)) err |= SV_ERRF_NONFINITE;
-        s_L[r] = static_cast<double>(M) + log2(zl);
-      }
+    }
+    float ms[4];
+    float M = mf;
+    for (int i = 0; i < n; ++i) {
+      if (rm[i] == 0ull || rs[i] == 0ull) err |= kErrInternal;
+      ms[i] = untag_float(rm[i]);
+      M = fmaxf(M, ms[i]);
+    }
+    for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+    double zl = (mf == -INFINITY) ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(M));
+    for (int i = 0; i < n; ++i)
+      if (ms[i] != -INFINITY) zl += untag_nonneg_double(rs[i]) * exp2(static_cast<double>(ms[i]) - static_cast<double>(M));
+    for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
+    if (row_ok && gl == 0) {
+      if (!(zl > 0.0) || !isfinite(zl) || !isfinite(M)) err |= SV_ERRF_NONFINITE;
+      s_L[r] = static_cast<double>(M) + log2(zl);
     }
   }
-  if (err != 0u) atomicOr(&s_err, err);
-  __syncthreads();
+  // s_L is written by the group leaders and read by other lanes of this wave.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
+  const float Tv = temperature_of(P.temperature, b);
+  if (!(Tv > 0.0f) || !isfinite(Tv)) err |= SV_ERRF_TEMPERATURE;
   const double c64 = static_cast<double>(c.hi) + static_cast<double>(c.lo);
-  if (tid < kWave) {
-    const int k = tid;
-    uint32_t e = 0u;
-    bool reject = false;
-    const float Tv = temperature_of(P.temperature, b);
-    if (!(Tv > 0.0f) || !isfinite(Tv)) e |= SV_ERRF_TEMPERATURE;
-    if (k < K) {
-      const int x = s_x[k];
-      float pf = NAN, qf = NAN;
-      if (x >= 0 && x < P.V) {
-        const double p = exp2(static_cast<double>(s_lt[k]) * c64 - s_L[k]);
-        const double q = exp2(static_cast<double>(s_ld[k]) * c64 - s_L[K + 1 + k]);
-        const double alpha = (p > 0.0) ? ((q > 0.0) ? fmin(1.0, p / q) : 1.0) : 0.0;
-        reject = !(static_cast<double>(s_u[k]) < alpha);
-        pf = static_cast<float>(p);
-        qf = static_cast<float>(q);
-      }
-      if (P.p_draft != nullptr) P.p_draft[static_cast<int64_t>(b) * K + k] = pf;
-      if (P.q_draft != nullptr) P.q_draft[static_cast<int64_t>(b) * K + k] = qf;
+  bool reject = false;
+  if (lane < K) {
+    float pf = NAN, qf = NAN;
+    if (x >= 0 && x < P.V) {
+      const double p = exp2(static_cast<double>(lt) * c64 - s_L[lane]);
+      const double q = exp2(static_cast<double>(ld) * c64 - s_L[K + 1 + lane]);
+      const double alpha = (p > 0.0) ? ((q > 0.0) ? fmin(1.0, p / q) : 1.0) : 0.0;
+      reject = !(static_cast<double>(u) < alpha);
+      pf = static_cast<float>(p);
+      qf = static_cast<float>(q);
     }
-    if (e != 0u) atomicOr(&s_err, e);
-    const uint64_t rej = __ballot(reject);
-    if (tid == 0) s_j = (rej != 0ull) ? (__ffsll(static_cast<unsigned long long>(rej)) - 1) : K;
+    if (P.p_draft != nullptr) P.p_draft[static_cast<int64_t>(b) * K + lane] = pf;
+    if (P.q_draft != nullptr) P.q_draft[static_cast<int64_t>(b) * K + lane] = qf;
   }
-  __syncthreads();
+  const uint64_t rej = __ballot(reject);
+  const int j = (rej != 0ull) ? (__ffsll(static_cast<unsigned long long>(rej)) - 1) : K;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) err |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(err), o, kWave));
+  const bool bad = err != 0u;
 
-  const uint32_t serr = s_err;
-  const bool bad = serr != 0u;
-  const int j = s_j;
-  for (int i = tid; i <= K; i += kThreads) {
-    if (i == j && !bad) continue;  // the drawn token: written by the sampling pass
-    P.out_tokens[static_cast<int64_t>(b) * (K + 1) + i] = (bad || i > j) ? -1 : s_x[i];
-  }
-  if (tid == 0) {
+  // Lane i writes out_tokens[i] (K + 1 <= 64): its own token up to j, -1 after;
+  // the drawn token at j is written by the sampling pass.
+  if (lane <= K && !(lane == j && !bad))
+    P.out_tokens[static_cast<int64_t>(b) * (K + 1) + lane] = (bad || lane > j) ? -1 : x;
+  if (lane == 0) {
     P.accept_len[b] = bad ? -1 : j;
     if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
-    raise_error(P.err_flags, serr);
+    raise_error(P.err_flags, err);
     SeqPlan pl;
     pl.j = bad ? -1 : j;
     pl.c_hi = c.hi;
@@ -434,17 +449,18 @@ __device__ void decide_seq(const ChainParams& P, int b) {
       pl.d_hi = 0.0f;
       pl.d_lo = 0.0f;
     }
-    pl.valid = 1u;
-    P.plan[b] = pl;
+    pl.pad = 0u;
+    publish_plan(P, b, pl);
+    *s_plan = pl;
   }
   // Consumed: the sequence's statistics pieces and gathered logits go back
   // to zero for the next call.
   const int64_t per_seq = slots_per_seq(P.L);
-  for (int64_t s = static_cast<int64_t>(b) * per_seq + tid; s < (static_cast<int64_t>(b) + 1) * per_seq; s += kThreads) {
-    P.part_m[s] = 0ull;
-    P.part_s[s] = 0ull;
+  for (int64_t sl = static_cast<int64_t>(b) * per_seq + lane; sl < (static_cast<int64_t>(b) + 1) * per_seq; sl += kWave) {
+    P.part_m[sl] = 0ull;
+    P.part_s[sl] = 0ull;
   }
-  if (tid < R) P.gat[static_cast<int64_t>(b) * R + tid] = 0ull;
+  for (int r = lane; r < R; r += kWave) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
 }
 
 template <class T>
@@ -710,22 +726,39 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   }
 }
 
-// Sampling work item `blk` of sequence b: the weights of tiles
-// [blk * TPB, blk * TPB + TPB) of the sampling row pair, published as
-// per-tile totals; the last item of the sequence to arrive draws the token
-// and returns the sequence's sampling workspace (tile totals, plan, counter)
-// to zero.
+// A sampling workgroup of sequence b. It takes the next ticket t of the
+// sequence; ticket 0 decides, the others wait for its plan. Then the weights
+// of tiles [t * TPB, t * TPB + TPB) of the sampling row pair, published as
+// per-tile totals; the last workgroup of the sequence to finish draws the
+// token and returns the sequence's sampling workspace (tile totals, plan,
+// ticket and arrival counters) to zero.
 template <class T>
-__device__ void sample_item(const ChainParams& P, int b, int blk) {
+__device__ void sample_seq(const ChainParams& P, int b) {
   constexpr int TPB = SampleTiles<T>::kPerBlock;
   constexpr int NV = kEptVecs<T>;
   __shared__ double s_red[TPB][kWaves];
   __shared__ int s_flag;
-  const SeqPlan pl = P.plan[b];  // written by the decision launch
-  if (pl.valid == 0u) {
-    raise_error(P.err_flags, threadIdx.x == 0 ? kErrInternal : 0u);
-    return;
+  __shared__ int s_ticket;
+  __shared__ SeqPlan s_plan;
+  if (threadIdx.x == 0)
+    s_ticket = static_cast<int>(__hip_atomic_fetch_add(&P.ticket[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  __syncthreads();
+  const int blk = s_ticket;
+  if (blk == 0) {
+    if (wave_id() == 0) decide_wave<T>(P, b, &s_plan);
+    __syncthreads();
+  } else {
+    if (threadIdx.x == 0) {
+      uint32_t err = 0u;
+      s_plan = await_plan(P, b, &err);
+      if (err != 0u) {
+        s_plan.j = -1;
+        raise_error(P.err_flags, err);
+      }
+    }
+    __syncthreads();
   }
+  const SeqPlan pl = s_plan;
 
   if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
     const SampleRows S = sample_rows<T>(P, b, pl, false);
@@ -756,12 +789,13 @@ __device__ void sample_item(const ChainParams& P, int b, int blk) {
 
   if (!arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(P.nblk_b), &s_flag)) return;
   if (pl.j >= 0) chain_draw<T>(P, b, pl);
-  // Every workgroup of the sequence has read the plan and published its
-  // totals: leave the sequence's sampling workspace all zero.
+  // Every workgroup of the sequence has taken its ticket, read the plan and
+  // published its totals: leave the sequence's sampling workspace all zero.
   __syncthreads();
   if (pl.j >= 0)
     for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
-  if (threadIdx.x == 0) P.plan[b] = SeqPlan{};
+  if (threadIdx.x < kPlanWords) clear_slot(&P.plan_w[static_cast<int64_t>(b) * kPlanWords + threadIdx.x]);
+  if (threadIdx.x == 0) __hip_atomic_store(&P.ticket[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   reset_counter(&P.cnt[b]);
 }
 
@@ -780,16 +814,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
     stats_segment<T>(P, b, rem / P.L.nseg, rem % P.L.nseg);
 }
 
-// Pass 2: one workgroup per sequence.
-template <class T>
-__global__ __launch_bounds__(kThreads) void chain_decide_kernel(ChainParams P) {
-  decide_seq<T>(P, blockIdx.x);
-}
-
-// Pass 3: nblk_b workgroups per sequence.
+// Pass 2: nblk_b workgroups per sequence, assigned round-robin over the
+// sequences: workgroups are dispatched in index order over a few
+// microseconds, so every sequence's first workgroup (its decider, usually)
+// starts among the first B.
 template <class T>
 __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
-  sample_item<T>(P, blockIdx.x / P.nblk_b, blockIdx.x % P.nblk_b);
+  sample_seq<T>(P, static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.B)));
 }
 
 // ---------------------------------------------------------------- launcher
@@ -803,9 +834,6 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
   hipExtLaunchKernelGGL(chain_stats_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream,
                         ev.before, ev.after, 0u, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chain_decide_kernel<T>, dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, stream, p);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chain_sample_kernel<T>, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();

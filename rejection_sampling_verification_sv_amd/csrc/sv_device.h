@@ -197,12 +197,14 @@ __device__ __forceinline__ uint64_t peek(const uint64_t* slot) {
 // wall time, or as soon as *abort is set by another expired wait, give up,
 // set *abort, flag kErrInternal and return 0 (so a failure drains the launch
 // quickly instead of spinning).
+// kSleep sets the pause between polls (s_sleep units of 64 cycles).
+template <int kSleep = 2>
 __device__ __forceinline__ uint64_t await_slot(uint64_t* slot, uint32_t* err, uint64_t* abort) {
   uint64_t v = peek(slot);
   if (v != 0ull) return v;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (;;) {
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(kSleep);
     v = peek(slot);
     if (v != 0ull) return v;
     if (peek(abort) != 0ull) break;

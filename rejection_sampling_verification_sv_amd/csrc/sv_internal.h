@@ -12,8 +12,8 @@
 namespace sv {
 
 // The decision of one sequence as the sampling step needs it: which row pair
-// to draw from and the rows' normalisers (written by the decision kernel,
-// read by every sampling workgroup of the sequence).
+// to draw from and the rows' normalisers (made by one sampling workgroup of
+// the sequence, handed to the others as kPlanWords tagged 32-bit words).
 struct SeqPlan {
   int32_t j;     // first rejected position; K = bonus draw; -1 = invalid row
   float c_hi;    // log2(e) / T as an unevaluated fp32 sum c_hi + c_lo
@@ -22,8 +22,9 @@ struct SeqPlan {
   float lt_lo;   //   c, as lt_hi + lt_lo:  p_t(v) = 2^(x_t c - L_t)
   float d_hi;    // D = L_d - L_t as d_hi + d_lo:  p_d(v) / p_t(v) =
   float d_lo;    //   2^((x_d - x_t) c - D)    (unused for the bonus draw)
-  uint32_t valid;  // 1 once written (the workspace is zero otherwise)
+  uint32_t pad;
 };
+constexpr int kPlanWords = 8;  // 32-bit fields of a SeqPlan
 
 // How a streaming pass cuts the logit rows of a call into work items, and
 // where each item publishes one 64-bit slot per row piece. Two layouts:
@@ -96,8 +97,9 @@ struct ChainParams {
   // workspace (all zero between calls)
   uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi)
   uint64_t* part_s;   // per row piece: tagged fp64 sum of 2^(x c - reference)
-  SeqPlan* plan;      // [B] decision -> sampling hand-off
-  uint32_t* cnt;      // [B] sampling arrivals
+  uint64_t* plan_w;   // [B, kPlanWords] tagged plan words, decider -> other sampling workgroups
+  uint32_t* ticket;   // [B] sampling workgroups started (ticket 0 decides)
+  uint32_t* cnt;      // [B] sampling workgroups finished
   uint64_t* tile_sum; // [B, ntiles] tagged fp64 sampling weight per tile
   uint64_t* gat;      // [B, 2K+1] tagged fp32 logit of row r at its drafted
                       // token (rows 0..K-1 and K+1..2K; set by the pass that
@@ -120,9 +122,13 @@ struct TreeParams {
 
 constexpr int kSampleEPT = 8;                      // sampling elements per thread per tile
 constexpr int kSampleTile = 256 * kSampleEPT;      // elements per sampling tile
-// Tiles per resolving workgroup: 16 KB of each sampled row either way.
-constexpr int kSampleTilesBF16 = 4;
-constexpr int kSampleTilesF32 = 2;
+// Tiles per sampling workgroup (the same bytes of each sampled row for both
+// dtypes).
+#ifndef SV_SAMPLE_TILES_BF16
+#define SV_SAMPLE_TILES_BF16 8
+#endif
+constexpr int kSampleTilesBF16 = SV_SAMPLE_TILES_BF16;
+constexpr int kSampleTilesF32 = kSampleTilesBF16 / 2;
 
 // Segments layout: kThreads * kStatsUnroll * kStatsBatches vectors per segment.
 constexpr int kStatsUnroll = 4;
@@ -154,7 +160,7 @@ struct PassEvents {
 };
 PassEvents take_pass_events();
 
-// The launches of a chain call (statistics, decision, sampling) and of a tree
+// The launches of a chain call (statistics; decision and sampling) and of a tree
 // call (argmax, decision); `ev` (possibly null events) become the start and
 // stop events of the streaming pass.
 hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
