@@ -27,9 +27,9 @@ int32_t stats_segments(int32_t V, sv_dtype d) {
 
 // A streaming pass over B sequences of `rows` rows of V elements, cut into
 // work items; `chunked` (rows of whole 16-byte vectors on 16-byte
-// boundaries) selects the chunked layout: about kChunksTarget chunks over the
+// boundaries) selects the chunked layout: about `chunks` chunks over the
 // call, each of at least kChunkMinVecs vectors, the same number per sequence.
-sv::PieceLayout piece_layout(int64_t B, int32_t rows, int32_t V, sv_dtype d, bool chunked) {
+sv::PieceLayout piece_layout(int64_t B, int32_t rows, int32_t V, sv_dtype d, bool chunked, int chunks) {
   sv::PieceLayout L{};
   L.rows = rows;
   L.nseg = stats_segments(V, d);
@@ -37,7 +37,7 @@ sv::PieceLayout piece_layout(int64_t B, int32_t rows, int32_t V, sv_dtype d, boo
   if (chunked) {
     const int64_t nvec = static_cast<int64_t>(V) * dtype_bytes(d) / 16;
     const int64_t seq_vecs = rows * nvec;
-    int64_t p = ceil_div(B * seq_vecs, sv::kChunksTarget);
+    int64_t p = ceil_div(B * seq_vecs, chunks);
     if (p < sv::kChunkMinVecs) p = sv::kChunkMinVecs;
     L.cps = static_cast<int32_t>(ceil_div(seq_vecs, p));
     L.per = ceil_div(seq_vecs, L.cps);
@@ -51,10 +51,10 @@ bool whole_vector_rows(int32_t V, sv_dtype d) { return (static_cast<int64_t>(V) 
 
 // Slots the pass needs under either layout (the workspace does not depend on
 // the alignment of the logits the call is made with).
-int64_t piece_slots(int64_t B, int32_t rows, int32_t V, sv_dtype d) {
-  const int64_t seg = B * sv::slots_per_seq(piece_layout(B, rows, V, d, false));
+int64_t piece_slots(int64_t B, int32_t rows, int32_t V, sv_dtype d, int chunks) {
+  const int64_t seg = B * sv::slots_per_seq(piece_layout(B, rows, V, d, false, chunks));
   if (!whole_vector_rows(V, d) || B == 0) return seg;
-  const int64_t ch = B * sv::slots_per_seq(piece_layout(B, rows, V, d, true));
+  const int64_t ch = B * sv::slots_per_seq(piece_layout(B, rows, V, d, true, chunks));
   return ch > seg ? ch : seg;
 }
 
@@ -69,7 +69,7 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
   L.tiles_per_block = d == SV_DTYPE_BF16 ? sv::kSampleTilesBF16 : sv::kSampleTilesF32;
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
-  const int64_t parts = piece_slots(B, R, V, d);
+  const int64_t parts = piece_slots(B, R, V, d, sv::kChunksChain);
   size_t off = 0;
   L.off_part_m = off;
   off = align_up(off + sizeof(uint64_t) * parts);
@@ -99,7 +99,7 @@ TreeLayout tree_layout(int32_t B, int32_t N, int32_t V, sv_dtype d) {
   TreeLayout L{};
   size_t off = 0;
   L.off_part = off;
-  off = align_up(off + sizeof(uint64_t) * piece_slots(B, N + 1, V, d));
+  off = align_up(off + sizeof(uint64_t) * piece_slots(B, N + 1, V, d, sv::kChunksTree));
   L.total = off;
   return L;
 }
@@ -175,7 +175,7 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   // The chunked layout needs every row on a 16-byte boundary.
   const bool chunked = whole_vector_rows(V, dtype) && aligned_to(target_logits, 16) &&
                        (K == 0 || aligned_to(draft_logits, 16));
-  p.L = piece_layout(B, 2 * K + 1, V, dtype, chunked);
+  p.L = piece_layout(B, 2 * K + 1, V, dtype, chunked, sv::kChunksChain);
   p.ntiles = L.ntiles;
   p.tiles_per_block = L.tiles_per_block;
   p.nblk_b = L.nblk_b;
@@ -226,7 +226,8 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
   p.B = B;
   p.N = N;
   p.V = V;
-  p.L = piece_layout(B, N + 1, V, dtype, whole_vector_rows(V, dtype) && aligned_to(target_logits, 16));
+  p.L = piece_layout(B, N + 1, V, dtype, whole_vector_rows(V, dtype) && aligned_to(target_logits, 16),
+                     sv::kChunksTree);
   if (static_cast<int64_t>(B) * sv::items_per_seq(p.L) > INT32_MAX) return SV_ERR_UNSUPPORTED;
   p.accept_len = accept_len;
   p.path_nodes = path_nodes;

@@ -142,12 +142,16 @@ constexpr int kStatsSegVecs = 256 * kStatsUnroll * kStatsBatches;
 #endif
 constexpr int kStreamU = SV_STREAM_U;
 
-// Chunked layout: about this many chunks per call, each with at least
-// kChunkMinVecs 16-byte vectors.
-#ifndef SV_CHUNKS
-#define SV_CHUNKS 4096
+// Chunked layout: about this many chunks per call (measured best for each
+// stream on c2 / c4), each with at least kChunkMinVecs 16-byte vectors.
+#ifndef SV_CHUNKS_CHAIN
+#define SV_CHUNKS_CHAIN 2048
 #endif
-constexpr int kChunksTarget = SV_CHUNKS;
+#ifndef SV_CHUNKS_TREE
+#define SV_CHUNKS_TREE 4096
+#endif
+constexpr int kChunksChain = SV_CHUNKS_CHAIN;
+constexpr int kChunksTree = SV_CHUNKS_TREE;
 constexpr int kChunkMinVecs = 256 * kStatsUnroll * 2;
 
 static_assert(kErrInternal == SV_ERRF_INTERNAL, "error bit mismatch");
