@@ -202,7 +202,7 @@ __device__ __forceinline__ void publish_gather(const ChainParams& P, int b, int 
   publish(&P.gat[static_cast<int64_t>(b) * (2 * P.K + 1) + r], tag_float(load_elem<T>(row, x)));
 }
 
-// Rows layout: segment `seg` of row r of sequence b (any alignment), its
+// Segments layout: segment `seg` of row r of sequence b (any alignment), its
 // (reference, sum) to slot (b * (2K+1) + r) * nseg + seg.
 template <class T>
 __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
@@ -623,49 +623,53 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   __syncthreads();
 
   // (1) total weight and the tile holding u * total (wave 0, fp64, tile order).
-  //     With at most 64 tiles the totals stay in registers between the passes.
+  //     Up to 64 tiles (the usual case) take one inclusive scan; more tiles
+  //     are scanned in rounds of 64, twice (total first, then the search).
   if (tid < kWave) {
     uint32_t err = 0u;
-    const bool one_chunk = P.ntiles <= kWave;
-    double v0 = (one_chunk && lane < P.ntiles) ? untag_nonneg_double(await_slot(&ts[lane], &err, P.abort)) : 0.0;
-    double carry = 0.0;
-    int last_pos = -1;
-    for (int base = 0; base < P.ntiles; base += kWave) {
-      const int t = base + lane;
-      const double v = one_chunk ? v0 : ((t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err, P.abort)) : 0.0);
-      double inc = v;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double n = __shfl_up(inc, o, kWave);
-        if (lane >= o) inc += n;
-      }
-      const uint64_t pos = __ballot(t < P.ntiles && v > 0.0);
-      if (pos != 0ull) last_pos = base + 63 - __clzll(static_cast<long long>(pos));
-      carry += __shfl(inc, kWave - 1, kWave);
-    }
-    const double total = carry;
-    const double target = u * total;
-    int found = -1;
-    double prefix = 0.0;
-    carry = 0.0;
-    for (int base = 0; base < P.ntiles && found < 0; base += kWave) {
-      const int t = base + lane;
-      const double v = one_chunk ? v0 : ((t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err, P.abort)) : 0.0);
-      double inc = v;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double n = __shfl_up(inc, o, kWave);
-        if (lane >= o) inc += n;
-      }
+    double total, target, prefix = 0.0;
+    int found = -1, last_pos = -1;
+    if (P.ntiles <= kWave) {
+      const double v = (lane < P.ntiles) ? untag_nonneg_double(await_slot(&ts[lane], &err, P.abort)) : 0.0;
+      const double inc = wave_inclusive_scan(v);
       double excl = __shfl_up(inc, 1, kWave);
       if (lane == 0) excl = 0.0;
-      const uint64_t hit = __ballot(t < P.ntiles && v > 0.0 && carry + inc > target);
+      const uint64_t pos = __ballot(lane < P.ntiles && v > 0.0);
+      if (pos != 0ull) last_pos = 63 - __clzll(static_cast<long long>(pos));
+      total = __shfl(inc, kWave - 1, kWave);
+      target = u * total;
+      const uint64_t hit = __ballot(lane < P.ntiles && v > 0.0 && inc > target);
       if (hit != 0ull) {
-        const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-        found = base + l;
-        prefix = carry + __shfl(excl, l, kWave);
+        found = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        prefix = __shfl(excl, found, kWave);
       }
-      carry += __shfl(inc, kWave - 1, kWave);
+    } else {
+      double carry = 0.0;
+      for (int base = 0; base < P.ntiles; base += kWave) {
+        const int t = base + lane;
+        const double v = (t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err, P.abort)) : 0.0;
+        const double inc = wave_inclusive_scan(v);
+        const uint64_t pos = __ballot(t < P.ntiles && v > 0.0);
+        if (pos != 0ull) last_pos = base + 63 - __clzll(static_cast<long long>(pos));
+        carry += __shfl(inc, kWave - 1, kWave);
+      }
+      total = carry;
+      target = u * total;
+      carry = 0.0;
+      for (int base = 0; base < P.ntiles && found < 0; base += kWave) {
+        const int t = base + lane;
+        const double v = (t < P.ntiles) ? untag_nonneg_double(peek(&ts[t])) : 0.0;  // seen above
+        const double inc = wave_inclusive_scan(v);
+        double excl = __shfl_up(inc, 1, kWave);
+        if (lane == 0) excl = 0.0;
+        const uint64_t hit = __ballot(t < P.ntiles && v > 0.0 && carry + inc > target);
+        if (hit != 0ull) {
+          const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+          found = base + l;
+          prefix = carry + __shfl(excl, l, kWave);
+        }
+        carry += __shfl(inc, kWave - 1, kWave);
+      }
     }
     if (err != 0u) atomicOr(&s_err, err);
     if (tid == 0) {

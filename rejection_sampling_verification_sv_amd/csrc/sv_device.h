@@ -94,6 +94,16 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// Inclusive prefix sum over the wave in lane order (fp64).
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double n = __shfl_up(v, o, kWave);
+    if ((threadIdx.x & (kWave - 1)) >= o) v += n;
+  }
+  return v;
+}
+
 __device__ __forceinline__ int wave_max_int(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));

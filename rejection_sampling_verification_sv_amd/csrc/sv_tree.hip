@@ -178,6 +178,102 @@ __device__ void tree_decide(const TreeParams& P, int b) {
     P.part[s] = 0ull;
 }
 
+// Trees of at most kWave nodes: the same decision made by one wave, one node
+// per lane, with cross-lane shuffles instead of LDS and block barriers.
+// Lane n also holds g at position n (lane 0 holds position 64 as well when
+// N = 64); pointer jumping takes 6 rounds (2^6 = 64 >= any depth); the path
+// is read off by walking up from the deepest accepted node.
+__device__ void tree_decide_wave(const TreeParams& P, int b) {
+  const int N = P.N;
+  const int N1 = N + 1;
+  const int lane = lane_id();
+  uint32_t err = 0u;
+
+  // g at positions lane and (lane 0 only) 64
+  const int pmax = max_pieces(P.L);
+  int g = 0, g64 = 0;
+  for (int rep = 0; rep < 2; ++rep) {
+    const int n = rep == 0 ? lane : kWave;
+    if (n >= N1 || (rep == 1 && lane != 0)) continue;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int p = 0; p < pmax; ++p) {
+      const int64_t sl = piece_slot(P.L, b, n, p);
+      if (sl < 0) break;
+      const uint64_t slot = load_ready(&P.part[sl], &err);
+      const float v = __uint_as_float(static_cast<uint32_t>(slot >> 32));
+      const int i = static_cast<int>(static_cast<uint32_t>(slot) - 1u);
+      if (better(v, i, bv, bi)) {
+        bv = v;
+        bi = i;
+      }
+    }
+    const int gi = (bi == INT_MAX) ? 0 : bi;  // a row of -inf only: its first index
+    if (rep == 0) g = gi; else g64 = gi;
+  }
+
+  // node `lane`: validity, match with its parent's argmax (every shuffle
+  // below is taken by the whole wave)
+  const bool node = lane < N;
+  int par = -1, tok = -1;
+  bool par_ok = true;
+  if (node) {
+    par = P.parents[lane];
+    tok = P.tokens[static_cast<int64_t>(b) * N + lane];
+    par_ok = (par == -1) || (par >= 0 && par < lane);
+    if (!par_ok) err |= SV_ERRF_PARENT;
+    if (tok < 0 || tok >= P.V) err |= SV_ERRF_TOKEN;
+    if (!par_ok) par = -1;
+  }
+  const int pos = par >= 0 ? par + 1 : 0;  // <= lane < 64: held by lane `pos`
+  const int want = __shfl(g, pos, kWave);
+  bool ok = node && par_ok && tok == want;
+  // Pointer jumping: anc = first ancestor not yet folded in, dep = nodes
+  // from this one up to (not including) anc, ok = AND of their matches.
+  int anc = par, dep = 1;
+#pragma unroll
+  for (int round = 0; round < 6; ++round) {
+    const int a = anc >= 0 ? anc : lane;
+    const int ok_a = __shfl(static_cast<int>(ok), a, kWave);
+    const int dep_a = __shfl(dep, a, kWave);
+    const int anc_a = __shfl(anc, a, kWave);
+    if (anc >= 0) {
+      ok = ok && ok_a != 0;
+      dep += dep_a;
+      anc = anc_a;
+    }
+  }
+  // deepest accepted node, lowest index on ties: max of (depth, 2047 - i)
+  int key = (node && ok) ? ((dep << 11) | (2047 - lane)) : -1;
+  key = wave_max_int(key);
+  const int best = key < 0 ? -1 : 2047 - (key & 2047);
+  const int depth = key < 0 ? 0 : (key >> 11);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) err |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(err), o, kWave));
+  const bool bad = err != 0u;
+
+  // the path, root side first: walk up from `best`, lane d keeps the node at depth d + 1
+  int mine = -1;
+  int k = best;
+  for (int d = depth - 1; d >= 0; --d) {
+    if (lane == d) mine = k;
+    k = __shfl(par, k, kWave);  // k is the same in every lane
+  }
+  for (int i = lane; i < N; i += kWave)
+    P.path_nodes[static_cast<int64_t>(b) * N + i] = (!bad && i < depth) ? mine : -1;
+  const int npos = best + 1;  // the position after the accepted path
+  const int g_next = npos < kWave ? __shfl(g, npos, kWave) : __shfl(g64, 0, kWave);
+  if (lane == 0) {
+    P.accept_len[b] = bad ? -1 : depth;
+    P.next_token[b] = bad ? -1 : g_next;
+    raise_error(P.err_flags, err);
+  }
+  // Consumed: the sequence's pieces go back to zero for the next call.
+  const int64_t per_seq = slots_per_seq(P.L);
+  for (int64_t sl = static_cast<int64_t>(b) * per_seq + lane; sl < (static_cast<int64_t>(b) + 1) * per_seq; sl += kWave)
+    P.part[sl] = 0ull;
+}
+
 // One thread's share of the vectors [p0, p1) of a row (16-byte aligned body):
 // full batches of kStatsUnroll vectors per thread without masking, then one
 // ragged batch padded with -inf. Each thread sees its elements in ascending
@@ -311,6 +407,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 
 __global__ __launch_bounds__(kThreads) void tree_decide_kernel(TreeParams P) { tree_decide(P, blockIdx.x); }
 
+// Trees of at most 64 nodes: one wave per sequence.
+__global__ __launch_bounds__(kWave) void tree_decide_wave_kernel(TreeParams P) { tree_decide_wave(P, blockIdx.x); }
+
 __global__ __launch_bounds__(kThreads) void tree_mask_kernel(const int32_t* parents, int N, uint8_t* mask,
                                                              int32_t* err_flags) {
   __shared__ uint32_t s_bits[SV_MAX_TREE_NODES / 32];
@@ -347,7 +446,10 @@ static hipError_t launch_tree_t(const TreeParams& p, const PassEvents& ev, hipSt
                         ev.before, ev.after, 0u, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tree_decide_kernel, dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, stream, p);
+  if (p.N <= kWave)
+    hipLaunchKernelGGL(tree_decide_wave_kernel, dim3(static_cast<uint32_t>(p.B)), dim3(kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL(tree_decide_kernel, dim3(static_cast<uint32_t>(p.B)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

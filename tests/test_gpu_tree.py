@@ -80,20 +80,36 @@ def test_random_trees(sv, B, N, V, dtype):
                  f"random tree B{B} N{N} V{V}")
 
 
-def test_chain_shaped_deep_tree(sv):
-    B, N, V = 4, 1024, 64
-    rng = np.random.Generator(np.random.Philox(310))
+@pytest.mark.parametrize("N", [64, 1024])
+def test_chain_shaped_deep_tree(sv, N):
+    """A chain of N nodes: depth N (all pointer-jumping rounds), cut at several depths."""
+    B, V = 4, 64
+    rng = np.random.Generator(np.random.Philox(310 + N))
     parents = np.arange(-1, N - 1, dtype=np.int32)
     target = torch.from_numpy(rng.standard_normal((B, N + 1, V))).float()
     g = target.numpy().argmax(-1)
     tokens = g[:, :N].copy().astype(np.int32)
-    cuts = [N, 1000, 3, 0]
+    cuts = [N, N - 24, 3, 0]
     for b, c in enumerate(cuts):
         if c < N:
             tokens[b, c] = (g[b, c] + 1) % V
     out, ref = _tree_parity(sv, target.cuda(), torch.from_numpy(tokens).cuda(), torch.from_numpy(parents).cuda(),
-                            "chain-shaped tree N1024")
+                            f"chain-shaped tree N{N}")
     np.testing.assert_array_equal(_np(out["accept_len"]), cuts)
+
+
+def test_star_tree_accepts_at_most_one(sv):
+    B, N, V = 6, 64, 500
+    rng = np.random.Generator(np.random.Philox(313))
+    parents = np.full(N, -1, dtype=np.int32)
+    target = torch.from_numpy(rng.standard_normal((B, N + 1, V)) * 2).to(torch.bfloat16)
+    g = target.float().numpy().argmax(-1)
+    tokens = rng.integers(0, V, (B, N)).astype(np.int32)
+    tokens[:3, 17] = g[:3, 0]   # a child of the root that matches
+    tokens[:2, 40] = g[:2, 0]   # a second matching child: the lower id wins
+    out, ref = _tree_parity(sv, target.cuda(), torch.from_numpy(tokens).cuda(), torch.from_numpy(parents).cuda(),
+                            "star tree N64")
+    assert np.all(ref["accept_len"] <= 1)
 
 
 def test_argmax_ties_lowest_id(sv):
