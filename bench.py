@@ -195,7 +195,7 @@ def main():
         config = {"workload": cfg.name, "B": B, "K": K, "V": V, "logits": cfg.dtype,
                   "temperature": cfg.temperature if cfg.temperature is not None else list(cfg.temperature_range),
                   "input_sets_rotated": len(sets)}
-        kernel_name = "chain_stats_kernel (statistics pass: every logit row once)"
+        kernel_name = "chain_stats_chunk_kernel (statistics pass: every logit row once)"
     else:
         cfg = TREE_CONFIGS[wl]
         B, N, V = cfg.B, cfg.N, cfg.V

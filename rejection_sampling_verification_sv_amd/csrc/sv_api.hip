@@ -25,21 +25,21 @@ int32_t stats_segments(int32_t V, sv_dtype d) {
   return static_cast<int32_t>(n < 1 ? 1 : n);
 }
 
+int64_t row_vecs(int32_t V, sv_dtype d) { return static_cast<int64_t>(V) * dtype_bytes(d) / 16; }
+
 // A streaming pass over B sequences of `rows` rows of V elements, cut into
 // work items; `chunked` (rows of whole 16-byte vectors on 16-byte
-// boundaries) selects the chunked layout: about `chunks` chunks over the
-// call, each of at least kChunkMinVecs vectors, the same number per sequence.
-sv::PieceLayout piece_layout(int64_t B, int32_t rows, int32_t V, sv_dtype d, bool chunked, int chunks) {
+// boundaries) selects the chunked layout: chunks of at most `chunk_vecs`
+// vectors, balanced within each sequence.
+sv::PieceLayout piece_layout(int32_t rows, int32_t V, sv_dtype d, bool chunked, int64_t chunk_vecs) {
   sv::PieceLayout L{};
   L.rows = rows;
   L.nseg = stats_segments(V, d);
   L.seg_vecs = sv::kStatsSegVecs;
   if (chunked) {
-    const int64_t nvec = static_cast<int64_t>(V) * dtype_bytes(d) / 16;
+    const int64_t nvec = row_vecs(V, d);
     const int64_t seq_vecs = rows * nvec;
-    int64_t p = ceil_div(B * seq_vecs, chunks);
-    if (p < sv::kChunkMinVecs) p = sv::kChunkMinVecs;
-    L.cps = static_cast<int32_t>(ceil_div(seq_vecs, p));
+    L.cps = static_cast<int32_t>(ceil_div(seq_vecs, chunk_vecs));
     L.per = ceil_div(seq_vecs, L.cps);
     L.nvec = nvec;
     L.kmax = static_cast<int32_t>((L.per + nvec - 2) / nvec + 1);
@@ -49,12 +49,19 @@ sv::PieceLayout piece_layout(int64_t B, int32_t rows, int32_t V, sv_dtype d, boo
 
 bool whole_vector_rows(int32_t V, sv_dtype d) { return (static_cast<int64_t>(V) * dtype_bytes(d)) % 16 == 0; }
 
+// Chunk size of a streaming pass cut into about `chunks` chunks per call,
+// each of at least kChunkMinVecs vectors.
+int64_t chunk_vecs(int64_t B, int32_t rows, int32_t V, sv_dtype d, int chunks) {
+  const int64_t p = ceil_div(B * rows * row_vecs(V, d), chunks);
+  return p < sv::kChunkMinVecs ? sv::kChunkMinVecs : p;
+}
+
 // Slots the pass needs under either layout (the workspace does not depend on
 // the alignment of the logits the call is made with).
-int64_t piece_slots(int64_t B, int32_t rows, int32_t V, sv_dtype d, int chunks) {
-  const int64_t seg = B * sv::slots_per_seq(piece_layout(B, rows, V, d, false, chunks));
+int64_t piece_slots(int64_t B, int32_t rows, int32_t V, sv_dtype d, int64_t chunk_vecs) {
+  const int64_t seg = B * sv::slots_per_seq(piece_layout(rows, V, d, false, chunk_vecs));
   if (!whole_vector_rows(V, d) || B == 0) return seg;
-  const int64_t ch = B * sv::slots_per_seq(piece_layout(B, rows, V, d, true, chunks));
+  const int64_t ch = B * sv::slots_per_seq(piece_layout(rows, V, d, true, chunk_vecs));
   return ch > seg ? ch : seg;
 }
 
@@ -69,7 +76,7 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
   L.tiles_per_block = d == SV_DTYPE_BF16 ? sv::kSampleTilesBF16 : sv::kSampleTilesF32;
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
-  const int64_t parts = piece_slots(B, R, V, d, sv::kChunksChain);
+  const int64_t parts = piece_slots(B, R, V, d, chunk_vecs(B, R, V, d, sv::kChunksChain));
   size_t off = 0;
   L.off_part_m = off;
   off = align_up(off + sizeof(uint64_t) * parts);
@@ -99,7 +106,7 @@ TreeLayout tree_layout(int32_t B, int32_t N, int32_t V, sv_dtype d) {
   TreeLayout L{};
   size_t off = 0;
   L.off_part = off;
-  off = align_up(off + sizeof(uint64_t) * piece_slots(B, N + 1, V, d, sv::kChunksTree));
+  off = align_up(off + sizeof(uint64_t) * piece_slots(B, N + 1, V, d, chunk_vecs(B, N + 1, V, d, sv::kChunksTree)));
   L.total = off;
   return L;
 }
@@ -175,7 +182,7 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   // The chunked layout needs every row on a 16-byte boundary.
   const bool chunked = whole_vector_rows(V, dtype) && aligned_to(target_logits, 16) &&
                        (K == 0 || aligned_to(draft_logits, 16));
-  p.L = piece_layout(B, 2 * K + 1, V, dtype, chunked, sv::kChunksChain);
+  p.L = piece_layout(2 * K + 1, V, dtype, chunked, chunk_vecs(B, 2 * K + 1, V, dtype, sv::kChunksChain));
   p.ntiles = L.ntiles;
   p.tiles_per_block = L.tiles_per_block;
   p.nblk_b = L.nblk_b;
@@ -226,8 +233,8 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
   p.B = B;
   p.N = N;
   p.V = V;
-  p.L = piece_layout(B, N + 1, V, dtype, whole_vector_rows(V, dtype) && aligned_to(target_logits, 16),
-                     sv::kChunksTree);
+  p.L = piece_layout(N + 1, V, dtype, whole_vector_rows(V, dtype) && aligned_to(target_logits, 16),
+                     chunk_vecs(B, N + 1, V, dtype, sv::kChunksTree));
   if (static_cast<int64_t>(B) * sv::items_per_seq(p.L) > INT32_MAX) return SV_ERR_UNSUPPORTED;
   p.accept_len = accept_len;
   p.path_nodes = path_nodes;

@@ -1,12 +1,15 @@
 // Chain verification kernels (modified rejection sampling over K proposals).
 //
-// Pass 1 — chain_stats_kernel. Streams every logit row of the call once (the
-// K+1 target rows and K draft rows of each sequence) with coalesced 16-byte
-// loads. Each thread keeps the running maximum m of its logits and the sum of
+// Pass 1 — chain_stats_chunk_kernel (or chain_stats_segment_kernel). Streams
+// every logit row of the call once (the K+1 target rows and K draft rows of
+// each sequence) with coalesced 16-byte non-temporal loads: the logits are
+// read once, and loads that do not allocate in the caches stream faster.
+// Each thread keeps the running maximum m of its logits and the sum of
 // 2^(x*c - m*c), c = log2(e)/T (one pass: a batch of values is reduced to its
 // maximum first, the sum is rescaled once per batch, then the batch's
-// exponentials are added). Each block combines its threads in fp64 and
-// publishes one (reference, sum) pair per row piece. Work items:
+// exponentials are added; two batch buffers alternate so that one batch is
+// always in flight). Each block combines its threads in fp64 and publishes
+// one (reference, sum) pair per row piece. Work items:
 //   chunked layout (rows on 16-byte boundaries, the usual case): each
 //     sequence's rows, laid end to end, are cut into equal chunks, so every
 //     block streams the same number of bytes;
@@ -137,13 +140,14 @@ __device__ __forceinline__ void split(double v, float& hi, float& lo) {
 
 // Block-wide combine of the threads' running states into (reference, sum):
 // the largest fl(mx*c_hi), and the fp64 sum of each thread's sum rescaled to it.
+template <int NW = kWaves>
 __device__ __forceinline__ void block_combine(const Running& st, Scale c, float* s_redf, double* s_redd, float* MC,
                                               double* S) {
   const float mc = (st.mx == -INFINITY) ? -INFINITY : st.mx * c.hi;
-  *MC = block_max(mc, s_redf);
+  *MC = block_max<NW>(mc, s_redf);
   double sd = 0.0;
   if (mc != -INFINITY) sd = static_cast<double>(st.s * fast_exp2(mc - *MC));
-  *S = block_sum(sd, s_redd);
+  *S = block_sum<NW>(sd, s_redd);
 }
 
 template <class T, int U = kStatsUnroll>
@@ -154,31 +158,76 @@ __device__ __forceinline__ void add_batch(Running& st, const uint4 (&raw)[U], Sc
   running_add(st, x, c);
 }
 
+// The exponent scale of a sequence, computed on first use: the statistics
+// pass issues its first loads before it waits for the temperature.
+struct LazyScale {
+  const float* temperature;
+  int b;
+  bool ready;
+  Scale c;
+  __device__ __forceinline__ const Scale& get() {
+    if (!ready) {
+      c = exponent_scale(temperature_of(temperature, b));
+      ready = true;
+    }
+    return c;
+  }
+};
+
 // One thread's share of the vectors [p0, p1) of a row: full batches of
 // kStreamU vectors per thread without any masking, then one ragged batch
-// whose missing vectors are replaced by -inf.
-template <class T>
-__device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, int64_t p1, Scale c, Running& st) {
-  constexpr int U = kStreamU;
-  constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
-  const int64_t nfull = (p1 - p0) / STEP;
-  const uint4* ptr = body + p0 + threadIdx.x;
-#pragma unroll 1
-  for (int64_t i = 0; i < nfull; ++i, ptr += STEP) {
-    uint4 raw[U];
+// whose missing vectors are replaced by -inf. Two batch buffers alternate, so
+// one batch's loads are always in flight while the other is reduced, and the
+// first loads go out before anything (the temperature) is waited for.
+template <class T, int U, int TPB>
+__device__ __forceinline__ void load_batch(const uint4* ptr, uint4 (&raw)[U]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) raw[u] = ptr[u * kThreads];
-    add_batch<T, U>(st, raw, c);
+  for (int u = 0; u < U; ++u) raw[u] = stream_load(ptr + u * TPB);
+  // keep the loads ahead of the reduction that follows them (the scheduler
+  // would otherwise sink them below the wait for the other buffer)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <class T, int TPB>
+__device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, int64_t p1, LazyScale& sc,
+                                                 Running& st) {
+  constexpr int U = kStreamU;
+  constexpr int STEP = TPB * U;
+  const int32_t nfull = static_cast<int32_t>((p1 - p0) / STEP);
+  const uint4* ptr = body + p0 + threadIdx.x;
+  if (nfull > 0) {
+    uint4 a[U], b[U];
+    load_batch<T, U, TPB>(ptr, a);
+    const Scale c = sc.get();
+    // invariant: `a` holds batch i - 1, which starts at ptr
+    int32_t i = 1;
+#pragma unroll 1
+    for (; i + 1 < nfull; i += 2) {
+      load_batch<T, U, TPB>(ptr + STEP, b);
+      add_batch<T, U>(st, a, c);
+      load_batch<T, U, TPB>(ptr + 2 * STEP, a);
+      add_batch<T, U>(st, b, c);
+      ptr += 2 * STEP;
+    }
+    if (i < nfull) {  // one batch left to load
+      load_batch<T, U, TPB>(ptr + STEP, b);
+      add_batch<T, U>(st, a, c);
+      add_batch<T, U>(st, b, c);
+      ptr += 2 * STEP;
+    } else {
+      add_batch<T, U>(st, a, c);
+      ptr += STEP;
+    }
   }
-  const int64_t rest = (p1 - p0) - nfull * STEP;  // vectors in the ragged batch
+  const int64_t rest = (p1 - p0) - static_cast<int64_t>(nfull) * STEP;  // vectors in the ragged batch
   if (rest > 0) {
     uint4 raw[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t k = static_cast<int64_t>(u) * kThreads + threadIdx.x;
-      raw[u] = (k < rest) ? ptr[u * kThreads] : neg_inf_vec<T>();
+      const int64_t k = static_cast<int64_t>(u) * TPB + threadIdx.x;
+      raw[u] = (k < rest) ? stream_load(ptr + u * TPB) : neg_inf_vec<T>();
     }
-    add_batch<T, U>(st, raw, c);
+    add_batch<T, U>(st, raw, sc.get());
   }
 }
 
@@ -233,7 +282,7 @@ __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t vi = base + static_cast<int64_t>(u) * kThreads;
-      raw[u] = (vi < v1) ? body[vi] : neg_inf_vec<T>();
+      raw[u] = (vi < v1) ? stream_load(body + vi) : neg_inf_vec<T>();
     }
     add_batch<T>(st, raw, c);
   }
@@ -254,27 +303,28 @@ __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
 // [ch * per, (ch + 1) * per) of the sequence's 2K+1 rows laid end to end,
 // streamed as one piece per row it touches; the piece of row r goes to slot
 // (b * cps + ch) * kmax + (r - first row of the chunk).
-template <class T>
+template <class T, int TPB>
 __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
-  __shared__ float s_redf[kWaves];
-  __shared__ double s_redd[kWaves];
+  constexpr int NW = TPB / kWave;
+  __shared__ float s_redf[NW];
+  __shared__ double s_redd[NW];
   const int R = 2 * P.K + 1;
   const int64_t nvec = P.L.nvec;
   const int64_t lo = static_cast<int64_t>(ch) * P.L.per;
   const int64_t hi = min(static_cast<int64_t>(R) * nvec, lo + P.L.per);
-  const int r_lo = static_cast<int>(lo / nvec);
-  const int r_hi = static_cast<int>((hi - 1) / nvec);
-  const Scale c = exponent_scale(temperature_of(P.temperature, b));
+  const int r_lo = static_cast<int>(div_nonneg(lo, nvec));
+  const int r_hi = static_cast<int>(div_nonneg(hi - 1, nvec));
+  LazyScale sc{P.temperature, b, false, Scale{0.0f, 0.0f}};
   for (int r = r_lo; r <= r_hi; ++r) {
     const int64_t p0 = max(lo, r * nvec) - r * nvec;
     const int64_t p1 = min(hi, (r + 1) * nvec) - r * nvec;
     const uint4* body = static_cast<const uint4*>(chain_row<T>(P, b, r));
-    const int x = threadIdx.x == 0 ? row_token(P, b, r) : -1;  // consumed after the piece
+    const int x = row_token(P, b, r);  // a uniform (scalar) load, consumed after the piece
     Running st{-INFINITY, 0.0f};
-    flat_piece_stats<T>(body, p0, p1, c, st);
+    flat_piece_stats<T, TPB>(body, p0, p1, sc, st);
     float MC;
     double S;
-    block_combine(st, c, s_redf, s_redd, &MC, &S);
+    block_combine<NW>(st, sc.get(), s_redf, s_redd, &MC, &S);
     if (threadIdx.x == 0) {
       const int64_t slot = (static_cast<int64_t>(b) * P.L.cps + ch) * P.L.kmax + (r - r_lo);
       publish(&P.part_m[slot], tag_float(MC));
@@ -361,41 +411,41 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan) {
     const int r = r0 + lane / G;
     const int gl = lane % G;
     const bool row_ok = r < R;
-    uint64_t rm[4], rs[4];
-    int n = 0;
-    float mf = -INFINITY;  // reference of the folded sum zf
+    // this lane's pieces p = gl, gl + G, ...: rounds of up to four loads in
+    // flight, each round folded into (mf, zf) = (reference, fp64 sum)
+    float mf = -INFINITY;
     double zf = 0.0;
-    for (int p = gl; row_ok && p < pmax; p += G) {
-      const int64_t sl = piece_slot(P.L, b, r, p);
-      if (sl < 0) break;
-      if (n < 4) {
-        rm[n] = P.part_m[sl];
-        rs[n] = P.part_s[sl];
-        ++n;
-      } else {
-        const float mm = untag_float(load_ready(&P.part_m[sl], &err));
-        const double sv = untag_nonneg_double(load_ready(&P.part_s[sl], &err));
-        if (mm != -INFINITY) {
-          if (mm > mf) {
-            zf = (mf == -INFINITY ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(mm))) + sv;
-            mf = mm;
-          } else {
-            zf += sv * exp2(static_cast<double>(mm) - static_cast<double>(mf));
-          }
+    bool more = row_ok;
+    for (int p0 = gl; more; p0 += 4 * G) {
+      uint64_t rm[4], rs[4];
+      int n = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t sl = (p0 + i * G < pmax) ? piece_slot(P.L, b, r, p0 + i * G) : -1;
+        if (sl >= 0 && n == i) {
+          rm[i] = P.part_m[sl];
+          rs[i] = P.part_s[sl];
+          n = i + 1;
+        }
+      }
+      more = (n == 4);
+      for (int i = 0; i < n; ++i) {
+        if (rm[i] == 0ull || rs[i] == 0ull) err |= kErrInternal;
+        const float mm = untag_float(rm[i]);
+        const double sv = untag_nonneg_double(rs[i]);
+        if (mm == -INFINITY) continue;
+        if (mm > mf) {
+          zf = (mf == -INFINITY ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(mm))) + sv;
+          mf = mm;
+        } else {
+          zf += sv * exp2(static_cast<double>(mm) - static_cast<double>(mf));
         }
       }
     }
-    float ms[4];
     float M = mf;
-    for (int i = 0; i < n; ++i) {
-      if (rm[i] == 0ull || rs[i] == 0ull) err |= kErrInternal;
-      ms[i] = untag_float(rm[i]);
-      M = fmaxf(M, ms[i]);
-    }
     for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
-    double zl = (mf == -INFINITY) ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(M));
-    for (int i = 0; i < n; ++i)
-      if (ms[i] != -INFINITY) zl += untag_nonneg_double(rs[i]) * exp2(static_cast<double>(ms[i]) - static_cast<double>(M));
+    const double zl0 = (mf == -INFINITY) ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(M));
+    double zl = zl0;
     for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
     if (row_ok && gl == 0) {
       if (!(zl > 0.0) || !isfinite(zl) || !isfinite(M)) err |= SV_ERRF_NONFINITE;
@@ -805,17 +855,22 @@ __device__ void sample_seq(const ChainParams& P, int b) {
 
 }  // namespace
 
-// Pass 1: one workgroup per statistics item (a chunk, or a row segment).
+// Pass 1, chunked layout: one workgroup per chunk.
 template <class T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_kernel(ChainParams P) {
-  const int64_t per_seq = items_per_seq(P.L);
-  const int64_t k = blockIdx.x;
-  const int b = static_cast<int>(k / per_seq);
-  const int rem = static_cast<int>(k % per_seq);
-  if (P.L.cps > 0)
-    stats_chunk<T>(P, b, rem);
-  else
-    stats_segment<T>(P, b, rem / P.L.nseg, rem % P.L.nseg);
+__global__ __launch_bounds__(kStatsTPB) __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES, SV_STATS_WAVES))) void chain_stats_chunk_kernel(ChainParams P) {
+  // blockIdx.x and the chunks per sequence fit 32 bits (checked on the host)
+  const uint32_t cps = static_cast<uint32_t>(P.L.cps);
+  const uint32_t b = blockIdx.x / cps;
+  stats_chunk<T, kStatsTPB>(P, static_cast<int>(b), static_cast<int>(blockIdx.x - b * cps));
+}
+
+// Pass 1, segments layout: one workgroup per row segment.
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_segment_kernel(ChainParams P) {
+  const uint32_t per_seq = static_cast<uint32_t>(items_per_seq(P.L));
+  const int b = static_cast<int>(blockIdx.x / per_seq);
+  const int rem = static_cast<int>(blockIdx.x - static_cast<uint32_t>(b) * per_seq);
+  stats_segment<T>(P, b, rem / P.L.nseg, rem % P.L.nseg);
 }
 
 // Pass 2: nblk_b workgroups per sequence, assigned round-robin over the
@@ -835,8 +890,12 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
   const int64_t grid_c = static_cast<int64_t>(p.B) * p.nblk_b;
   if (grid_a > INT32_MAX || grid_c > INT32_MAX) return hipErrorInvalidConfiguration;
   // Armed events take the statistics kernel's own start and end timestamps.
-  hipExtLaunchKernelGGL(chain_stats_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream,
-                        ev.before, ev.after, 0u, p);
+  if (p.L.cps > 0)
+    hipExtLaunchKernelGGL(chain_stats_chunk_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kStatsTPB), 0,
+                          stream, ev.before, ev.after, 0u, p);
+  else
+    hipExtLaunchKernelGGL(chain_stats_segment_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0,
+                          stream, ev.before, ev.after, 0u, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(chain_sample_kernel<T>, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream, p);

@@ -141,16 +141,27 @@ constexpr int kStatsSegVecs = 256 * kStatsUnroll * kStatsBatches;
 #define SV_STREAM_U 2
 #endif
 constexpr int kStreamU = SV_STREAM_U;
+// Threads per workgroup of the chunked statistics stream.
+#ifndef SV_STATS_TPB
+#define SV_STATS_TPB 256
+#endif
+constexpr int kStatsTPB = SV_STATS_TPB;
+// Waves per SIMD the chunked statistics stream is compiled for (8: at most 64
+// VGPRs; 4: at most 128).
+#ifndef SV_STATS_WAVES
+#define SV_STATS_WAVES 8
+#endif
 
-// Chunked layout: about this many chunks per call (measured best for each
-// stream on c2 / c4), each with at least kChunkMinVecs 16-byte vectors.
+// Chunked layouts: about this many chunks per call (one workgroup each;
+// measured best for each stream on c2 / c4), each with at least
+// kChunkMinVecs 16-byte vectors.
 #ifndef SV_CHUNKS_CHAIN
 #define SV_CHUNKS_CHAIN 2048
 #endif
+constexpr int kChunksChain = SV_CHUNKS_CHAIN;
 #ifndef SV_CHUNKS_TREE
 #define SV_CHUNKS_TREE 4096
 #endif
-constexpr int kChunksChain = SV_CHUNKS_CHAIN;
 constexpr int kChunksTree = SV_CHUNKS_TREE;
 constexpr int kChunkMinVecs = 256 * kStatsUnroll * 2;
 

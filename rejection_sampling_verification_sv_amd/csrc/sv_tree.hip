@@ -291,12 +291,14 @@ __device__ __forceinline__ void piece_argmax(const uint4* body, int64_t p0, int6
     uint4 raw[U];
     if (i < nfull) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) raw[u] = body[v + u * kThreads];
+      for (int u = 0; u < U; ++u) raw[u] = stream_load(body + v + u * kThreads);
     } else {
       if (rest == 0) break;
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        raw[u] = (u * kThreads + static_cast<int64_t>(threadIdx.x) < rest) ? body[v + u * kThreads] : neg_inf_vec<T>();
+        raw[u] = (u * kThreads + static_cast<int64_t>(threadIdx.x) < rest)
+                     ? stream_load(body + v + u * kThreads)
+                     : neg_inf_vec<T>();
     }
     float x[U * VEC];
     float bm = -INFINITY;

@@ -57,6 +57,16 @@ def test_workspace_sizes(lib):
     assert lib.sv_chain_workspace_bytes(128, 5, 128256, 1) > lib.sv_chain_workspace_bytes(64, 5, 128256, 1)
 
 
+def test_workspace_sizes_every_row_width(lib):
+    # rows narrower than, equal to and just past one 16-byte vector, and wide
+    # ones: the host layout arithmetic holds for every width
+    for dt in (0, 1):
+        for V in list(range(1, 41)) + [127, 128, 129, 32000, 128256, 152064, 256000]:
+            for B, K in ((1, 0), (7, 1), (64, 5), (1024, 8)):
+                assert lib.sv_chain_workspace_bytes(B, K, V, dt) > 0, (B, K, V, dt)
+            assert lib.sv_tree_workspace_bytes(32, 64, V, dt) > 0, (V, dt)
+
+
 FAKE = 0x10000  # a non-NULL address that is never dereferenced on these paths
 
 
