@@ -67,7 +67,7 @@ int64_t piece_slots(int64_t B, int32_t rows, int32_t V, sv_dtype d, int64_t chun
 
 struct ChainLayout {
   int32_t ntiles, tiles_per_block, nblk_b;
-  size_t off_part_m, off_part_s, off_plan, off_ticket, off_cnt, off_tiles, off_gat, off_abort, total;
+  size_t off_part_m, off_part_s, off_cnt, off_tiles, off_gat, off_abort, total;
 };
 
 ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
@@ -82,10 +82,6 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   off = align_up(off + sizeof(uint64_t) * parts);
   L.off_part_s = off;
   off = align_up(off + sizeof(uint64_t) * parts);
-  L.off_plan = off;
-  off = align_up(off + sizeof(uint64_t) * sv::kPlanWords * static_cast<int64_t>(B));
-  L.off_ticket = off;
-  off = align_up(off + sizeof(uint32_t) * B);
   L.off_cnt = off;
   off = align_up(off + sizeof(uint32_t) * B);
   L.off_tiles = off;
@@ -194,8 +190,6 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.err_flags = err_flags;
   p.part_m = reinterpret_cast<uint64_t*>(ws + L.off_part_m);
   p.part_s = reinterpret_cast<uint64_t*>(ws + L.off_part_s);
-  p.plan_w = reinterpret_cast<uint64_t*>(ws + L.off_plan);
-  p.ticket = reinterpret_cast<uint32_t*>(ws + L.off_ticket);
   p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
   p.tile_sum = reinterpret_cast<uint64_t*>(ws + L.off_tiles);
   p.gat = reinterpret_cast<uint64_t*>(ws + L.off_gat);

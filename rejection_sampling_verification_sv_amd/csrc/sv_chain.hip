@@ -16,19 +16,19 @@
 //   segments layout (any row alignment): one item per (row, segment).
 // The piece holding a drafted token also publishes that token's logit.
 //
-// Pass 2 — chain_sample_kernel, nblk_b workgroups per sequence, which take
-// tickets from a per-sequence counter:
-//   1. ticket 0 makes the decision: combines the pieces of the sequence's
-//      2K+1 rows into their log-normalisers L = log2 sum_v 2^(x_v c) (fp64),
-//      forms p_k(x_k) and q_k(x_k) in fp64, alpha_k = min(1, p/q), accepts
-//      while u_k < alpha_k and takes j = the first rejection with a wave
-//      ballot; it writes the accepted prefix and hands a sampling plan to the
-//      other tickets, which wait for it (the holder of ticket 0 is running and
-//      waits on nothing, so every wait ends);
+// Pass 2 — chain_sample_kernel, nblk_b workgroups per sequence (workgroup
+// g of sequence b is block g * B + b):
+//   1. each workgroup makes the sequence's decision for itself (the same
+//      inputs and operations, so the same plan everywhere; no workgroup
+//      waits for another): combines the pieces of the sequence's 2K+1 rows
+//      into their log-normalisers L = log2 sum_v 2^(x_v c) (fp64), forms
+//      p_k(x_k) and q_k(x_k) in fp64, alpha_k = min(1, p/q), accepts while
+//      u_k < alpha_k and takes j = the first rejection with a wave ballot;
+//      workgroup 0 writes the accepted prefix;
 //      [Topologies] "Speculative Decoding & Draft Model Topologies", section 2
 //      (acceptance-probability equation, timeline figure steps 2-3);
 //      [In Production] "Speculative Decoding in Production", section 2.
-//   2. ticket t re-reads tiles [t * TPB, t * TPB + TPB) of row j (target, and
+//   2. workgroup g re-reads tiles [g * TPB, g * TPB + TPB) of row j (target, and
 //      draft when j < K), forms the weights max(0, p_j - q_j) (or p_K for the
 //      bonus draw) and publishes each tile's total;
 //   3. the last workgroup of the sequence scans the tile totals, finds the
@@ -337,76 +337,88 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
 
 // ---------------------------------------------------------------- pass 2
 
-// The sampling plan travels as kPlanWords tagged 32-bit payloads (each word
-// is (1 << 32) | payload, never zero), so a reader can wait for each word.
-__device__ __forceinline__ void publish_plan(const ChainParams& P, int b, const SeqPlan& pl) {
-  static_assert(sizeof(SeqPlan) == 4 * kPlanWords, "plan layout");
-  uint32_t w[kPlanWords];
-  __builtin_memcpy(w, &pl, sizeof(SeqPlan));
+// The decision of sequence b, made by wave 0 of every sampling workgroup of
+// the sequence (the same inputs and operations give every one the same
+// plan, so no workgroup waits for another). All of its loads are issued
+// before any of them is used: one round trip. The rows' log-normalisers come
+// from the statistics pieces (G lanes per row, G the largest power of two
+// that fits all 2K+1 rows in one wave or covers a row's pieces; rounds of up
+// to four pieces per lane): group max of the references M, each lane
+// rescales its sums by 2^(m - M) in fp64, group sum Z, L = M + log2 Z. Lane
+// k < K holds drafted token k, its uniform and the logits pass 1 published
+// for it; p_k(x_k), q_k(x_k) in fp64, alpha_k = min(1, p/q), acceptance while
+// u_k < alpha_k, j = the first rejection (ballot). Leaves the sampling plan in
+// *s_plan; the `writer` also writes accept_len, the accepted prefix of
+// out_tokens, p_draft / q_draft and the error bits.
+// Issue the loads of pieces p0, p0 + G, p0 + 2G, p0 + 3G of row r (r < 0:
+// none) and return how many exist; every lane issues all eight loads (the
+// missing ones read any_slot and are dropped), so they are in flight together.
+__device__ __forceinline__ int issue_pieces(const ChainParams& P, int b, int r, int p0, int G, int pmax,
+                                            int64_t any_slot, uint64_t (&rm)[4], uint64_t (&rs)[4]) {
+  int64_t sl[4];
+  int n = 0;
+  if (P.L.cps > 0 && r >= 0) {
+    // chunked: row r's pieces are chunks ch0 .. chl; only the first one can
+    // start in an earlier row (three divisions per lane, not three per piece)
+    const PieceLayout& L = P.L;
+    const int64_t ch0 = div_nonneg(r * L.nvec, L.per);
+    const int64_t chl = div_nonneg((r + 1) * L.nvec - 1, L.per);
+    const int64_t first_row0 = div_nonneg(ch0 * L.per, L.nvec);
+    const int64_t base = static_cast<int64_t>(b) * L.cps;
 #pragma unroll
-  for (int i = 0; i < kPlanWords; ++i) publish(&P.plan_w[static_cast<int64_t>(b) * kPlanWords + i], (1ull << 32) | w[i]);
-}
-
-// One thread waits for the plan words (all loads issued before any value is
-// inspected) and unpacks them.
-__device__ __forceinline__ SeqPlan await_plan(const ChainParams& P, int b, uint32_t* err) {
-  uint64_t* base = P.plan_w + static_cast<int64_t>(b) * kPlanWords;
-  uint64_t v[kPlanWords];
+    for (int i = 0; i < 4; ++i) {
+      const int p = p0 + i * G;
+      const int64_t ch = ch0 + p;
+      sl[i] = (ch <= chl) ? (base + ch) * L.kmax + (p == 0 ? r - first_row0 : 0) : -1;
+      if (sl[i] >= 0 && n == i) n = i + 1;
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < kPlanWords; ++i) v[i] = peek(base + i);
-  uint32_t w[kPlanWords];
-#pragma unroll
-  for (int i = 0; i < kPlanWords; ++i) {
-    if (v[i] == 0ull) v[i] = await_slot<8>(base + i, err, P.abort);
-    w[i] = static_cast<uint32_t>(v[i]);
+    for (int i = 0; i < 4; ++i) {
+      sl[i] = (r >= 0 && p0 + i * G < pmax) ? piece_slot(P.L, b, r, p0 + i * G) : -1;
+      if (sl[i] >= 0 && n == i) n = i + 1;
+    }
   }
-  SeqPlan pl;
-  __builtin_memcpy(&pl, w, sizeof(SeqPlan));
-  return pl;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t a = i < n ? sl[i] : any_slot;
+    rm[i] = P.part_m[a];
+    rs[i] = P.part_s[a];
+  }
+  return n;
 }
 
-// The decision of sequence b, made by wave 0 of the sequence's ticket-0
-// workgroup alone: no block barrier, so it never waits for the other waves of
-// its workgroup to be launched. The rows' log-normalisers come from the
-// statistics pieces (G lanes per row, G the largest power of two that fits
-// all 2K+1 rows in one wave or covers a row's pieces; up to four pieces per
-// lane loaded at once, further ones folded in one at a time): group max of
-// the references M, each lane rescales its sums by 2^(m - M) in fp64, group
-// sum Z, L = M + log2 Z. Lane k < K holds drafted token k, its uniform and
-// the logits pass 1 published for it; p_k(x_k), q_k(x_k) in fp64,
-// alpha_k = min(1, p/q), acceptance while u_k < alpha_k, j = the first
-// rejection (ballot). Writes accept_len, the accepted prefix of out_tokens,
-// p_draft / q_draft and the error bits, publishes the sampling plan and
-// leaves it in *s_plan, and returns the pieces and gathered logits it
-// consumed to zero.
 template <class T>
-__device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan) {
+__device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
   const int K = P.K;
   const int R = 2 * K + 1;
   const int lane = lane_id();
-  const Scale c = exponent_scale(temperature_of(P.temperature, b));
   uint32_t err = 0u;
-
-  int x = -1;
-  float u = 0.0f, lt = 0.0f, ld = 0.0f;
-  if (lane < K) {
-    x = P.tokens[static_cast<int64_t>(b) * K + lane];
-    u = P.uniforms[static_cast<int64_t>(b) * (K + 1) + lane];
-    const uint64_t vt = P.gat[static_cast<int64_t>(b) * R + lane];
-    const uint64_t vd = P.gat[static_cast<int64_t>(b) * R + K + 1 + lane];
-    if (x < 0 || x >= P.V) {
-      err |= SV_ERRF_TOKEN;
-    } else {
-      if (vt == 0ull || vd == 0ull) err |= kErrInternal;
-      lt = untag_float(vt);
-      ld = untag_float(vd);
-    }
-  }
 
   const int pmax = max_pieces(P.L);
   int G = 1;
   while (G < pmax && R * 2 * G <= kWave) G <<= 1;
+  const int64_t any_slot = static_cast<int64_t>(b) * slots_per_seq(P.L);  // a valid address
+
+  // The loads of the usual case all go out before any is used: the first
+  // round of this lane's statistics pieces (every piece when the rows fit
+  // one wave and have at most 4 G pieces), then the drafted tokens' inputs.
+  uint64_t rm0[4], rs0[4];
+  const int n0 = issue_pieces(P, b, lane / G < R ? lane / G : -1, lane % G, G, pmax, any_slot, rm0, rs0);
+  const float Tv = temperature_of(P.temperature, b);
+  int x = -1;
+  float u = 0.0f;
+  uint64_t vt = 0ull, vd = 0ull;
+  if (K > 0) {  // every lane loads (lanes past K repeat lane K - 1's values and drop them)
+    const int k = min(lane, K - 1);
+    x = P.tokens[static_cast<int64_t>(b) * K + k];
+    u = P.uniforms[static_cast<int64_t>(b) * (K + 1) + k];
+    vt = P.gat[static_cast<int64_t>(b) * R + k];
+    vd = P.gat[static_cast<int64_t>(b) * R + K + 1 + k];
+    if (lane >= K) x = -1;
+  }
+
   for (int r0 = 0; r0 < R; r0 += kWave / G) {
     const int r = r0 + lane / G;
     const int gl = lane % G;
@@ -418,15 +430,16 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan) {
     bool more = row_ok;
     for (int p0 = gl; more; p0 += 4 * G) {
       uint64_t rm[4], rs[4];
-      int n = 0;
+      int n;
+      if (r0 == 0 && p0 == gl) {
+        n = n0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t sl = (p0 + i * G < pmax) ? piece_slot(P.L, b, r, p0 + i * G) : -1;
-        if (sl >= 0 && n == i) {
-          rm[i] = P.part_m[sl];
-          rs[i] = P.part_s[sl];
-          n = i + 1;
+        for (int i = 0; i < 4; ++i) {
+          rm[i] = rm0[i];
+          rs[i] = rs0[i];
         }
+      } else {
+        n = issue_pieces(P, b, r, p0, G, pmax, any_slot, rm, rs);
       }
       more = (n == 4);
       for (int i = 0; i < n; ++i) {
@@ -457,7 +470,17 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan) {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  const float Tv = temperature_of(P.temperature, b);
+  float lt = 0.0f, ld = 0.0f;
+  if (lane < K) {
+    if (x < 0 || x >= P.V) {
+      err |= SV_ERRF_TOKEN;
+    } else {
+      if (vt == 0ull || vd == 0ull) err |= kErrInternal;
+      lt = untag_float(vt);
+      ld = untag_float(vd);
+    }
+  }
+  const Scale c = exponent_scale(Tv);
   if (!(Tv > 0.0f) || !isfinite(Tv)) err |= SV_ERRF_TEMPERATURE;
   const double c64 = static_cast<double>(c.hi) + static_cast<double>(c.lo);
   bool reject = false;
@@ -471,8 +494,8 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan) {
       pf = static_cast<float>(p);
       qf = static_cast<float>(q);
     }
-    if (P.p_draft != nullptr) P.p_draft[static_cast<int64_t>(b) * K + lane] = pf;
-    if (P.q_draft != nullptr) P.q_draft[static_cast<int64_t>(b) * K + lane] = qf;
+    if (writer && P.p_draft != nullptr) P.p_draft[static_cast<int64_t>(b) * K + lane] = pf;
+    if (writer && P.q_draft != nullptr) P.q_draft[static_cast<int64_t>(b) * K + lane] = qf;
   }
   const uint64_t rej = __ballot(reject);
   const int j = (rej != 0ull) ? (__ffsll(static_cast<unsigned long long>(rej)) - 1) : K;
@@ -482,12 +505,14 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan) {
 
   // Lane i writes out_tokens[i] (K + 1 <= 64): its own token up to j, -1 after;
   // the drawn token at j is written by the sampling pass.
-  if (lane <= K && !(lane == j && !bad))
+  if (writer && lane <= K && !(lane == j && !bad))
     P.out_tokens[static_cast<int64_t>(b) * (K + 1) + lane] = (bad || lane > j) ? -1 : x;
   if (lane == 0) {
-    P.accept_len[b] = bad ? -1 : j;
-    if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
-    raise_error(P.err_flags, err);
+    if (writer) {
+      P.accept_len[b] = bad ? -1 : j;
+      if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
+      raise_error(P.err_flags, err);
+    }
     SeqPlan pl;
     pl.j = bad ? -1 : j;
     pl.c_hi = c.hi;
@@ -500,17 +525,8 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan) {
       pl.d_lo = 0.0f;
     }
     pl.pad = 0u;
-    publish_plan(P, b, pl);
     *s_plan = pl;
   }
-  // Consumed: the sequence's statistics pieces and gathered logits go back
-  // to zero for the next call.
-  const int64_t per_seq = slots_per_seq(P.L);
-  for (int64_t sl = static_cast<int64_t>(b) * per_seq + lane; sl < (static_cast<int64_t>(b) + 1) * per_seq; sl += kWave) {
-    P.part_m[sl] = 0ull;
-    P.part_s[sl] = 0ull;
-  }
-  for (int r = lane; r < R; r += kWave) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
 }
 
 template <class T>
@@ -780,38 +796,21 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   }
 }
 
-// A sampling workgroup of sequence b. It takes the next ticket t of the
-// sequence; ticket 0 decides, the others wait for its plan. Then the weights
-// of tiles [t * TPB, t * TPB + TPB) of the sampling row pair, published as
-// per-tile totals; the last workgroup of the sequence to finish draws the
-// token and returns the sequence's sampling workspace (tile totals, plan,
-// ticket and arrival counters) to zero.
+// Sampling workgroup g of sequence b: its wave 0 makes the sequence's
+// decision (group 0 writes it out), then the workgroup forms the weights of
+// tiles [g * TPB, g * TPB + TPB) of the sampling row pair and publishes
+// their totals; the last workgroup of the sequence to finish draws the token
+// and returns the sequence's workspace (statistics pieces, gathered logits,
+// tile totals, arrival counter) to zero.
 template <class T>
-__device__ void sample_seq(const ChainParams& P, int b) {
+__device__ void sample_seq(const ChainParams& P, int b, int blk) {
   constexpr int TPB = SampleTiles<T>::kPerBlock;
   constexpr int NV = kEptVecs<T>;
   __shared__ double s_red[TPB][kWaves];
   __shared__ int s_flag;
-  __shared__ int s_ticket;
   __shared__ SeqPlan s_plan;
-  if (threadIdx.x == 0)
-    s_ticket = static_cast<int>(__hip_atomic_fetch_add(&P.ticket[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (wave_id() == 0) decide_wave<T>(P, b, &s_plan, blk == 0);
   __syncthreads();
-  const int blk = s_ticket;
-  if (blk == 0) {
-    if (wave_id() == 0) decide_wave<T>(P, b, &s_plan);
-    __syncthreads();
-  } else {
-    if (threadIdx.x == 0) {
-      uint32_t err = 0u;
-      s_plan = await_plan(P, b, &err);
-      if (err != 0u) {
-        s_plan.j = -1;
-        raise_error(P.err_flags, err);
-      }
-    }
-    __syncthreads();
-  }
   const SeqPlan pl = s_plan;
 
   if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
@@ -843,13 +842,19 @@ __device__ void sample_seq(const ChainParams& P, int b) {
 
   if (!arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(P.nblk_b), &s_flag)) return;
   if (pl.j >= 0) chain_draw<T>(P, b, pl);
-  // Every workgroup of the sequence has taken its ticket, read the plan and
-  // published its totals: leave the sequence's sampling workspace all zero.
+  // Every workgroup of the sequence has read the statistics pieces and
+  // published its totals: leave the sequence's workspace all zero.
   __syncthreads();
   if (pl.j >= 0)
     for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
-  if (threadIdx.x < kPlanWords) clear_slot(&P.plan_w[static_cast<int64_t>(b) * kPlanWords + threadIdx.x]);
-  if (threadIdx.x == 0) __hip_atomic_store(&P.ticket[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t per_seq = slots_per_seq(P.L);
+  for (int64_t sl = static_cast<int64_t>(b) * per_seq + threadIdx.x; sl < (static_cast<int64_t>(b) + 1) * per_seq;
+       sl += kThreads) {
+    P.part_m[sl] = 0ull;
+    P.part_s[sl] = 0ull;
+  }
+  const int R = 2 * P.K + 1;
+  for (int r = threadIdx.x; r < R; r += kThreads) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
   reset_counter(&P.cnt[b]);
 }
 
@@ -879,7 +884,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 // starts among the first B.
 template <class T>
 __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
-  sample_seq<T>(P, static_cast<int>(blockIdx.x % static_cast<uint32_t>(P.B)));
+  const uint32_t B = static_cast<uint32_t>(P.B);
+  sample_seq<T>(P, static_cast<int>(blockIdx.x % B), static_cast<int>(blockIdx.x / B));
 }
 
 // ---------------------------------------------------------------- launcher

@@ -12,8 +12,8 @@
 namespace sv {
 
 // The decision of one sequence as the sampling step needs it: which row pair
-// to draw from and the rows' normalisers (made by one sampling workgroup of
-// the sequence, handed to the others as kPlanWords tagged 32-bit words).
+// to draw from and the rows' normalisers (made by every sampling workgroup
+// of the sequence for itself).
 struct SeqPlan {
   int32_t j;     // first rejected position; K = bonus draw; -1 = invalid row
   float c_hi;    // log2(e) / T as an unevaluated fp32 sum c_hi + c_lo
@@ -24,7 +24,6 @@ struct SeqPlan {
   float d_lo;    //   2^((x_d - x_t) c - D)    (unused for the bonus draw)
   uint32_t pad;
 };
-constexpr int kPlanWords = 8;  // 32-bit fields of a SeqPlan
 
 // How a streaming pass cuts the logit rows of a call into work items, and
 // where each item publishes one 64-bit slot per row piece. Two layouts:
@@ -97,8 +96,6 @@ struct ChainParams {
   // workspace (all zero between calls)
   uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi)
   uint64_t* part_s;   // per row piece: tagged fp64 sum of 2^(x c - reference)
-  uint64_t* plan_w;   // [B, kPlanWords] tagged plan words, decider -> other sampling workgroups
-  uint32_t* ticket;   // [B] sampling workgroups started (ticket 0 decides)
   uint32_t* cnt;      // [B] sampling workgroups finished
   uint64_t* tile_sum; // [B, ntiles] tagged fp64 sampling weight per tile
   uint64_t* gat;      // [B, 2K+1] tagged fp32 logit of row r at its drafted
@@ -125,7 +122,7 @@ constexpr int kSampleTile = 256 * kSampleEPT;      // elements per sampling tile
 // Tiles per sampling workgroup (the same bytes of each sampled row for both
 // dtypes).
 #ifndef SV_SAMPLE_TILES_BF16
-#define SV_SAMPLE_TILES_BF16 8
+#define SV_SAMPLE_TILES_BF16 4
 #endif
 constexpr int kSampleTilesBF16 = SV_SAMPLE_TILES_BF16;
 constexpr int kSampleTilesF32 = kSampleTilesBF16 / 2;
