@@ -9,6 +9,7 @@ from .specverify_oracle import (  # noqa: F401
     acceptance_probability,
     residual_weights,
     inverse_cdf,
+    sample_rows,
     verify_chain,
     node_depths,
     verify_tree_greedy,

@@ -117,6 +117,31 @@ def inverse_cdf(weights, u):
     return t, lo_u, hi_u
 
 
+# ----------------------------------------------------------------------------- draft-side sampling
+
+def sample_rows(logits, temperature, uniforms):
+    """Draw one token per row from its temperature softmax (the drafter's step).
+
+    [In Production] section 2 (each step the draft model samples a candidate
+    x ~ q(x)); [Draft-and-Verify] "The draft-and-verify loop" (the draft model
+    proposes its tokens one position at a time). Readings 2 and 4: the row's
+    temperature divides its logits, and the draw is the inverse CDF over
+    ascending token id with the row's uniform, as for the replacement draw.
+
+    Shapes: ``logits [R, V]``, ``temperature [R]`` (or None for T = 1),
+    ``uniforms [R]``. Returns ``tokens [R]`` int64, ``prob [R]`` (q of the drawn
+    token), and the drawn token's CDF boundaries ``lo_u, hi_u [R]`` in u-space
+    (a uniform within FLAG_WINDOW of either boundary is a near-boundary draw).
+    """
+    logits = np.asarray(logits, dtype=np.float64)
+    R = logits.shape[0]
+    T = np.ones(R) if temperature is None else np.asarray(temperature, dtype=np.float64)
+    q = temperature_softmax(logits, T)
+    t, lo_u, hi_u = inverse_cdf(q, np.asarray(uniforms, dtype=np.float64))
+    prob = np.take_along_axis(q, t[:, None], axis=1)[:, 0]
+    return t.astype(np.int64), prob, lo_u, hi_u
+
+
 # ----------------------------------------------------------------------------- chain verification
 
 def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniforms):

@@ -18,6 +18,7 @@ from .synth import (  # noqa: F401
     chain_uniforms,
     chain_temperatures,
     mc_chain_inputs,
+    sample_inputs,
     tree_parents_ranked,
     tree_inputs,
     sample_draft_tokens_gumbel,

@@ -21,7 +21,12 @@ stream, iteration])))``. On a GPU device the same SeedSequence seeds a
 ``torch.Generator`` on that device (Philox4x32-10 in PyTorch's ROCm build), so a
 CPU draw and a GPU draw of the same configuration are different (equally valid)
 samples. Stream ids: 0 target logits, 1 draft noise, 2 draft-token Gumbel
-noise, 3 uniforms, 4 temperatures, 5 tree token replacement.
+noise, 3 uniforms, 4 temperatures, 5 tree token replacement, 6 uniforms of
+the draft-side sampling workload.
+
+* draft-side sampling: the draft logits of a chain configuration taken as
+  ``B * K`` independent rows ``[B*K, V]``, each with its sequence's
+  temperature and one uniform in [0, 1).
 
 Gumbel-max (argmax of logits/T + Gumbel noise) is how the *drafter* side draws
 its proposals; it belongs to input generation, not to the verification step,
@@ -44,6 +49,7 @@ STREAM_DRAFT_TOKENS = 2
 STREAM_UNIFORMS = 3
 STREAM_TEMPERATURE = 4
 STREAM_TREE_REPLACE = 5
+STREAM_SAMPLE_UNIFORMS = 6
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -282,6 +288,32 @@ def chain_inputs(cfg: ChainConfig, device="cpu", iteration: int = 0) -> dict:
         "temperature": temperature,
         "uniforms": chain_uniforms(cfg, iteration, device),
     }
+
+
+def sample_inputs(cfg: ChainConfig, device="cpu", iteration: int = 0) -> dict:
+    """Inputs of one draft-side sampling call built from a chain configuration.
+
+    Keys: ``logits [B*K, V]`` (the configuration's draft logits, one row per
+    drafted position), ``temperature [B*K]`` float32 (each sequence's
+    temperature repeated over its positions) and ``uniforms [B*K]`` float32 in
+    [0, 1) from stream 6. The logits do not depend on ``iteration``; the
+    uniforms do.
+    """
+    if cfg.K < 1:
+        raise ValueError("draft-side sampling needs K >= 1 drafted positions")
+    if _is_cpu(device):
+        _, draft = _chain_logits_cpu(cfg)
+    else:
+        _, draft = _chain_logits_device(cfg, device)
+    rows = cfg.B * cfg.K
+    temperature = chain_temperatures(cfg, device).repeat_interleave(cfg.K)
+    if _is_cpu(device):
+        g = seed_stream(cfg.config_id, cfg.variant, STREAM_SAMPLE_UNIFORMS, iteration)
+        u = torch.from_numpy(g.random(rows, dtype=np.float32))
+    else:
+        g = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_SAMPLE_UNIFORMS, iteration)
+        u = torch.rand((rows,), generator=g, device=device, dtype=torch.float32)
+    return {"logits": draft.reshape(rows, cfg.V), "temperature": temperature, "uniforms": u}
 
 
 def mc_chain_inputs(cfg: ChainConfig = MC_CONFIG, trials: Optional[int] = None) -> dict:
