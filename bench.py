@@ -11,7 +11,9 @@ log-prior, draft = target + N(0, 0.8^2)). Three independent input sets
 step from the previous one; every input is resident in HBM before the timed
 region starts. Other workloads (--workload c1, c3_s0.3, c3_s1.0, c3_s3.0, c5,
 c4) print a line of the same form; c5 rotates its ten iterations (one set of
-logits, fresh uniforms each), c4 is the greedy tree call.
+logits, fresh uniforms each), c4 is the greedy tree call. The s1, s2 and s3
+workloads time draft-side sampling (sv_sample_rows) over the draft rows of c1,
+c2 and c3_s1.0 (B*K rows each, one token drawn per row).
 
 Prints one JSON line: rows x vocab elements verified per second over the
 whole call, the roofline of the dominant kernel (the streaming pass, timed
@@ -39,6 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "rejection_sampling_verification_sv_amd", "csrc")
 KERNEL_SOURCES = {
     "chain": ["sv_chain.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
+    "sample": ["sv_chain.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
     "tree": ["sv_tree.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
 }
 
@@ -48,7 +51,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c2", help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain) or c4 (tree)")
+    ap.add_argument("--workload", default="c2",
+                    help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain), c4 (tree) or s1, s2, s3 (draft-side sampling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle sample's wall time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -146,6 +150,32 @@ def cpu_baseline_tree(inp, cfg, budget_s: float) -> dict:
     }
 
 
+# draft-side sampling workloads: the draft rows of a chain configuration
+SAMPLE_WORKLOADS = {"s1": "c1", "s2": "c2", "s3": "c3_s1.0"}
+
+
+def cpu_baseline_sample(inp, cfg, budget_s: float) -> dict:
+    """The oracle's draft-side sampling, 16 rows at a time."""
+    import oracle
+
+    R = inp["logits"].shape[0]
+    jobs = []
+    for r0 in range(0, R, 16):
+        s = slice(r0, min(R, r0 + 16))
+        jobs.append((lambda s=s: (inp["logits"][s].double().numpy(), inp["temperature"][s].double().numpy(),
+                                  inp["uniforms"][s].double().numpy()),
+                     oracle.sample_rows, s.stop - s.start))
+    done, wall, cpu = _timed_oracle(jobs, budget_s)
+    return {
+        "value": done * cfg.V / wall,
+        "unit": "rows·vocab/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"{done} rows ({done / R:.2f} passes over the {R} rows) of the same workload, float64 numpy, "
+                  f"{wall:.1f} s in the oracle, {cpu:.1f} s CPU",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -156,7 +186,7 @@ def main():
     import torch
 
     import rejection_sampling_verification_sv_amd as sv
-    from workloads import CHAIN_CONFIGS, TREE_CONFIGS, chain_inputs, chain_uniforms, tree_inputs
+    from workloads import CHAIN_CONFIGS, TREE_CONFIGS, chain_inputs, chain_uniforms, sample_inputs, tree_inputs
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     sv.library()
@@ -171,8 +201,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = args.workload
-    kind = "tree" if wl in TREE_CONFIGS else "chain"
-    if kind == "chain":
+    kind = "tree" if wl in TREE_CONFIGS else ("sample" if wl in SAMPLE_WORKLOADS else "chain")
+    if kind == "sample":
+        cfg = CHAIN_CONFIGS[SAMPLE_WORKLOADS[wl]]
+        R, V = cfg.B * cfg.K, cfg.V
+        rows = R
+        eb = 2 if cfg.dtype == "bf16" else 4
+        sets = [sample_inputs(cfg.with_(variant=cfg.variant + 10 * i) if i else cfg, device=dev)
+                for i in range(N_SETS)]
+        calls = [sv.PreparedSampleCall(s["logits"], s["temperature"], s["uniforms"], stream=stream) for s in sets]
+        stream_bytes = R * V * eb
+        call_bytes = stream_bytes + R * 4 * 4  # plus temperature, uniform, token and probability per row
+        config = {"workload": f"sample_r{R}_v{V}_{cfg.dtype}", "rows": R, "V": V, "logits": cfg.dtype,
+                  "from": cfg.name, "input_sets_rotated": len(sets)}
+        kernel_name = "chain_stats_chunk_kernel (statistics pass over the rows)"
+    elif kind == "chain":
         cfg = CHAIN_CONFIGS[wl]
         B, K, V = cfg.B, cfg.K, cfg.V
         rows = B * (2 * K + 1)
@@ -265,7 +308,9 @@ def main():
     achieved = stream_bytes / (kern_avg_ms * 1e-3) / 1e9
     traffic = counted_traffic(wl, kind)
     result = {
-        "metric": METRIC if wl == "c2" else f"verify throughput: rows·vocab/s + HBM GB/s vs peak, {cfg.name}",
+        "metric": (METRIC if wl == "c2" else
+                   f"sampling throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}" if kind == "sample"
+                   else f"verify throughput: rows·vocab/s + HBM GB/s vs peak, {cfg.name}"),
         "value": elems / (ms_per_step * 1e-3),
         "unit": "rows·vocab/s",
         "n_gpus": 1,
@@ -301,6 +346,8 @@ def main():
         cpu_inp = {k: v.cpu() for k, v in sets[0].items()}
         if kind == "chain":
             result["cpu_baseline"] = cpu_baseline_chain(cpu_inp, cfg, args.cpu_seconds)
+        elif kind == "sample":
+            result["cpu_baseline"] = cpu_baseline_sample(cpu_inp, cfg, args.cpu_seconds)
         else:
             result["cpu_baseline"] = cpu_baseline_tree(cpu_inp, cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -151,6 +151,50 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Draft-side sampling.
+ *
+ * Bytes of device workspace sv_sample_rows needs; 0 for invalid sizes. Same
+ * zero-fill contract as the chain workspace (a call leaves it all zero).
+ */
+size_t sv_sample_workspace_bytes(int32_t R, int32_t V, sv_dtype dtype);
+
+/*
+ * One token drawn per row from the row's temperature softmax: the drafter's
+ * step x ~ q(x) before verification ([In Production] section 2: each step the
+ * draft model samples a candidate; [Draft-and-Verify] "The draft-and-verify
+ * loop": the draft proposes its tokens one position at a time). For row r,
+ * with T = temperature[r]:
+ *
+ *   q = softmax(logits[r,:] / T)
+ *   out_tokens[r] = the first t (ascending token id) whose cumulative q
+ *                   exceeds uniforms[r] * sum(q); if rounding leaves none,
+ *                   the last t with q(t) > 0
+ *
+ * This is the bonus draw of sv_verify_chain with K = 0, and it runs the same
+ * kernels: one pass over the logits, then a re-read of the row's tiles.
+ *
+ * Arguments (device pointers unless noted):
+ *   logits       [R, V] dtype, row-major, element-aligned (read only)
+ *   dtype        SV_DTYPE_F32 or SV_DTYPE_BF16
+ *   temperature  [R] float32, each > 0 and finite; NULL means 1.0 for all
+ *   uniforms     [R] float32 in [0, 1)
+ *   R, V         host ints: 0 <= R, 1 <= V
+ *   out_tokens   [R] int32 out: the drawn token, or -1 on a data error
+ *   out_prob     [R] float32 out or NULL: q(out_tokens[r]) (NaN on a data
+ *                error)
+ *   err_flags    [1] int32 in/out or NULL: SV_ERRF_* bits are OR-ed in
+ *                (SV_ERRF_TEMPERATURE, SV_ERRF_NONFINITE, SV_ERRF_INTERNAL)
+ *   workspace    device buffer of at least sv_sample_workspace_bytes() bytes
+ *   stream       HIP stream the kernels are enqueued on (NULL = default)
+ * Returns SV_ERR_INVALID_ARGUMENT for bad sizes, a bad dtype or a NULL
+ * required pointer, SV_ERR_WORKSPACE for a missing or short workspace, and
+ * SV_ERR_HIP when a launch fails; nothing is enqueued then.
+ */
+sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temperature, const float* uniforms,
+                         int32_t R, int32_t V, int32_t* out_tokens, float* out_prob, int32_t* err_flags,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Greedy tree verification.
  *
  * Bytes of device workspace sv_verify_tree_greedy needs; 0 for invalid sizes.

@@ -6,6 +6,7 @@ ctypes binding. Build with ``python -m rejection_sampling_verification_sv_amd.bu
 """
 from .specverify import (  # noqa: F401
     PreparedChainCall,
+    PreparedSampleCall,
     PreparedTreeCall,
     SpecVerifyError,
     SV_DTYPE_BF16,
@@ -21,6 +22,8 @@ from .specverify import (  # noqa: F401
     reset_workspaces,
     sv_build_tree_mask,
     sv_chain_workspace_bytes,
+    sv_sample_rows,
+    sv_sample_workspace_bytes,
     sv_status_string,
     sv_time_next_stream_pass,
     sv_tree_workspace_bytes,

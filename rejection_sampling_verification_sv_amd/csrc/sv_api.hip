@@ -74,7 +74,8 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   ChainLayout L{};
   const int32_t R = 2 * K + 1;
   L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
-  L.tiles_per_block = d == SV_DTYPE_BF16 ? sv::kSampleTilesBF16 : sv::kSampleTilesF32;
+  L.tiles_per_block = (d == SV_DTYPE_BF16 ? sv::kSampleTilesBF16 : sv::kSampleTilesF32) *
+                      (K == 0 ? sv::kSampleTilesK0Factor : 1);
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
   const int64_t parts = piece_slots(B, R, V, d, chunk_vecs(B, R, V, d, sv::kChunksChain));
   size_t off = 0;
@@ -149,16 +150,20 @@ size_t sv_chain_workspace_bytes(int32_t B, int32_t K, int32_t V, sv_dtype dtype)
   return chain_layout(B, K, V, dtype).total;
 }
 
-sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,
-                          const int32_t* draft_tokens, const float* temperature, const float* uniforms,
-                          int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
-                          float* p_draft, float* q_draft, float* residual_mass, int32_t* err_flags,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  const sv::PassEvents ev = sv::take_pass_events();
+}  // extern "C"
+
+namespace {
+
+// A chain verification call; draft-side sampling is the K = 0 case with the
+// drawn token's probability requested.
+sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dtype dtype, const int32_t* draft_tokens,
+                     const float* temperature, const float* uniforms, int32_t B, int32_t K, int32_t V,
+                     int32_t* accept_len, int32_t* out_tokens, float* p_draft, float* q_draft, float* residual_mass,
+                     float* drawn_prob, int32_t* err_flags, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, const sv::PassEvents& ev) {
   if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return SV_ERR_INVALID_ARGUMENT;
   if (B == 0) return SV_OK;
-  if (target_logits == nullptr || uniforms == nullptr || accept_len == nullptr || out_tokens == nullptr)
-    return SV_ERR_INVALID_ARGUMENT;
+  if (target_logits == nullptr || uniforms == nullptr || out_tokens == nullptr) return SV_ERR_INVALID_ARGUMENT;
   if (K > 0 && (draft_logits == nullptr || draft_tokens == nullptr)) return SV_ERR_INVALID_ARGUMENT;
   const int eb = dtype_bytes(dtype);
   if (!aligned_to(target_logits, eb) || (draft_logits != nullptr && !aligned_to(draft_logits, eb)))
@@ -187,6 +192,7 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   p.p_draft = p_draft;
   p.q_draft = q_draft;
   p.residual_mass = residual_mass;
+  p.drawn_prob = drawn_prob;
   p.err_flags = err_flags;
   p.part_m = reinterpret_cast<uint64_t*>(ws + L.off_part_m);
   p.part_s = reinterpret_cast<uint64_t*>(ws + L.off_part_s);
@@ -198,6 +204,41 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   if (static_cast<int64_t>(B) * sv::items_per_seq(p.L) > INT32_MAX || static_cast<int64_t>(B) * p.nblk_b > INT32_MAX)
     return SV_ERR_UNSUPPORTED;
   return from_hip(sv::launch_chain(p, dtype, ev, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                          const int32_t* draft_tokens, const float* temperature, const float* uniforms,
+                          int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
+                          float* p_draft, float* q_draft, float* residual_mass, int32_t* err_flags,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const sv::PassEvents ev = sv::take_pass_events();
+  if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return SV_ERR_INVALID_ARGUMENT;
+  if (B > 0 && accept_len == nullptr) return SV_ERR_INVALID_ARGUMENT;
+  return chain_call(target_logits, draft_logits, dtype, draft_tokens, temperature, uniforms, B, K, V, accept_len,
+                    out_tokens, p_draft, q_draft, residual_mass, nullptr, err_flags, workspace, workspace_bytes,
+                    stream, ev);
+}
+
+size_t sv_sample_workspace_bytes(int32_t R, int32_t V, sv_dtype dtype) {
+  if (!chain_sizes_ok(R, 0, V) || !dtype_ok(dtype)) return 0;
+  return chain_layout(R, 0, V, dtype).total;  // the chain workspace of R sequences with K = 0
+}
+
+sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temperature, const float* uniforms,
+                         int32_t R, int32_t V, int32_t* out_tokens, float* out_prob, int32_t* err_flags,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const sv::PassEvents ev = sv::take_pass_events();
+  if (!dtype_ok(dtype) || !chain_sizes_ok(R, 0, V)) return SV_ERR_INVALID_ARGUMENT;
+  if (R == 0) return SV_OK;
+  if (logits == nullptr || uniforms == nullptr || out_tokens == nullptr) return SV_ERR_INVALID_ARGUMENT;
+  if (workspace == nullptr || workspace_bytes < sv_sample_workspace_bytes(R, V, dtype) || !aligned_to(workspace, 8))
+    return SV_ERR_WORKSPACE;
+  return chain_call(logits, nullptr, dtype, nullptr, temperature, uniforms, R, 0, V, nullptr, out_tokens, nullptr,
+                    nullptr, nullptr, out_prob, err_flags, workspace, workspace_bytes, stream, ev);
 }
 
 size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype) {

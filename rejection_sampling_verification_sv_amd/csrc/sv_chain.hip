@@ -509,8 +509,9 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
     P.out_tokens[static_cast<int64_t>(b) * (K + 1) + lane] = (bad || lane > j) ? -1 : x;
   if (lane == 0) {
     if (writer) {
-      P.accept_len[b] = bad ? -1 : j;
+      if (P.accept_len != nullptr) P.accept_len[b] = bad ? -1 : j;
       if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
+      if (bad && P.drawn_prob != nullptr) P.drawn_prob[b] = NAN;
       raise_error(P.err_flags, err);
     }
     SeqPlan pl;
@@ -792,6 +793,16 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   if (tid == 0) {
     P.out_tokens[static_cast<int64_t>(b) * (P.K + 1) + pl.j] = token;
     if (P.residual_mass != nullptr) P.residual_mass[b] = (pl.j < P.K) ? static_cast<float>(S_res) : -1.0f;
+    if (P.drawn_prob != nullptr) {
+      // p_j of the drawn token in fp64 from its logit and the plan: 2^(x c - L_j)
+      float pr = NAN;
+      if (token >= 0) {
+        const double x = static_cast<double>(load_elem<T>(chain_row<T>(P, b, pl.j), token));
+        const double c64 = static_cast<double>(pl.c_hi) + static_cast<double>(pl.c_lo);
+        pr = static_cast<float>(exp2(x * c64 - (static_cast<double>(pl.lt_hi) + static_cast<double>(pl.lt_lo))));
+      }
+      P.drawn_prob[b] = pr;
+    }
     raise_error(P.err_flags, s_err);
   }
 }
@@ -802,9 +813,8 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
 // their totals; the last workgroup of the sequence to finish draws the token
 // and returns the sequence's workspace (statistics pieces, gathered logits,
 // tile totals, arrival counter) to zero.
-template <class T>
+template <class T, int TPB, bool kDraft>
 __device__ void sample_seq(const ChainParams& P, int b, int blk) {
-  constexpr int TPB = SampleTiles<T>::kPerBlock;
   constexpr int NV = kEptVecs<T>;
   __shared__ double s_red[TPB][kWaves];
   __shared__ int s_flag;
@@ -816,19 +826,20 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
   if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
     const SampleRows S = sample_rows<T>(P, b, pl, false);
     const int t0 = blk * TPB;
-    uint4 rt[TPB][NV], rd[TPB][NV] = {};
+    uint4 rt[TPB][NV], rd[kDraft ? TPB : 1][NV] = {};
 #pragma unroll
     for (int i = 0; i < TPB; ++i) {  // every load of the item in flight at once
       if (t0 + i < P.ntiles) {
         const int64_t e0 = static_cast<int64_t>(t0 + i) * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
         load_raw<T>(S.t, e0, P.V, rt[i]);
-        if (S.d != nullptr) load_raw<T>(S.d, e0, P.V, rd[i]);
+        if (kDraft && S.d != nullptr) load_raw<T>(S.d, e0, P.V, rd[kDraft ? i : 0]);
       }
     }
 #pragma unroll
     for (int i = 0; i < TPB; ++i) {
       float w[kSampleEPT];
-      const double part = (t0 + i < P.ntiles) ? wave_sum(static_cast<double>(tile_compute<T>(S, rt[i], rd[i], w))) : 0.0;
+      const double part =
+          (t0 + i < P.ntiles) ? wave_sum(static_cast<double>(tile_compute<T>(S, rt[i], rd[kDraft ? i : 0], w))) : 0.0;
       if (lane_id() == 0) s_red[i][wave_id()] = part;
     }
     __syncthreads();
@@ -885,7 +896,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 template <class T>
 __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
   const uint32_t B = static_cast<uint32_t>(P.B);
-  sample_seq<T>(P, static_cast<int>(blockIdx.x % B), static_cast<int>(blockIdx.x / B));
+  sample_seq<T, SampleTiles<T>::kPerBlock, true>(P, static_cast<int>(blockIdx.x % B), static_cast<int>(blockIdx.x / B));
+}
+
+// K = 0 (draft-side sampling): one row per draw, more tiles per workgroup.
+template <class T>
+__global__ __launch_bounds__(kThreads) void chain_sample_one_row_kernel(ChainParams P) {
+  const uint32_t B = static_cast<uint32_t>(P.B);
+  sample_seq<T, SampleTiles<T>::kPerBlock * kSampleTilesK0Factor, false>(P, static_cast<int>(blockIdx.x % B),
+                                                                          static_cast<int>(blockIdx.x / B));
 }
 
 // ---------------------------------------------------------------- launcher
@@ -904,7 +923,11 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
                           stream, ev.before, ev.after, 0u, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(chain_sample_kernel<T>, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream, p);
+  if (p.K == 0)
+    hipLaunchKernelGGL(chain_sample_one_row_kernel<T>, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream,
+                       p);
+  else
+    hipLaunchKernelGGL(chain_sample_kernel<T>, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

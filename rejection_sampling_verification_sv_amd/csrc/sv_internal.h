@@ -87,11 +87,12 @@ struct ChainParams {
   int32_t ntiles;
   int32_t tiles_per_block;
   int32_t nblk_b;
-  int32_t* accept_len;
+  int32_t* accept_len;  // null only for draft-side sampling (K = 0)
   int32_t* out_tokens;
   float* p_draft;
   float* q_draft;
   float* residual_mass;
+  float* drawn_prob;  // [B] or null: p of the token drawn at j (draft-side sampling, K = 0)
   int32_t* err_flags;
   // workspace (all zero between calls)
   uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi)
@@ -126,6 +127,12 @@ constexpr int kSampleTile = 256 * kSampleEPT;      // elements per sampling tile
 #endif
 constexpr int kSampleTilesBF16 = SV_SAMPLE_TILES_BF16;
 constexpr int kSampleTilesF32 = kSampleTilesBF16 / 2;
+// With K = 0 (draft-side sampling) only one row is drawn from, and each
+// workgroup takes this many times as many tiles.
+#ifndef SV_SAMPLE_TILES_K0_FACTOR
+#define SV_SAMPLE_TILES_K0_FACTOR 4
+#endif
+constexpr int kSampleTilesK0Factor = SV_SAMPLE_TILES_K0_FACTOR;
 
 // Segments layout: kThreads * kStatsUnroll * kStatsBatches vectors per segment.
 constexpr int kStatsUnroll = 4;

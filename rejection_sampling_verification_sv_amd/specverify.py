@@ -73,6 +73,12 @@ def _load():
         lib.sv_verify_tree_greedy.restype = ctypes.c_int
         lib.sv_build_tree_mask.argtypes = [_c_ptr, _c_i32, _c_ptr, _c_ptr, _c_ptr]
         lib.sv_build_tree_mask.restype = ctypes.c_int
+        lib.sv_sample_workspace_bytes.argtypes = [_c_i32, _c_i32, ctypes.c_int]
+        lib.sv_sample_workspace_bytes.restype = _c_size
+        lib.sv_sample_rows.argtypes = [
+            _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
+        ]
+        lib.sv_sample_rows.restype = ctypes.c_int
         lib.sv_time_next_stream_pass.argtypes = [_c_ptr, _c_ptr]
         lib.sv_time_next_stream_pass.restype = ctypes.c_int
         _lib = lib
@@ -224,6 +230,48 @@ def sv_verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_t
     return out
 
 
+def sv_sample_workspace_bytes(R: int, V: int, dtype: torch.dtype) -> int:
+    return int(_load().sv_sample_workspace_bytes(R, V, _DTYPES[dtype]))
+
+
+def sv_sample_rows(logits: torch.Tensor, temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
+                   out_tokens=None, out_prob=None, err_flags=None, workspace_tensor=None, stream=None,
+                   want_prob: bool = True) -> dict:
+    """Draft-side sampling (``sv_sample_rows``): one token per row of
+    ``logits [R, V]`` from its temperature softmax, with ``uniforms [R]``.
+
+    Returns a dict with ``tokens [R]`` int32, ``prob [R]`` float32 (when
+    ``want_prob``) and ``err_flags [1]``. Outputs are ready once the stream
+    has been synchronised.
+    """
+    lib = _load()
+    if logits.dim() != 2:
+        raise ValueError("logits must be [R, V]")
+    R, V = logits.shape
+    dev = logits.device
+    code = _dtype_code(logits)
+    _dev(logits, "logits")
+    if temperature is not None:
+        _dev(temperature, "temperature", dtype=torch.float32, shape=(R,), device=dev)
+    _dev(uniforms, "uniforms", dtype=torch.float32, shape=(R,), device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    out_tokens = torch.empty((R,), **i32) if out_tokens is None else _dev(out_tokens, "out_tokens", torch.int32, (R,), dev)
+    if want_prob:
+        out_prob = (torch.empty((R,), dtype=torch.float32, device=dev) if out_prob is None
+                    else _dev(out_prob, "out_prob", torch.float32, (R,), dev))
+    err_flags = torch.zeros((1,), **i32) if err_flags is None else _dev(err_flags, "err_flags", torch.int32, (1,), dev)
+    nbytes = int(lib.sv_sample_workspace_bytes(R, V, code))
+    ws = workspace(dev, nbytes, stream) if workspace_tensor is None else workspace_tensor
+    st = lib.sv_sample_rows(_ptr(logits), code, _ptr(temperature), _ptr(uniforms), R, V, _ptr(out_tokens),
+                            _ptr(out_prob) if want_prob else None, _ptr(err_flags), _ptr(ws), ws.numel(),
+                            _stream_handle(dev, stream))
+    _check(st, "sv_sample_rows")
+    out = {"tokens": out_tokens, "err_flags": err_flags}
+    if want_prob:
+        out["prob"] = out_prob
+    return out
+
+
 def sv_verify_tree_greedy(target: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor, *,
                           accept_len=None, path_nodes=None, next_token=None, err_flags=None,
                           workspace_tensor=None, stream=None) -> dict:
@@ -309,6 +357,35 @@ class PreparedChainCall:
         st = self._fn(*self._args)
         if st != SV_OK:
             _check(st, "sv_verify_chain")
+        return self.out
+
+
+class PreparedSampleCall:
+    """``sv_sample_rows`` with every argument checked and marshalled once
+    (calling the object only enqueues the kernels)."""
+
+    def __init__(self, logits, temperature, uniforms, *, stream=None, want_prob=True):
+        R, V = logits.shape
+        dev = logits.device
+        self.out = {"tokens": torch.empty((R,), dtype=torch.int32, device=dev),
+                    "err_flags": torch.zeros((1,), dtype=torch.int32, device=dev)}
+        if want_prob:
+            self.out["prob"] = torch.empty((R,), dtype=torch.float32, device=dev)
+        sv_sample_rows(logits, temperature, uniforms, stream=stream, want_prob=want_prob,
+                       out_tokens=self.out["tokens"], out_prob=self.out.get("prob"), err_flags=self.out["err_flags"])
+        lib = _load()
+        self._ws = workspace(dev, int(lib.sv_sample_workspace_bytes(R, V, _dtype_code(logits))), stream)
+        self._keep = (logits, temperature, uniforms)
+        o = self.out
+        self._fn = lib.sv_sample_rows
+        self._args = (_ptr(logits), _dtype_code(logits), _ptr(temperature), _ptr(uniforms), R, V, _ptr(o["tokens"]),
+                      _ptr(o.get("prob")), _ptr(o["err_flags"]), _ptr(self._ws), self._ws.numel(),
+                      _stream_handle(dev, stream))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SV_OK:
+            _check(st, "sv_sample_rows")
         return self.out
 
 

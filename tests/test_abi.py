@@ -115,6 +115,20 @@ def test_tree_and_mask_argument_errors(lib):
     assert lib.sv_build_tree_mask(FAKE, 1025, FAKE, None, None) == INV
 
 
+def test_sample_argument_errors(lib):
+    def call(**kw):
+        a = dict(x=FAKE, dt=1, T=None, u=FAKE, R=4, V=100, out=FAKE, p=None, err=None, ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return lib.sv_sample_rows(a["x"], a["dt"], a["T"], a["u"], a["R"], a["V"], a["out"], a["p"], a["err"],
+                                  a["ws"], a["wsb"], None)
+    assert call(x=None, u=None, out=None, ws=None, R=0) == 0      # nothing to do
+    assert call(x=None) == 1 and call(u=None) == 1 and call(out=None) == 1
+    assert call(dt=5) == 1 and call(V=0) == 1 and call(R=-1) == 1
+    assert call(ws=None) == 3 and call(wsb=16) == 3
+    assert lib.sv_sample_workspace_bytes(320, 128256, 1) == lib.sv_chain_workspace_bytes(320, 0, 128256, 1)
+    assert lib.sv_sample_workspace_bytes(4, 0, 1) == 0
+
+
 def test_stream_pass_hook_arguments(lib):
     INV = 1
     f = lib.sv_time_next_stream_pass

@@ -79,3 +79,28 @@ def test_workspace_returns_to_zero(sv):
         ref = oracle.verify_tree_greedy(target.float().numpy(), tokens, parents)
         np.testing.assert_array_equal(out["accept_len"].cpu().numpy(), ref["accept_len"])
         np.testing.assert_array_equal(out["next_token"].cpu().numpy(), ref["next_token"])
+
+
+def test_sampling_leaves_the_workspace_zero(sv):
+    # draft-side sampling on a shared workspace, including a bad-temperature row
+    rng = np.random.Generator(np.random.Philox(407))
+    R, V = 40, 6000
+    ws = torch.zeros(sv.sv_sample_workspace_bytes(R, V, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    for label, bad in (("clean rows", None), ("a row with T = 0", 3)):
+        _say("sampling workspace:", label)
+        logits = torch.from_numpy(rng.normal(0, 2, (R, V)).astype(np.float32)).to(torch.bfloat16).cuda()
+        T = torch.full((R,), 0.9, device="cuda")
+        if bad is not None:
+            T[bad] = 0.0
+        u = torch.from_numpy(rng.random(R, dtype=np.float32)).cuda()
+        out = sv.sv_sample_rows(logits, T, u, workspace_tensor=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero().item()) == 0, f"workspace dirty after {label}"
+        tok = out["tokens"].cpu().numpy()
+        if bad is None:
+            assert int(out["err_flags"].item()) == 0
+            ref, _, _, _ = oracle.sample_rows(logits.float().cpu().numpy(), T.cpu().numpy(), u.cpu().numpy())
+            assert (tok == ref).mean() > 0.97
+        else:
+            assert int(out["err_flags"].item()) & sv.SV_ERRF_TEMPERATURE
+            assert tok[bad] == -1 and np.all(np.delete(tok, bad) >= 0)
