@@ -41,7 +41,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "rejection_sampling_verification_sv_amd", "csrc")
 KERNEL_SOURCES = {
     "chain": ["sv_chain.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
-    "sample": ["sv_chain.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
+    "sample": ["sv_sample.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
     "tree": ["sv_tree.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
 }
 
@@ -214,7 +214,7 @@ def main():
         call_bytes = stream_bytes + R * 4 * 4  # plus temperature, uniform, token and probability per row
         config = {"workload": f"sample_r{R}_v{V}_{cfg.dtype}", "rows": R, "V": V, "logits": cfg.dtype,
                   "from": cfg.name, "input_sets_rotated": len(sets)}
-        kernel_name = "chain_stats_chunk_kernel (statistics pass over the rows)"
+        kernel_name = "sample_stream_kernel (one pass over the rows: a record per run of 128 vectors)"
     elif kind == "chain":
         cfg = CHAIN_CONFIGS[wl]
         B, K, V = cfg.B, cfg.K, cfg.V

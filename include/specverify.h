@@ -170,8 +170,12 @@ size_t sv_sample_workspace_bytes(int32_t R, int32_t V, sv_dtype dtype);
  *                   exceeds uniforms[r] * sum(q); if rounding leaves none,
  *                   the last t with q(t) > 0
  *
- * This is the bonus draw of sv_verify_chain with K = 0, and it runs the same
- * kernels: one pass over the logits, then a re-read of the row's tiles.
+ * When every row starts on a 16-byte boundary (V * element size a multiple
+ * of 16 and a 16-byte-aligned base, the usual case), the logits are read
+ * once: the streaming pass reduces each run of 1024 bf16 (512 fp32) tokens to
+ * one (reference, sum) record, and the draw re-reads only the run holding the
+ * drawn token. Other rows take the bonus-draw kernels of sv_verify_chain with
+ * K = 0 (a second pass over the row).
  *
  * Arguments (device pointers unless noted):
  *   logits       [R, V] dtype, row-major, element-aligned (read only)

@@ -95,6 +95,23 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   return L;
 }
 
+// One-pass draft-side sampling: runs of kRunVecs vectors per row, split
+// evenly into cps chunks per row (about kChunksSample chunks per call, each of
+// at least kChunkMinVecs vectors), one record per run.
+struct RunLayout {
+  int32_t nrun, cps;
+  size_t total;
+};
+
+RunLayout run_layout(int32_t R, int32_t V, sv_dtype d) {
+  RunLayout L{};
+  L.nrun = static_cast<int32_t>(ceil_div(row_vecs(V, d), sv::kRunVecs));
+  const int64_t runs = ceil_div(chunk_vecs(R, 1, V, d, sv::kChunksSample), sv::kRunVecs);
+  L.cps = static_cast<int32_t>(ceil_div(L.nrun, runs));
+  L.total = align_up(sizeof(uint64_t) * static_cast<int64_t>(R) * L.nrun);
+  return L;
+}
+
 struct TreeLayout {
   size_t off_part, total;
 };
@@ -225,7 +242,11 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
 
 size_t sv_sample_workspace_bytes(int32_t R, int32_t V, sv_dtype dtype) {
   if (!chain_sizes_ok(R, 0, V) || !dtype_ok(dtype)) return 0;
-  return chain_layout(R, 0, V, dtype).total;  // the chain workspace of R sequences with K = 0
+  // rows on 16-byte boundaries use the run records, others the chain
+  // workspace of R sequences with K = 0; both start at offset 0
+  const size_t chain = chain_layout(R, 0, V, dtype).total;
+  const size_t runs = whole_vector_rows(V, dtype) ? run_layout(R, V, dtype).total : 0;
+  return chain > runs ? chain : runs;
 }
 
 sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temperature, const float* uniforms,
@@ -237,8 +258,26 @@ sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temper
   if (logits == nullptr || uniforms == nullptr || out_tokens == nullptr) return SV_ERR_INVALID_ARGUMENT;
   if (workspace == nullptr || workspace_bytes < sv_sample_workspace_bytes(R, V, dtype) || !aligned_to(workspace, 8))
     return SV_ERR_WORKSPACE;
-  return chain_call(logits, nullptr, dtype, nullptr, temperature, uniforms, R, 0, V, nullptr, out_tokens, nullptr,
-                    nullptr, nullptr, out_prob, err_flags, workspace, workspace_bytes, stream, ev);
+  if (!aligned_to(logits, dtype_bytes(dtype))) return SV_ERR_INVALID_ARGUMENT;
+  if (!whole_vector_rows(V, dtype) || !aligned_to(logits, 16))  // rows off 16-byte boundaries: two passes
+    return chain_call(logits, nullptr, dtype, nullptr, temperature, uniforms, R, 0, V, nullptr, out_tokens, nullptr,
+                      nullptr, nullptr, out_prob, err_flags, workspace, workspace_bytes, stream, ev);
+  const RunLayout L = run_layout(R, V, dtype);
+  if (static_cast<int64_t>(R) * L.cps > INT32_MAX) return SV_ERR_UNSUPPORTED;
+  sv::SampleParams p{};
+  p.logits = logits;
+  p.temperature = temperature;
+  p.uniforms = uniforms;
+  p.R = R;
+  p.V = V;
+  p.nvec = row_vecs(V, dtype);
+  p.nrun = L.nrun;
+  p.cps = L.cps;
+  p.out_tokens = out_tokens;
+  p.out_prob = out_prob;
+  p.err_flags = err_flags;
+  p.rec = static_cast<uint64_t*>(workspace);
+  return from_hip(sv::launch_sample(p, dtype, ev, stream));
 }
 
 size_t sv_tree_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype) {

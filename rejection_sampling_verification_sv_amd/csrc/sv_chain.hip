@@ -62,39 +62,6 @@ __device__ __forceinline__ const void* chain_row(const ChainParams& P, int b, in
   return base + row * static_cast<int64_t>(P.V) * T::kBytes;
 }
 
-__device__ __forceinline__ float temperature_of(const float* temperature, int b) {
-  return temperature != nullptr ? temperature[b] : 1.0f;
-}
-
-// c = log2(e) / T as an unevaluated sum of two fp32 values (c_hi carries the
-// leading 24 bits, c_lo the next ones), so that exponents x*c are formed at
-// the requested temperature rather than at the nearest fp32 one. c_hi is
-// rounded toward zero and c_lo is kept strictly positive: an x of -inf then
-// gives -inf in both products (never -inf + inf), i.e. a weight of exactly 0.
-struct Scale {
-  float hi;
-  float lo;
-};
-
-__device__ __forceinline__ Scale exponent_scale(float T) {
-  const double c = 1.4426950408889634 / static_cast<double>(T);
-  float hi = __double2float_rz(c);
-  // exactly representable c (c_lo would be 0): step c_hi one ulp toward zero
-  if (static_cast<double>(hi) == c && hi > 0.0f) hi = __uint_as_float(__float_as_uint(hi) - 1u);
-  return Scale{hi, static_cast<float>(c - static_cast<double>(hi))};
-}
-
-// The fp32 reference of a running maximum: fl(mx * c_hi), and -inf while
-// nothing finite has been seen (so that -inf logits contribute 0, not NaN).
-__device__ __forceinline__ float neg_reference(float mx, Scale c) {
-  return mx == -INFINITY ? -INFINITY : -(mx * c.hi);
-}
-
-// x*c - m with m an fp32 reference: one product exact inside each fma.
-__device__ __forceinline__ float scaled_arg(float x, Scale c, float neg_m) {
-  return fmaf(x, c.lo, fmaf(x, c.hi, neg_m));
-}
-
 // Running (max, sum) of one thread. `mx` is the largest raw logit seen and
 // `s` = sum of 2^(x*c - fl(mx*c_hi)) over the logits seen.
 struct Running {

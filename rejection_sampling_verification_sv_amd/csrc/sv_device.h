@@ -89,11 +89,52 @@ __device__ __forceinline__ uint4 neg_inf_vec<F32>() {
 // v_exp_f32: 2^x (about 1 ulp; inputs below -126 give 0 or a denormal).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- temperature scale
+
+__device__ __forceinline__ float temperature_of(const float* temperature, int b) {
+  return temperature != nullptr ? temperature[b] : 1.0f;
+}
+
+// c = log2(e) / T as an unevaluated sum of two fp32 values (c_hi carries the
+// leading 24 bits, c_lo the next ones), so that exponents x*c are formed at
+// the requested temperature rather than at the nearest fp32 one. c_hi is
+// rounded toward zero and c_lo is kept strictly positive: an x of -inf then
+// gives -inf in both products (never -inf + inf), i.e. a weight of exactly 0.
+struct Scale {
+  float hi;
+  float lo;
+};
+
+__device__ __forceinline__ Scale exponent_scale(float T) {
+  const double c = 1.4426950408889634 / static_cast<double>(T);
+  float hi = __double2float_rz(c);
+  // exactly representable c (c_lo would be 0): step c_hi one ulp toward zero
+  if (static_cast<double>(hi) == c && hi > 0.0f) hi = __uint_as_float(__float_as_uint(hi) - 1u);
+  return Scale{hi, static_cast<float>(c - static_cast<double>(hi))};
+}
+
+// The fp32 reference of a running maximum: fl(mx * c_hi), and -inf while
+// nothing finite has been seen (so that -inf logits contribute 0, not NaN).
+__device__ __forceinline__ float neg_reference(float mx, Scale c) {
+  return mx == -INFINITY ? -INFINITY : -(mx * c.hi);
+}
+
+// x*c - m with m an fp32 reference: one product exact inside each fma.
+__device__ __forceinline__ float scaled_arg(float x, Scale c, float neg_m) {
+  return fmaf(x, c.lo, fmaf(x, c.hi, neg_m));
+}
+
 // ---------------------------------------------------------------- wave64 reductions
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
 
@@ -111,6 +152,33 @@ __device__ __forceinline__ double wave_inclusive_scan(double v) {
     if ((threadIdx.x & (kWave - 1)) >= o) v += n;
   }
   return v;
+}
+
+// Wave-uniform maximum / sum through DPP row permutes (xor 1, xor 2, half-row
+// mirror, row mirror: every lane of a 16-lane row then holds the row's
+// result) and the four rows' results read from lanes 0, 16, 32, 48, combined
+// in a fixed order. Much shorter latency than the shuffle forms (each step of
+// those is an LDS permute); the same inputs give bit-identical results.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_read(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_move<0xb1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_move<0x4e>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_move<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_move<0x140>(v));  // row_mirror
+  return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_move<0xb1>(v);
+  v += dpp_move<0x4e>(v);
+  v += dpp_move<0x141>(v);
+  v += dpp_move<0x140>(v);
+  return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
 }
 
 __device__ __forceinline__ int wave_max_int(int v) {

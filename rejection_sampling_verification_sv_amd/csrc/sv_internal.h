@@ -118,6 +118,38 @@ struct TreeParams {
   uint64_t* part;     // per row piece: (max value bits << 32) | (lowest index + 1)
 };
 
+// One-pass draft-side sampling (rows on 16-byte boundaries): each row is cut
+// into runs of kRunVecs 16-byte vectors (the last run of a row may be
+// short); the streaming pass reduces every run to one tagged record
+// (reference, sum) and the draw re-reads one run per row. The runs of a row
+// are split evenly into cps chunks (one workgroup each), about
+// kChunksSample chunks per call. Runs of 128 vectors (1024 bf16 tokens) and
+// about 4096 chunks measured best on 320 and 2048 rows of V = 128256 and
+// 152064 (256-vector runs and 2048 chunks: up to 20 % slower).
+#ifndef SV_RUN_VECS
+#define SV_RUN_VECS 128
+#endif
+constexpr int kRunVecs = SV_RUN_VECS;
+constexpr int kRunLaneVecs = kRunVecs / kWave;  // vectors per lane per run
+#ifndef SV_CHUNKS_SAMPLE
+#define SV_CHUNKS_SAMPLE 4096
+#endif
+constexpr int kChunksSample = SV_CHUNKS_SAMPLE;
+
+struct SampleParams {
+  const void* logits;
+  const float* temperature;
+  const float* uniforms;
+  int32_t R, V;
+  int64_t nvec;        // 16-byte vectors per row
+  int32_t nrun;        // runs per row
+  int32_t cps;         // chunks per row (<= nrun)
+  int32_t* out_tokens;
+  float* out_prob;
+  int32_t* err_flags;
+  uint64_t* rec;       // workspace [R, nrun]: record of run g of row r
+};
+
 constexpr int kSampleEPT = 8;                      // sampling elements per thread per tile
 constexpr int kSampleTile = 256 * kSampleEPT;      // elements per sampling tile
 // Tiles per sampling workgroup (the same bytes of each sampled row for both
@@ -183,6 +215,7 @@ PassEvents take_pass_events();
 // call (argmax, decision); `ev` (possibly null events) become the start and
 // stop events of the streaming pass.
 hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
+hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
                             hipStream_t stream);

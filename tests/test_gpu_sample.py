@@ -173,3 +173,17 @@ def test_repeat_is_bit_identical(sv):
     a = _run(sv, inp)
     b = _run(sv, inp)
     assert torch.equal(a["tokens"], b["tokens"]) and torch.equal(a["prob"], b["prob"])
+
+
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 600000), (torch.float32, 300000)])
+def test_long_rows_reread_records(sv, dtype, V):
+    # more than 256 runs of 256 vectors per row: the draw re-reads its records
+    _say("long rows: R = 5, V =", V, dtype, "Philox seed 34")
+    rng = np.random.Generator(np.random.Philox(34))
+    R = 5
+    logits = torch.from_numpy(rng.normal(0, 3, (R, V)).astype(np.float32)).to(dtype).cuda()
+    T = torch.from_numpy(rng.uniform(0.5, 1.5, R).astype(np.float32)).cuda()
+    u = torch.from_numpy(rng.random(R, dtype=np.float32)).cuda()
+    out = _run(sv, {"logits": logits, "temperature": T, "uniforms": u})
+    assert int(out["err_flags"].item()) == 0
+    _compare(out, logits, T, u)
