@@ -6,6 +6,7 @@ never by the product library or its binding.
 from .specverify_oracle import (  # noqa: F401
     FLAG_WINDOW,
     temperature_softmax,
+    entropy,
     acceptance_probability,
     residual_weights,
     inverse_cdf,

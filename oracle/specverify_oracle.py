@@ -65,6 +65,21 @@ def temperature_softmax(logits, temperature):
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def entropy(p):
+    """Shannon entropy in nats over the last axis: H = -sum_v p(v) ln p(v), 0 ln 0 = 0.
+
+    [At Scale] section 3 (engineering recommendations): the speculation
+    length K is to be tuned from the entropy of the predictions (lower K where
+    the models diverge). The pages name the quantity without a formula; this
+    is the textbook definition, applied to the temperature softmax p of one
+    position.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        terms = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
+    return -terms.sum(axis=-1)
+
+
 def acceptance_probability(p_x, q_x):
     """alpha = min(1, p(x) / q(x)) for a drafted token x.
 
@@ -169,7 +184,8 @@ def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniform
     Returns a dict of numpy arrays: ``accept_len [B]`` (j, or -1 for an invalid
     row), ``out_tokens [B, K+1]`` (-1 after position j), ``p_draft``,
     ``q_draft [B, K]`` (p_k(x_k), q_k(x_k) for every k), ``residual_mass [B]``
-    (sum max(0, p_j - q_j), -1 when all K are accepted), and diagnostics:
+    (sum max(0, p_j - q_j), -1 when all K are accepted), ``entropy [B, 2K+1]``
+    (the entropy in nats of p_0 .. p_K, then of q_0 .. q_{K-1}), and diagnostics:
     ``alpha [B, K]``, ``margin_accept [B, K]`` (|u_k - alpha_k| for the checked
     positions, +inf for the others), ``margin_sample [B]`` (distance of u_K to
     the nearest CDF boundary of the drawn token), ``flagged [B]`` (a margin
@@ -233,12 +249,15 @@ def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniform
     accept_len = np.where(valid, j, -1).astype(np.int64)
     out[~valid] = -1
     residual_mass[~valid] = -1.0
+    # per-position entropy of every distribution of the step
+    ent = np.concatenate([entropy(p), entropy(q)], axis=1)
     return {
         "accept_len": accept_len,
         "out_tokens": out,
         "p_draft": p_x,
         "q_draft": q_x,
         "residual_mass": residual_mass,
+        "entropy": ent,
         "alpha": alpha,
         "margin_accept": margin_accept,
         "margin_sample": margin_sample,
