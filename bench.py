@@ -54,6 +54,8 @@ def parse():
     ap.add_argument("--workload", default="c2",
                     help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain), c4 (tree) or s1, s2, s3 (draft-side sampling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--entropy", action="store_true",
+                    help="chain workloads: also request every position's entropy (the stream's entropy variant)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle sample's wall time")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run three plain device-to-device copies of MIB MiB (untimed), the known-size "
@@ -231,14 +233,18 @@ def main():
             for i in range(N_SETS):
                 sets.append(chain_inputs(cfg.with_(variant=cfg.variant + 10 * i) if i else cfg, device=dev))
         calls = [sv.PreparedChainCall(s["target"], s["draft"], s["draft_tokens"], s["temperature"], s["uniforms"],
-                                      stream=stream) for s in sets]
+                                      stream=stream, want_entropy=args.entropy) for s in sets]
         # every logit once, plus tokens (gathered by the stream), uniforms and temperatures
         stream_bytes = rows * V * eb + B * K * 4
         call_bytes = stream_bytes + B * (K + 1) * 4 + B * 4
-        config = {"workload": cfg.name, "B": B, "K": K, "V": V, "logits": cfg.dtype,
+        config = {"workload": cfg.name + ("_entropy" if args.entropy else ""), "B": B, "K": K, "V": V,
+                  "logits": cfg.dtype,
                   "temperature": cfg.temperature if cfg.temperature is not None else list(cfg.temperature_range),
                   "input_sets_rotated": len(sets)}
-        kernel_name = "chain_stats_chunk_kernel (statistics pass: every logit row once)"
+        if args.entropy:
+            config["entropy"] = "every position, [B, 2K+1]"
+        kernel_name = ("chain_stats_chunk_entropy_kernel (statistics pass with the entropy: every logit row once)"
+                       if args.entropy else "chain_stats_chunk_kernel (statistics pass: every logit row once)")
     else:
         cfg = TREE_CONFIGS[wl]
         B, N, V = cfg.B, cfg.N, cfg.V
@@ -308,9 +314,9 @@ def main():
     achieved = stream_bytes / (kern_avg_ms * 1e-3) / 1e9
     traffic = counted_traffic(wl, kind)
     result = {
-        "metric": (METRIC if wl == "c2" else
+        "metric": (METRIC if wl == "c2" and not args.entropy else
                    f"sampling throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}" if kind == "sample"
-                   else f"verify throughput: rows·vocab/s + HBM GB/s vs peak, {cfg.name}"),
+                   else f"verify throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}"),
         "value": elems / (ms_per_step * 1e-3),
         "unit": "rows·vocab/s",
         "n_gpus": 1,

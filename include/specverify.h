@@ -139,6 +139,14 @@ size_t sv_chain_workspace_bytes(int32_t B, int32_t K, int32_t V, sv_dtype dtype)
  *   q_draft        [B, K] float32 out or NULL: q_k(x_k) for every k < K
  *   residual_mass  [B] float32 out or NULL: sum max(0, p_j - q_j) when j < K,
  *                  -1 when all K were kept
+ *   entropy        [B, 2K+1] float32 out or NULL: the entropy in nats,
+ *                  -sum_v p(v) ln p(v), of every distribution of the step:
+ *                  p_0 .. p_K, then q_0 .. q_{K-1} ([At Scale] section 3:
+ *                  the speculation length is tuned from the predictions'
+ *                  entropy). Computed by the same single pass over the
+ *                  logits (one more accumulator per element); NaN for a row
+ *                  whose statistics are not finite or whose temperature is
+ *                  invalid. NULL skips it (the pass is then the plain one).
  *   err_flags      [1] int32 in/out or NULL: SV_ERRF_* bits are OR-ed in
  *   workspace      device buffer of at least sv_chain_workspace_bytes() bytes
  *   stream         HIP stream the kernels are enqueued on (NULL = default)
@@ -147,8 +155,9 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
                           const int32_t* draft_tokens, const float* temperature,
                           const float* uniforms, int32_t B, int32_t K, int32_t V,
                           int32_t* accept_len, int32_t* out_tokens, float* p_draft,
-                          float* q_draft, float* residual_mass, int32_t* err_flags,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+                          float* q_draft, float* residual_mass, float* entropy,
+                          int32_t* err_flags, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Draft-side sampling.

@@ -67,7 +67,7 @@ int64_t piece_slots(int64_t B, int32_t rows, int32_t V, sv_dtype d, int64_t chun
 
 struct ChainLayout {
   int32_t ntiles, tiles_per_block, nblk_b;
-  size_t off_part_m, off_part_s, off_cnt, off_tiles, off_gat, off_abort, total;
+  size_t off_part_m, off_part_s, off_part_a, off_cnt, off_tiles, off_gat, off_abort, total;
 };
 
 ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
@@ -82,6 +82,8 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   L.off_part_m = off;
   off = align_up(off + sizeof(uint64_t) * parts);
   L.off_part_s = off;
+  off = align_up(off + sizeof(uint64_t) * parts);
+  L.off_part_a = off;
   off = align_up(off + sizeof(uint64_t) * parts);
   L.off_cnt = off;
   off = align_up(off + sizeof(uint32_t) * B);
@@ -176,7 +178,7 @@ namespace {
 sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dtype dtype, const int32_t* draft_tokens,
                      const float* temperature, const float* uniforms, int32_t B, int32_t K, int32_t V,
                      int32_t* accept_len, int32_t* out_tokens, float* p_draft, float* q_draft, float* residual_mass,
-                     float* drawn_prob, int32_t* err_flags, void* workspace, size_t workspace_bytes,
+                     float* entropy, float* drawn_prob, int32_t* err_flags, void* workspace, size_t workspace_bytes,
                      hipStream_t stream, const sv::PassEvents& ev) {
   if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return SV_ERR_INVALID_ARGUMENT;
   if (B == 0) return SV_OK;
@@ -210,9 +212,11 @@ sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dty
   p.q_draft = q_draft;
   p.residual_mass = residual_mass;
   p.drawn_prob = drawn_prob;
+  p.entropy = entropy;
   p.err_flags = err_flags;
   p.part_m = reinterpret_cast<uint64_t*>(ws + L.off_part_m);
   p.part_s = reinterpret_cast<uint64_t*>(ws + L.off_part_s);
+  p.part_a = reinterpret_cast<uint64_t*>(ws + L.off_part_a);
   p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
   p.tile_sum = reinterpret_cast<uint64_t*>(ws + L.off_tiles);
   p.gat = reinterpret_cast<uint64_t*>(ws + L.off_gat);
@@ -230,14 +234,14 @@ extern "C" {
 sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,
                           const int32_t* draft_tokens, const float* temperature, const float* uniforms,
                           int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
-                          float* p_draft, float* q_draft, float* residual_mass, int32_t* err_flags,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          float* p_draft, float* q_draft, float* residual_mass, float* entropy,
+                          int32_t* err_flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const sv::PassEvents ev = sv::take_pass_events();
   if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return SV_ERR_INVALID_ARGUMENT;
   if (B > 0 && accept_len == nullptr) return SV_ERR_INVALID_ARGUMENT;
   return chain_call(target_logits, draft_logits, dtype, draft_tokens, temperature, uniforms, B, K, V, accept_len,
-                    out_tokens, p_draft, q_draft, residual_mass, nullptr, err_flags, workspace, workspace_bytes,
-                    stream, ev);
+                    out_tokens, p_draft, q_draft, residual_mass, entropy, nullptr, err_flags, workspace,
+                    workspace_bytes, stream, ev);
 }
 
 size_t sv_sample_workspace_bytes(int32_t R, int32_t V, sv_dtype dtype) {
@@ -261,7 +265,7 @@ sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temper
   if (!aligned_to(logits, dtype_bytes(dtype))) return SV_ERR_INVALID_ARGUMENT;
   if (!whole_vector_rows(V, dtype) || !aligned_to(logits, 16))  // rows off 16-byte boundaries: two passes
     return chain_call(logits, nullptr, dtype, nullptr, temperature, uniforms, R, 0, V, nullptr, out_tokens, nullptr,
-                      nullptr, nullptr, out_prob, err_flags, workspace, workspace_bytes, stream, ev);
+                      nullptr, nullptr, nullptr, out_prob, err_flags, workspace, workspace_bytes, stream, ev);
   const RunLayout L = run_layout(R, V, dtype);
   if (static_cast<int64_t>(R) * L.cps > INT32_MAX) return SV_ERR_UNSUPPORTED;
   sv::SampleParams p{};

@@ -63,13 +63,21 @@ __device__ __forceinline__ const void* chain_row(const ChainParams& P, int b, in
 }
 
 // Running (max, sum) of one thread. `mx` is the largest raw logit seen and
-// `s` = sum of 2^(x*c - fl(mx*c_hi)) over the logits seen.
+// `s` = sum of 2^a over the logits seen, a = x*c - fl(mx*c_hi). With the
+// entropy requested (kEnt) it also keeps `a` = sum of 2^a * a (<= 0 up to
+// rounding): for p = 2^a / s, the entropy is ln 2 * (log2 s - A / s). When the
+// reference rises by d, every a falls by d: s -> 2^-d s, A -> 2^-d (A - d s).
+// Arguments are clamped at -256 before the product (2^a is already 0 there),
+// so -inf logits add 0, not 0 * -inf.
 struct Running {
   float mx;
   float s;
+  float a;
 };
 
-template <int N>
+constexpr float kArgFloor = -256.0f;
+
+template <int N, bool kEnt = false>
 __device__ __forceinline__ void running_add(Running& st, const float (&x)[N], Scale c) {
   float bm = x[0];
 #pragma unroll
@@ -78,26 +86,41 @@ __device__ __forceinline__ void running_add(Running& st, const float (&x)[N], Sc
   // when the maximum did not move, 0 while nothing finite had been seen).
   const float m_new = fmaxf(st.mx, bm);
   const float scale = (st.mx == -INFINITY) ? 0.0f : fast_exp2(st.mx * c.hi - m_new * c.hi);
+  if constexpr (kEnt) st.a = (st.mx == -INFINITY) ? 0.0f : scale * (st.a - (m_new * c.hi - st.mx * c.hi) * st.s);
   st.mx = m_new;
   const float neg_m = neg_reference(m_new, c);
   // four partial sums, pairwise inside each group of 8
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acca[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int g = 0; g < N; g += 8) {
-    float e[8];
+    float e[8], ea[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = (g + i < N) ? fast_exp2(scaled_arg(x[g + i], c, neg_m)) : 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      const float arg = (g + i < N) ? scaled_arg(x[g + i], c, neg_m) : -INFINITY;
+      e[i] = (g + i < N) ? fast_exp2(arg) : 0.0f;
+      if constexpr (kEnt) ea[i] = e[i] * fmaxf(arg, kArgFloor);
+    }
     acc[(g / 8) & 3] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    if constexpr (kEnt) acca[(g / 8) & 3] += ((ea[0] + ea[1]) + (ea[2] + ea[3])) + ((ea[4] + ea[5]) + (ea[6] + ea[7]));
   }
   st.s = st.s * scale + ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+  if constexpr (kEnt) st.a += (acca[0] + acca[1]) + (acca[2] + acca[3]);
 }
 
+template <bool kEnt = false>
 __device__ __forceinline__ void running_add1(Running& st, float x, Scale c) {
   if (x > st.mx) {
+    if constexpr (kEnt)
+      st.a = (st.mx == -INFINITY) ? 0.0f
+                                  : fast_exp2(st.mx * c.hi - x * c.hi) * (st.a - (x * c.hi - st.mx * c.hi) * st.s);
     st.s = (st.mx == -INFINITY) ? 0.0f : st.s * fast_exp2(st.mx * c.hi - x * c.hi);
     st.mx = x;
   }
-  st.s += fast_exp2(scaled_arg(x, c, neg_reference(st.mx, c)));
+  const float arg = scaled_arg(x, c, neg_reference(st.mx, c));
+  const float e = fast_exp2(arg);
+  st.s += e;
+  if constexpr (kEnt) st.a += e * fmaxf(arg, kArgFloor);
 }
 
 __device__ __forceinline__ void split(double v, float& hi, float& lo) {
@@ -106,23 +129,69 @@ __device__ __forceinline__ void split(double v, float& hi, float& lo) {
 }
 
 // Block-wide combine of the threads' running states into (reference, sum):
-// the largest fl(mx*c_hi), and the fp64 sum of each thread's sum rescaled to it.
-template <int NW = kWaves>
+// the largest fl(mx*c_hi), and the fp64 sum of each thread's sum rescaled to it
+// (with kEnt also the fp64 sum of each thread's A rescaled to it, into *A).
+template <int NW = kWaves, bool kEnt = false>
 __device__ __forceinline__ void block_combine(const Running& st, Scale c, float* s_redf, double* s_redd, float* MC,
-                                              double* S) {
+                                              double* S, double* A = nullptr) {
   const float mc = (st.mx == -INFINITY) ? -INFINITY : st.mx * c.hi;
   *MC = block_max<NW>(mc, s_redf);
-  double sd = 0.0;
-  if (mc != -INFINITY) sd = static_cast<double>(st.s * fast_exp2(mc - *MC));
+  double sd = 0.0, ad = 0.0;
+  if (mc != -INFINITY) {
+    const float f = fast_exp2(mc - *MC);
+    sd = static_cast<double>(st.s * f);
+    if constexpr (kEnt)
+      ad = static_cast<double>(f) * (static_cast<double>(st.a) -
+                                     (static_cast<double>(*MC) - static_cast<double>(mc)) * static_cast<double>(st.s));
+  }
   *S = block_sum<NW>(sd, s_redd);
+  if constexpr (kEnt) *A = block_sum<NW>(ad, s_redd);
 }
 
-template <class T, int U = kStatsUnroll>
+template <class T, int U = kStatsUnroll, bool kEnt = false>
 __device__ __forceinline__ void add_batch(Running& st, const uint4 (&raw)[U], Scale c) {
-  float x[U * T::kVec];
+  if constexpr (kEnt && T::kVec == 8) {
+    // bf16 with the entropy: the same operations in the same order as
+    // running_add (one group of 8 per vector), with the values widened twice
+    // from the raw vectors (for the maximum, then behind an empty asm for
+    // the exponentials) so that 16 floats do not stay live across both
+    float bm = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < U; ++u) unpack<T>(raw[u], &x[u * T::kVec]);
-  running_add(st, x, c);
+    for (int u = 0; u < U; ++u) {
+      float t[8];
+      unpack<T>(raw[u], t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bm = fmaxf(bm, t[i]);
+    }
+    const float m_new = fmaxf(st.mx, bm);
+    const float scale = (st.mx == -INFINITY) ? 0.0f : fast_exp2(st.mx * c.hi - m_new * c.hi);
+    st.a = (st.mx == -INFINITY) ? 0.0f : scale * (st.a - (m_new * c.hi - st.mx * c.hi) * st.s);
+    st.mx = m_new;
+    const float neg_m = neg_reference(m_new, c);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float acca = st.a;  // A feeds only the entropy: one fma chain
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint4 r = raw[u];
+      asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w));
+      float t[8], e[8];
+      unpack<T>(r, t);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float arg = scaled_arg(t[i], c, neg_m);
+        e[i] = fast_exp2(arg);
+        acca = fmaf(e[i], fmaxf(arg, kArgFloor), acca);
+      }
+      acc[u & 3] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    }
+    st.s = st.s * scale + ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    st.a = acca;
+  } else {
+    float x[U * T::kVec];
+#pragma unroll
+    for (int u = 0; u < U; ++u) unpack<T>(raw[u], &x[u * T::kVec]);
+    running_add<U * T::kVec, kEnt>(st, x, c);
+  }
 }
 
 // The exponent scale of a sequence, computed on first use: the statistics
@@ -155,10 +224,9 @@ __device__ __forceinline__ void load_batch(const uint4* ptr, uint4 (&raw)[U]) {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <class T, int TPB>
+template <class T, int TPB, bool kEnt = false, int U = kStreamU>
 __device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, int64_t p1, LazyScale& sc,
                                                  Running& st) {
-  constexpr int U = kStreamU;
   constexpr int STEP = TPB * U;
   const int32_t nfull = static_cast<int32_t>((p1 - p0) / STEP);
   const uint4* ptr = body + p0 + threadIdx.x;
@@ -171,18 +239,18 @@ __device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, 
 #pragma unroll 1
     for (; i + 1 < nfull; i += 2) {
       load_batch<T, U, TPB>(ptr + STEP, b);
-      add_batch<T, U>(st, a, c);
+      add_batch<T, U, kEnt>(st, a, c);
       load_batch<T, U, TPB>(ptr + 2 * STEP, a);
-      add_batch<T, U>(st, b, c);
+      add_batch<T, U, kEnt>(st, b, c);
       ptr += 2 * STEP;
     }
     if (i < nfull) {  // one batch left to load
       load_batch<T, U, TPB>(ptr + STEP, b);
-      add_batch<T, U>(st, a, c);
-      add_batch<T, U>(st, b, c);
+      add_batch<T, U, kEnt>(st, a, c);
+      add_batch<T, U, kEnt>(st, b, c);
       ptr += 2 * STEP;
     } else {
-      add_batch<T, U>(st, a, c);
+      add_batch<T, U, kEnt>(st, a, c);
       ptr += STEP;
     }
   }
@@ -194,7 +262,7 @@ __device__ __forceinline__ void flat_piece_stats(const uint4* body, int64_t p0, 
       const int64_t k = static_cast<int64_t>(u) * TPB + threadIdx.x;
       raw[u] = (k < rest) ? stream_load(ptr + u * TPB) : neg_inf_vec<T>();
     }
-    add_batch<T, U>(st, raw, sc.get());
+    add_batch<T, U, kEnt>(st, raw, sc.get());
   }
 }
 
@@ -220,7 +288,7 @@ __device__ __forceinline__ void publish_gather(const ChainParams& P, int b, int 
 
 // Segments layout: segment `seg` of row r of sequence b (any alignment), its
 // (reference, sum) to slot (b * (2K+1) + r) * nseg + seg.
-template <class T>
+template <class T, bool kEnt>
 __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
   __shared__ float s_redf[kWaves];
   __shared__ double s_redd[kWaves];
@@ -242,8 +310,8 @@ __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
   const uint4* body = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + head * T::kBytes);
 
   const int x = (seg == 0 && tid == 0) ? row_token(P, b, r) : -1;
-  Running st{-INFINITY, 0.0f};
-  if (seg == 0 && tid < head) running_add1(st, load_elem<T>(row, tid), c);
+  Running st{-INFINITY, 0.0f, 0.0f};
+  if (seg == 0 && tid < head) running_add1<kEnt>(st, load_elem<T>(row, tid), c);
   for (int64_t base = v0 + tid; base < v1; base += static_cast<int64_t>(kThreads) * U) {
     uint4 raw[U];
 #pragma unroll
@@ -251,17 +319,18 @@ __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
       const int64_t vi = base + static_cast<int64_t>(u) * kThreads;
       raw[u] = (vi < v1) ? stream_load(body + vi) : neg_inf_vec<T>();
     }
-    add_batch<T>(st, raw, c);
+    add_batch<T, U, kEnt>(st, raw, c);
   }
-  if (seg == P.L.nseg - 1 && tid < tail) running_add1(st, load_elem<T>(row, head + nvec * VEC + tid), c);
+  if (seg == P.L.nseg - 1 && tid < tail) running_add1<kEnt>(st, load_elem<T>(row, head + nvec * VEC + tid), c);
 
   float MC;
-  double S;
-  block_combine(st, c, s_redf, s_redd, &MC, &S);
+  double S, A = 0.0;
+  block_combine<kWaves, kEnt>(st, c, s_redf, s_redd, &MC, &S, &A);
   if (tid == 0) {
     const int64_t slot = (static_cast<int64_t>(b) * R + r) * P.L.nseg + seg;
     publish(&P.part_m[slot], tag_float(MC));
     publish(&P.part_s[slot], tag_nonneg_double(S));
+    if constexpr (kEnt) publish(&P.part_a[slot], static_cast<uint64_t>(__double_as_longlong(A)));
     if (x >= 0 && x < P.V) publish_gather<T>(P, b, r, row, x);
   }
 }
@@ -270,7 +339,7 @@ __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
 // [ch * per, (ch + 1) * per) of the sequence's 2K+1 rows laid end to end,
 // streamed as one piece per row it touches; the piece of row r goes to slot
 // (b * cps + ch) * kmax + (r - first row of the chunk).
-template <class T, int TPB>
+template <class T, int TPB, bool kEnt>
 __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
   constexpr int NW = TPB / kWave;
   __shared__ float s_redf[NW];
@@ -287,15 +356,16 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
     const int64_t p1 = min(hi, (r + 1) * nvec) - r * nvec;
     const uint4* body = static_cast<const uint4*>(chain_row<T>(P, b, r));
     const int x = row_token(P, b, r);  // a uniform (scalar) load, consumed after the piece
-    Running st{-INFINITY, 0.0f};
-    flat_piece_stats<T, TPB>(body, p0, p1, sc, st);
+    Running st{-INFINITY, 0.0f, 0.0f};
+    flat_piece_stats<T, TPB, kEnt, kEnt ? kStreamUEnt : kStreamU>(body, p0, p1, sc, st);
     float MC;
-    double S;
-    block_combine<NW>(st, sc.get(), s_redf, s_redd, &MC, &S);
+    double S, A = 0.0;
+    block_combine<NW, kEnt>(st, sc.get(), s_redf, s_redd, &MC, &S, &A);
     if (threadIdx.x == 0) {
       const int64_t slot = (static_cast<int64_t>(b) * P.L.cps + ch) * P.L.kmax + (r - r_lo);
       publish(&P.part_m[slot], tag_float(MC));
       publish(&P.part_s[slot], tag_nonneg_double(S));
+      if constexpr (kEnt) publish(&P.part_a[slot], static_cast<uint64_t>(__double_as_longlong(A)));
       // the piece holding the drafted token publishes its logit
       if (x >= 0 && x < P.V && x / T::kVec >= p0 && x / T::kVec < p1) publish_gather<T>(P, b, r, body, x);
     }
@@ -321,7 +391,8 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
 // none) and return how many exist; every lane issues all eight loads (the
 // missing ones read any_slot and are dropped), so they are in flight together.
 __device__ __forceinline__ int issue_pieces(const ChainParams& P, int b, int r, int p0, int G, int pmax,
-                                            int64_t any_slot, uint64_t (&rm)[4], uint64_t (&rs)[4]) {
+                                            int64_t any_slot, uint64_t (&rm)[4], uint64_t (&rs)[4],
+                                            uint64_t (&ra)[4]) {
   int64_t sl[4];
   int n = 0;
   if (P.L.cps > 0 && r >= 0) {
@@ -351,6 +422,7 @@ __device__ __forceinline__ int issue_pieces(const ChainParams& P, int b, int r, 
     const int64_t a = i < n ? sl[i] : any_slot;
     rm[i] = P.part_m[a];
     rs[i] = P.part_s[a];
+    ra[i] = (P.entropy != nullptr) ? P.part_a[a] : 0ull;
   }
   return n;
 }
@@ -371,8 +443,8 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
   // The loads of the usual case all go out before any is used: the first
   // round of this lane's statistics pieces (every piece when the rows fit
   // one wave and have at most 4 G pieces), then the drafted tokens' inputs.
-  uint64_t rm0[4], rs0[4];
-  const int n0 = issue_pieces(P, b, lane / G < R ? lane / G : -1, lane % G, G, pmax, any_slot, rm0, rs0);
+  uint64_t rm0[4], rs0[4], ra0[4];
+  const int n0 = issue_pieces(P, b, lane / G < R ? lane / G : -1, lane % G, G, pmax, any_slot, rm0, rs0, ra0);
   const float Tv = temperature_of(P.temperature, b);
   int x = -1;
   float u = 0.0f;
@@ -392,11 +464,15 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
     const bool row_ok = r < R;
     // this lane's pieces p = gl, gl + G, ...: rounds of up to four loads in
     // flight, each round folded into (mf, zf) = (reference, fp64 sum)
+    // (and with the entropy requested, af = the fp64 sum of 2^a * a at the
+    // reference mf: a piece moved to a reference higher by d contributes
+    // 2^-d (A - d S))
+    const bool ent = P.entropy != nullptr;
     float mf = -INFINITY;
-    double zf = 0.0;
+    double zf = 0.0, af = 0.0;
     bool more = row_ok;
     for (int p0 = gl; more; p0 += 4 * G) {
-      uint64_t rm[4], rs[4];
+      uint64_t rm[4], rs[4], ra[4];
       int n;
       if (r0 == 0 && p0 == gl) {
         n = n0;
@@ -404,32 +480,51 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
         for (int i = 0; i < 4; ++i) {
           rm[i] = rm0[i];
           rs[i] = rs0[i];
+          ra[i] = ra0[i];
         }
       } else {
-        n = issue_pieces(P, b, r, p0, G, pmax, any_slot, rm, rs);
+        n = issue_pieces(P, b, r, p0, G, pmax, any_slot, rm, rs, ra);
       }
       more = (n == 4);
       for (int i = 0; i < n; ++i) {
         if (rm[i] == 0ull || rs[i] == 0ull) err |= kErrInternal;
         const float mm = untag_float(rm[i]);
         const double sv = untag_nonneg_double(rs[i]);
+        const double av = __longlong_as_double(static_cast<long long>(ra[i]));
         if (mm == -INFINITY) continue;
         if (mm > mf) {
-          zf = (mf == -INFINITY ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(mm))) + sv;
+          const double d = static_cast<double>(mm) - static_cast<double>(mf);
+          const double f = (mf == -INFINITY) ? 0.0 : exp2(-d);
+          if (ent) af = (mf == -INFINITY ? 0.0 : f * (af - d * zf)) + av;
+          zf = zf * f + sv;
           mf = mm;
         } else {
-          zf += sv * exp2(static_cast<double>(mm) - static_cast<double>(mf));
+          const double d = static_cast<double>(mf) - static_cast<double>(mm);
+          const double f = exp2(-d);
+          zf += sv * f;
+          if (ent) af += f * (av - d * sv);
         }
       }
     }
     float M = mf;
     for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
-    const double zl0 = (mf == -INFINITY) ? 0.0 : zf * exp2(static_cast<double>(mf) - static_cast<double>(M));
-    double zl = zl0;
+    const double dl = static_cast<double>(M) - static_cast<double>(mf);
+    const double fl = (mf == -INFINITY) ? 0.0 : exp2(-dl);
+    double zl = zf * fl;
     for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
+    double al = 0.0;
+    if (ent) {
+      al = (mf == -INFINITY) ? 0.0 : fl * (af - dl * zf);
+      for (int o = 1; o < G; o <<= 1) al += __shfl_xor(al, o, kWave);
+    }
     if (row_ok && gl == 0) {
-      if (!(zl > 0.0) || !isfinite(zl) || !isfinite(M)) err |= SV_ERRF_NONFINITE;
+      const bool fin = (zl > 0.0) && isfinite(zl) && isfinite(M);
+      if (!fin) err |= SV_ERRF_NONFINITE;
       s_L[r] = static_cast<double>(M) + log2(zl);
+      // H = ln 2 * (log2 Z - A / Z); NaN for a row without finite statistics
+      if (ent && writer)
+        P.entropy[static_cast<int64_t>(b) * R + r] =
+            (fin && Tv > 0.0f && isfinite(Tv)) ? static_cast<float>(0.6931471805599453 * (log2(zl) - al / zl)) : NAN;
     }
   }
   // s_L is written by the group leaders and read by other lanes of this wave.
@@ -830,6 +925,7 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
        sl += kThreads) {
     P.part_m[sl] = 0ull;
     P.part_s[sl] = 0ull;
+    if (P.entropy != nullptr) P.part_a[sl] = 0ull;
   }
   const int R = 2 * P.K + 1;
   for (int r = threadIdx.x; r < R; r += kThreads) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
@@ -839,21 +935,33 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
 }  // namespace
 
 // Pass 1, chunked layout: one workgroup per chunk.
-template <class T>
-__global__ __launch_bounds__(kStatsTPB) __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES, SV_STATS_WAVES))) void chain_stats_chunk_kernel(ChainParams P) {
+template <class T, bool kEnt>
+__device__ __forceinline__ void stats_chunk_item(const ChainParams& P) {
   // blockIdx.x and the chunks per sequence fit 32 bits (checked on the host)
   const uint32_t cps = static_cast<uint32_t>(P.L.cps);
   const uint32_t b = blockIdx.x / cps;
-  stats_chunk<T, kStatsTPB>(P, static_cast<int>(b), static_cast<int>(blockIdx.x - b * cps));
+  stats_chunk<T, kStatsTPB, kEnt>(P, static_cast<int>(b), static_cast<int>(blockIdx.x - b * cps));
+}
+
+template <class T>
+__global__ __launch_bounds__(kStatsTPB) __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES, SV_STATS_WAVES))) void chain_stats_chunk_kernel(ChainParams P) {
+  stats_chunk_item<T, false>(P);
+}
+
+// The same pass with the entropy of every row requested (one more
+// accumulator per thread), compiled for its own occupancy.
+template <class T>
+__global__ __launch_bounds__(kStatsTPB) __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES_ENT, SV_STATS_WAVES_ENT))) void chain_stats_chunk_entropy_kernel(ChainParams P) {
+  stats_chunk_item<T, true>(P);
 }
 
 // Pass 1, segments layout: one workgroup per row segment.
-template <class T>
+template <class T, bool kEnt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void chain_stats_segment_kernel(ChainParams P) {
   const uint32_t per_seq = static_cast<uint32_t>(items_per_seq(P.L));
   const int b = static_cast<int>(blockIdx.x / per_seq);
   const int rem = static_cast<int>(blockIdx.x - static_cast<uint32_t>(b) * per_seq);
-  stats_segment<T>(P, b, rem / P.L.nseg, rem % P.L.nseg);
+  stats_segment<T, kEnt>(P, b, rem / P.L.nseg, rem % P.L.nseg);
 }
 
 // Pass 2: nblk_b workgroups per sequence, assigned round-robin over the
@@ -882,12 +990,13 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
   const int64_t grid_c = static_cast<int64_t>(p.B) * p.nblk_b;
   if (grid_a > INT32_MAX || grid_c > INT32_MAX) return hipErrorInvalidConfiguration;
   // Armed events take the statistics kernel's own start and end timestamps.
+  const bool ent = p.entropy != nullptr;
   if (p.L.cps > 0)
-    hipExtLaunchKernelGGL(chain_stats_chunk_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kStatsTPB), 0,
-                          stream, ev.before, ev.after, 0u, p);
+    hipExtLaunchKernelGGL(ent ? chain_stats_chunk_entropy_kernel<T> : chain_stats_chunk_kernel<T>,
+                          dim3(static_cast<uint32_t>(grid_a)), dim3(kStatsTPB), 0, stream, ev.before, ev.after, 0u, p);
   else
-    hipExtLaunchKernelGGL(chain_stats_segment_kernel<T>, dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0,
-                          stream, ev.before, ev.after, 0u, p);
+    hipExtLaunchKernelGGL(ent ? chain_stats_segment_kernel<T, true> : chain_stats_segment_kernel<T, false>,
+                          dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, ev.before, ev.after, 0u, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.K == 0)

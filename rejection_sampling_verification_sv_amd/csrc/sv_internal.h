@@ -93,10 +93,13 @@ struct ChainParams {
   float* q_draft;
   float* residual_mass;
   float* drawn_prob;  // [B] or null: p of the token drawn at j (draft-side sampling, K = 0)
+  float* entropy;     // [B, 2K+1] or null: entropy (nats) of every row's distribution
   int32_t* err_flags;
   // workspace (all zero between calls)
   uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi)
   uint64_t* part_s;   // per row piece: tagged fp64 sum of 2^(x c - reference)
+  uint64_t* part_a;   // per row piece, entropy only: fp64 bits of the sum of
+                      // 2^a * a, a = x c - reference (untagged)
   uint32_t* cnt;      // [B] sampling workgroups finished
   uint64_t* tile_sum; // [B, ntiles] tagged fp64 sampling weight per tile
   uint64_t* gat;      // [B, 2K+1] tagged fp32 logit of row r at its drafted
@@ -177,6 +180,12 @@ constexpr int kStatsSegVecs = 256 * kStatsUnroll * kStatsBatches;
 #define SV_STREAM_U 2
 #endif
 constexpr int kStreamU = SV_STREAM_U;
+// The same for the entropy variant of the stream (2: the same batches, so the
+// same rounding of every other output, as the plain stream).
+#ifndef SV_STREAM_U_ENT
+#define SV_STREAM_U_ENT 2
+#endif
+constexpr int kStreamUEnt = SV_STREAM_U_ENT;
 // Threads per workgroup of the chunked statistics stream.
 #ifndef SV_STATS_TPB
 #define SV_STATS_TPB 256
@@ -186,6 +195,14 @@ constexpr int kStatsTPB = SV_STATS_TPB;
 // VGPRs; 4: at most 128).
 #ifndef SV_STATS_WAVES
 #define SV_STATS_WAVES 8
+#endif
+// The same for the entropy variant of the stream: its extra accumulator does
+// not fit 64 VGPRs with two batches of two vectors in flight (82 VGPRs, 5
+// waves/SIMD at run time). Measured on c2: 41.7 us; one vector per batch at
+// 8 waves/SIMD 39.1 us but with other rounding of p and q; 8 waves with
+// spills 61 us.
+#ifndef SV_STATS_WAVES_ENT
+#define SV_STATS_WAVES_ENT 4
 #endif
 
 // Chunked layouts: about this many chunks per call (one workgroup each;

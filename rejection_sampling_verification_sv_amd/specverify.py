@@ -61,7 +61,7 @@ def _load():
         lib.sv_chain_workspace_bytes.restype = _c_size
         lib.sv_verify_chain.argtypes = [
             _c_ptr, _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
-            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
         ]
         lib.sv_verify_chain.restype = ctypes.c_int
         lib.sv_tree_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int]
@@ -186,12 +186,15 @@ def sv_tree_workspace_bytes(B: int, N: int, V: int, dtype: torch.dtype) -> int:
 def sv_verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
                     temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
                     accept_len=None, out_tokens=None, p_draft=None, q_draft=None, residual_mass=None,
-                    err_flags=None, workspace_tensor=None, stream=None, want_probs: bool = True) -> dict:
+                    entropy=None, err_flags=None, workspace_tensor=None, stream=None, want_probs: bool = True,
+                    want_entropy: bool = False) -> dict:
     """Chain verification (``sv_verify_chain``). Shapes as in include/specverify.h.
 
     Returns a dict with ``accept_len [B]``, ``out_tokens [B,K+1]``, and when
-    ``want_probs`` ``p_draft``, ``q_draft [B,K]``, ``residual_mass [B]``, plus
-    ``err_flags [1]``. Outputs are ready once the stream has been synchronised.
+    ``want_probs`` ``p_draft``, ``q_draft [B,K]``, ``residual_mass [B]``, when
+    ``want_entropy`` (or an ``entropy`` tensor is passed) ``entropy [B,2K+1]``,
+    plus ``err_flags [1]``. Outputs are ready once the stream has been
+    synchronised.
     """
     lib = _load()
     if target.dim() != 3:
@@ -215,18 +218,24 @@ def sv_verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_t
         p_draft = torch.empty((B, K), **f32) if p_draft is None else _dev(p_draft, "p_draft", torch.float32, (B, K), dev)
         q_draft = torch.empty((B, K), **f32) if q_draft is None else _dev(q_draft, "q_draft", torch.float32, (B, K), dev)
         residual_mass = torch.empty((B,), **f32) if residual_mass is None else _dev(residual_mass, "residual_mass", torch.float32, (B,), dev)
+    if entropy is not None:
+        _dev(entropy, "entropy", torch.float32, (B, 2 * K + 1), dev)
+    elif want_entropy:
+        entropy = torch.empty((B, 2 * K + 1), **f32)
     err_flags = torch.zeros((1,), **i32) if err_flags is None else _dev(err_flags, "err_flags", torch.int32, (1,), dev)
     nbytes = int(lib.sv_chain_workspace_bytes(B, K, V, code))
     ws = workspace(dev, nbytes, stream) if workspace_tensor is None else workspace_tensor
     st = lib.sv_verify_chain(
         _ptr(target), _ptr(draft) if K > 0 else None, code, _ptr(draft_tokens) if K > 0 else None,
         _ptr(temperature), _ptr(uniforms), B, K, V,
-        _ptr(accept_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft), _ptr(residual_mass), _ptr(err_flags),
-        _ptr(ws), ws.numel(), _stream_handle(dev, stream))
+        _ptr(accept_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft), _ptr(residual_mass), _ptr(entropy),
+        _ptr(err_flags), _ptr(ws), ws.numel(), _stream_handle(dev, stream))
     _check(st, "sv_verify_chain")
     out = {"accept_len": accept_len, "out_tokens": out_tokens, "err_flags": err_flags}
     if want_probs:
         out.update(p_draft=p_draft, q_draft=q_draft, residual_mass=residual_mass)
+    if entropy is not None:
+        out["entropy"] = entropy
     return out
 
 
@@ -324,7 +333,8 @@ class PreparedChainCall:
     passed at construction are kept alive and reused by every call.
     """
 
-    def __init__(self, target, draft, draft_tokens, temperature, uniforms, *, stream=None, want_probs=True):
+    def __init__(self, target, draft, draft_tokens, temperature, uniforms, *, stream=None, want_probs=True,
+                 want_entropy=False):
         B, K1, V = target.shape
         K = K1 - 1
         dev = target.device
@@ -337,6 +347,8 @@ class PreparedChainCall:
             self.out["p_draft"] = torch.empty((B, K), dtype=torch.float32, device=dev)
             self.out["q_draft"] = torch.empty((B, K), dtype=torch.float32, device=dev)
             self.out["residual_mass"] = torch.empty((B,), dtype=torch.float32, device=dev)
+        if want_entropy:
+            self.out["entropy"] = torch.empty((B, 2 * K + 1), dtype=torch.float32, device=dev)
         # one checked call through the regular path validates every argument
         sv_verify_chain(target, draft, draft_tokens, temperature, uniforms, stream=stream,
                         want_probs=want_probs, **self.out)
@@ -350,8 +362,8 @@ class PreparedChainCall:
             _ptr(target), _ptr(draft) if K > 0 else None, code, _ptr(draft_tokens) if K > 0 else None,
             _ptr(temperature), _ptr(uniforms), B, K, V,
             _ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o.get("p_draft")), _ptr(o.get("q_draft")),
-            _ptr(o.get("residual_mass")), _ptr(o["err_flags"]), _ptr(self._ws), self._ws.numel(),
-            _stream_handle(dev, stream))
+            _ptr(o.get("residual_mass")), _ptr(o.get("entropy")), _ptr(o["err_flags"]), _ptr(self._ws),
+            self._ws.numel(), _stream_handle(dev, stream))
 
     def __call__(self):
         st = self._fn(*self._args)

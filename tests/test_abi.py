@@ -72,10 +72,10 @@ FAKE = 0x10000  # a non-NULL address that is never dereferenced on these paths
 
 def _chain(lib, **kw):
     a = dict(t=FAKE, d=FAKE, dt=1, x=FAKE, T=None, u=FAKE, B=4, K=4, V=100, acc=FAKE, out=FAKE,
-             p=None, q=None, s=None, err=None, ws=FAKE, wsb=1 << 20, stream=None)
+             p=None, q=None, s=None, h=None, err=None, ws=FAKE, wsb=1 << 20, stream=None)
     a.update(kw)
     return lib.sv_verify_chain(a["t"], a["d"], a["dt"], a["x"], a["T"], a["u"], a["B"], a["K"], a["V"],
-                               a["acc"], a["out"], a["p"], a["q"], a["s"], a["err"], a["ws"], a["wsb"],
+                               a["acc"], a["out"], a["p"], a["q"], a["s"], a["h"], a["err"], a["ws"], a["wsb"],
                                a["stream"])
 
 
@@ -125,7 +125,13 @@ def test_sample_argument_errors(lib):
     assert call(x=None) == 1 and call(u=None) == 1 and call(out=None) == 1
     assert call(dt=5) == 1 and call(V=0) == 1 and call(R=-1) == 1
     assert call(ws=None) == 3 and call(wsb=16) == 3
-    assert lib.sv_sample_workspace_bytes(320, 128256, 1) == lib.sv_chain_workspace_bytes(320, 0, 128256, 1)
+    # the sampling workspace covers the K = 0 chain layout (rows off 16-byte
+    # boundaries) and one 8-byte record per run of 128 vectors (aligned rows)
+    for R, V, dt in ((320, 128256, 1), (2048, 152064, 1), (5, 600000, 1), (7, 4099, 1), (16, 32000, 0)):
+        ws = lib.sv_sample_workspace_bytes(R, V, dt)
+        assert ws >= lib.sv_chain_workspace_bytes(R, 0, V, dt)
+        if (V * (2 if dt else 4)) % 16 == 0:
+            assert ws >= 8 * R * -(-(V * (2 if dt else 4) // 16) // 128)
     assert lib.sv_sample_workspace_bytes(4, 0, 1) == 0
 
 
