@@ -159,7 +159,7 @@ def sample_rows(logits, temperature, uniforms):
 
 # ----------------------------------------------------------------------------- chain verification
 
-def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniforms):
+def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniforms, with_entropy=False):
     """One verification step of chain speculative sampling for a batch of sequences.
 
     Shapes: target ``[B, K+1, V]``, draft ``[B, K, V]``, draft_tokens ``[B, K]``,
@@ -184,8 +184,9 @@ def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniform
     Returns a dict of numpy arrays: ``accept_len [B]`` (j, or -1 for an invalid
     row), ``out_tokens [B, K+1]`` (-1 after position j), ``p_draft``,
     ``q_draft [B, K]`` (p_k(x_k), q_k(x_k) for every k), ``residual_mass [B]``
-    (sum max(0, p_j - q_j), -1 when all K are accepted), ``entropy [B, 2K+1]``
-    (the entropy in nats of p_0 .. p_K, then of q_0 .. q_{K-1}), and diagnostics:
+    (sum max(0, p_j - q_j), -1 when all K are accepted), with ``with_entropy``
+    ``entropy [B, 2K+1]`` (the entropy in nats of p_0 .. p_K, then of
+    q_0 .. q_{K-1}), and diagnostics:
     ``alpha [B, K]``, ``margin_accept [B, K]`` (|u_k - alpha_k| for the checked
     positions, +inf for the others), ``margin_sample [B]`` (distance of u_K to
     the nearest CDF boundary of the drawn token), ``flagged [B]`` (a margin
@@ -249,21 +250,21 @@ def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniform
     accept_len = np.where(valid, j, -1).astype(np.int64)
     out[~valid] = -1
     residual_mass[~valid] = -1.0
-    # per-position entropy of every distribution of the step
-    ent = np.concatenate([entropy(p), entropy(q)], axis=1)
-    return {
+    res = {
         "accept_len": accept_len,
         "out_tokens": out,
         "p_draft": p_x,
         "q_draft": q_x,
         "residual_mass": residual_mass,
-        "entropy": ent,
         "alpha": alpha,
         "margin_accept": margin_accept,
         "margin_sample": margin_sample,
         "flagged": flagged & valid,
         "valid": valid,
     }
+    if with_entropy:  # per-position entropy of every distribution of the step
+        res["entropy"] = np.concatenate([entropy(p), entropy(q)], axis=1)
+    return res
 
 
 # ----------------------------------------------------------------------------- tree verification

@@ -74,8 +74,13 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   ChainLayout L{};
   const int32_t R = 2 * K + 1;
   L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
-  L.tiles_per_block = (d == SV_DTYPE_BF16 ? sv::kSampleTilesBF16 : sv::kSampleTilesF32) *
-                      (K == 0 ? sv::kSampleTilesK0Factor : 1);
+  // groups of tiles whose loads a sampling workgroup keeps in flight together;
+  // each workgroup takes enough groups to keep about kSampleBlocks workgroups
+  // per call (its decision is redone by every workgroup)
+  const int64_t group = (d == SV_DTYPE_BF16 ? sv::kSampleTilesBF16 : sv::kSampleTilesF32) *
+                        (K == 0 ? sv::kSampleTilesK0Factor : 1);
+  const int64_t groups = ceil_div(static_cast<int64_t>(B) * ceil_div(L.ntiles, group), sv::kSampleBlocks);
+  L.tiles_per_block = static_cast<int32_t>(group * (groups < 1 ? 1 : groups));
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
   const int64_t parts = piece_slots(B, R, V, d, chunk_vecs(B, R, V, d, sv::kChunksChain));
   size_t off = 0;

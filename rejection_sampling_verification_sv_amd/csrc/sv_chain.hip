@@ -390,6 +390,7 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
 // Issue the loads of pieces p0, p0 + G, p0 + 2G, p0 + 3G of row r (r < 0:
 // none) and return how many exist; every lane issues all eight loads (the
 // missing ones read any_slot and are dropped), so they are in flight together.
+template <bool kEnt>
 __device__ __forceinline__ int issue_pieces(const ChainParams& P, int b, int r, int p0, int G, int pmax,
                                             int64_t any_slot, uint64_t (&rm)[4], uint64_t (&rs)[4],
                                             uint64_t (&ra)[4]) {
@@ -422,12 +423,12 @@ __device__ __forceinline__ int issue_pieces(const ChainParams& P, int b, int r, 
     const int64_t a = i < n ? sl[i] : any_slot;
     rm[i] = P.part_m[a];
     rs[i] = P.part_s[a];
-    ra[i] = (P.entropy != nullptr) ? P.part_a[a] : 0ull;
+    ra[i] = kEnt ? P.part_a[a] : 0ull;
   }
   return n;
 }
 
-template <class T>
+template <class T, bool kEnt>
 __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
   const int K = P.K;
@@ -444,7 +445,7 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
   // round of this lane's statistics pieces (every piece when the rows fit
   // one wave and have at most 4 G pieces), then the drafted tokens' inputs.
   uint64_t rm0[4], rs0[4], ra0[4];
-  const int n0 = issue_pieces(P, b, lane / G < R ? lane / G : -1, lane % G, G, pmax, any_slot, rm0, rs0, ra0);
+  const int n0 = issue_pieces<kEnt>(P, b, lane / G < R ? lane / G : -1, lane % G, G, pmax, any_slot, rm0, rs0, ra0);
   const float Tv = temperature_of(P.temperature, b);
   int x = -1;
   float u = 0.0f;
@@ -467,7 +468,7 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
     // (and with the entropy requested, af = the fp64 sum of 2^a * a at the
     // reference mf: a piece moved to a reference higher by d contributes
     // 2^-d (A - d S))
-    const bool ent = P.entropy != nullptr;
+    constexpr bool ent = kEnt;
     float mf = -INFINITY;
     double zf = 0.0, af = 0.0;
     bool more = row_ok;
@@ -483,7 +484,7 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
           ra[i] = ra0[i];
         }
       } else {
-        n = issue_pieces(P, b, r, p0, G, pmax, any_slot, rm, rs, ra);
+        n = issue_pieces<kEnt>(P, b, r, p0, G, pmax, any_slot, rm, rs, ra);
       }
       more = (n == 4);
       for (int i = 0; i < n; ++i) {
@@ -495,14 +496,14 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
         if (mm > mf) {
           const double d = static_cast<double>(mm) - static_cast<double>(mf);
           const double f = (mf == -INFINITY) ? 0.0 : exp2(-d);
-          if (ent) af = (mf == -INFINITY ? 0.0 : f * (af - d * zf)) + av;
+          if constexpr (ent) af = (mf == -INFINITY ? 0.0 : f * (af - d * zf)) + av;
           zf = zf * f + sv;
           mf = mm;
         } else {
           const double d = static_cast<double>(mf) - static_cast<double>(mm);
           const double f = exp2(-d);
           zf += sv * f;
-          if (ent) af += f * (av - d * sv);
+          if constexpr (ent) af += f * (av - d * sv);
         }
       }
     }
@@ -513,7 +514,7 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
     double zl = zf * fl;
     for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
     double al = 0.0;
-    if (ent) {
+    if constexpr (ent) {
       al = (mf == -INFINITY) ? 0.0 : fl * (af - dl * zf);
       for (int o = 1; o < G; o <<= 1) al += __shfl_xor(al, o, kWave);
     }
@@ -871,45 +872,52 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
 
 // Sampling workgroup g of sequence b: its wave 0 makes the sequence's
 // decision (group 0 writes it out), then the workgroup forms the weights of
-// tiles [g * TPB, g * TPB + TPB) of the sampling row pair and publishes
-// their totals; the last workgroup of the sequence to finish draws the token
+// tiles [g * tiles_per_block, (g + 1) * tiles_per_block) of the sampling row
+// pair, TPB at a time, and publishes their totals; the last workgroup of the sequence to finish draws the token
 // and returns the sequence's workspace (statistics pieces, gathered logits,
 // tile totals, arrival counter) to zero.
-template <class T, int TPB, bool kDraft>
+template <class T, int TPB, bool kDraft, bool kEnt>
 __device__ void sample_seq(const ChainParams& P, int b, int blk) {
   constexpr int NV = kEptVecs<T>;
   __shared__ double s_red[TPB][kWaves];
   __shared__ int s_flag;
   __shared__ SeqPlan s_plan;
-  if (wave_id() == 0) decide_wave<T>(P, b, &s_plan, blk == 0);
+  if (wave_id() == 0) decide_wave<T, kEnt>(P, b, &s_plan, blk == 0);
   __syncthreads();
   const SeqPlan pl = s_plan;
 
   if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
     const SampleRows S = sample_rows<T>(P, b, pl, false);
-    const int t0 = blk * TPB;
-    uint4 rt[TPB][NV], rd[kDraft ? TPB : 1][NV] = {};
+    // this workgroup's tiles, in groups of TPB whose loads are all in flight at once
+    const int t_begin = blk * P.tiles_per_block;
+    const int t_end = min(t_begin + P.tiles_per_block, P.ntiles);
+#pragma unroll 1
+    for (int t0 = t_begin; t0 < t_end; t0 += TPB) {
+      uint4 rt[TPB][NV], rd[kDraft ? TPB : 1][NV] = {};
 #pragma unroll
-    for (int i = 0; i < TPB; ++i) {  // every load of the item in flight at once
-      if (t0 + i < P.ntiles) {
-        const int64_t e0 = static_cast<int64_t>(t0 + i) * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
-        load_raw<T>(S.t, e0, P.V, rt[i]);
-        if (kDraft && S.d != nullptr) load_raw<T>(S.d, e0, P.V, rd[kDraft ? i : 0]);
+      for (int i = 0; i < TPB; ++i) {
+        if (t0 + i < t_end) {
+          const int64_t e0 =
+              static_cast<int64_t>(t0 + i) * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
+          load_raw<T>(S.t, e0, P.V, rt[i]);
+          if (kDraft && S.d != nullptr) load_raw<T>(S.d, e0, P.V, rd[kDraft ? i : 0]);
+        }
       }
-    }
 #pragma unroll
-    for (int i = 0; i < TPB; ++i) {
-      float w[kSampleEPT];
-      const double part =
-          (t0 + i < P.ntiles) ? wave_sum(static_cast<double>(tile_compute<T>(S, rt[i], rd[kDraft ? i : 0], w))) : 0.0;
-      if (lane_id() == 0) s_red[i][wave_id()] = part;
-    }
-    __syncthreads();
-    if (threadIdx.x < TPB && t0 + static_cast<int>(threadIdx.x) < P.ntiles) {
-      double tot = 0.0;
+      for (int i = 0; i < TPB; ++i) {
+        float w[kSampleEPT];
+        const double part =
+            (t0 + i < t_end) ? wave_sum(static_cast<double>(tile_compute<T>(S, rt[i], rd[kDraft ? i : 0], w))) : 0.0;
+        if (lane_id() == 0) s_red[i][wave_id()] = part;
+      }
+      __syncthreads();
+      if (threadIdx.x < TPB && t0 + static_cast<int>(threadIdx.x) < t_end) {
+        double tot = 0.0;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) tot += s_red[threadIdx.x][w];
-      publish(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t0 + threadIdx.x], tag_nonneg_double(tot));
+        for (int w = 0; w < kWaves; ++w) tot += s_red[threadIdx.x][w];
+        publish(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t0 + threadIdx.x], tag_nonneg_double(tot));
+      }
+      __syncthreads();  // s_red is reused by the next group
     }
   }
 
@@ -925,7 +933,7 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
        sl += kThreads) {
     P.part_m[sl] = 0ull;
     P.part_s[sl] = 0ull;
-    if (P.entropy != nullptr) P.part_a[sl] = 0ull;
+    if constexpr (kEnt) P.part_a[sl] = 0ull;
   }
   const int R = 2 * P.K + 1;
   for (int r = threadIdx.x; r < R; r += kThreads) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
@@ -968,18 +976,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
 // sequences: workgroups are dispatched in index order over a few
 // microseconds, so every sequence's first workgroup (its decider, usually)
 // starts among the first B.
-template <class T>
+// kEnt: the statistics pass also published A per piece (entropy requested).
+template <class T, bool kEnt>
 __global__ __launch_bounds__(kThreads) void chain_sample_kernel(ChainParams P) {
   const uint32_t B = static_cast<uint32_t>(P.B);
-  sample_seq<T, SampleTiles<T>::kPerBlock, true>(P, static_cast<int>(blockIdx.x % B), static_cast<int>(blockIdx.x / B));
+  sample_seq<T, SampleTiles<T>::kPerBlock, true, kEnt>(P, static_cast<int>(blockIdx.x % B),
+                                                       static_cast<int>(blockIdx.x / B));
 }
 
 // K = 0 (draft-side sampling): one row per draw, more tiles per workgroup.
-template <class T>
+template <class T, bool kEnt>
 __global__ __launch_bounds__(kThreads) void chain_sample_one_row_kernel(ChainParams P) {
   const uint32_t B = static_cast<uint32_t>(P.B);
-  sample_seq<T, SampleTiles<T>::kPerBlock * kSampleTilesK0Factor, false>(P, static_cast<int>(blockIdx.x % B),
-                                                                          static_cast<int>(blockIdx.x / B));
+  sample_seq<T, SampleTiles<T>::kPerBlock * kSampleTilesK0Factor, false, kEnt>(P, static_cast<int>(blockIdx.x % B),
+                                                                                static_cast<int>(blockIdx.x / B));
 }
 
 // ---------------------------------------------------------------- launcher
@@ -999,11 +1009,12 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
                           dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, ev.before, ev.after, 0u, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  void (*sample)(ChainParams);
   if (p.K == 0)
-    hipLaunchKernelGGL(chain_sample_one_row_kernel<T>, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream,
-                       p);
+    sample = ent ? chain_sample_one_row_kernel<T, true> : chain_sample_one_row_kernel<T, false>;
   else
-    hipLaunchKernelGGL(chain_sample_kernel<T>, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream, p);
+    sample = ent ? chain_sample_kernel<T, true> : chain_sample_kernel<T, false>;
+  hipLaunchKernelGGL(sample, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

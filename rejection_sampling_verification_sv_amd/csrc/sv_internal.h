@@ -83,7 +83,7 @@ struct ChainParams {
   int32_t B, K, V;
   PieceLayout L;           // statistics pass; rows = 2K+1 (target 0..K, then draft)
   // Sampling: nblk_b workgroups per sequence, each over tiles_per_block
-  // tiles of kSampleTile tokens.
+  // tiles of kSampleTile tokens (a multiple of the kernel's group of tiles).
   int32_t ntiles;
   int32_t tiles_per_block;
   int32_t nblk_b;
@@ -168,6 +168,12 @@ constexpr int kSampleTilesF32 = kSampleTilesBF16 / 2;
 #define SV_SAMPLE_TILES_K0_FACTOR 4
 #endif
 constexpr int kSampleTilesK0Factor = SV_SAMPLE_TILES_K0_FACTOR;
+// Sampling workgroups per call the tile groups are spread over (a workgroup
+// takes several groups in turn when B * ntiles is large).
+#ifndef SV_SAMPLE_BLOCKS
+#define SV_SAMPLE_BLOCKS 2048
+#endif
+constexpr int kSampleBlocks = SV_SAMPLE_BLOCKS;
 
 // Segments layout: kThreads * kStatsUnroll * kStatsBatches vectors per segment.
 constexpr int kStatsUnroll = 4;

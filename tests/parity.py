@@ -65,7 +65,7 @@ def _rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
     return err
 
 
-def oracle_chain(inp: dict, rows=None) -> dict:
+def oracle_chain(inp: dict, rows=None, with_entropy: bool = False) -> dict:
     """The oracle on (a subset of the sequences of) a chain input dict of tensors."""
     sel = slice(None) if rows is None else rows
     draft = inp["draft"][sel] if inp["draft"] is not None else None
@@ -76,7 +76,7 @@ def oracle_chain(inp: dict, rows=None) -> dict:
     x = to_np_i(inp["draft_tokens"][sel]) if K > 0 else np.zeros((t.shape[0], 0), np.int64)
     T = to_np64(inp["temperature"][sel]) if inp.get("temperature") is not None else np.ones(t.shape[0])
     u = to_np64(inp["uniforms"][sel])
-    return oracle.verify_chain(t, d, x, T, u)
+    return oracle.verify_chain(t, d, x, T, u, with_entropy=with_entropy)
 
 
 def compare_chain(gpu: dict, ref: dict, rows=None) -> ChainReport:

@@ -46,7 +46,7 @@ def _check(sv, inp, rows=None, label=""):
     withh = _call(sv, inp, want_entropy=True)
     for k in ("accept_len", "out_tokens", "p_draft", "q_draft", "residual_mass", "err_flags"):
         assert torch.equal(plain[k], withh[k]), f"{label}: {k} changed when the entropy was requested"
-    ref = oracle_chain(inp, rows)
+    ref = oracle_chain(inp, rows, with_entropy=True)
     h = to_np64(withh["entropy"] if rows is None else withh["entropy"][rows.cuda() if torch.is_tensor(rows) else rows])
     valid = ref["valid"]
     err = np.abs(h[valid] - ref["entropy"][valid])
@@ -110,7 +110,7 @@ def test_entropy_with_masked_tokens_and_bad_rows(sv):
     assert np.all(np.isnan(h[2])), "an invalid temperature gives NaN entropy"
     keep = [0, 1, 3]
     sub = {k: (v[keep] if torch.is_tensor(v) else v) for k, v in inp.items()}
-    ref = oracle_chain(sub)
+    ref = oracle_chain(sub, with_entropy=True)
     err = np.abs(h[keep] - ref["entropy"])
     assert np.all(err <= H_REL * ref["entropy"] + H_ABS), err.max()
     assert h[1, 0] < 1e-3 and np.all((h >= -H_ABS) | np.isnan(h))

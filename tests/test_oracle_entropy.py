@@ -80,7 +80,7 @@ def test_chain_reports_the_entropy_of_every_position():
     d = t[:, :K] + rng.normal(0, 1, (B, K, V))
     T = np.array([0.7, 1.0, 1.3])
     x = rng.integers(0, V, (B, K))
-    out = verify_chain(t, d, x, T, rng.random((B, K + 1)))
+    out = verify_chain(t, d, x, T, rng.random((B, K + 1)), with_entropy=True)
     for b in range(B):
         a_t = t[b] / T[b]
         a_d = d[b] / T[b]
