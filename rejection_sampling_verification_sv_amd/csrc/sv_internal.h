@@ -211,11 +211,14 @@ constexpr int kStatsTPB = SV_STATS_TPB;
 #define SV_STATS_WAVES_ENT 4
 #endif
 
-// Chunked layouts: about this many chunks per call (one workgroup each;
-// measured best for each stream on c2 / c4), each with at least
-// kChunkMinVecs 16-byte vectors.
+// Chunked layouts: each row is cut into k equal chunks (one workgroup each),
+// k the nearest integer to this target over the rows of the call, each chunk
+// of at least kChunkMinVecs 16-byte vectors. Measured best: 2816 for the
+// chain stream (quarter rows on B=64 K=5 V=128256), 4096 for the tree stream
+// (half rows on B=32 N=64 V=128256: 82-84 us against 85 us for 4096 chunks
+// cut across rows).
 #ifndef SV_CHUNKS_CHAIN
-#define SV_CHUNKS_CHAIN 2048
+#define SV_CHUNKS_CHAIN 2816
 #endif
 constexpr int kChunksChain = SV_CHUNKS_CHAIN;
 #ifndef SV_CHUNKS_TREE
