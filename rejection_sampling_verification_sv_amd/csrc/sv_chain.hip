@@ -428,6 +428,42 @@ __device__ __forceinline__ int issue_pieces(const ChainParams& P, int b, int r, 
   return n;
 }
 
+// 2^(lo - hi) for two fp32 references lo <= hi, as an fp64 factor: v_exp_f32
+// of the fp32 difference. A factor multiplies an fp32 partial sum, so its
+// error of about one fp32 ulp is of the order of that sum's own rounding.
+__device__ __forceinline__ double ref_factor(float lo, float hi) { return static_cast<double>(fast_exp2(lo - hi)); }
+
+// 2^a for an fp64 argument: a power of two times v_exp_f32 of the fraction in
+// [-1/2, 1/2] (relative error about one fp32 ulp; the software fp64 exp2 is
+// several times longer on this path, which every sampling workgroup runs).
+__device__ __forceinline__ double exp2_split(double a) {
+  if (!(a > -1100.0)) return (a != a) ? a : 0.0;  // NaN stays NaN; far below the fp64 range: 0
+  if (a > 1100.0) return INFINITY;
+  const double n = rint(a);
+  return ldexp(static_cast<double>(fast_exp2(static_cast<float>(a - n))), static_cast<int>(n));
+}
+
+// log2 z for a finite z > 0: the fp64 exponent plus v_log_f32 of the
+// mantissa in [1/2, 1) (absolute error about 1e-7; a row's log-normaliser
+// needs no more, its sums being fp32-rounded).
+__device__ __forceinline__ double log2_fast(double z) {
+  int e;
+  const double m = frexp(z, &e);
+  return static_cast<double>(e) + static_cast<double>(__builtin_amdgcn_logf(static_cast<float>(m)));
+}
+
+// OR of the error bits (SV_ERRF_*, bits 0..4) over the wave: one ballot per
+// bit instead of a chain of shuffles.
+__device__ __forceinline__ uint32_t wave_or_err(uint32_t v) {
+  static_assert((SV_ERRF_TOKEN | SV_ERRF_TEMPERATURE | SV_ERRF_PARENT | SV_ERRF_NONFINITE | SV_ERRF_INTERNAL) == 0x1f,
+                "error bits are bits 0..4");
+  uint32_t r = 0u;
+#pragma unroll
+  for (int bit = 0; bit < 5; ++bit)
+    if (__ballot((v >> bit) & 1u) != 0ull) r |= 1u << bit;
+  return r;
+}
+
 template <class T, bool kEnt>
 __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
@@ -495,13 +531,13 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
         if (mm == -INFINITY) continue;
         if (mm > mf) {
           const double d = static_cast<double>(mm) - static_cast<double>(mf);
-          const double f = (mf == -INFINITY) ? 0.0 : exp2(-d);
+          const double f = (mf == -INFINITY) ? 0.0 : ref_factor(mf, mm);
           if constexpr (ent) af = (mf == -INFINITY ? 0.0 : f * (af - d * zf)) + av;
           zf = zf * f + sv;
           mf = mm;
         } else {
           const double d = static_cast<double>(mf) - static_cast<double>(mm);
-          const double f = exp2(-d);
+          const double f = ref_factor(mm, mf);
           zf += sv * f;
           if constexpr (ent) af += f * (av - d * sv);
         }
@@ -510,7 +546,7 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
     float M = mf;
     for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
     const double dl = static_cast<double>(M) - static_cast<double>(mf);
-    const double fl = (mf == -INFINITY) ? 0.0 : exp2(-dl);
+    const double fl = (mf == -INFINITY) ? 0.0 : ref_factor(mf, M);
     double zl = zf * fl;
     for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
     double al = 0.0;
@@ -521,11 +557,12 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
     if (row_ok && gl == 0) {
       const bool fin = (zl > 0.0) && isfinite(zl) && isfinite(M);
       if (!fin) err |= SV_ERRF_NONFINITE;
-      s_L[r] = static_cast<double>(M) + log2(zl);
+      const double lz = fin ? log2_fast(zl) : log2(zl);
+      s_L[r] = static_cast<double>(M) + lz;
       // H = ln 2 * (log2 Z - A / Z); NaN for a row without finite statistics
       if (ent && writer)
         P.entropy[static_cast<int64_t>(b) * R + r] =
-            (fin && Tv > 0.0f && isfinite(Tv)) ? static_cast<float>(0.6931471805599453 * (log2(zl) - al / zl)) : NAN;
+            (fin && Tv > 0.0f && isfinite(Tv)) ? static_cast<float>(0.6931471805599453 * (lz - al / zl)) : NAN;
     }
   }
   // s_L is written by the group leaders and read by other lanes of this wave.
@@ -550,9 +587,12 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
   if (lane < K) {
     float pf = NAN, qf = NAN;
     if (x >= 0 && x < P.V) {
-      const double p = exp2(static_cast<double>(lt) * c64 - s_L[lane]);
-      const double q = exp2(static_cast<double>(ld) * c64 - s_L[K + 1 + lane]);
-      const double alpha = (p > 0.0) ? ((q > 0.0) ? fmin(1.0, p / q) : 1.0) : 0.0;
+      // p = 2^ap, q = 2^aq; alpha = min(1, p / q) = 2^min(0, ap - aq)
+      const double ap = static_cast<double>(lt) * c64 - s_L[lane];
+      const double aq = static_cast<double>(ld) * c64 - s_L[K + 1 + lane];
+      const double p = exp2_split(ap);
+      const double q = exp2_split(aq);
+      const double alpha = (p > 0.0) ? ((q > 0.0) ? ((ap >= aq) ? 1.0 : exp2_split(ap - aq)) : 1.0) : 0.0;
       reject = !(static_cast<double>(u) < alpha);
       pf = static_cast<float>(p);
       qf = static_cast<float>(q);
@@ -562,8 +602,7 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
   }
   const uint64_t rej = __ballot(reject);
   const int j = (rej != 0ull) ? (__ffsll(static_cast<unsigned long long>(rej)) - 1) : K;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) err |= static_cast<uint32_t>(__shfl_xor(static_cast<int>(err), o, kWave));
+  err = wave_or_err(err);
   const bool bad = err != 0u;
 
   // Lane i writes out_tokens[i] (K + 1 <= 64): its own token up to j, -1 after;

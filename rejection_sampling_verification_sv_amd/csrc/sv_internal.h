@@ -225,7 +225,10 @@ constexpr int kChunksChain = SV_CHUNKS_CHAIN;
 #define SV_CHUNKS_TREE 4096
 #endif
 constexpr int kChunksTree = SV_CHUNKS_TREE;
-constexpr int kChunkMinVecs = 256 * kStatsUnroll * 2;
+#ifndef SV_CHUNK_MIN_VECS
+#define SV_CHUNK_MIN_VECS 2048
+#endif
+constexpr int kChunkMinVecs = SV_CHUNK_MIN_VECS;
 
 static_assert(kErrInternal == SV_ERRF_INTERNAL, "error bit mismatch");
 
