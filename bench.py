@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--workload", default="c2",
                     help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain), c4 (tree) or s1, s2, s3 (draft-side sampling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of each call captured in a HIP graph (the call's launches without the "
+                         "host-side launch path)")
     ap.add_argument("--entropy", action="store_true",
                     help="chain workloads: also request every position's entropy (the stream's entropy variant)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle sample's wall time")
@@ -193,7 +196,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     sv.library()
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
+    # a captured graph needs a capture stream other than the default one
+    stream = torch.cuda.Stream(dev) if args.graph else torch.cuda.current_stream(dev)
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -214,7 +218,8 @@ def main():
         calls = [sv.PreparedSampleCall(s["logits"], s["temperature"], s["uniforms"], stream=stream) for s in sets]
         stream_bytes = R * V * eb
         call_bytes = stream_bytes + R * 4 * 4  # plus temperature, uniform, token and probability per row
-        config = {"workload": f"sample_r{R}_v{V}_{cfg.dtype}", "rows": R, "V": V, "logits": cfg.dtype,
+        config = {"workload": f"sample_r{R}_v{V}_{cfg.dtype}" + ("_graph" if args.graph else ""), "rows": R, "V": V,
+                  "logits": cfg.dtype,
                   "from": cfg.name, "input_sets_rotated": len(sets)}
         kernel_name = "sample_stream_kernel (one pass over the rows: a record per run of 128 vectors)"
     elif kind == "chain":
@@ -237,7 +242,8 @@ def main():
         # every logit once, plus tokens (gathered by the stream), uniforms and temperatures
         stream_bytes = rows * V * eb + B * K * 4
         call_bytes = stream_bytes + B * (K + 1) * 4 + B * 4
-        config = {"workload": cfg.name + ("_entropy" if args.entropy else ""), "B": B, "K": K, "V": V,
+        config = {"workload": cfg.name + ("_entropy" if args.entropy else "") + ("_graph" if args.graph else ""),
+                  "B": B, "K": K, "V": V,
                   "logits": cfg.dtype,
                   "temperature": cfg.temperature if cfg.temperature is not None else list(cfg.temperature_range),
                   "input_sets_rotated": len(sets)}
@@ -255,25 +261,39 @@ def main():
         calls = [sv.PreparedTreeCall(s["target"], s["node_tokens"], s["parents"], stream=stream) for s in sets]
         stream_bytes = rows * V * eb
         call_bytes = stream_bytes + B * N * 4 + N * 4
-        config = {"workload": cfg.name, "B": B, "N": N, "V": V, "logits": cfg.dtype,
+        config = {"workload": cfg.name + ("_graph" if args.graph else ""), "B": B, "N": N, "V": V, "logits": cfg.dtype,
                   "branching": list(cfg.branching), "input_sets_rotated": len(sets)}
         kernel_name = "tree_argmax_kernel (argmax pass with the path decision of the last workgroup)"
     elems = rows * V
     torch.cuda.synchronize()
     nsets = len(calls)
+    steps = calls
+    if args.graph:
+        graphs = []
+        for c in calls:
+            c()  # one call on the capture stream before capturing
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                c()
+            graphs.append(g)
+        steps = [g.replay for g in graphs]
+        torch.cuda.synchronize()
 
-    for i in range(args.warmup):
-        calls[i % nsets]()
+    with torch.cuda.stream(stream):  # graph replays go to the current stream
+        for i in range(args.warmup):
+            steps[i % nsets]()
     torch.cuda.synchronize()
 
     # Timed region: K steps, events around each call on the library's stream.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        calls[i % nsets]()
-        ev[i + 1].record(stream)
+    with torch.cuda.stream(stream):
+        ev[0].record(stream)
+        for i in range(args.steps):
+            steps[i % nsets]()
+            ev[i + 1].record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall0
     total_ms = ev[0].elapsed_time(ev[-1])
@@ -314,7 +334,7 @@ def main():
     achieved = stream_bytes / (kern_avg_ms * 1e-3) / 1e9
     traffic = counted_traffic(wl, kind)
     result = {
-        "metric": (METRIC if wl == "c2" and not args.entropy else
+        "metric": (METRIC if wl == "c2" and not args.entropy and not args.graph else
                    f"sampling throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}" if kind == "sample"
                    else f"verify throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}"),
         "value": elems / (ms_per_step * 1e-3),

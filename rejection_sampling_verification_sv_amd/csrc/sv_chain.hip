@@ -1041,11 +1041,11 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
   // Armed events take the statistics kernel's own start and end timestamps.
   const bool ent = p.entropy != nullptr;
   if (p.L.cps > 0)
-    hipExtLaunchKernelGGL(ent ? chain_stats_chunk_entropy_kernel<T> : chain_stats_chunk_kernel<T>,
-                          dim3(static_cast<uint32_t>(grid_a)), dim3(kStatsTPB), 0, stream, ev.before, ev.after, 0u, p);
+    launch_stream_pass(ent ? chain_stats_chunk_entropy_kernel<T> : chain_stats_chunk_kernel<T>,
+                       dim3(static_cast<uint32_t>(grid_a)), dim3(kStatsTPB), stream, ev, p);
   else
-    hipExtLaunchKernelGGL(ent ? chain_stats_segment_kernel<T, true> : chain_stats_segment_kernel<T, false>,
-                          dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), 0, stream, ev.before, ev.after, 0u, p);
+    launch_stream_pass(ent ? chain_stats_segment_kernel<T, true> : chain_stats_segment_kernel<T, false>,
+                       dim3(static_cast<uint32_t>(grid_a)), dim3(kThreads), stream, ev, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   void (*sample)(ChainParams);

@@ -2,6 +2,7 @@
 // kernels. Not installed; the public contract is include/specverify.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -239,6 +240,18 @@ struct PassEvents {
   hipEvent_t after;
 };
 PassEvents take_pass_events();
+
+// Launch a streaming kernel: with armed events through hipExtLaunchKernel
+// (the events then carry that kernel's own start and end), otherwise as a
+// plain launch, the form a stream capture records.
+template <class Params>
+inline void launch_stream_pass(void (*kernel)(Params), dim3 grid, dim3 block, hipStream_t stream,
+                               const PassEvents& ev, const Params& p) {
+  if (ev.before != nullptr)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev.before, ev.after, 0u, p);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+}
 
 // The launches of a chain call (statistics; decision and sampling) and of a tree
 // call (argmax, decision); `ev` (possibly null events) become the start and

@@ -332,8 +332,7 @@ static hipError_t launch_sample_t(const SampleParams& p, const PassEvents& ev, h
   const int64_t grid = static_cast<int64_t>(p.R) * p.cps;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
   // Armed events take the streaming kernel's own start and end timestamps.
-  hipExtLaunchKernelGGL(sample_stream_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
-                        ev.before, ev.after, 0u, p);
+  launch_stream_pass(sample_stream_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), stream, ev, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sample_draw_kernel<T>, dim3(static_cast<uint32_t>(p.R)), dim3(kWave), 0, stream, p);

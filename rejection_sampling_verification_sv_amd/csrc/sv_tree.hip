@@ -444,8 +444,7 @@ static hipError_t launch_tree_t(const TreeParams& p, const PassEvents& ev, hipSt
   const int64_t grid = static_cast<int64_t>(p.B) * items_per_seq(p.L);
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
   // Armed events take the argmax kernel's own start and end timestamps.
-  hipExtLaunchKernelGGL(tree_argmax_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
-                        ev.before, ev.after, 0u, p);
+  launch_stream_pass(tree_argmax_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), stream, ev, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.N <= kWave)
