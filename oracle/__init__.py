@@ -14,5 +14,7 @@ from .specverify_oracle import (  # noqa: F401
     verify_chain,
     node_depths,
     verify_tree_greedy,
+    verify_tree_stochastic,
+    children_in_order,
     tree_mask,
 )

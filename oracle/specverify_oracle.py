@@ -37,7 +37,11 @@ its reason, in the design notes of the repository):
    lowest node id; node i is verified at position i + 1, the root at 0;
 7. the tree mask covers nodes only: M[i, j] = 1 iff j is i or an ancestor of i;
 8. rows with an out-of-range token, a non-positive / non-finite temperature or
-   a bad parent are reported with accept_len = -1 (library contract).
+   a bad parent are reported with accept_len = -1 (library contract);
+9. sampling tree verification: the children of a node are tried in ascending
+   index against the current P, each rejection replacing P by its normalised
+   residual against the node's draft distribution q; the walk stops at a node
+   whose children are all rejected (or a leaf) and draws from P there.
 """
 from __future__ import annotations
 
@@ -346,6 +350,107 @@ def verify_tree_greedy(target_logits, node_tokens, parents):
         path[b, :len(chain)] = chain
         nxt[b] = g[b, best + 1]
     return {"accept_len": accept_len, "path_nodes": path, "next_token": nxt, "argmax": g}
+
+
+def children_in_order(parents):
+    """Children of the root (key -1) and of every node, in ascending node index."""
+    parents = np.asarray(parents, dtype=np.int64)
+    kids = {-1: []}
+    for i in range(len(parents)):
+        kids[i] = []
+    for i, par in enumerate(parents):
+        kids[int(par)].append(i)
+    return kids
+
+
+def verify_tree_stochastic(target_logits, draft_logits, node_tokens, parents, temperature, uniforms):
+    """Lossless sampling verification of a candidate tree, per sequence.
+
+    The pages verify a tree of competing branches in one target pass and keep
+    the longest accepted path ([Topologies] section 4 figure; [In Production]
+    section 4, after SpecInfer), and state the per-token rule for sampling
+    (acceptance probability min(1, p/q), residual max(0, p - q) normalised;
+    [Topologies] section 2; [In Production] section 2). They give no rule for
+    several candidates at one position. Reading taken (multi-step speculative
+    sampling, the rule of the SpecInfer paper the pages cite): at the current
+    node, with P = p (the target's distribution at its position) and q (the
+    draft's distribution its children were drawn from, i.i.d.), the children
+    are tried in ascending node index; child v with token x is accepted iff
+    u_v < min(1, P(x) / q(x)); a rejection replaces P by
+    max(0, P - q) / sum(max(0, P - q)) (unchanged if that sum is 0) before the
+    next child; an accepted child becomes the current node; when no child is
+    accepted (or the node is a leaf), one token is drawn from P by the inverse
+    CDF with the final uniform. With one child per node this is chain
+    verification exactly.
+
+    Shapes: target and draft ``[B, N+1, V]`` (position 0: after the root,
+    position i+1: after node i; the draft row at a node's position is the
+    distribution its children were sampled from), node_tokens ``[B, N]``,
+    parents ``[N]``, temperature ``[B]`` (the same T for p and q), uniforms
+    ``[B, N+1]`` (column v tests node v, column N drives the final draw).
+    Returns ``accept_len [B]`` (-1 for an invalid row), ``path_nodes [B, N]``,
+    ``next_token [B]``, ``emitted [B, N+1]`` (the path's tokens then the drawn
+    token, -1 padded), ``flagged [B]`` (a tested uniform within FLAG_WINDOW of
+    its acceptance probability, or the final uniform within FLAG_WINDOW of a
+    CDF boundary of the drawn token), ``valid [B]``, ``tests [B]`` (how many
+    children were tested), ``margin [B]`` (the smallest of those distances).
+    """
+    t = np.asarray(target_logits, dtype=np.float64)
+    d = np.asarray(draft_logits, dtype=np.float64)
+    tok = np.asarray(node_tokens, dtype=np.int64)
+    parents = np.asarray(parents, dtype=np.int64)
+    T = np.asarray(temperature, dtype=np.float64)
+    u = np.asarray(uniforms, dtype=np.float64)
+    B, N1, V = t.shape
+    N = N1 - 1
+    if d.shape != t.shape or tok.shape != (B, N) or parents.shape != (N,) or T.shape != (B,) or u.shape != (B, N1):
+        raise ValueError("inconsistent shapes")
+    accept_len = np.full(B, -1, dtype=np.int64)
+    path = np.full((B, N), -1, dtype=np.int64)
+    nxt = np.full(B, -1, dtype=np.int64)
+    emitted = np.full((B, N1), -1, dtype=np.int64)
+    flagged = np.zeros(B, dtype=bool)
+    valid = np.zeros(B, dtype=bool)
+    tests = np.zeros(B, dtype=np.int64)
+    margin = np.full(B, np.inf)
+    if not _check_parents(parents):
+        return {"accept_len": accept_len, "path_nodes": path, "next_token": nxt, "emitted": emitted,
+                "flagged": flagged, "valid": valid, "tests": tests, "margin": margin}
+    kids = children_in_order(parents)
+    for b in range(B):
+        if not (np.isfinite(T[b]) and T[b] > 0) or (N and not np.all((tok[b] >= 0) & (tok[b] < V))):
+            continue
+        valid[b] = True
+        node, pos, chain = -1, 0, []
+        while True:
+            P = temperature_softmax(t[b, pos], T[b])
+            q = temperature_softmax(d[b, pos], T[b])
+            taken = None
+            for v in kids[node]:
+                x = tok[b, v]
+                alpha = float(acceptance_probability(P[x], q[x]))
+                tests[b] += 1
+                margin[b] = min(margin[b], abs(u[b, v] - alpha))
+                if u[b, v] < alpha:
+                    taken = v
+                    break
+                r = residual_weights(P, q)
+                s = r.sum()
+                if s > 0:
+                    P = r / s
+            if taken is None:
+                break
+            chain.append(taken)
+            node, pos = taken, taken + 1
+        drawn, lo, hi = inverse_cdf(P, u[b, N])
+        accept_len[b] = len(chain)
+        path[b, :len(chain)] = chain
+        nxt[b] = int(drawn)
+        emitted[b, :len(chain)] = tok[b, chain] if chain else []
+        emitted[b, len(chain)] = int(drawn)
+        flagged[b] = margin[b] < FLAG_WINDOW or min(u[b, N] - lo, hi - u[b, N]) < FLAG_WINDOW
+    return {"accept_len": accept_len, "path_nodes": path, "next_token": nxt, "emitted": emitted,
+            "flagged": flagged, "valid": valid, "tests": tests, "margin": margin}
 
 
 def tree_mask(parents):

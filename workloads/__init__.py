@@ -12,6 +12,9 @@ from .synth import (  # noqa: F401
     TreeConfig,
     CHAIN_CONFIGS,
     TREE_CONFIGS,
+    SampleTreeConfig,
+    SAMPLE_TREE_CONFIGS,
+    sample_tree_inputs,
     MC_CONFIG,
     seed_stream,
     chain_inputs,

@@ -144,6 +144,46 @@ TREE_CONFIGS = {
 }
 
 
+@dataclasses.dataclass(frozen=True)
+class SampleTreeConfig:
+    """One sampling tree-verification workload: the candidate tree of a greedy
+    configuration, draft logits at every position, node tokens drawn from the
+    draft distribution at their parent's position (siblings independently)."""
+
+    name: str
+    config_id: int
+    B: int
+    N: int
+    V: int
+    dtype: str
+    target_sigma: float
+    draft_sigma: float
+    temperature: float
+    branching: Tuple[int, ...]
+    variant: int = 0
+
+    @property
+    def rows(self) -> int:
+        return 2 * self.B * (self.N + 1)
+
+    @property
+    def elements(self) -> int:
+        return self.rows * self.V
+
+    @property
+    def logit_bytes(self) -> int:
+        return self.elements * (4 if self.dtype == "f32" else 2)
+
+    def with_(self, **kw) -> "SampleTreeConfig":
+        return dataclasses.replace(self, **kw)
+
+
+SAMPLE_TREE_CONFIGS = {
+    "c4s": SampleTreeConfig("tree_sampling_b32_n64_v128256_bf16", 6, 32, 64, 128256, "bf16", 3.0, 1.0, 1.0,
+                            (4, 3, 2, 2, 1)),
+}
+
+
 # ----------------------------------------------------------------------------- seeds
 
 def _seed_sequence(config_id: int, variant: int, stream: int, iteration: int) -> np.random.SeedSequence:
@@ -426,3 +466,59 @@ def tree_inputs(cfg: TreeConfig, device="cpu") -> dict:
         "node_tokens": node_tokens,
         "parents": torch.from_numpy(parents).to(device),
     }
+
+
+def sample_tree_inputs(cfg: SampleTreeConfig, device="cpu") -> dict:
+    """Inputs of one sampling tree-verification call on ``device``.
+
+    Keys: ``target``, ``draft [B,N+1,V]`` (position 0 = the root, position
+    i+1 = node i; draft = target + N(0, draft_sigma^2), each rounded to the
+    storage dtype on its own), ``node_tokens [B,N]`` int32 (node i drawn from
+    the stored draft distribution at its parent's position at temperature T,
+    Gumbel-max, siblings independently), ``parents [N]``, ``temperature [B]``,
+    ``uniforms [B,N+1]`` in [0, 1) (column i tests node i, column N drives the
+    final draw). Streams: 0 target, 1 draft noise, 2 token Gumbel noise,
+    3 uniforms.
+    """
+    B, N, V = cfg.B, cfg.N, cfg.V
+    dt = _TORCH_DTYPES[cfg.dtype]
+    parents, _ = tree_parents_ranked(cfg.branching, N)
+    pos_parent = torch.from_numpy(np.where(parents < 0, 0, parents + 1).astype(np.int64))
+    T = torch.full((B,), float(cfg.temperature), dtype=torch.float32)
+    if _is_cpu(device):
+        gt = seed_stream(cfg.config_id, cfg.variant, STREAM_TARGET)
+        gd = seed_stream(cfg.config_id, cfg.variant, STREAM_DRAFT_NOISE)
+        target = torch.empty((B, N + 1, V), dtype=dt)
+        draft = torch.empty((B, N + 1, V), dtype=dt)
+        for b in range(B):
+            t64 = gt.standard_normal((N + 1, V)) * cfg.target_sigma
+            target[b] = torch.from_numpy(t64).to(dt)
+            draft[b] = torch.from_numpy(t64 + gd.standard_normal((N + 1, V)) * cfg.draft_sigma).to(dt)
+        gx = seed_stream(cfg.config_id, cfg.variant, STREAM_DRAFT_TOKENS)
+        gu = seed_stream(cfg.config_id, cfg.variant, STREAM_UNIFORMS)
+        uniforms = torch.from_numpy(gu.random((B, N + 1), dtype=np.float32))
+    else:
+        gt = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_TARGET)
+        gd = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_DRAFT_NOISE)
+        target = torch.empty((B, N + 1, V), dtype=dt, device=device)
+        draft = torch.empty((B, N + 1, V), dtype=dt, device=device)
+        per = max(1, (1 << 26) // max(1, (N + 1) * V))
+        for b0 in range(0, B, per):
+            b1 = min(B, b0 + per)
+            t32 = torch.randn((b1 - b0, N + 1, V), generator=gt, device=device) * cfg.target_sigma
+            target[b0:b1] = t32.to(dt)
+            draft[b0:b1] = (t32 + torch.randn(t32.shape, generator=gd, device=device) * cfg.draft_sigma).to(dt)
+            del t32
+        gx = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_DRAFT_TOKENS)
+        gu = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_UNIFORMS)
+        uniforms = torch.rand((B, N + 1), generator=gu, device=device, dtype=torch.float32)
+        T = T.to(device)
+        pos_parent = pos_parent.to(device)
+    tokens = torch.empty((B, N), dtype=torch.int32, device=target.device)
+    per_seq = max(1, (1 << 24) // max(1, N * V))
+    for b0 in range(0, B, per_seq):
+        b1 = min(B, b0 + per_seq)
+        rows = draft[b0:b1][:, pos_parent]  # [nb, N, V]: each node's parent-position draft row
+        tokens[b0:b1] = sample_draft_tokens_gumbel(rows, T[b0:b1], gx)
+    return {"target": target, "draft": draft, "node_tokens": tokens,
+            "parents": torch.from_numpy(parents).to(target.device), "temperature": T, "uniforms": uniforms}
