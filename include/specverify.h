@@ -249,6 +249,84 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype,
                                 int32_t* next_token, int32_t* err_flags, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Sampling verification of a candidate tree.
+ *
+ * Bytes of device workspace sv_verify_tree_sampling needs (one 8-byte record
+ * per 128 16-byte vectors of each target and draft row); 0 for invalid sizes.
+ * Same zero-fill contract as the chain workspace (a call leaves it all zero).
+ */
+size_t sv_tree_sampling_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype);
+
+/*
+ * Lossless sampling verification of one candidate tree per sequence: the
+ * tree is checked in one target pass and the longest accepted path kept
+ * ([Topologies] section 4 figure; [In Production] section 4, a tree of
+ * competing branches after SpecInfer), each node by the acceptance rule
+ * min(1, p/q) with the residual max(0, p - q) normalised on a rejection
+ * ([Topologies] section 2; [In Production] section 2). The children of a
+ * node are taken to be drawn independently from the draft's distribution at
+ * that node; for several children at one position the rule is multi-step
+ * speculative sampling (the SpecInfer paper's): for sequence b, T =
+ * temperature[b], p_n = softmax(target_logits[b,n,:] / T), q_n =
+ * softmax(draft_logits[b,n,:] / T), starting at the root (node -1,
+ * position 0) with P = p_0:
+ *
+ *   the children v of the current node (ascending index), token x =
+ *   node_tokens[b,v], are tried in turn: v is accepted iff
+ *   uniforms[b,v] < min(1, P(x) / q(x)) (0 if P(x) = 0, 1 if q(x) = 0 < P(x));
+ *   a rejection sets P <- max(0, P - q) / sum(max(0, P - q)) (P unchanged if
+ *   that sum, formed from fp32 weights, is below 2^-126, the smallest normal
+ *   fp32 number), q being q_pos of the current position (pos = 0 at the
+ *   root, v + 1 at node v); an accepted child v becomes the current node,
+ *   with P = p_{v+1};
+ *   when every child of the current node is rejected, or it has none, one
+ *   token is drawn from P with uniforms[b,N] by the inverse CDF in ascending
+ *   token id (the first t whose cumulative weight exceeds uniforms[b,N] *
+ *   total). With one child per node this is sv_verify_chain's rule.
+ *
+ * Arguments (device pointers unless noted):
+ *   target_logits  [B, N+1, V] dtype: position 0 = after the root, position
+ *                  i+1 = after node i (read only)
+ *   draft_logits   [B, N+1, V] dtype, the same positions: the draft's
+ *                  distribution the children of each node were drawn from
+ *                  (rows of nodes without children are read but do not
+ *                  matter) (read only)
+ *   dtype          SV_DTYPE_F32 or SV_DTYPE_BF16, for both logit tensors
+ *   node_tokens    [B, N] int32 in [0, V)
+ *   parents        [N] int32, shared by all sequences: -1 or an earlier
+ *                  node's index
+ *   temperature    [B] float32 > 0, or NULL for T = 1 (one T for p and q)
+ *   uniforms       [B, N+1] float32 in [0, 1): column v tests node v,
+ *                  column N drives the final draw
+ *   B, N, V        host ints: 0 <= B, 1 <= N <= SV_MAX_TREE_NODES, 1 <= V,
+ *                  2 B (N+1) <= INT32_MAX
+ *   accept_len     [B] int32 out: accepted nodes on the path, -1 on a data
+ *                  error (TOKEN, TEMPERATURE, PARENT, NONFINITE)
+ *   path_nodes     [B, N] int32 out: the accepted node ids from the root
+ *                  side, -1 padded
+ *   next_token     [B] int32 out: the drawn token after the path (-1 on a
+ *                  data error)
+ *   err_flags      [1] int32 in/out or NULL
+ *   workspace      device buffer of at least
+ *                  sv_tree_sampling_workspace_bytes() bytes, 8-byte aligned
+ *   stream         HIP stream (NULL = default)
+ *
+ * Returns SV_ERR_INVALID_ARGUMENT for bad sizes, a bad dtype, a NULL required
+ * pointer or logits not aligned to their element; SV_ERR_WORKSPACE for a
+ * missing or short workspace; SV_ERR_UNSUPPORTED when a row of either
+ * tensor does not start on a 16-byte boundary (V * element size not a
+ * multiple of 16, or a base pointer off 16 bytes) or V exceeds 1024 * 128
+ * vectors (1 048 576 bf16, 524 288 fp32 tokens); SV_ERR_HIP when a launch
+ * fails. Nothing is enqueued on an error return.
+ */
+sv_status sv_verify_tree_sampling(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                                  const int32_t* node_tokens, const int32_t* parents,
+                                  const float* temperature, const float* uniforms, int32_t B, int32_t N,
+                                  int32_t V, int32_t* accept_len, int32_t* path_nodes, int32_t* next_token,
+                                  int32_t* err_flags, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+
 /*
  * Ancestor mask of a candidate tree ([Topologies] section 4 figure: all nodes
  * verified through one 2D tree-masked attention; [In Production] section 4:
@@ -268,11 +346,12 @@ sv_status sv_build_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, i
 /* ------------------------------------------------------------------------
  * Profiling hook (not part of the verification contract).
  *
- * Arms the calling host thread's NEXT sv_verify_chain or sv_verify_tree_greedy
- * call to launch its streaming pass (the kernel that reads every logit once:
- * chain statistics, tree argmax) with `before` and `after` as the launch's
- * start and stop events (hipExtLaunchKernel), so that they carry that kernel's
- * own start and end timestamps; the call then disarms the hook. A call that
+ * Arms the calling host thread's NEXT sv_verify_chain, sv_verify_tree_greedy,
+ * sv_sample_rows or sv_verify_tree_sampling call to launch its streaming pass
+ * (the kernel that reads every logit once: chain statistics, tree argmax, run
+ * records) with `before` and `after` as the launch's start and stop events
+ * (hipExtLaunchKernel), so that they carry that kernel's own start and end
+ * timestamps; the call then disarms the hook. A call that
  * fails its argument checks records nothing and also disarms it.
  * hipEventElapsedTime(before, after) is then that one kernel's duration.
  *

@@ -8,6 +8,7 @@ from .specverify import (  # noqa: F401
     PreparedChainCall,
     PreparedSampleCall,
     PreparedTreeCall,
+    PreparedTreeSamplingCall,
     SpecVerifyError,
     SV_DTYPE_BF16,
     SV_DTYPE_F32,
@@ -26,7 +27,9 @@ from .specverify import (  # noqa: F401
     sv_sample_workspace_bytes,
     sv_status_string,
     sv_time_next_stream_pass,
+    sv_tree_sampling_workspace_bytes,
     sv_tree_workspace_bytes,
     sv_verify_chain,
     sv_verify_tree_greedy,
+    sv_verify_tree_sampling,
 )

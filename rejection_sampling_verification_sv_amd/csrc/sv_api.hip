@@ -160,6 +160,13 @@ bool aligned_to(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(
 
 sv_status from_hip(hipError_t e) { return e == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
+// Sampling verification of a tree: the run records of the B (N+1) target rows
+// then of the B (N+1) draft rows.
+bool tree_sampling_rows(int32_t B, int32_t N, int64_t* rows) {
+  *rows = 2LL * B * (N + 1);
+  return *rows <= INT32_MAX;
+}
+
 thread_local sv::PassEvents g_pass_events{nullptr, nullptr};
 
 }  // namespace
@@ -294,6 +301,9 @@ sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temper
   if (static_cast<int64_t>(R) * L.cps > INT32_MAX) return SV_ERR_UNSUPPORTED;
   sv::SampleParams p{};
   p.logits = logits;
+  p.logits2 = nullptr;
+  p.R1 = R;
+  p.temp_rows = 1;
   p.temperature = temperature;
   p.uniforms = uniforms;
   p.R = R;
@@ -344,6 +354,68 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
   p.err_flags = err_flags;
   p.part = reinterpret_cast<uint64_t*>(ws + L.off_part);
   return from_hip(sv::launch_tree(p, dtype, ev, stream));
+}
+
+size_t sv_tree_sampling_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype) {
+  int64_t rows = 0;
+  if (!tree_sizes_ok(B, N, V) || !dtype_ok(dtype) || !tree_sampling_rows(B, N, &rows)) return 0;
+  return run_layout(static_cast<int32_t>(rows), V, dtype).total;
+}
+
+sv_status sv_verify_tree_sampling(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                                  const int32_t* node_tokens, const int32_t* parents, const float* temperature,
+                                  const float* uniforms, int32_t B, int32_t N, int32_t V, int32_t* accept_len,
+                                  int32_t* path_nodes, int32_t* next_token, int32_t* err_flags, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  const sv::PassEvents ev = sv::take_pass_events();
+  int64_t rows = 0;
+  if (!dtype_ok(dtype) || !tree_sizes_ok(B, N, V)) return SV_ERR_INVALID_ARGUMENT;
+  if (!tree_sampling_rows(B, N, &rows)) return SV_ERR_UNSUPPORTED;
+  if (B == 0) return SV_OK;
+  if (target_logits == nullptr || draft_logits == nullptr || node_tokens == nullptr || parents == nullptr ||
+      uniforms == nullptr || accept_len == nullptr || path_nodes == nullptr || next_token == nullptr)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (!aligned_to(target_logits, dtype_bytes(dtype)) || !aligned_to(draft_logits, dtype_bytes(dtype)))
+    return SV_ERR_INVALID_ARGUMENT;
+  const RunLayout L = run_layout(static_cast<int32_t>(rows), V, dtype);
+  if (workspace == nullptr || workspace_bytes < L.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
+  // the walk reads rows as 16-byte vectors and keeps one total per run in LDS
+  if (!whole_vector_rows(V, dtype) || !aligned_to(target_logits, 16) || !aligned_to(draft_logits, 16) ||
+      L.nrun > sv::kMaxWalkRuns || rows * L.cps > INT32_MAX)
+    return SV_ERR_UNSUPPORTED;
+
+  sv::SampleParams sp{};
+  sp.logits = target_logits;
+  sp.logits2 = draft_logits;
+  sp.R1 = B * (N + 1);
+  sp.temp_rows = N + 1;
+  sp.temperature = temperature;
+  sp.R = static_cast<int32_t>(rows);
+  sp.V = V;
+  sp.nvec = row_vecs(V, dtype);
+  sp.nrun = L.nrun;
+  sp.cps = L.cps;
+  sp.err_flags = err_flags;
+  sp.rec = static_cast<uint64_t*>(workspace);
+
+  sv::TreeSampleParams p{};
+  p.target = target_logits;
+  p.draft = draft_logits;
+  p.tokens = node_tokens;
+  p.parents = parents;
+  p.temperature = temperature;
+  p.uniforms = uniforms;
+  p.B = B;
+  p.N = N;
+  p.V = V;
+  p.nvec = sp.nvec;
+  p.nrun = L.nrun;
+  p.rec = sp.rec;
+  p.accept_len = accept_len;
+  p.path_nodes = path_nodes;
+  p.next_token = next_token;
+  p.err_flags = err_flags;
+  return from_hip(sv::launch_tree_sample(sp, p, dtype, ev, stream));
 }
 
 sv_status sv_time_next_stream_pass(hipEvent_t before, hipEvent_t after) {

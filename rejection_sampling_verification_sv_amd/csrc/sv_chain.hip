@@ -428,30 +428,6 @@ __device__ __forceinline__ int issue_pieces(const ChainParams& P, int b, int r, 
   return n;
 }
 
-// 2^(lo - hi) for two fp32 references lo <= hi, as an fp64 factor: v_exp_f32
-// of the fp32 difference. A factor multiplies an fp32 partial sum, so its
-// error of about one fp32 ulp is of the order of that sum's own rounding.
-__device__ __forceinline__ double ref_factor(float lo, float hi) { return static_cast<double>(fast_exp2(lo - hi)); }
-
-// 2^a for an fp64 argument: a power of two times v_exp_f32 of the fraction in
-// [-1/2, 1/2] (relative error about one fp32 ulp; the software fp64 exp2 is
-// several times longer on this path, which every sampling workgroup runs).
-__device__ __forceinline__ double exp2_split(double a) {
-  if (!(a > -1100.0)) return (a != a) ? a : 0.0;  // NaN stays NaN; far below the fp64 range: 0
-  if (a > 1100.0) return INFINITY;
-  const double n = rint(a);
-  return ldexp(static_cast<double>(fast_exp2(static_cast<float>(a - n))), static_cast<int>(n));
-}
-
-// log2 z for a finite z > 0: the fp64 exponent plus v_log_f32 of the
-// mantissa in [1/2, 1) (absolute error about 1e-7; a row's log-normaliser
-// needs no more, its sums being fp32-rounded).
-__device__ __forceinline__ double log2_fast(double z) {
-  int e;
-  const double m = frexp(z, &e);
-  return static_cast<double>(e) + static_cast<double>(__builtin_amdgcn_logf(static_cast<float>(m)));
-}
-
 // OR of the error bits (SV_ERRF_*, bits 0..4) over the wave: one ballot per
 // bit instead of a chain of shuffles.
 __device__ __forceinline__ uint32_t wave_or_err(uint32_t v) {

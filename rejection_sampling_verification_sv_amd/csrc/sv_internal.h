@@ -109,6 +109,29 @@ struct ChainParams {
   uint64_t* abort;    // [1] set when a bounded wait expires (drains the launch)
 };
 
+// Sampling verification of a candidate tree: the run records of the target
+// rows [B, N+1, V] (records rows 0 .. B(N+1)-1) and of the draft rows
+// (records rows B(N+1) ..), then one walk per sequence.
+struct TreeSampleParams {
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const int32_t* parents;
+  const float* temperature;
+  const float* uniforms;   // [B, N+1]
+  int32_t B, N, V;
+  int64_t nvec;            // 16-byte vectors per row
+  int32_t nrun;            // runs per row
+  uint64_t* rec;           // workspace [2 B (N+1), nrun]
+  int32_t* accept_len;
+  int32_t* path_nodes;
+  int32_t* next_token;
+  int32_t* err_flags;
+};
+
+// Runs per row the walk keeps totals of in LDS.
+constexpr int kMaxWalkRuns = 1024;
+
 struct TreeParams {
   const void* target;
   const int32_t* tokens;
@@ -141,7 +164,10 @@ constexpr int kRunLaneVecs = kRunVecs / kWave;  // vectors per lane per run
 constexpr int kChunksSample = SV_CHUNKS_SAMPLE;
 
 struct SampleParams {
-  const void* logits;
+  const void* logits;      // rows [0, R1)
+  const void* logits2;     // rows [R1, R) (the stream only; null when R1 == R)
+  int32_t R1;
+  int32_t temp_rows;       // rows per temperature entry: row r of either array uses temperature[r / temp_rows]
   const float* temperature;
   const float* uniforms;
   int32_t R, V;
@@ -153,6 +179,17 @@ struct SampleParams {
   int32_t* err_flags;
   uint64_t* rec;       // workspace [R, nrun]: record of run g of row r
 };
+
+// A run record: the fp32 reference in the upper half, the fp32 sum with its
+// sign bit set in the lower half (so a written record is never zero).
+__device__ __forceinline__ uint64_t tag_run(float ref, float sum) {
+  return (static_cast<uint64_t>(__float_as_uint(ref)) << 32) |
+         static_cast<uint64_t>(__float_as_uint(sum) | 0x80000000u);
+}
+__device__ __forceinline__ float run_ref(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
+__device__ __forceinline__ float run_sum(uint64_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) & 0x7fffffffu);
+}
 
 constexpr int kSampleEPT = 8;                      // sampling elements per thread per tile
 constexpr int kSampleTile = 256 * kSampleEPT;      // elements per sampling tile
@@ -258,6 +295,10 @@ inline void launch_stream_pass(void (*kernel)(Params), dim3 grid, dim3 block, hi
 // stop events of the streaming pass.
 hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
+// The run records of every row of `p` (the streaming kernel of launch_sample alone).
+hipError_t launch_sample_stream(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
+hipError_t launch_tree_sample(const SampleParams& sp, const TreeSampleParams& p, sv_dtype dtype,
+                              const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
                             hipStream_t stream);

@@ -32,18 +32,8 @@ namespace sv {
 
 namespace {
 
-// A run record: the fp32 reference in the upper half, the fp32 sum with its
-// sign bit set in the lower half (so a written record is never zero).
-__device__ __forceinline__ uint64_t tag_run(float ref, float sum) {
-  return (static_cast<uint64_t>(__float_as_uint(ref)) << 32) |
-         static_cast<uint64_t>(__float_as_uint(sum) | 0x80000000u);
-}
-__device__ __forceinline__ float run_ref(uint64_t v) { return __uint_as_float(static_cast<uint32_t>(v >> 32)); }
-__device__ __forceinline__ float run_sum(uint64_t v) {
-  return __uint_as_float(static_cast<uint32_t>(v) & 0x7fffffffu);
-}
-
 __device__ __forceinline__ const uint4* sample_row(const SampleParams& P, int64_t r, int eb) {
+  if (r >= P.R1) return reinterpret_cast<const uint4*>(static_cast<const char*>(P.logits2) + (r - P.R1) * P.V * eb);
   return reinterpret_cast<const uint4*>(static_cast<const char*>(P.logits) + r * P.V * eb);
 }
 
@@ -132,7 +122,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
   uint64_t* rec = P.rec + static_cast<int64_t>(r) * P.nrun;
   uint4 a[kRunLaneVecs], b[kRunLaneVecs];
   load_run<T>(row, g0, P.nvec, a);
-  const Scale c = exponent_scale(temperature_of(P.temperature, static_cast<int>(r)));
+  const uint32_t rr = (r >= static_cast<uint32_t>(P.R1)) ? r - static_cast<uint32_t>(P.R1) : r;
+  const Scale c = exponent_scale(temperature_of(P.temperature, static_cast<int>(rr / static_cast<uint32_t>(P.temp_rows))));
   // invariant: `a` holds this wave's run i - 1
   int32_t i = 1;
 #pragma unroll 1
@@ -328,12 +319,22 @@ __global__ __launch_bounds__(kWave) void sample_draw_kernel(SampleParams P) {
 }
 
 template <class T>
-static hipError_t launch_sample_t(const SampleParams& p, const PassEvents& ev, hipStream_t stream) {
+static hipError_t launch_sample_stream_t(const SampleParams& p, const PassEvents& ev, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(p.R) * p.cps;
   if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
   // Armed events take the streaming kernel's own start and end timestamps.
   launch_stream_pass(sample_stream_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), stream, ev, p);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_sample_stream(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream) {
+  return dtype == SV_DTYPE_BF16 ? launch_sample_stream_t<BF16>(p, ev, stream)
+                                : launch_sample_stream_t<F32>(p, ev, stream);
+}
+
+template <class T>
+static hipError_t launch_sample_t(const SampleParams& p, const PassEvents& ev, hipStream_t stream) {
+  const hipError_t e = launch_sample_stream_t<T>(p, ev, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(sample_draw_kernel<T>, dim3(static_cast<uint32_t>(p.R)), dim3(kWave), 0, stream, p);
   return hipGetLastError();

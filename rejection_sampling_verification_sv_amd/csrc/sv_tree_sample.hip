@@ -1,0 +1,432 @@
+// Sampling (stochastic) verification of a candidate tree: lossless
+// speculative sampling over a tree whose children at each node were drawn
+// independently from the draft's distribution at that node ([Topologies]
+// "Speculative Decoding & Draft Model Topologies", section 4 figure: every
+// node checked in one target pass, the longest accepted path kept;
+// [In Production] "Speculative Decoding in Production", section 4: a tree of
+// competing branches after SpecInfer; section 2 and [Topologies] section 2:
+// the per-token acceptance probability min(1, p/q) and the residual
+// max(0, p - q) normalised). The pages give no rule for several candidates at
+// one position; the rule taken is multi-step speculative sampling, as in the
+// SpecInfer paper they cite: the children of the current node are tried in
+// ascending node index against the current distribution P (first the
+// target's p at the node), a rejection replacing P by
+// max(0, P - q) / sum(max(0, P - q)) (unchanged if that sum is 0); an
+// accepted child becomes the current node; where every child is rejected, or
+// at a leaf, one token is drawn from P by the inverse CDF (ascending token id,
+// the final uniform).
+//
+// Pass 1 — sample_stream_kernel (sv_sample.hip) over the target rows and the
+// draft rows of the call: one (reference, sum) record per run of kRunVecs
+// vectors of every row, one read of every logit.
+//
+// Pass 2 — tree_sample_walk_kernel, one 1024-thread workgroup per sequence,
+// all threads following the same walk (every decision is computed by every
+// thread from the same shared values):
+//   at each node: its children by one ballot per wave over the parent array
+//   (one node per thread), their tokens, uniforms and logits at the node's
+//   position prefetched into LDS; the log-normalisers of the node's target
+//   and draft rows from their run records (fp64);
+//   each child's test in fp64: P_r(x) = max(0, P_{r-1}(x) - q(x)) / Z_r
+//   applied r times to p(x), alpha = min(1, P_r(x) / q(x));
+//   each rejection: one block-wide pass over the row pair forming
+//   max(0, P_r - q) per token in fp32 (per-run totals kept in LDS) and
+//   Z_{r+1} = their sum in fp64;
+//   the final draw: the run holding u * total by a scan of the per-run
+//   totals, then a one-wave rescan of that run.
+#include <float.h>
+#include <math.h>
+
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kWalkThreads = 1024;
+constexpr int kWalkWaves = kWalkThreads / kWave;
+
+// The exponent scale and the two rows' log-normalisers split for fp32 use:
+// p(v) = 2^(x_t c - L_t), q(v) = 2^(x_d c - L_d).
+struct WalkRows {
+  Scale c;
+  float nlt_hi, nlt_lo, nld_hi, nld_lo;  // -L_t, -L_d as hi + lo
+};
+
+__device__ __forceinline__ void split_neg(double v, float& hi, float& lo) {
+  hi = static_cast<float>(-v);
+  lo = static_cast<float>(-v - static_cast<double>(hi));
+}
+
+// Weight of one token in fp32: the current distribution P_r (kResid false)
+// or its residual max(0, P_r - q) (kResid true), P_0 = p, each earlier
+// rejection k applying max(0, . - q) * invZ[k].
+template <bool kResid>
+__device__ __forceinline__ float walk_weight(float xt, float xd, const WalkRows& w, int r, const float* invZ) {
+  const float p = fast_exp2(scaled_arg(xt, w.c, w.nlt_hi) + w.nlt_lo);
+  const float q = fast_exp2(scaled_arg(xd, w.c, w.nld_hi) + w.nld_lo);
+  float val = p;
+  for (int k = 0; k < r; ++k) val = fmaxf(val - q, 0.0f) * invZ[k];
+  return kResid ? fmaxf(val - q, 0.0f) : val;
+}
+
+// This lane's vectors of run g of a row (vectors g * kRunVecs + lane + 64 i),
+// -inf past the end of the row.
+template <class T>
+__device__ __forceinline__ void walk_load(const uint4* row, int64_t g, int64_t nvec, uint4 (&a)[kRunLaneVecs]) {
+  const int64_t v0 = g * kRunVecs + lane_id();
+#pragma unroll
+  for (int i = 0; i < kRunLaneVecs; ++i) {
+    const int64_t v = v0 + static_cast<int64_t>(i) * kWave;
+    a[i] = (v < nvec) ? row[v] : neg_inf_vec<T>();
+  }
+}
+
+template <class T, bool kResid>
+__device__ __forceinline__ float walk_run_sum(const uint4 (&at)[kRunLaneVecs], const uint4 (&ad)[kRunLaneVecs],
+                                              const WalkRows& w, int r, const float* invZ) {
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRunLaneVecs; ++i) {
+    float xt[T::kVec], xd[T::kVec];
+    unpack<T>(at[i], xt);
+    unpack<T>(ad[i], xd);
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) s += walk_weight<kResid>(xt[e], xd[e], w, r, invZ);
+  }
+  return s;
+}
+
+// One pass over the row pair by the whole workgroup: s_run[g] = the fp32
+// total of the weights of run g (wave w takes runs w, w + 16, ..., the next
+// run's loads in flight while the current one is reduced). No barrier.
+template <class T, bool kResid>
+__device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
+                          const float* invZ, double* s_run) {
+  int g = wave_id();
+  if (g >= nrun) return;
+  uint4 at[kRunLaneVecs], ad[kRunLaneVecs];
+  walk_load<T>(rt, g, nvec, at);
+  walk_load<T>(rd, g, nvec, ad);
+  for (;;) {
+    const int gn = g + kWalkWaves;
+    uint4 bt[kRunLaneVecs], bd[kRunLaneVecs];
+    if (gn < nrun) {
+      walk_load<T>(rt, gn, nvec, bt);
+      walk_load<T>(rd, gn, nvec, bd);
+    }
+    const float s = wave_sum_dpp(walk_run_sum<T, kResid>(at, ad, w, r, invZ));
+    if (lane_id() == 0) s_run[g] = static_cast<double>(s);
+    if (gn >= nrun) break;
+    g = gn;
+#pragma unroll
+    for (int i = 0; i < kRunLaneVecs; ++i) {
+      at[i] = bt[i];
+      ad[i] = bd[i];
+    }
+  }
+}
+
+// One wave: (M, Z) of a row from its run records, M = the largest reference,
+// Z = sum of sum * 2^(ref - M) in fp64 (fixed order).
+__device__ void row_norm_wave(const uint64_t* rec, int nrun, float* M, double* Z, uint32_t* err) {
+  const int lane = lane_id();
+  float m = -INFINITY;
+  for (int g = lane; g < nrun; g += kWave) {
+    const uint64_t v = rec[g];
+    if (v == 0ull) *err |= kErrInternal;
+    m = fmaxf(m, run_ref(v));
+  }
+  m = wave_max_dpp(m);
+  double z = 0.0;
+  for (int g = lane; g < nrun; g += kWave) {
+    const uint64_t v = rec[g];
+    const float ref = run_ref(v);
+    const float s = run_sum(v);
+    if (s != s) z += static_cast<double>(s);
+    else if (ref != -INFINITY && s > 0.0f) z += static_cast<double>(s) * ref_factor(ref, m);
+  }
+  *M = m;
+  *Z = wave_sum(z);
+}
+
+// The final draw by one wave: the run whose inclusive total first exceeds
+// u * (sum of the run totals) (the last run with weight if rounding leaves
+// none), then that run rescanned in ascending token order (lane l holds its
+// vectors kRunLaneVecs * l ..) with the first token whose cumulative weight
+// exceeds the remainder (the last token with weight if none). -1 if no run
+// has weight.
+template <class T, bool kResid>
+__device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
+                         const float* invZ, const double* s_run, double u) {
+  const int lane = lane_id();
+  double carry = 0.0;
+  for (int base = 0; base < nrun; base += kWave) carry += __shfl(wave_inclusive_scan(base + lane < nrun ? s_run[base + lane] : 0.0), kWave - 1, kWave);
+  const double total = carry;
+  const double target = u * total;
+  int found = -1, last_pos = -1;
+  double prefix = 0.0;
+  carry = 0.0;
+  for (int base = 0; base < nrun && found < 0; base += kWave) {
+    const double v = base + lane < nrun ? s_run[base + lane] : 0.0;
+    const double inc = wave_inclusive_scan(v);
+    const uint64_t pos = __ballot(v > 0.0);
+    if (pos != 0ull) last_pos = base + 63 - __clzll(static_cast<long long>(pos));
+    const uint64_t hit = __ballot(v > 0.0 && carry + inc > target);
+    if (hit != 0ull) {
+      const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      double excl = __shfl_up(inc, 1, kWave);
+      if (lane == 0) excl = 0.0;
+      found = base + l;
+      prefix = carry + __shfl(excl, l, kWave);
+    }
+    carry += __shfl(inc, kWave - 1, kWave);
+  }
+  const int g = found >= 0 ? found : last_pos;
+  if (g < 0) return -1;
+  const double tk = found >= 0 ? target - prefix : INFINITY;
+  // lane l: vectors g * kRunVecs + kRunLaneVecs * l + i, its tokens in ascending order
+  const int64_t vb = static_cast<int64_t>(g) * kRunVecs + kRunLaneVecs * lane;
+  constexpr int NE = kRunLaneVecs * T::kVec;
+  float wv[NE];
+  float lane_tot = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kRunLaneVecs; ++i) {
+    const uint4 qt = (vb + i < nvec) ? rt[vb + i] : neg_inf_vec<T>();
+    const uint4 qd = (vb + i < nvec) ? rd[vb + i] : neg_inf_vec<T>();
+    float xt[T::kVec], xd[T::kVec];
+    unpack<T>(qt, xt);
+    unpack<T>(qd, xd);
+#pragma unroll
+    for (int e = 0; e < T::kVec; ++e) {
+      wv[i * T::kVec + e] = walk_weight<kResid>(xt[e], xd[e], w, r, invZ);
+      lane_tot += wv[i * T::kVec + e];
+    }
+  }
+  const double inc = wave_inclusive_scan(static_cast<double>(lane_tot));
+  double excl = __shfl_up(inc, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  int first = -1, last = -1;
+  float run = 0.0f;
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    run += wv[e];
+    if (wv[e] > 0.0f) {
+      if (first < 0 && excl + static_cast<double>(run) > tk) first = e;
+      last = e;
+    }
+  }
+  const uint64_t hit = __ballot(first >= 0);
+  const uint64_t any = __ballot(last >= 0);
+  int sel = -1, e = 0;
+  if (hit != 0ull) {
+    sel = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+    e = __shfl(first, sel, kWave);
+  } else if (any != 0ull) {
+    sel = 63 - __clzll(static_cast<long long>(any));
+    e = __shfl(last, sel, kWave);
+  }
+  if (sel < 0) return -1;
+  return static_cast<int>((static_cast<int64_t>(g) * kRunVecs + kRunLaneVecs * sel) * T::kVec + e);
+}
+
+}  // namespace
+
+template <class T>
+__global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSampleParams P) {
+  __shared__ int s_par[SV_MAX_TREE_NODES];
+  __shared__ int s_kids[SV_MAX_TREE_NODES];
+  __shared__ float s_klt[SV_MAX_TREE_NODES];
+  __shared__ float s_kld[SV_MAX_TREE_NODES];
+  __shared__ float s_ku[SV_MAX_TREE_NODES];
+  __shared__ int s_path[SV_MAX_TREE_NODES];
+  __shared__ double s_run[kMaxWalkRuns];
+  __shared__ double s_Z[SV_MAX_TREE_NODES];
+  __shared__ float s_invZ[SV_MAX_TREE_NODES];
+  __shared__ uint64_t s_mask[kWalkWaves];
+  __shared__ float s_M[2];
+  __shared__ double s_Zr[2];
+  __shared__ double s_sum;
+  __shared__ int s_token;
+  __shared__ uint32_t s_err;
+
+  const int b = static_cast<int>(blockIdx.x);
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = lane_id();
+  const int wv = wave_id();
+  const int N = P.N;
+  const int64_t N1 = N + 1;
+  const float Tv = temperature_of(P.temperature, b);
+  const Scale c = exponent_scale(Tv);
+  const double c64 = static_cast<double>(c.hi) + static_cast<double>(c.lo);
+  const char* tbase = static_cast<const char*>(P.target);
+  const char* dbase = static_cast<const char*>(P.draft);
+  const int64_t row_bytes = static_cast<int64_t>(P.V) * T::kBytes;
+
+  if (tid == 0) {
+    s_err = (!(Tv > 0.0f) || !isfinite(Tv)) ? static_cast<uint32_t>(SV_ERRF_TEMPERATURE) : 0u;
+    s_token = -1;
+  }
+  __syncthreads();
+  for (int v = tid; v < N; v += kWalkThreads) {
+    const int par = P.parents[v];
+    s_par[v] = par;
+    if (!(par == -1 || (par >= 0 && par < v))) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_PARENT));
+    const int x = P.tokens[static_cast<int64_t>(b) * N + v];
+    if (x < 0 || x >= P.V) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_TOKEN));
+  }
+  __syncthreads();
+
+  int depth = 0;
+  if (s_err == 0u) {  // block-uniform from here: every thread takes the same decisions
+    int node = -1, pos = 0;
+    for (;;) {
+      // the children of `node`, ascending (thread v owns node v; N <= kWalkThreads)
+      const bool mine = tid < N && s_par[tid] == node;
+      const uint64_t m = __ballot(mine);
+      if (lane == 0) s_mask[wv] = m;
+      const int64_t rowt = static_cast<int64_t>(b) * N1 + pos;
+      const int64_t rowd = static_cast<int64_t>(P.B) * N1 + rowt;
+      if (wv < 2) {
+        uint32_t e = 0u;
+        float M;
+        double Z;
+        row_norm_wave(P.rec + (wv == 0 ? rowt : rowd) * P.nrun, P.nrun, &M, &Z, &e);
+        if (lane == 0) {
+          s_M[wv] = M;
+          s_Zr[wv] = Z;
+        }
+        if (e != 0u) atomicOr(&s_err, e);
+      }
+      __syncthreads();
+      int nkids = 0, before = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kWalkWaves; ++w2) {
+        const int pc = __popcll(s_mask[w2]);
+        if (w2 < wv) before += pc;
+        nkids += pc;
+      }
+      const uint4* rt = reinterpret_cast<const uint4*>(tbase + rowt * row_bytes);
+      const uint4* rd = reinterpret_cast<const uint4*>(dbase + (rowt)*row_bytes);
+      if (mine) {
+        const int i = before + __popcll(m & ((1ull << lane) - 1ull));
+        const int x = P.tokens[static_cast<int64_t>(b) * N + tid];
+        s_kids[i] = tid;
+        s_klt[i] = load_elem<T>(rt, x);
+        s_kld[i] = load_elem<T>(rd, x);
+        s_ku[i] = P.uniforms[static_cast<int64_t>(b) * N1 + tid];
+      }
+      __syncthreads();
+      const float Mt = s_M[0], Md = s_M[1];
+      const double Zt = s_Zr[0], Zd = s_Zr[1];
+      if (s_err != 0u || !(Zt > 0.0) || !(Zd > 0.0) || !isfinite(Zt) || !isfinite(Zd) || !isfinite(Mt) ||
+          !isfinite(Md)) {
+        if (tid == 0) s_err |= SV_ERRF_NONFINITE;
+        break;
+      }
+      const double Lt = static_cast<double>(Mt) + log2_fast(Zt);
+      const double Ld = static_cast<double>(Md) + log2_fast(Zd);
+      WalkRows w;
+      w.c = c;
+      split_neg(Lt, w.nlt_hi, w.nlt_lo);
+      split_neg(Ld, w.nld_hi, w.nld_lo);
+      int r = 0;
+      bool taken = false, resid_totals = false;
+      for (int i = 0; i < nkids; ++i) {
+        const double ap = static_cast<double>(s_klt[i]) * c64 - Lt;
+        const double aq = static_cast<double>(s_kld[i]) * c64 - Ld;
+        const double p = exp2_split(ap);
+        const double q = exp2_split(aq);
+        double val = p;
+        for (int k = 0; k < r; ++k) val = fmax(val - q, 0.0) / s_Z[k];
+        const double alpha = (val > 0.0) ? ((q > 0.0) ? fmin(1.0, val / q) : 1.0) : 0.0;
+        if (static_cast<double>(s_ku[i]) < alpha) {
+          node = s_kids[i];
+          pos = node + 1;
+          if (tid == 0) s_path[depth] = node;
+          ++depth;
+          taken = true;
+          break;
+        }
+        // rejected: the residual max(0, P_r - q), per run and in total
+        walk_pass<T, true>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, s_run);
+        __syncthreads();
+        if (wv == 0) {
+          double z = 0.0;
+          for (int g = lane; g < P.nrun; g += kWave) z += s_run[g];
+          z = wave_sum(z);
+          if (lane == 0) s_sum = z;
+        }
+        __syncthreads();
+        const double Zr = s_sum;
+        if (Zr >= static_cast<double>(FLT_MIN)) {  // 1 / Zr stays a finite fp32 factor
+          if (tid == 0) {
+            s_Z[r] = Zr;
+            s_invZ[r] = static_cast<float>(1.0 / Zr);
+          }
+          ++r;
+          resid_totals = true;
+        } else {
+          resid_totals = false;  // a residual of no (representable) mass: P unchanged
+        }
+        __syncthreads();
+      }
+      if (taken) {
+        __syncthreads();  // s_kids, s_klt, ... are rewritten for the next node
+        continue;
+      }
+      // no child accepted (or a leaf): draw from P_r at this position
+      const double u = static_cast<double>(P.uniforms[static_cast<int64_t>(b) * N1 + N]);
+      if (resid_totals) {  // s_run holds the totals of max(0, P_{r-1} - q), proportional to P_r
+        if (wv == 0) {
+          const int t = walk_draw<T, true>(rt, rd, P.nvec, P.nrun, w, r - 1, s_invZ, s_run, u);
+          if (lane == 0) s_token = t;
+        }
+      } else {
+        walk_pass<T, false>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, s_run);
+        __syncthreads();
+        if (wv == 0) {
+          const int t = walk_draw<T, false>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, s_run, u);
+          if (lane == 0) s_token = t;
+        }
+      }
+      break;
+    }
+  }
+  __syncthreads();
+  // no token with weight in a distribution that passed the normaliser checks
+  // would take every weight underflowing: reported as a zero normaliser
+  const uint32_t err = s_err | ((s_err == 0u && s_token < 0) ? static_cast<uint32_t>(SV_ERRF_NONFINITE) : 0u);
+  const bool bad = err != 0u;
+  if (tid == 0) {
+    P.accept_len[b] = bad ? -1 : depth;
+    P.next_token[b] = bad ? -1 : s_token;
+    raise_error(P.err_flags, err);
+  }
+  for (int i = tid; i < N; i += kWalkThreads)
+    P.path_nodes[static_cast<int64_t>(b) * N + i] = (!bad && i < depth) ? s_path[i] : -1;
+  // every record of the sequence's rows has been read: leave them zero
+  const int64_t per = N1 * P.nrun;
+  uint64_t* rec_t = P.rec + static_cast<int64_t>(b) * per;
+  uint64_t* rec_d = P.rec + (static_cast<int64_t>(P.B) + b) * per;
+  for (int64_t i = tid; i < per; i += kWalkThreads) {
+    rec_t[i] = 0ull;
+    rec_d[i] = 0ull;
+  }
+}
+
+hipError_t launch_tree_sample(const SampleParams& sp, const TreeSampleParams& p, sv_dtype dtype, const PassEvents& ev,
+                              hipStream_t stream) {
+  const hipError_t e = launch_sample_stream(sp, dtype, ev, stream);
+  if (e != hipSuccess) return e;
+  if (dtype == SV_DTYPE_BF16)
+    hipLaunchKernelGGL(tree_sample_walk_kernel<BF16>, dim3(static_cast<uint32_t>(p.B)), dim3(kWalkThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(tree_sample_walk_kernel<F32>, dim3(static_cast<uint32_t>(p.B)), dim3(kWalkThreads), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -71,6 +71,13 @@ def _load():
             _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
         ]
         lib.sv_verify_tree_greedy.restype = ctypes.c_int
+        lib.sv_tree_sampling_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int]
+        lib.sv_tree_sampling_workspace_bytes.restype = _c_size
+        lib.sv_verify_tree_sampling.argtypes = [
+            _c_ptr, _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
+        ]
+        lib.sv_verify_tree_sampling.restype = ctypes.c_int
         lib.sv_build_tree_mask.argtypes = [_c_ptr, _c_i32, _c_ptr, _c_ptr, _c_ptr]
         lib.sv_build_tree_mask.restype = ctypes.c_int
         lib.sv_sample_workspace_bytes.argtypes = [_c_i32, _c_i32, ctypes.c_int]
@@ -310,6 +317,51 @@ def sv_verify_tree_greedy(target: torch.Tensor, node_tokens: torch.Tensor, paren
     return {"accept_len": accept_len, "path_nodes": path_nodes, "next_token": next_token, "err_flags": err_flags}
 
 
+def sv_tree_sampling_workspace_bytes(B: int, N: int, V: int, dtype: torch.dtype) -> int:
+    return int(_load().sv_tree_sampling_workspace_bytes(B, N, V, _DTYPES[dtype]))
+
+
+def sv_verify_tree_sampling(target: torch.Tensor, draft: torch.Tensor, node_tokens: torch.Tensor,
+                            parents: torch.Tensor, temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
+                            accept_len=None, path_nodes=None, next_token=None, err_flags=None,
+                            workspace_tensor=None, stream=None) -> dict:
+    """Sampling verification of a candidate tree (``sv_verify_tree_sampling``).
+
+    ``target`` and ``draft`` are ``[B, N+1, V]`` logits of one dtype,
+    ``node_tokens [B, N]`` and ``parents [N]`` int32, ``temperature [B]``
+    (or None for 1) and ``uniforms [B, N+1]`` float32. Returns a dict with
+    ``accept_len [B]``, ``path_nodes [B, N]``, ``next_token [B]`` and
+    ``err_flags [1]``.
+    """
+    lib = _load()
+    if target.dim() != 3:
+        raise ValueError("target must be [B, N+1, V]")
+    B, N1, V = target.shape
+    N = N1 - 1
+    dev = target.device
+    code = _dtype_code(target)
+    _dev(target, "target")
+    _dev(draft, "draft", target.dtype, (B, N1, V), dev)
+    _dev(node_tokens, "node_tokens", torch.int32, (B, N), dev)
+    _dev(parents, "parents", torch.int32, (N,), dev)
+    if temperature is not None:
+        _dev(temperature, "temperature", torch.float32, (B,), dev)
+    _dev(uniforms, "uniforms", torch.float32, (B, N1), dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    accept_len = torch.empty((B,), **i32) if accept_len is None else _dev(accept_len, "accept_len", torch.int32, (B,), dev)
+    path_nodes = torch.empty((B, N), **i32) if path_nodes is None else _dev(path_nodes, "path_nodes", torch.int32, (B, N), dev)
+    next_token = torch.empty((B,), **i32) if next_token is None else _dev(next_token, "next_token", torch.int32, (B,), dev)
+    err_flags = torch.zeros((1,), **i32) if err_flags is None else _dev(err_flags, "err_flags", torch.int32, (1,), dev)
+    nbytes = int(lib.sv_tree_sampling_workspace_bytes(B, N, V, code))
+    ws = workspace(dev, nbytes, stream) if workspace_tensor is None else workspace_tensor
+    st = lib.sv_verify_tree_sampling(
+        _ptr(target), _ptr(draft), code, _ptr(node_tokens), _ptr(parents), _ptr(temperature), _ptr(uniforms),
+        B, N, V, _ptr(accept_len), _ptr(path_nodes), _ptr(next_token), _ptr(err_flags),
+        _ptr(ws), ws.numel(), _stream_handle(dev, stream))
+    _check(st, "sv_verify_tree_sampling")
+    return {"accept_len": accept_len, "path_nodes": path_nodes, "next_token": next_token, "err_flags": err_flags}
+
+
 def sv_build_tree_mask(parents: torch.Tensor, *, mask=None, err_flags=None, stream=None) -> dict:
     """Tree ancestor mask (``sv_build_tree_mask``): uint8 ``[N, N]``."""
     lib = _load()
@@ -432,4 +484,39 @@ class PreparedTreeCall:
         st = self._fn(*self._args)
         if st != SV_OK:
             _check(st, "sv_verify_tree_greedy")
+        return self.out
+
+
+class PreparedTreeSamplingCall:
+    """``sv_verify_tree_sampling`` with every argument checked and marshalled
+    once (calling the object only enqueues the kernels)."""
+
+    def __init__(self, target, draft, node_tokens, parents, temperature, uniforms, *, stream=None):
+        B, N1, V = target.shape
+        N = N1 - 1
+        dev = target.device
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.out = {
+            "accept_len": torch.empty((B,), **i32),
+            "path_nodes": torch.empty((B, N), **i32),
+            "next_token": torch.empty((B,), **i32),
+            "err_flags": torch.zeros((1,), **i32),
+        }
+        sv_verify_tree_sampling(target, draft, node_tokens, parents, temperature, uniforms, stream=stream,
+                                **self.out)
+        lib = _load()
+        code = _dtype_code(target)
+        self._ws = workspace(dev, int(lib.sv_tree_sampling_workspace_bytes(B, N, V, code)), stream)
+        self._keep = (target, draft, node_tokens, parents, temperature, uniforms)
+        o = self.out
+        self._fn = lib.sv_verify_tree_sampling
+        self._args = (
+            _ptr(target), _ptr(draft), code, _ptr(node_tokens), _ptr(parents), _ptr(temperature), _ptr(uniforms),
+            B, N, V, _ptr(o["accept_len"]), _ptr(o["path_nodes"]), _ptr(o["next_token"]), _ptr(o["err_flags"]),
+            _ptr(self._ws), self._ws.numel(), _stream_handle(dev, stream))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SV_OK:
+            _check(st, "sv_verify_tree_sampling")
         return self.out

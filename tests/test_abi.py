@@ -115,6 +115,36 @@ def test_tree_and_mask_argument_errors(lib):
     assert lib.sv_build_tree_mask(FAKE, 1025, FAKE, None, None) == INV
 
 
+def test_tree_sampling_argument_errors(lib):
+    INV, UNS, WS = 1, 2, 3
+    f = lib.sv_verify_tree_sampling
+
+    def call(**kw):
+        a = dict(t=FAKE, d=FAKE, dt=1, x=FAKE, par=FAKE, T=None, u=FAKE, B=4, N=8, V=128, acc=FAKE, path=FAKE,
+                 nxt=FAKE, err=None, ws=FAKE, wsb=1 << 20)
+        a.update(kw)
+        return f(a["t"], a["d"], a["dt"], a["x"], a["par"], a["T"], a["u"], a["B"], a["N"], a["V"], a["acc"],
+                 a["path"], a["nxt"], a["err"], a["ws"], a["wsb"], None)
+    assert call(t=None, d=None, x=None, par=None, u=None, acc=None, path=None, nxt=None, ws=None, B=0) == 0
+    for k in ("t", "d", "x", "par", "u", "acc", "path", "nxt"):
+        assert call(**{k: None}) == INV, k
+    assert call(N=0) == INV and call(N=1025) == INV and call(V=0) == INV and call(B=-1) == INV
+    assert call(dt=5) == INV
+    assert call(t=FAKE + 1) == INV and call(d=FAKE + 1) == INV      # not element-aligned
+    assert call(ws=None) == WS and call(wsb=16) == WS
+    # valid but outside the one-pass walk: rows off 16-byte boundaries, more
+    # than 1024 runs of 128 vectors per row
+    assert call(V=100) == UNS
+    assert call(t=FAKE + 2) == UNS and call(d=FAKE + 2) == UNS
+    assert call(B=1, N=1, V=1048584) == UNS
+    # one 8-byte record per run of 128 vectors of each of the 2 B (N+1) rows
+    for B, N, V, dt in ((32, 64, 128256, 1), (1, 1, 8, 1), (3, 5, 1000, 0)):
+        ws = lib.sv_tree_sampling_workspace_bytes(B, N, V, dt)
+        assert ws >= 8 * 2 * B * (N + 1) * -(-(V * (2 if dt else 4) // 16) // 128)
+    assert lib.sv_tree_sampling_workspace_bytes(4, 0, 128, 1) == 0
+    assert lib.sv_tree_sampling_workspace_bytes(4, 8, 128, 9) == 0
+
+
 def test_sample_argument_errors(lib):
     def call(**kw):
         a = dict(x=FAKE, dt=1, T=None, u=FAKE, R=4, V=100, out=FAKE, p=None, err=None, ws=FAKE, wsb=1 << 20)

@@ -468,7 +468,7 @@ def tree_inputs(cfg: TreeConfig, device="cpu") -> dict:
     }
 
 
-def sample_tree_inputs(cfg: SampleTreeConfig, device="cpu") -> dict:
+def sample_tree_inputs(cfg: SampleTreeConfig, device="cpu", parents=None) -> dict:
     """Inputs of one sampling tree-verification call on ``device``.
 
     Keys: ``target``, ``draft [B,N+1,V]`` (position 0 = the root, position
@@ -478,11 +478,17 @@ def sample_tree_inputs(cfg: SampleTreeConfig, device="cpu") -> dict:
     Gumbel-max, siblings independently), ``parents [N]``, ``temperature [B]``,
     ``uniforms [B,N+1]`` in [0, 1) (column i tests node i, column N drives the
     final draw). Streams: 0 target, 1 draft noise, 2 token Gumbel noise,
-    3 uniforms.
+    3 uniforms. ``parents`` (int array of length N) replaces the tree cut
+    from ``cfg.branching``.
     """
     B, N, V = cfg.B, cfg.N, cfg.V
     dt = _TORCH_DTYPES[cfg.dtype]
-    parents, _ = tree_parents_ranked(cfg.branching, N)
+    if parents is None:
+        parents, _ = tree_parents_ranked(cfg.branching, N)
+    else:
+        parents = np.asarray(parents, dtype=np.int32)
+        if parents.shape != (N,):
+            raise ValueError(f"parents must have length N = {N}")
     pos_parent = torch.from_numpy(np.where(parents < 0, 0, parents + 1).astype(np.int64))
     T = torch.full((B,), float(cfg.temperature), dtype=torch.float32)
     if _is_cpu(device):
