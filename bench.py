@@ -10,8 +10,10 @@ log-prior, draft = target + N(0, 0.8^2)). Three independent input sets
 (3 x 180.6 MB) are rotated so that the 256 MB last-level cache cannot serve a
 step from the previous one; every input is resident in HBM before the timed
 region starts. Other workloads (--workload c1, c3_s0.3, c3_s1.0, c3_s3.0, c5,
-c4) print a line of the same form; c5 rotates its ten iterations (one set of
-logits, fresh uniforms each), c4 is the greedy tree call. The s1, s2 and s3
+c4, c4s) print a line of the same form; c5 rotates its ten iterations (one
+set of logits, fresh uniforms each), c4 is the greedy tree call, c4s the
+sampling tree call (B=32, N=64, V=128256 bf16, target and draft rows at every
+position: 2 x 534 MB per input set). The s1, s2 and s3
 workloads time draft-side sampling (sv_sample_rows) over the draft rows of c1,
 c2 and c3_s1.0 (B*K rows each, one token drawn per row).
 
@@ -43,6 +45,8 @@ KERNEL_SOURCES = {
     "chain": ["sv_chain.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
     "sample": ["sv_sample.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
     "tree": ["sv_tree.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
+    # the counted kernel is the run-record stream; the walk (sv_tree_sample.hip) is not part of it
+    "treesample": ["sv_sample.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
 }
 
 
@@ -52,7 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain), c4 (tree) or s1, s2, s3 (draft-side sampling)")
+                    help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain), c4 (greedy tree), c4s (sampling tree) "
+                         "or s1, s2, s3 (draft-side sampling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of each call captured in a HIP graph (the call's launches without the "
@@ -155,6 +160,26 @@ def cpu_baseline_tree(inp, cfg, budget_s: float) -> dict:
     }
 
 
+def cpu_baseline_tree_sampling(inp, cfg, budget_s: float) -> dict:
+    """The oracle's sampling tree verification, one sequence at a time."""
+    import oracle
+
+    parents = inp["parents"].numpy().astype("int64")
+    jobs = [(lambda b=b: (inp["target"][b:b + 1].double().numpy(), inp["draft"][b:b + 1].double().numpy(),
+                          inp["node_tokens"][b:b + 1].numpy().astype("int64"), parents,
+                          inp["temperature"][b:b + 1].double().numpy(), inp["uniforms"][b:b + 1].double().numpy()),
+             oracle.verify_tree_stochastic, 1) for b in range(cfg.B)]
+    done, wall, cpu = _timed_oracle(jobs, budget_s)
+    return {
+        "value": done * 2 * (cfg.N + 1) * cfg.V / wall,
+        "unit": "rows·vocab/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"{done} sequences ({done / cfg.B:.2f} passes over the {cfg.B}-sequence batch) of the same "
+                  f"workload, float64 numpy, {wall:.1f} s in the oracle, {cpu:.1f} s CPU",
+    }
+
+
 # draft-side sampling workloads: the draft rows of a chain configuration
 SAMPLE_WORKLOADS = {"s1": "c1", "s2": "c2", "s3": "c3_s1.0"}
 
@@ -191,7 +216,8 @@ def main():
     import torch
 
     import rejection_sampling_verification_sv_amd as sv
-    from workloads import CHAIN_CONFIGS, TREE_CONFIGS, chain_inputs, chain_uniforms, sample_inputs, tree_inputs
+    from workloads import (CHAIN_CONFIGS, SAMPLE_TREE_CONFIGS, TREE_CONFIGS, chain_inputs, chain_uniforms,
+                           sample_inputs, sample_tree_inputs, tree_inputs)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     sv.library()
@@ -207,8 +233,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = args.workload
-    kind = "tree" if wl in TREE_CONFIGS else ("sample" if wl in SAMPLE_WORKLOADS else "chain")
-    if kind == "sample":
+    kind = ("tree" if wl in TREE_CONFIGS else "treesample" if wl in SAMPLE_TREE_CONFIGS
+            else "sample" if wl in SAMPLE_WORKLOADS else "chain")
+    if kind == "treesample":
+        cfg = SAMPLE_TREE_CONFIGS[wl]
+        B, N, V = cfg.B, cfg.N, cfg.V
+        rows = cfg.rows  # target and draft rows
+        eb = 2 if cfg.dtype == "bf16" else 4
+        sets = [sample_tree_inputs(cfg.with_(variant=cfg.variant + 10 * i) if i else cfg, device=dev)
+                for i in range(N_SETS)]
+        calls = [sv.PreparedTreeSamplingCall(s["target"], s["draft"], s["node_tokens"], s["parents"],
+                                             s["temperature"], s["uniforms"], stream=stream) for s in sets]
+        stream_bytes = rows * V * eb
+        # plus tokens, parents, uniforms and temperatures (the walk's re-reads of
+        # the rows it visits are not counted)
+        call_bytes = stream_bytes + B * N * 4 + N * 4 + B * (N + 1) * 4 + B * 4
+        config = {"workload": cfg.name + ("_graph" if args.graph else ""), "B": B, "N": N, "V": V,
+                  "logits": cfg.dtype, "temperature": cfg.temperature, "branching": list(cfg.branching),
+                  "input_sets_rotated": len(sets)}
+        kernel_name = "sample_stream_kernel (one pass over every target and draft row: a record per run of 128 vectors)"
+    elif kind == "sample":
         cfg = CHAIN_CONFIGS[SAMPLE_WORKLOADS[wl]]
         R, V = cfg.B * cfg.K, cfg.V
         rows = R
@@ -336,6 +380,8 @@ def main():
     result = {
         "metric": (METRIC if wl == "c2" and not args.entropy and not args.graph else
                    f"sampling throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}" if kind == "sample"
+                   else f"tree sampling verify throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}"
+                   if kind == "treesample"
                    else f"verify throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}"),
         "value": elems / (ms_per_step * 1e-3),
         "unit": "rows·vocab/s",
@@ -374,6 +420,8 @@ def main():
             result["cpu_baseline"] = cpu_baseline_chain(cpu_inp, cfg, args.cpu_seconds)
         elif kind == "sample":
             result["cpu_baseline"] = cpu_baseline_sample(cpu_inp, cfg, args.cpu_seconds)
+        elif kind == "treesample":
+            result["cpu_baseline"] = cpu_baseline_tree_sampling(cpu_inp, cfg, args.cpu_seconds)
         else:
             result["cpu_baseline"] = cpu_baseline_tree(cpu_inp, cfg, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -9,7 +9,8 @@ checks every replay bit for bit against the eager call on the same inputs.
 import pytest
 import torch
 
-from workloads import CHAIN_CONFIGS, TREE_CONFIGS, chain_inputs, sample_inputs, tree_inputs
+from workloads import (CHAIN_CONFIGS, SAMPLE_TREE_CONFIGS, TREE_CONFIGS, chain_inputs, sample_inputs,
+                       sample_tree_inputs, tree_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +118,34 @@ def test_tree_call_in_a_graph(sv):
         call()
     _replay_and_compare(g, outs, {k: ref[k] for k in ("accept_len", "path_nodes", "next_token")},
                         lambda: sv.sv_verify_tree_greedy(inp["target"], inp["node_tokens"], inp["parents"]))
+
+
+def test_tree_sampling_call_in_a_graph(sv):
+    cfg = SAMPLE_TREE_CONFIGS["c4s"].with_(B=8)
+    _say("graph: sampling tree", cfg.name, "B = 8")
+    inp = sample_tree_inputs(cfg, device="cuda")
+    keys = ("target", "draft", "node_tokens", "parents", "temperature", "uniforms")
+    ref = sv.sv_verify_tree_sampling(*(inp[k] for k in keys))
+    torch.cuda.synchronize()
+    B, N1, V = inp["target"].shape
+    N = N1 - 1
+    outs = {"accept_len": torch.empty(B, dtype=torch.int32, device="cuda"),
+            "path_nodes": torch.empty(B, N, dtype=torch.int32, device="cuda"),
+            "next_token": torch.empty(B, dtype=torch.int32, device="cuda"),
+            "err_flags": torch.zeros(1, dtype=torch.int32, device="cuda")}
+    ws = torch.zeros(sv.sv_tree_sampling_workspace_bytes(B, N, V, inp["target"].dtype), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        sv.sv_verify_tree_sampling(*(inp[k] for k in keys), workspace_tensor=ws, **outs)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    alt = sample_tree_inputs(cfg.with_(variant=cfg.variant + 10), device="cuda")
+    _replay_and_compare(g, outs, {k: ref[k] for k in ("accept_len", "path_nodes", "next_token")},
+                        lambda: sv.sv_verify_tree_sampling(*(alt[k] for k in keys)))
+    assert int(outs["err_flags"].item()) == 0
