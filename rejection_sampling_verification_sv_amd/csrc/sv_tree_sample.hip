@@ -46,6 +46,9 @@ namespace {
 
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / kWave;
+// Rejections at one node whose factors a pass keeps in registers (more fall
+// back to reading them from LDS per token).
+constexpr int kWalkHoist = 3;
 
 // The exponent scale and the two rows' log-normalisers split for fp32 use:
 // p(v) = 2^(x_t c - L_t), q(v) = 2^(x_d c - L_d).
@@ -61,13 +64,21 @@ __device__ __forceinline__ void split_neg(double v, float& hi, float& lo) {
 
 // Weight of one token in fp32: the current distribution P_r (kResid false)
 // or its residual max(0, P_r - q) (kResid true), P_0 = p, each earlier
-// rejection k applying max(0, . - q) * invZ[k].
-template <bool kResid>
-__device__ __forceinline__ float walk_weight(float xt, float xd, const WalkRows& w, int r, const float* invZ) {
+// rejection k applying max(0, . - q) * invZ[k]. R >= 0: r = R, with the
+// factors in registers (iz); R < 0: any r, the factors read from invZ in LDS.
+// Both forms take the same operations in the same order.
+template <bool kResid, int R>
+__device__ __forceinline__ float walk_weight(float xt, float xd, const WalkRows& w, int r, const float* invZ,
+                                             const float (&iz)[kWalkHoist]) {
   const float p = fast_exp2(scaled_arg(xt, w.c, w.nlt_hi) + w.nlt_lo);
   const float q = fast_exp2(scaled_arg(xd, w.c, w.nld_hi) + w.nld_lo);
   float val = p;
-  for (int k = 0; k < r; ++k) val = fmaxf(val - q, 0.0f) * invZ[k];
+  if constexpr (R >= 0) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) val = fmaxf(val - q, 0.0f) * iz[k];
+  } else {
+    for (int k = 0; k < r; ++k) val = fmaxf(val - q, 0.0f) * invZ[k];
+  }
   return kResid ? fmaxf(val - q, 0.0f) : val;
 }
 
@@ -83,9 +94,10 @@ __device__ __forceinline__ void walk_load(const uint4* row, int64_t g, int64_t n
   }
 }
 
-template <class T, bool kResid>
+template <class T, bool kResid, int R>
 __device__ __forceinline__ float walk_run_sum(const uint4 (&at)[kRunLaneVecs], const uint4 (&ad)[kRunLaneVecs],
-                                              const WalkRows& w, int r, const float* invZ) {
+                                              const WalkRows& w, int r, const float* invZ,
+                                              const float (&iz)[kWalkHoist]) {
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < kRunLaneVecs; ++i) {
@@ -93,7 +105,7 @@ __device__ __forceinline__ float walk_run_sum(const uint4 (&at)[kRunLaneVecs], c
     unpack<T>(at[i], xt);
     unpack<T>(ad[i], xd);
 #pragma unroll
-    for (int e = 0; e < T::kVec; ++e) s += walk_weight<kResid>(xt[e], xd[e], w, r, invZ);
+    for (int e = 0; e < T::kVec; ++e) s += walk_weight<kResid, R>(xt[e], xd[e], w, r, invZ, iz);
   }
   return s;
 }
@@ -101,11 +113,15 @@ __device__ __forceinline__ float walk_run_sum(const uint4 (&at)[kRunLaneVecs], c
 // One pass over the row pair by the whole workgroup: s_run[g] = the fp32
 // total of the weights of run g (wave w takes runs w, w + 16, ..., the next
 // run's loads in flight while the current one is reduced). No barrier.
-template <class T, bool kResid>
-__device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
-                          const float* invZ, double* s_run) {
-  int g = wave_id();
-  if (g >= nrun) return;
+template <class T, bool kResid, int R>
+__device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
+                            const float* invZ, double* s_run) {
+  const int g0 = wave_id();
+  if (g0 >= nrun) return;
+  float iz[kWalkHoist];
+#pragma unroll
+  for (int k = 0; k < kWalkHoist; ++k) iz[k] = (k < R) ? invZ[k] : 0.0f;
+  int g = g0;
   uint4 at[kRunLaneVecs], ad[kRunLaneVecs];
   walk_load<T>(rt, g, nvec, at);
   walk_load<T>(rd, g, nvec, ad);
@@ -116,7 +132,7 @@ __device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int nr
       walk_load<T>(rt, gn, nvec, bt);
       walk_load<T>(rd, gn, nvec, bd);
     }
-    const float s = wave_sum_dpp(walk_run_sum<T, kResid>(at, ad, w, r, invZ));
+    const float s = wave_sum_dpp(walk_run_sum<T, kResid, R>(at, ad, w, r, invZ, iz));
     if (lane_id() == 0) s_run[g] = static_cast<double>(s);
     if (gn >= nrun) break;
     g = gn;
@@ -125,6 +141,21 @@ __device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int nr
       at[i] = bt[i];
       ad[i] = bd[i];
     }
+  }
+}
+
+// walk_pass_r for the r at hand: 0 .. kWalkHoist rejections with their
+// factors in registers, more with the factors read from LDS.
+template <class T, bool kResid>
+__device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
+                          const float* invZ, double* s_run) {
+  static_assert(kWalkHoist == 3, "one case per hoisted count");
+  switch (r) {
+    case 0: walk_pass_r<T, kResid, 0>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
+    case 1: walk_pass_r<T, kResid, 1>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
+    case 2: walk_pass_r<T, kResid, 2>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
+    case 3: walk_pass_r<T, kResid, 3>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
+    default: walk_pass_r<T, kResid, -1>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
   }
 }
 
@@ -188,6 +219,7 @@ __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nru
   const double tk = found >= 0 ? target - prefix : INFINITY;
   // lane l: vectors g * kRunVecs + kRunLaneVecs * l + i, its tokens in ascending order
   const int64_t vb = static_cast<int64_t>(g) * kRunVecs + kRunLaneVecs * lane;
+  constexpr float kNoFactors[kWalkHoist] = {};
   constexpr int NE = kRunLaneVecs * T::kVec;
   float wv[NE];
   float lane_tot = 0.0f;
@@ -200,7 +232,7 @@ __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nru
     unpack<T>(qd, xd);
 #pragma unroll
     for (int e = 0; e < T::kVec; ++e) {
-      wv[i * T::kVec + e] = walk_weight<kResid>(xt[e], xd[e], w, r, invZ);
+      wv[i * T::kVec + e] = walk_weight<kResid, -1>(xt[e], xd[e], w, r, invZ, kNoFactors);
       lane_tot += wv[i * T::kVec + e];
     }
   }
@@ -269,12 +301,16 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
     s_token = -1;
   }
   __syncthreads();
-  for (int v = tid; v < N; v += kWalkThreads) {
-    const int par = P.parents[v];
-    s_par[v] = par;
-    if (!(par == -1 || (par >= 0 && par < v))) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_PARENT));
-    const int x = P.tokens[static_cast<int64_t>(b) * N + v];
-    if (x < 0 || x >= P.V) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_TOKEN));
+  // thread v owns node v (N <= kWalkThreads): its parent, token and uniform
+  int my_x = 0;
+  float my_u = 0.0f;
+  if (tid < N) {
+    const int par = P.parents[tid];
+    s_par[tid] = par;
+    if (!(par == -1 || (par >= 0 && par < tid))) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_PARENT));
+    my_x = P.tokens[static_cast<int64_t>(b) * N + tid];
+    my_u = P.uniforms[static_cast<int64_t>(b) * N1 + tid];
+    if (my_x < 0 || my_x >= P.V) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_TOKEN));
   }
   __syncthreads();
 
@@ -288,6 +324,14 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
       if (lane == 0) s_mask[wv] = m;
       const int64_t rowt = static_cast<int64_t>(b) * N1 + pos;
       const int64_t rowd = static_cast<int64_t>(P.B) * N1 + rowt;
+      const uint4* rt = reinterpret_cast<const uint4*>(tbase + rowt * row_bytes);
+      const uint4* rd = reinterpret_cast<const uint4*>(dbase + (rowt)*row_bytes);
+      // a child's two logits at this position, loading while the normalisers are formed
+      float klt = 0.0f, kld = 0.0f;
+      if (mine) {
+        klt = load_elem<T>(rt, my_x);
+        kld = load_elem<T>(rd, my_x);
+      }
       if (wv < 2) {
         uint32_t e = 0u;
         float M;
@@ -307,15 +351,12 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
         if (w2 < wv) before += pc;
         nkids += pc;
       }
-      const uint4* rt = reinterpret_cast<const uint4*>(tbase + rowt * row_bytes);
-      const uint4* rd = reinterpret_cast<const uint4*>(dbase + (rowt)*row_bytes);
       if (mine) {
         const int i = before + __popcll(m & ((1ull << lane) - 1ull));
-        const int x = P.tokens[static_cast<int64_t>(b) * N + tid];
         s_kids[i] = tid;
-        s_klt[i] = load_elem<T>(rt, x);
-        s_kld[i] = load_elem<T>(rd, x);
-        s_ku[i] = P.uniforms[static_cast<int64_t>(b) * N1 + tid];
+        s_klt[i] = klt;
+        s_kld[i] = kld;
+        s_ku[i] = my_u;
       }
       __syncthreads();
       const float Mt = s_M[0], Md = s_M[1];
