@@ -253,8 +253,11 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype,
  * Sampling verification of a candidate tree.
  *
  * Bytes of device workspace sv_verify_tree_sampling needs (one 8-byte record
- * per 128 16-byte vectors of each target and draft row); 0 for invalid sizes.
- * Same zero-fill contract as the chain workspace (a call leaves it all zero).
+ * per 128 16-byte vectors of each target and draft row, two 8-byte exchange
+ * slots per such run of each sequence, B + 2 counters and an abort flag);
+ * 0 for invalid sizes. Same zero-fill contract as the chain workspace (a
+ * call leaves it all zero; after SV_ERRF_INTERNAL it must be zero-filled
+ * again).
  */
 size_t sv_tree_sampling_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype);
 
@@ -319,6 +322,12 @@ size_t sv_tree_sampling_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtyp
  * multiple of 16, or a base pointer off 16 bytes) or V exceeds 1024 * 128
  * vectors (1 048 576 bf16, 524 288 fp32 tokens); SV_ERR_HIP when a launch
  * fails. Nothing is enqueued on an error return.
+ *
+ * When B is small against the device's compute units, several workgroups
+ * (up to 8) follow each sequence's walk and share its passes over the row
+ * pairs, exchanging run totals through the workspace with bounded waits:
+ * the outputs are the same as with one workgroup per sequence. A wait that
+ * expires (100 ms) sets SV_ERRF_INTERNAL.
  */
 sv_status sv_verify_tree_sampling(const void* target_logits, const void* draft_logits, sv_dtype dtype,
                                   const int32_t* node_tokens, const int32_t* parents,

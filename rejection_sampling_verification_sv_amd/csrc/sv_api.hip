@@ -167,6 +167,42 @@ bool tree_sampling_rows(int32_t B, int32_t N, int64_t* rows) {
   return *rows <= INT32_MAX;
 }
 
+// Workspace of a sampling-tree call: the run records, then the walk's
+// exchange slots (two per run of each sequence), counters and abort flag.
+struct TreeSamplingLayout {
+  RunLayout runs;
+  size_t off_slots, off_cnt, off_abort, total;
+};
+
+TreeSamplingLayout tree_sampling_layout(int32_t B, int32_t N, int32_t V, sv_dtype d) {
+  TreeSamplingLayout L{};
+  L.runs = run_layout(static_cast<int32_t>(2LL * B * (N + 1)), V, d);
+  size_t off = L.runs.total;
+  L.off_slots = off;
+  off = align_up(off + sizeof(uint64_t) * 2 * static_cast<int64_t>(B) * L.runs.nrun);
+  L.off_cnt = off;
+  off = align_up(off + sizeof(uint32_t) * (static_cast<int64_t>(B) + 2));
+  L.off_abort = off;
+  off = align_up(off + sizeof(uint64_t));
+  L.total = off;
+  return L;
+}
+
+// Walk workgroups per sequence: enough to spread the call's passes over the
+// compute units (B G about the number of compute units), each with at least
+// one run per wave, at most kMaxWalkGroups.
+int32_t walk_groups(int32_t B, int32_t nrun) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 1;
+  const int64_t by_cus = cus / (B > 0 ? B : 1);
+  const int64_t by_runs = ceil_div(nrun, 16);
+  int64_t g = by_cus < by_runs ? by_cus : by_runs;
+  if (g > sv::kMaxWalkGroups) g = sv::kMaxWalkGroups;
+  return g < 1 ? 1 : static_cast<int32_t>(g);
+}
+
 thread_local sv::PassEvents g_pass_events{nullptr, nullptr};
 
 }  // namespace
@@ -359,7 +395,7 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype, const
 size_t sv_tree_sampling_workspace_bytes(int32_t B, int32_t N, int32_t V, sv_dtype dtype) {
   int64_t rows = 0;
   if (!tree_sizes_ok(B, N, V) || !dtype_ok(dtype) || !tree_sampling_rows(B, N, &rows)) return 0;
-  return run_layout(static_cast<int32_t>(rows), V, dtype).total;
+  return tree_sampling_layout(B, N, V, dtype).total;
 }
 
 sv_status sv_verify_tree_sampling(const void* target_logits, const void* draft_logits, sv_dtype dtype,
@@ -377,8 +413,9 @@ sv_status sv_verify_tree_sampling(const void* target_logits, const void* draft_l
     return SV_ERR_INVALID_ARGUMENT;
   if (!aligned_to(target_logits, dtype_bytes(dtype)) || !aligned_to(draft_logits, dtype_bytes(dtype)))
     return SV_ERR_INVALID_ARGUMENT;
-  const RunLayout L = run_layout(static_cast<int32_t>(rows), V, dtype);
-  if (workspace == nullptr || workspace_bytes < L.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
+  const TreeSamplingLayout TL = tree_sampling_layout(B, N, V, dtype);
+  const RunLayout& L = TL.runs;
+  if (workspace == nullptr || workspace_bytes < TL.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
   // the walk reads rows as 16-byte vectors and keeps one total per run in LDS
   if (!whole_vector_rows(V, dtype) || !aligned_to(target_logits, 16) || !aligned_to(draft_logits, 16) ||
       L.nrun > sv::kMaxWalkRuns || rows * L.cps > INT32_MAX)
@@ -415,6 +452,12 @@ sv_status sv_verify_tree_sampling(const void* target_logits, const void* draft_l
   p.path_nodes = path_nodes;
   p.next_token = next_token;
   p.err_flags = err_flags;
+  char* ws = static_cast<char*>(workspace);
+  p.G = walk_groups(B, L.nrun);
+  if (static_cast<int64_t>(B) * p.G > INT32_MAX) p.G = 1;
+  p.slots = reinterpret_cast<uint64_t*>(ws + TL.off_slots);
+  p.cnt = reinterpret_cast<uint32_t*>(ws + TL.off_cnt);
+  p.abort = reinterpret_cast<uint64_t*>(ws + TL.off_abort);
   return from_hip(sv::launch_tree_sample(sp, p, dtype, ev, stream));
 }
 

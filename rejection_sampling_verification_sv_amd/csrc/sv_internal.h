@@ -127,7 +127,15 @@ struct TreeSampleParams {
   int32_t* path_nodes;
   int32_t* next_token;
   int32_t* err_flags;
+  // G > 1: G walk workgroups per sequence share every pass over a row pair
+  int32_t G;
+  uint64_t* slots;         // workspace [B, 2, nrun]: a pass's run totals, tagged with the pass number
+  uint32_t* cnt;           // workspace [B + 2]: per sequence walk workgroups finished; ticket; grid finished
+  uint64_t* abort;         // workspace [1]: set when a bounded wait expires
 };
+
+// Walk workgroups per sequence, at most.
+constexpr int kMaxWalkGroups = 8;
 
 // Runs per row the walk keeps totals of in LDS.
 constexpr int kMaxWalkRuns = 1024;

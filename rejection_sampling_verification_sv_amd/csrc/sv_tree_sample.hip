@@ -110,14 +110,15 @@ __device__ __forceinline__ float walk_run_sum(const uint4 (&at)[kRunLaneVecs], c
   return s;
 }
 
-// One pass over the row pair by the whole workgroup: s_run[g] = the fp32
-// total of the weights of run g (wave w takes runs w, w + 16, ..., the next
-// run's loads in flight while the current one is reduced). No barrier.
+// One pass of the workgroup over runs [lo, hi) of the row pair: s_run[g] =
+// the fp32 total of the weights of run g (wave w takes runs lo + w,
+// lo + w + 16, ..., the next run's loads in flight while the current one is
+// reduced). No barrier.
 template <class T, bool kResid, int R>
-__device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
+__device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int lo, int hi, const WalkRows& w, int r,
                             const float* invZ, double* s_run) {
-  const int g0 = wave_id();
-  if (g0 >= nrun) return;
+  const int g0 = lo + wave_id();
+  if (g0 >= hi) return;
   float iz[kWalkHoist];
 #pragma unroll
   for (int k = 0; k < kWalkHoist; ++k) iz[k] = (k < R) ? invZ[k] : 0.0f;
@@ -128,13 +129,13 @@ __device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int 
   for (;;) {
     const int gn = g + kWalkWaves;
     uint4 bt[kRunLaneVecs], bd[kRunLaneVecs];
-    if (gn < nrun) {
+    if (gn < hi) {
       walk_load<T>(rt, gn, nvec, bt);
       walk_load<T>(rd, gn, nvec, bd);
     }
     const float s = wave_sum_dpp(walk_run_sum<T, kResid, R>(at, ad, w, r, invZ, iz));
     if (lane_id() == 0) s_run[g] = static_cast<double>(s);
-    if (gn >= nrun) break;
+    if (gn >= hi) break;
     g = gn;
 #pragma unroll
     for (int i = 0; i < kRunLaneVecs; ++i) {
@@ -147,16 +148,59 @@ __device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int 
 // walk_pass_r for the r at hand: 0 .. kWalkHoist rejections with their
 // factors in registers, more with the factors read from LDS.
 template <class T, bool kResid>
-__device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
+__device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int lo, int hi, const WalkRows& w, int r,
                           const float* invZ, double* s_run) {
   static_assert(kWalkHoist == 3, "one case per hoisted count");
   switch (r) {
-    case 0: walk_pass_r<T, kResid, 0>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
-    case 1: walk_pass_r<T, kResid, 1>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
-    case 2: walk_pass_r<T, kResid, 2>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
-    case 3: walk_pass_r<T, kResid, 3>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
-    default: walk_pass_r<T, kResid, -1>(rt, rd, nvec, nrun, w, r, invZ, s_run); break;
+    case 0: walk_pass_r<T, kResid, 0>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
+    case 1: walk_pass_r<T, kResid, 1>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
+    case 2: walk_pass_r<T, kResid, 2>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
+    case 3: walk_pass_r<T, kResid, 3>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
+    default: walk_pass_r<T, kResid, -1>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
   }
+}
+
+// Wait until *slot holds the totals of pass `pass` (its upper half) and
+// return it; bounded like await_slot (kErrInternal and 0 on expiry or abort).
+__device__ __forceinline__ uint64_t await_pass(uint64_t* slot, uint32_t pass, uint32_t* err, uint64_t* abort) {
+  uint64_t v = peek(slot);
+  if (static_cast<uint32_t>(v >> 32) == pass) return v;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (;;) {
+    __builtin_amdgcn_s_sleep(2);
+    v = peek(slot);
+    if (static_cast<uint32_t>(v >> 32) == pass) return v;
+    if (peek(abort) != 0ull) break;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      publish(abort, 1ull);
+      break;
+    }
+  }
+  *err |= kErrInternal;
+  return 0ull;
+}
+
+// Exchange of one pass among the G workgroups of a sequence (after a
+// barrier of the workgroup): this workgroup's run totals [lo, hi) go out
+// tagged with the pass number (never 0), and the others' are read back
+// into s_run, so every workgroup then holds the totals of all runs, the
+// same values as one workgroup computing them all. Pass k uses buffer k % 2:
+// a workgroup publishes pass k + 2 only after it has read every
+// workgroup's pass k + 1, which each wrote after reading pass k.
+__device__ void walk_exchange(const TreeSampleParams& P, int b, uint32_t pass, int lo, int hi, double* s_run,
+                              uint32_t* s_err) {
+  uint64_t* slots = P.slots + (static_cast<int64_t>(b) * 2 + (pass & 1u)) * P.nrun;
+  const int tid = static_cast<int>(threadIdx.x);
+  for (int g = lo + tid; g < hi; g += kWalkThreads)
+    publish(&slots[g], (static_cast<uint64_t>(pass) << 32) |
+                           static_cast<uint64_t>(__float_as_uint(static_cast<float>(s_run[g]))));
+  uint32_t err = 0u;
+  for (int g = tid; g < P.nrun; g += kWalkThreads) {
+    if (g >= lo && g < hi) continue;
+    const uint64_t v = await_pass(&slots[g], pass, &err, P.abort);
+    s_run[g] = static_cast<double>(__uint_as_float(static_cast<uint32_t>(v)));
+  }
+  if (err != 0u) atomicOr(s_err, err);
 }
 
 // One wave: (M, Z) of a row from its run records, M = the largest reference,
@@ -282,9 +326,37 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
   __shared__ double s_sum;
   __shared__ int s_token;
   __shared__ uint32_t s_err;
+  __shared__ int s_role;
 
-  const int b = static_cast<int>(blockIdx.x);
   const int tid = static_cast<int>(threadIdx.x);
+  // Role: sequence b, slice gi of G. With G > 1 the roles go by a ticket
+  // taken when the workgroup starts, so the workgroups of a sequence start
+  // one after another: a workgroup waits only for siblings that are running
+  // or next in line for a compute unit, never for one stuck behind it.
+  const int G = P.G;
+  int b = static_cast<int>(blockIdx.x), gi = 0;
+  if (G > 1) {
+    if (tid == 0)
+      s_role = static_cast<int>(__hip_atomic_fetch_add(&P.cnt[P.B], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    __syncthreads();
+    if (s_role < 0 || s_role >= P.B * G) {
+      // a ticket counter not left at zero (a workspace not re-zeroed after an
+      // expired wait): no role; flag it, release any waiting sibling, leave
+      __shared__ int s_flag0;
+      if (tid == 0) {
+        raise_error(P.err_flags, kErrInternal);
+        publish(P.abort, 1ull);
+      }
+      arrive_and_check_last(&P.cnt[P.B + 1], static_cast<uint32_t>(P.B * G), &s_flag0);
+      return;
+    }
+    b = s_role / G;
+    gi = s_role - b * G;
+  }
+  // this workgroup's runs of every pass
+  const int lo = static_cast<int>(static_cast<int64_t>(gi) * P.nrun / G);
+  const int hi = static_cast<int>(static_cast<int64_t>(gi + 1) * P.nrun / G);
+  uint32_t pass = 0u;
   const int lane = lane_id();
   const int wv = wave_id();
   const int N = P.N;
@@ -391,8 +463,12 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
           break;
         }
         // rejected: the residual max(0, P_r - q), per run and in total
-        walk_pass<T, true>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, s_run);
+        walk_pass<T, true>(rt, rd, P.nvec, lo, hi, w, r, s_invZ, s_run);
         __syncthreads();
+        if (G > 1) {
+          walk_exchange(P, b, ++pass, lo, hi, s_run, &s_err);
+          __syncthreads();
+        }
         if (wv == 0) {
           double z = 0.0;
           for (int g = lane; g < P.nrun; g += kWave) z += s_run[g];
@@ -420,14 +496,18 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
       // no child accepted (or a leaf): draw from P_r at this position
       const double u = static_cast<double>(P.uniforms[static_cast<int64_t>(b) * N1 + N]);
       if (resid_totals) {  // s_run holds the totals of max(0, P_{r-1} - q), proportional to P_r
-        if (wv == 0) {
+        if (wv == 0 && gi == 0) {
           const int t = walk_draw<T, true>(rt, rd, P.nvec, P.nrun, w, r - 1, s_invZ, s_run, u);
           if (lane == 0) s_token = t;
         }
       } else {
-        walk_pass<T, false>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, s_run);
+        walk_pass<T, false>(rt, rd, P.nvec, lo, hi, w, r, s_invZ, s_run);
         __syncthreads();
-        if (wv == 0) {
+        if (G > 1) {
+          walk_exchange(P, b, ++pass, lo, hi, s_run, &s_err);
+          __syncthreads();
+        }
+        if (wv == 0 && gi == 0) {
           const int t = walk_draw<T, false>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, s_run, u);
           if (lane == 0) s_token = t;
         }
@@ -438,22 +518,47 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
   __syncthreads();
   // no token with weight in a distribution that passed the normaliser checks
   // would take every weight underflowing: reported as a zero normaliser
-  const uint32_t err = s_err | ((s_err == 0u && s_token < 0) ? static_cast<uint32_t>(SV_ERRF_NONFINITE) : 0u);
-  const bool bad = err != 0u;
-  if (tid == 0) {
-    P.accept_len[b] = bad ? -1 : depth;
-    P.next_token[b] = bad ? -1 : s_token;
-    raise_error(P.err_flags, err);
+  if (gi == 0) {  // the sequence's outputs
+    const uint32_t err = s_err | ((s_err == 0u && s_token < 0) ? static_cast<uint32_t>(SV_ERRF_NONFINITE) : 0u);
+    const bool bad = err != 0u;
+    if (tid == 0) {
+      P.accept_len[b] = bad ? -1 : depth;
+      P.next_token[b] = bad ? -1 : s_token;
+      raise_error(P.err_flags, err);
+    }
+    for (int i = tid; i < N; i += kWalkThreads)
+      P.path_nodes[static_cast<int64_t>(b) * N + i] = (!bad && i < depth) ? s_path[i] : -1;
+  } else if (tid == 0) {
+    raise_error(P.err_flags, s_err);  // an expired wait of this workgroup
   }
-  for (int i = tid; i < N; i += kWalkThreads)
-    P.path_nodes[static_cast<int64_t>(b) * N + i] = (!bad && i < depth) ? s_path[i] : -1;
-  // every record of the sequence's rows has been read: leave them zero
-  const int64_t per = N1 * P.nrun;
-  uint64_t* rec_t = P.rec + static_cast<int64_t>(b) * per;
-  uint64_t* rec_d = P.rec + (static_cast<int64_t>(P.B) + b) * per;
-  for (int64_t i = tid; i < per; i += kWalkThreads) {
-    rec_t[i] = 0ull;
-    rec_d[i] = 0ull;
+  // Every record of the sequence's rows (and every exchange slot) has been
+  // read once all its workgroups are here: the last one leaves them zero.
+  if (G > 1) {
+    __shared__ int s_flag;
+    if (arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(G), &s_flag)) {
+      const int64_t per = N1 * P.nrun;
+      uint64_t* rec_t = P.rec + static_cast<int64_t>(b) * per;
+      uint64_t* rec_d = P.rec + (static_cast<int64_t>(P.B) + b) * per;
+      for (int64_t i = tid; i < per; i += kWalkThreads) {
+        rec_t[i] = 0ull;
+        rec_d[i] = 0ull;
+      }
+      for (int i = tid; i < 2 * P.nrun; i += kWalkThreads) clear_slot(&P.slots[static_cast<int64_t>(b) * 2 * P.nrun + i]);
+      reset_counter(&P.cnt[b]);
+    }
+    // the last workgroup of the launch returns the ticket counter to zero
+    if (arrive_and_check_last(&P.cnt[P.B + 1], static_cast<uint32_t>(P.B * G), &s_flag) && tid == 0) {
+      __hip_atomic_store(&P.cnt[P.B], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&P.cnt[P.B + 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    const int64_t per = N1 * P.nrun;
+    uint64_t* rec_t = P.rec + static_cast<int64_t>(b) * per;
+    uint64_t* rec_d = P.rec + (static_cast<int64_t>(P.B) + b) * per;
+    for (int64_t i = tid; i < per; i += kWalkThreads) {
+      rec_t[i] = 0ull;
+      rec_d[i] = 0ull;
+    }
   }
 }
 
@@ -461,12 +566,11 @@ hipError_t launch_tree_sample(const SampleParams& sp, const TreeSampleParams& p,
                               hipStream_t stream) {
   const hipError_t e = launch_sample_stream(sp, dtype, ev, stream);
   if (e != hipSuccess) return e;
+  const uint32_t grid = static_cast<uint32_t>(p.B) * static_cast<uint32_t>(p.G);
   if (dtype == SV_DTYPE_BF16)
-    hipLaunchKernelGGL(tree_sample_walk_kernel<BF16>, dim3(static_cast<uint32_t>(p.B)), dim3(kWalkThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL(tree_sample_walk_kernel<BF16>, dim3(grid), dim3(kWalkThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL(tree_sample_walk_kernel<F32>, dim3(static_cast<uint32_t>(p.B)), dim3(kWalkThreads), 0,
-                       stream, p);
+    hipLaunchKernelGGL(tree_sample_walk_kernel<F32>, dim3(grid), dim3(kWalkThreads), 0, stream, p);
   return hipGetLastError();
 }
 

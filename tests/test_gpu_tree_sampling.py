@@ -279,6 +279,49 @@ def test_workspace_reuse_across_shapes(sv):
         assert int(ws.count_nonzero().item()) == 0
 
 
+def test_split_walk_parity_and_workspace(sv):
+    # Few sequences of long rows: each sequence's walk is shared by several
+    # workgroups (up to eight, one slice of the runs of every pass each).
+    base = SAMPLE_TREE_CONFIGS["c4s"]
+    cases = [
+        base.with_(name="tree_sampling_split_b3_v128256", B=3, N=30, V=128256, variant=61),
+        base.with_(name="tree_sampling_split_b5_v64000", B=5, N=64, V=64000, variant=62),
+        base.with_(name="tree_sampling_split_b2_v40000_f32", B=2, N=20, V=40000, dtype="f32", variant=63),
+    ]
+    star = base.with_(name="tree_sampling_split_star", B=4, N=40, V=128256, variant=64)
+    nbytes = max(sv.sv_tree_sampling_workspace_bytes(c.B, c.N, c.V, torch.float32 if c.dtype == "f32"
+                                                     else torch.bfloat16) for c in cases + [star])
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for round_ in range(2):
+        for cfg in cases:
+            _say("split walk round", round_, cfg.name)
+            inp = sample_tree_inputs(cfg, device="cuda")
+            out = _call(sv, inp, workspace_tensor=ws)
+            assert int(out["err_flags"].item()) == 0
+            assert int(ws.count_nonzero().item()) == 0, f"workspace dirty after {cfg.name}"
+            _compare(out, _oracle(inp), cfg.name)
+    # a star of 40 children (many passes at the root), and per-sequence errors
+    cfg = star
+    inp = sample_tree_inputs(cfg, device="cuda", parents=np.full(cfg.N, -1))
+    ref = _oracle(inp)
+    _say("split walk star tree")
+    out = _call(sv, inp, workspace_tensor=ws)
+    assert int(out["err_flags"].item()) == 0
+    assert int(ws.count_nonzero().item()) == 0
+    _compare(out, ref, cfg.name)
+    inp["node_tokens"][1, 3] = -1                 # a token outside [0, V)
+    inp["target"][2, 0, 17] = float("nan")        # a non-finite root row
+    _say("split walk star tree with error sequences")
+    out = _call(sv, inp, workspace_tensor=ws)
+    assert int(out["err_flags"].item()) == sv.SV_ERRF_TOKEN | sv.SV_ERRF_NONFINITE
+    assert int(ws.count_nonzero().item()) == 0
+    acc = _np(out["accept_len"])
+    assert acc[1] == -1 and acc[2] == -1
+    good = [0, 3]
+    _compare({k: v[good] for k, v in out.items() if k != "err_flags"}, {k: v[good] for k, v in ref.items()},
+             cfg.name + " (clean sequences)")
+
+
 def _chi2_ok(counts, probs, label, min_expected=5.0):
     from scipy import stats
     n = counts.sum()
