@@ -42,11 +42,11 @@ N_SETS = 3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "rejection_sampling_verification_sv_amd", "csrc")
 KERNEL_SOURCES = {
-    "chain": ["sv_chain.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
+    "chain": ["sv_chain.hip", "sv_stream.h", "sv_device.h", "sv_internal.h", "sv_api.hip"],
     "sample": ["sv_sample.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
     "tree": ["sv_tree.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
-    # the counted kernel is the run-record stream; the walk (sv_tree_sample.hip) is not part of it
-    "treesample": ["sv_sample.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
+    # the counted kernel is the statistics stream of sv_tree_sample.hip (the walk shares the file)
+    "treesample": ["sv_tree_sample.hip", "sv_stream.h", "sv_device.h", "sv_internal.h", "sv_api.hip"],
 }
 
 
@@ -251,7 +251,7 @@ def main():
         config = {"workload": cfg.name + ("_graph" if args.graph else ""), "B": B, "N": N, "V": V,
                   "logits": cfg.dtype, "temperature": cfg.temperature, "branching": list(cfg.branching),
                   "input_sets_rotated": len(sets)}
-        kernel_name = "sample_stream_kernel (one pass over every target and draft row: a record per run of 128 vectors)"
+        kernel_name = "tree_stats_kernel (one pass over every target and draft row: a record per row chunk)"
     elif kind == "sample":
         cfg = CHAIN_CONFIGS[SAMPLE_WORKLOADS[wl]]
         R, V = cfg.B * cfg.K, cfg.V

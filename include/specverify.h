@@ -253,8 +253,9 @@ sv_status sv_verify_tree_greedy(const void* target_logits, sv_dtype dtype,
  * Sampling verification of a candidate tree.
  *
  * Bytes of device workspace sv_verify_tree_sampling needs (one 8-byte record
- * per 128 16-byte vectors of each target and draft row, two 8-byte exchange
- * slots per such run of each sequence, B + 2 counters and an abort flag);
+ * per statistics chunk of each target and draft row, whole rows cut into
+ * about 8192 chunks per call; two 8-byte exchange slots per run of 128
+ * 16-byte vectors of each sequence; B + 2 counters and an abort flag);
  * 0 for invalid sizes. Same zero-fill contract as the chain workspace (a
  * call leaves it all zero; after SV_ERRF_INTERNAL it must be zero-filled
  * again).

@@ -167,19 +167,24 @@ bool tree_sampling_rows(int32_t B, int32_t N, int64_t* rows) {
   return *rows <= INT32_MAX;
 }
 
-// Workspace of a sampling-tree call: the run records, then the walk's
-// exchange slots (two per run of each sequence), counters and abort flag.
+// Workspace of a sampling-tree call: the statistics records (nrec chunks of
+// every target and draft row), then the walk's exchange slots (two per run of
+// each sequence), counters and abort flag.
 struct TreeSamplingLayout {
-  RunLayout runs;
+  int32_t nrun, nrec;
   size_t off_slots, off_cnt, off_abort, total;
 };
 
 TreeSamplingLayout tree_sampling_layout(int32_t B, int32_t N, int32_t V, sv_dtype d) {
   TreeSamplingLayout L{};
-  L.runs = run_layout(static_cast<int32_t>(2LL * B * (N + 1)), V, d);
-  size_t off = L.runs.total;
+  const int64_t rows = 2LL * B * (N + 1);
+  const int64_t nvec = row_vecs(V, d);
+  L.nrun = static_cast<int32_t>(ceil_div(nvec, sv::kRunVecs));
+  L.nrec = static_cast<int32_t>(ceil_div(nvec, row_chunk_vecs(1, static_cast<int32_t>(rows), V, d,
+                                                              sv::kChunksTreeSample)));
+  size_t off = align_up(sizeof(uint64_t) * rows * L.nrec);
   L.off_slots = off;
-  off = align_up(off + sizeof(uint64_t) * 2 * static_cast<int64_t>(B) * L.runs.nrun);
+  off = align_up(off + sizeof(uint64_t) * 2 * static_cast<int64_t>(B) * L.nrun);
   L.off_cnt = off;
   off = align_up(off + sizeof(uint32_t) * (static_cast<int64_t>(B) + 2));
   L.off_abort = off;
@@ -414,26 +419,11 @@ sv_status sv_verify_tree_sampling(const void* target_logits, const void* draft_l
   if (!aligned_to(target_logits, dtype_bytes(dtype)) || !aligned_to(draft_logits, dtype_bytes(dtype)))
     return SV_ERR_INVALID_ARGUMENT;
   const TreeSamplingLayout TL = tree_sampling_layout(B, N, V, dtype);
-  const RunLayout& L = TL.runs;
   if (workspace == nullptr || workspace_bytes < TL.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
   // the walk reads rows as 16-byte vectors and keeps one total per run in LDS
   if (!whole_vector_rows(V, dtype) || !aligned_to(target_logits, 16) || !aligned_to(draft_logits, 16) ||
-      L.nrun > sv::kMaxWalkRuns || rows * L.cps > INT32_MAX)
+      TL.nrun > sv::kMaxWalkRuns || rows * TL.nrec > INT32_MAX)
     return SV_ERR_UNSUPPORTED;
-
-  sv::SampleParams sp{};
-  sp.logits = target_logits;
-  sp.logits2 = draft_logits;
-  sp.R1 = B * (N + 1);
-  sp.temp_rows = N + 1;
-  sp.temperature = temperature;
-  sp.R = static_cast<int32_t>(rows);
-  sp.V = V;
-  sp.nvec = row_vecs(V, dtype);
-  sp.nrun = L.nrun;
-  sp.cps = L.cps;
-  sp.err_flags = err_flags;
-  sp.rec = static_cast<uint64_t*>(workspace);
 
   sv::TreeSampleParams p{};
   p.target = target_logits;
@@ -445,20 +435,21 @@ sv_status sv_verify_tree_sampling(const void* target_logits, const void* draft_l
   p.B = B;
   p.N = N;
   p.V = V;
-  p.nvec = sp.nvec;
-  p.nrun = L.nrun;
-  p.rec = sp.rec;
+  p.nvec = row_vecs(V, dtype);
+  p.nrun = TL.nrun;
+  p.nrec = TL.nrec;
+  p.rec = static_cast<uint64_t*>(workspace);
   p.accept_len = accept_len;
   p.path_nodes = path_nodes;
   p.next_token = next_token;
   p.err_flags = err_flags;
   char* ws = static_cast<char*>(workspace);
-  p.G = walk_groups(B, L.nrun);
+  p.G = walk_groups(B, TL.nrun);
   if (static_cast<int64_t>(B) * p.G > INT32_MAX) p.G = 1;
   p.slots = reinterpret_cast<uint64_t*>(ws + TL.off_slots);
   p.cnt = reinterpret_cast<uint32_t*>(ws + TL.off_cnt);
   p.abort = reinterpret_cast<uint64_t*>(ws + TL.off_abort);
-  return from_hip(sv::launch_tree_sample(sp, p, dtype, ev, stream));
+  return from_hip(sv::launch_tree_sample(p, dtype, ev, stream));
 }
 
 sv_status sv_time_next_stream_pass(hipEvent_t before, hipEvent_t after) {

@@ -121,8 +121,9 @@ struct TreeSampleParams {
   const float* uniforms;   // [B, N+1]
   int32_t B, N, V;
   int64_t nvec;            // 16-byte vectors per row
-  int32_t nrun;            // runs per row
-  uint64_t* rec;           // workspace [2 B (N+1), nrun]
+  int32_t nrun;            // runs of kRunVecs vectors per row (the walk's passes)
+  int32_t nrec;            // statistics records (row chunks) per row
+  uint64_t* rec;           // workspace [2 B (N+1), nrec]: (reference, sum) of chunk c of row r
   int32_t* accept_len;
   int32_t* path_nodes;
   int32_t* next_token;
@@ -136,6 +137,12 @@ struct TreeSampleParams {
 
 // Walk workgroups per sequence, at most.
 constexpr int kMaxWalkGroups = 8;
+// Statistics chunks per sampling-tree call, about (every row cut into the
+// same whole number of chunks).
+#ifndef SV_CHUNKS_TREE_SAMPLE
+#define SV_CHUNKS_TREE_SAMPLE 8192
+#endif
+constexpr int kChunksTreeSample = SV_CHUNKS_TREE_SAMPLE;
 
 // Runs per row the walk keeps totals of in LDS.
 constexpr int kMaxWalkRuns = 1024;
@@ -305,7 +312,7 @@ hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& 
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 // The run records of every row of `p` (the streaming kernel of launch_sample alone).
 hipError_t launch_sample_stream(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
-hipError_t launch_tree_sample(const SampleParams& sp, const TreeSampleParams& p, sv_dtype dtype,
+hipError_t launch_tree_sample(const TreeSampleParams& p, sv_dtype dtype,
                               const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,

@@ -16,9 +16,11 @@
 // at a leaf, one token is drawn from P by the inverse CDF (ascending token id,
 // the final uniform).
 //
-// Pass 1 — sample_stream_kernel (sv_sample.hip) over the target rows and the
-// draft rows of the call: one (reference, sum) record per run of kRunVecs
-// vectors of every row, one read of every logit.
+// Pass 1 — tree_stats_kernel over the target rows and the draft rows of the
+// call: every row cut into nrec equal chunks, one workgroup streaming each
+// with the chain's one-pass statistics (per-thread online maximum and sum,
+// fp64 block combine) into one (reference, sum) record; one read of every
+// logit.
 //
 // Pass 2 — tree_sample_walk_kernel, one 1024-thread workgroup per sequence,
 // all threads following the same walk (every decision is computed by every
@@ -39,6 +41,7 @@
 
 #include "sv_device.h"
 #include "sv_internal.h"
+#include "sv_stream.h"
 
 namespace sv {
 
@@ -309,6 +312,33 @@ __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nru
 
 }  // namespace
 
+// Pass 1: workgroup c of row r streams the vectors [c nvec / nrec,
+// (c + 1) nvec / nrec) of the row (target rows 0 .. B(N+1)-1, then the draft
+// rows) and writes its record: the largest fl(x * c_hi) over the chunk and
+// the fp64 sum of 2^(x c - reference), rounded to fp32.
+template <class T>
+__global__ __launch_bounds__(kStatsTPB) __attribute__((amdgpu_waves_per_eu(SV_STATS_WAVES, SV_STATS_WAVES))) void tree_stats_kernel(TreeSampleParams P) {
+  constexpr int NW = kStatsTPB / kWave;
+  __shared__ float s_redf[NW];
+  __shared__ double s_redd[NW];
+  const uint32_t nrec = static_cast<uint32_t>(P.nrec);
+  const uint32_t r = blockIdx.x / nrec;
+  const int64_t ch = static_cast<int64_t>(blockIdx.x - r * nrec);
+  const int64_t p0 = div_nonneg(ch * P.nvec, nrec);
+  const int64_t p1 = div_nonneg((ch + 1) * P.nvec, nrec);
+  const int64_t R1 = static_cast<int64_t>(P.B) * (P.N + 1);
+  const int64_t rr = (static_cast<int64_t>(r) < R1) ? static_cast<int64_t>(r) : static_cast<int64_t>(r) - R1;
+  const char* base = static_cast<const char*>(static_cast<int64_t>(r) < R1 ? P.target : P.draft);
+  const uint4* row = reinterpret_cast<const uint4*>(base + rr * P.nvec * 16);
+  LazyScale sc{P.temperature, static_cast<int>(rr / (P.N + 1)), false, Scale{}};
+  Running st{-INFINITY, 0.0f, 0.0f};
+  flat_piece_stats<T, kStatsTPB>(row, p0, p1, sc, st);
+  float MC;
+  double S;
+  block_combine<NW>(st, sc.get(), s_redf, s_redd, &MC, &S);
+  if (threadIdx.x == 0) P.rec[static_cast<int64_t>(r) * nrec + ch] = tag_run(MC, static_cast<float>(S));
+}
+
 template <class T>
 __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSampleParams P) {
   __shared__ int s_par[SV_MAX_TREE_NODES];
@@ -408,7 +438,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
         uint32_t e = 0u;
         float M;
         double Z;
-        row_norm_wave(P.rec + (wv == 0 ? rowt : rowd) * P.nrun, P.nrun, &M, &Z, &e);
+        row_norm_wave(P.rec + (wv == 0 ? rowt : rowd) * P.nrec, P.nrec, &M, &Z, &e);
         if (lane == 0) {
           s_M[wv] = M;
           s_Zr[wv] = Z;
@@ -536,7 +566,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
   if (G > 1) {
     __shared__ int s_flag;
     if (arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(G), &s_flag)) {
-      const int64_t per = N1 * P.nrun;
+      const int64_t per = N1 * P.nrec;
       uint64_t* rec_t = P.rec + static_cast<int64_t>(b) * per;
       uint64_t* rec_d = P.rec + (static_cast<int64_t>(P.B) + b) * per;
       for (int64_t i = tid; i < per; i += kWalkThreads) {
@@ -552,7 +582,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
       __hip_atomic_store(&P.cnt[P.B + 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
-    const int64_t per = N1 * P.nrun;
+    const int64_t per = N1 * P.nrec;
     uint64_t* rec_t = P.rec + static_cast<int64_t>(b) * per;
     uint64_t* rec_d = P.rec + (static_cast<int64_t>(P.B) + b) * per;
     for (int64_t i = tid; i < per; i += kWalkThreads) {
@@ -562,9 +592,13 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
   }
 }
 
-hipError_t launch_tree_sample(const SampleParams& sp, const TreeSampleParams& p, sv_dtype dtype, const PassEvents& ev,
-                              hipStream_t stream) {
-  const hipError_t e = launch_sample_stream(sp, dtype, ev, stream);
+hipError_t launch_tree_sample(const TreeSampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream) {
+  const uint32_t grid_a = static_cast<uint32_t>(2LL * p.B * (p.N + 1) * p.nrec);  // checked on the host
+  if (dtype == SV_DTYPE_BF16)
+    launch_stream_pass(tree_stats_kernel<BF16>, dim3(grid_a), dim3(kStatsTPB), stream, ev, p);
+  else
+    launch_stream_pass(tree_stats_kernel<F32>, dim3(grid_a), dim3(kStatsTPB), stream, ev, p);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const uint32_t grid = static_cast<uint32_t>(p.B) * static_cast<uint32_t>(p.G);
   if (dtype == SV_DTYPE_BF16)

@@ -137,10 +137,12 @@ def test_tree_sampling_argument_errors(lib):
     assert call(V=100) == UNS
     assert call(t=FAKE + 2) == UNS and call(d=FAKE + 2) == UNS
     assert call(B=1, N=1, V=1048584) == UNS
-    # one 8-byte record per run of 128 vectors of each of the 2 B (N+1) rows
+    # at least one 8-byte record per row of the 2 B (N+1) target and draft rows,
+    # and two 8-byte exchange slots per run of 128 vectors of each sequence
     for B, N, V, dt in ((32, 64, 128256, 1), (1, 1, 8, 1), (3, 5, 1000, 0)):
         ws = lib.sv_tree_sampling_workspace_bytes(B, N, V, dt)
-        assert ws >= 8 * 2 * B * (N + 1) * -(-(V * (2 if dt else 4) // 16) // 128)
+        nrun = -(-(V * (2 if dt else 4) // 16) // 128)
+        assert ws >= 8 * 2 * B * (N + 1) + 8 * 2 * B * nrun
     assert lib.sv_tree_sampling_workspace_bytes(4, 0, 128, 1) == 0
     assert lib.sv_tree_sampling_workspace_bytes(4, 8, 128, 9) == 0
 
