@@ -322,6 +322,40 @@ def test_split_walk_parity_and_workspace(sv):
              cfg.name + " (clean sequences)")
 
 
+def test_split_walks_on_concurrent_streams(sv):
+    # Two calls whose split walks together hold more workgroups than the GPU
+    # has compute units, launched on two streams at once: every wait must end
+    # and both must give the same outputs as when each runs alone.
+    base = SAMPLE_TREE_CONFIGS["c4s"]
+    cfg_a = base.with_(name="tree_sampling_concurrent_a", B=24, N=30, V=128256, variant=71)
+    cfg_b = base.with_(name="tree_sampling_concurrent_b", B=16, N=64, V=100000, variant=72)
+    inp_a = sample_tree_inputs(cfg_a, device="cuda")
+    inp_b = sample_tree_inputs(cfg_b, device="cuda")
+    _say("concurrent split walks: references")
+    ref_a = _call(sv, inp_a)
+    ref_b = _call(sv, inp_b)
+    assert int(ref_a["err_flags"].item()) == 0 and int(ref_b["err_flags"].item()) == 0
+    _compare(ref_a, _oracle(inp_a), cfg_a.name)
+    _compare(ref_b, _oracle(inp_b), cfg_b.name)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    _say("concurrent split walks: two streams")
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            oa = sv.sv_verify_tree_sampling(inp_a["target"], inp_a["draft"], inp_a["node_tokens"], inp_a["parents"],
+                                            inp_a["temperature"], inp_a["uniforms"], stream=s1)
+        with torch.cuda.stream(s2):
+            ob = sv.sv_verify_tree_sampling(inp_b["target"], inp_b["draft"], inp_b["node_tokens"], inp_b["parents"],
+                                            inp_b["temperature"], inp_b["uniforms"], stream=s2)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert int(oa["err_flags"].item()) == 0 and int(ob["err_flags"].item()) == 0
+        for k in ("accept_len", "path_nodes", "next_token"):
+            assert torch.equal(oa[k], ref_a[k]), k
+            assert torch.equal(ob[k], ref_b[k]), k
+
+
 def _chi2_ok(counts, probs, label, min_expected=5.0):
     from scipy import stats
     n = counts.sum()
