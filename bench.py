@@ -209,7 +209,7 @@ def cpu_baseline_sample(inp, cfg, budget_s: float) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); specverify runs on one GPU and has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
 
