@@ -342,9 +342,6 @@ sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temper
   if (static_cast<int64_t>(R) * L.cps > INT32_MAX) return SV_ERR_UNSUPPORTED;
   sv::SampleParams p{};
   p.logits = logits;
-  p.logits2 = nullptr;
-  p.R1 = R;
-  p.temp_rows = 1;
   p.temperature = temperature;
   p.uniforms = uniforms;
   p.R = R;

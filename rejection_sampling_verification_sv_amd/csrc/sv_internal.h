@@ -179,10 +179,7 @@ constexpr int kRunLaneVecs = kRunVecs / kWave;  // vectors per lane per run
 constexpr int kChunksSample = SV_CHUNKS_SAMPLE;
 
 struct SampleParams {
-  const void* logits;      // rows [0, R1)
-  const void* logits2;     // rows [R1, R) (the stream only; null when R1 == R)
-  int32_t R1;
-  int32_t temp_rows;       // rows per temperature entry: row r of either array uses temperature[r / temp_rows]
+  const void* logits;      // [R, V] rows; row r uses temperature[r]
   const float* temperature;
   const float* uniforms;
   int32_t R, V;
@@ -310,8 +307,6 @@ inline void launch_stream_pass(void (*kernel)(Params), dim3 grid, dim3 block, hi
 // stop events of the streaming pass.
 hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_sample(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
-// The run records of every row of `p` (the streaming kernel of launch_sample alone).
-hipError_t launch_sample_stream(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree_sample(const TreeSampleParams& p, sv_dtype dtype,
                               const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);

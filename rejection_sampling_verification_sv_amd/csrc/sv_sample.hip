@@ -33,7 +33,6 @@ namespace sv {
 namespace {
 
 __device__ __forceinline__ const uint4* sample_row(const SampleParams& P, int64_t r, int eb) {
-  if (r >= P.R1) return reinterpret_cast<const uint4*>(static_cast<const char*>(P.logits2) + (r - P.R1) * P.V * eb);
   return reinterpret_cast<const uint4*>(static_cast<const char*>(P.logits) + r * P.V * eb);
 }
 
@@ -122,8 +121,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8))
   uint64_t* rec = P.rec + static_cast<int64_t>(r) * P.nrun;
   uint4 a[kRunLaneVecs], b[kRunLaneVecs];
   load_run<T>(row, g0, P.nvec, a);
-  const uint32_t rr = (r >= static_cast<uint32_t>(P.R1)) ? r - static_cast<uint32_t>(P.R1) : r;
-  const Scale c = exponent_scale(temperature_of(P.temperature, static_cast<int>(rr / static_cast<uint32_t>(P.temp_rows))));
+  const Scale c = exponent_scale(temperature_of(P.temperature, static_cast<int>(r)));
   // invariant: `a` holds this wave's run i - 1
   int32_t i = 1;
 #pragma unroll 1
@@ -325,11 +323,6 @@ static hipError_t launch_sample_stream_t(const SampleParams& p, const PassEvents
   // Armed events take the streaming kernel's own start and end timestamps.
   launch_stream_pass(sample_stream_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), stream, ev, p);
   return hipGetLastError();
-}
-
-hipError_t launch_sample_stream(const SampleParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream) {
-  return dtype == SV_DTYPE_BF16 ? launch_sample_stream_t<BF16>(p, ev, stream)
-                                : launch_sample_stream_t<F32>(p, ev, stream);
 }
 
 template <class T>
