@@ -223,6 +223,27 @@ def test_max_width_star(sv):
     _structure(out, parents, N, cfg.V)
 
 
+def test_max_width_star_split_walk(sv):
+    # SV_MAX_TREE_NODES children of the root on long rows: the walk is shared by
+    # eight workgroups and exchanges run totals after each of hundreds of
+    # rejections (both slot buffers, pass numbers past a thousand)
+    N = sv.SV_MAX_TREE_NODES
+    parents = np.full(N, -1, dtype=np.int32)
+    cfg = SAMPLE_TREE_CONFIGS["c4s"].with_(name="tree_sampling_max_width_split", B=1, N=N, V=128256, dtype="bf16",
+                                           target_sigma=1.0, draft_sigma=3.0, variant=13)
+    inp = sample_tree_inputs(cfg, device="cuda", parents=parents)
+    ws = torch.zeros(sv.sv_tree_sampling_workspace_bytes(cfg.B, N, cfg.V, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    _say("max-width star, split walk")
+    out = _call(sv, inp, workspace_tensor=ws)
+    assert int(out["err_flags"].item()) == 0
+    assert int(ws.count_nonzero().item()) == 0
+    _structure(out, parents, N, cfg.V)
+    ref = _oracle(inp)
+    print(f"children tested {int(ref['tests'].sum())}", flush=True)
+    _compare(out, ref, cfg.name)
+
+
 def test_temperature_none_is_one(sv):
     cfg = SAMPLE_TREE_CONFIGS["c4s"].with_(name="tree_sampling_t1", B=8, N=10, V=2048, variant=21)
     inp = sample_tree_inputs(cfg, device="cuda")
