@@ -12,6 +12,8 @@ from .specverify_oracle import (  # noqa: F401
     inverse_cdf,
     sample_rows,
     verify_chain,
+    verify_chain_distributions,
+    chain_rows_valid,
     node_depths,
     verify_tree_greedy,
     verify_tree_stochastic,

@@ -185,36 +185,76 @@ def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniform
     5. Output: x_0..x_{j-1}, then the drawn token: between 1 and K+1 tokens
        ([Draft-and-Verify] loop).
 
+    Step 1 is done here; steps 2 to 5 by :func:`verify_chain_distributions`,
+    which also serves callers that verify the same distributions with several
+    sets of uniforms.
+
     Returns a dict of numpy arrays: ``accept_len [B]`` (j, or -1 for an invalid
     row), ``out_tokens [B, K+1]`` (-1 after position j), ``p_draft``,
     ``q_draft [B, K]`` (p_k(x_k), q_k(x_k) for every k), ``residual_mass [B]``
     (sum max(0, p_j - q_j), -1 when all K are accepted), with ``with_entropy``
     ``entropy [B, 2K+1]`` (the entropy in nats of p_0 .. p_K, then of
-    q_0 .. q_{K-1}), and diagnostics:
-    ``alpha [B, K]``, ``margin_accept [B, K]`` (|u_k - alpha_k| for the checked
-    positions, +inf for the others), ``margin_sample [B]`` (distance of u_K to
-    the nearest CDF boundary of the drawn token), ``flagged [B]`` (a margin
-    below FLAG_WINDOW), ``valid [B]``.
+    q_0 .. q_{K-1}), and the diagnostics listed under
+    :func:`verify_chain_distributions`.
     """
     t = np.asarray(target_logits, dtype=np.float64)
     d = np.asarray(draft_logits, dtype=np.float64)
     x = np.asarray(draft_tokens, dtype=np.int64)
     T = np.asarray(temperature, dtype=np.float64)
-    u = np.asarray(uniforms, dtype=np.float64)
     B, K1, V = t.shape
     K = K1 - 1
-    if d.shape != (B, K, V) or x.shape != (B, K) or T.shape != (B,) or u.shape != (B, K1):
+    if d.shape != (B, K, V) or x.shape != (B, K) or T.shape != (B,):
         raise ValueError("inconsistent shapes")
-
-    valid = np.isfinite(T) & (T > 0)
-    if K:
-        valid &= np.all((x >= 0) & (x < V), axis=1)
+    valid = chain_rows_valid(x, T, V)
     T_safe = np.where(valid, T, 1.0)
-    x_safe = np.where((x >= 0) & (x < V), x, 0)
 
     # 1. target and draft distributions at every position
     p = temperature_softmax(t, T_safe[:, None])  # [B, K+1, V]
     q = temperature_softmax(d, T_safe[:, None])  # [B, K, V]
+    res = verify_chain_distributions(p, q, x, uniforms, valid)
+    if with_entropy:  # per-position entropy of every distribution of the step
+        res["entropy"] = np.concatenate([entropy(p), entropy(q)], axis=1)
+    return res
+
+
+def chain_rows_valid(draft_tokens, temperature, V):
+    """Rows the library verifies (reading 8): a positive finite temperature and
+    every drafted token in [0, V)."""
+    x = np.asarray(draft_tokens, dtype=np.int64)
+    T = np.asarray(temperature, dtype=np.float64)
+    valid = np.isfinite(T) & (T > 0)
+    if x.shape[1]:
+        valid &= np.all((x >= 0) & (x < V), axis=1)
+    return valid
+
+
+def verify_chain_distributions(p, q, draft_tokens, uniforms, valid):
+    """Steps 2 to 5 of :func:`verify_chain` on given distributions.
+
+    ``p [B, K+1, V]`` and ``q [B, K, V]`` are the target and draft
+    distributions (step 1), ``draft_tokens [B, K]``, ``uniforms [B, K+1]``,
+    ``valid [B]`` (see :func:`chain_rows_valid`). Returns the outputs of
+    :func:`verify_chain` and these diagnostics: ``alpha [B, K]``,
+    ``margin_accept [B, K]`` (|u_k - alpha_k| for the checked positions, +inf
+    for the others), ``margin_sample [B]`` (distance of u_K to the nearest CDF
+    boundary of the drawn token), ``flagged [B]`` (a margin below
+    FLAG_WINDOW), ``valid [B]``, and ``flag_rate [B]``: for uniforms drawn
+    afresh, about how likely a row with this j is to be flagged: for each
+    checked accept test the length of [alpha_k - FLAG_WINDOW, alpha_k +
+    FLAG_WINDOW] inside [0, 1), plus, for the draw, sum_v min(w_v / sum(w),
+    2 FLAG_WINDOW) over the normalised sampling weights (the chance that u_K
+    lands within the window of a boundary of the token it selects).
+    """
+    p = np.asarray(p, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    x = np.asarray(draft_tokens, dtype=np.int64)
+    u = np.asarray(uniforms, dtype=np.float64)
+    valid = np.asarray(valid, dtype=bool)
+    B, K1, V = p.shape
+    K = K1 - 1
+    if q.shape != (B, K, V) or x.shape != (B, K) or u.shape != (B, K1) or valid.shape != (B,):
+        raise ValueError("inconsistent shapes")
+    x_safe = np.where((x >= 0) & (x < V), x, 0)
 
     # 2. acceptance probability of each drafted token
     bi = np.arange(B)[:, None]
@@ -250,11 +290,16 @@ def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniform
     margin_accept = np.where(checked, np.abs(u[:, :K] - alpha), np.inf)
     margin_sample = np.minimum(u[:, K] - lo_u, hi_u - u[:, K])
     flagged = (margin_accept.min(axis=1, initial=np.inf) < FLAG_WINDOW) | (margin_sample < FLAG_WINDOW)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        wsum = weights.sum(axis=1, keepdims=True)
+        wn = np.where(wsum > 0, weights / np.where(wsum > 0, wsum, 1.0), 0.0)
+    window = np.minimum(alpha + FLAG_WINDOW, 1.0) - np.maximum(alpha - FLAG_WINDOW, 0.0)  # inside [0, 1)
+    flag_rate = np.minimum(wn, 2 * FLAG_WINDOW).sum(axis=1) + np.where(checked, window, 0.0).sum(axis=1)
 
     accept_len = np.where(valid, j, -1).astype(np.int64)
     out[~valid] = -1
     residual_mass[~valid] = -1.0
-    res = {
+    return {
         "accept_len": accept_len,
         "out_tokens": out,
         "p_draft": p_x,
@@ -264,11 +309,9 @@ def verify_chain(target_logits, draft_logits, draft_tokens, temperature, uniform
         "margin_accept": margin_accept,
         "margin_sample": margin_sample,
         "flagged": flagged & valid,
+        "flag_rate": np.where(valid, flag_rate, 0.0),
         "valid": valid,
     }
-    if with_entropy:  # per-position entropy of every distribution of the step
-        res["entropy"] = np.concatenate([entropy(p), entropy(q)], axis=1)
-    return res
 
 
 # ----------------------------------------------------------------------------- tree verification

@@ -3,14 +3,18 @@
 Each ``sv_*`` function here has the name of the C entry point it calls. It
 checks that the tensors are contiguous device tensors of the expected dtype
 and shape, allocates outputs (and a zero-filled workspace) with PyTorch when
-the caller does not pass them, and forwards raw device pointers and the
-current HIP stream. Every step of the computation runs in the library's HIP
+the caller does not pass them, and forwards raw device pointers and the HIP
+stream of the call (``stream=``, default: the current stream). Everything the
+binding allocates or zero-fills for a call is enqueued on that same stream,
+so it is ordered before the call's kernels. Every step of the computation runs in the library's HIP
 kernels; there is no CPU or PyTorch fallback: a missing library or a CPU
 tensor raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 import threading
 from typing import Dict, Optional
@@ -137,6 +141,49 @@ def _stream_handle(device, stream) -> int:
     return s.cuda_stream
 
 
+@contextlib.contextmanager
+def _on_call_stream(device, stream):
+    """Make the call's stream current for the body: the binding's allocations,
+    zero-fills and the library's launches are then all ordered on it (the
+    caching allocator also ties every tensor allocated here to that stream).
+    Yields (call stream, the stream that was current before)."""
+    outer = torch.cuda.current_stream(device)
+    s = outer if stream is None else stream
+    with torch.cuda.stream(s):
+        yield s, outer
+
+
+def _used_on(s, outer, tensors) -> None:
+    """Caller tensors read or written on a stream other than the caller's
+    current one: tell the caching allocator, so that freeing them on the
+    caller's side cannot hand their memory out while the call still runs."""
+    if s == outer:
+        return
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.device.type == "cuda":
+            t.record_stream(s)
+
+
+def _stream_ordered(fn):
+    """Run a binding call with its ``stream=`` argument (default: the current
+    stream) made current, so that the outputs, err_flags and workspace the
+    binding allocates and zero-fills are ordered before the library's
+    kernels on that stream; then record that stream on every tensor argument
+    when it is not the caller's current one."""
+
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        first = args[0] if args else None
+        if not isinstance(first, torch.Tensor) or first.device.type != "cuda":
+            return fn(*args, stream=stream, **kw)  # the body raises the argument error
+        with _on_call_stream(first.device, stream) as (s, outer):
+            out = fn(*args, stream=s, **kw)
+            _used_on(s, outer, list(args) + list(kw.values()))
+        return out
+
+    return call
+
+
 def sv_time_next_stream_pass(before: Optional[torch.cuda.Event], after: Optional[torch.cuda.Event]) -> None:
     """Arm this thread's next chain / tree call to launch its streaming pass with
     ``before`` and ``after`` as start / stop events (both None disarms).
@@ -160,26 +207,37 @@ def sv_time_next_stream_pass(before: Optional[torch.cuda.Event], after: Optional
 # workspace to all-zero counters at the end of each call, so a workspace can
 # be reused by the next call on the same stream. A call whose err_flags show
 # SV_ERRF_INTERNAL leaves it dirty: reset_workspaces() zero-fills them again.
-_workspaces: Dict[tuple, torch.Tensor] = {}
+# Each entry is (workspace, the stream it serves); the workspace is allocated
+# and zero-filled on that stream, so the fill is ordered before the first
+# kernel that uses it, and a workspace replaced by a larger one is only
+# handed out again by the caching allocator to work ordered after its last
+# use on that stream.
+_workspaces: Dict[tuple, tuple] = {}
 
 
 def reset_workspaces() -> None:
     """Zero-fill every cached workspace (after a call raised SV_ERRF_INTERNAL).
 
-    Each fill is ordered on the current stream of its device; call it from the
-    stream the workspaces serve, or synchronise first.
+    Each fill is enqueued on the stream its workspace serves, behind the
+    calls already enqueued there.
     """
-    for ws in _workspaces.values():
-        ws.zero_()
+    for ws, s in _workspaces.values():
+        with torch.cuda.stream(s):
+            ws.zero_()
 
 
 def workspace(device, nbytes: int, stream=None) -> torch.Tensor:
-    key = (torch.device(device).index, _stream_handle(device, stream))
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
-    return ws
+    """The cached zero-filled workspace of (device, stream) with at least
+    ``nbytes`` bytes (``stream`` None: the device's current stream)."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (torch.device(device).index, s.cuda_stream)
+    ent = _workspaces.get(key)
+    if ent is None or ent[0].numel() < nbytes:
+        with torch.cuda.stream(s):
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = (ws, s)
+        return ws
+    return ent[0]
 
 
 def sv_chain_workspace_bytes(B: int, K: int, V: int, dtype: torch.dtype) -> int:
@@ -190,6 +248,7 @@ def sv_tree_workspace_bytes(B: int, N: int, V: int, dtype: torch.dtype) -> int:
     return int(_load().sv_tree_workspace_bytes(B, N, V, _DTYPES[dtype]))
 
 
+@_stream_ordered
 def sv_verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
                     temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
                     accept_len=None, out_tokens=None, p_draft=None, q_draft=None, residual_mass=None,
@@ -250,6 +309,7 @@ def sv_sample_workspace_bytes(R: int, V: int, dtype: torch.dtype) -> int:
     return int(_load().sv_sample_workspace_bytes(R, V, _DTYPES[dtype]))
 
 
+@_stream_ordered
 def sv_sample_rows(logits: torch.Tensor, temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
                    out_tokens=None, out_prob=None, err_flags=None, workspace_tensor=None, stream=None,
                    want_prob: bool = True) -> dict:
@@ -288,6 +348,7 @@ def sv_sample_rows(logits: torch.Tensor, temperature: Optional[torch.Tensor], un
     return out
 
 
+@_stream_ordered
 def sv_verify_tree_greedy(target: torch.Tensor, node_tokens: torch.Tensor, parents: torch.Tensor, *,
                           accept_len=None, path_nodes=None, next_token=None, err_flags=None,
                           workspace_tensor=None, stream=None) -> dict:
@@ -321,6 +382,7 @@ def sv_tree_sampling_workspace_bytes(B: int, N: int, V: int, dtype: torch.dtype)
     return int(_load().sv_tree_sampling_workspace_bytes(B, N, V, _DTYPES[dtype]))
 
 
+@_stream_ordered
 def sv_verify_tree_sampling(target: torch.Tensor, draft: torch.Tensor, node_tokens: torch.Tensor,
                             parents: torch.Tensor, temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
                             accept_len=None, path_nodes=None, next_token=None, err_flags=None,
@@ -362,6 +424,7 @@ def sv_verify_tree_sampling(target: torch.Tensor, draft: torch.Tensor, node_toke
     return {"accept_len": accept_len, "path_nodes": path_nodes, "next_token": next_token, "err_flags": err_flags}
 
 
+@_stream_ordered
 def sv_build_tree_mask(parents: torch.Tensor, *, mask=None, err_flags=None, stream=None) -> dict:
     """Tree ancestor mask (``sv_build_tree_mask``): uint8 ``[N, N]``."""
     lib = _load()
@@ -385,8 +448,8 @@ class PreparedChainCall:
     passed at construction are kept alive and reused by every call.
     """
 
-    def __init__(self, target, draft, draft_tokens, temperature, uniforms, *, stream=None, want_probs=True,
-                 want_entropy=False):
+    def _init(self, target, draft, draft_tokens, temperature, uniforms, *, stream=None, want_probs=True,
+              want_entropy=False):
         B, K1, V = target.shape
         K = K1 - 1
         dev = target.device
@@ -417,6 +480,14 @@ class PreparedChainCall:
             _ptr(o.get("residual_mass")), _ptr(o.get("entropy")), _ptr(o["err_flags"]), _ptr(self._ws),
             self._ws.numel(), _stream_handle(dev, stream))
 
+    def __init__(self, *args, stream=None, **kw):
+        # outputs and the workspace are allocated and zero-filled on the
+        # stream the calls will run on (the caller's current one by default)
+        first = args[0]
+        with _on_call_stream(first.device, stream) as (s, outer):
+            self._init(*args, stream=s, **kw)
+            _used_on(s, outer, list(args))
+
     def __call__(self):
         st = self._fn(*self._args)
         if st != SV_OK:
@@ -428,7 +499,7 @@ class PreparedSampleCall:
     """``sv_sample_rows`` with every argument checked and marshalled once
     (calling the object only enqueues the kernels)."""
 
-    def __init__(self, logits, temperature, uniforms, *, stream=None, want_prob=True):
+    def _init(self, logits, temperature, uniforms, *, stream=None, want_prob=True):
         R, V = logits.shape
         dev = logits.device
         self.out = {"tokens": torch.empty((R,), dtype=torch.int32, device=dev),
@@ -446,6 +517,14 @@ class PreparedSampleCall:
                       _ptr(o.get("prob")), _ptr(o["err_flags"]), _ptr(self._ws), self._ws.numel(),
                       _stream_handle(dev, stream))
 
+    def __init__(self, *args, stream=None, **kw):
+        # outputs and the workspace are allocated and zero-filled on the
+        # stream the calls will run on (the caller's current one by default)
+        first = args[0]
+        with _on_call_stream(first.device, stream) as (s, outer):
+            self._init(*args, stream=s, **kw)
+            _used_on(s, outer, list(args))
+
     def __call__(self):
         st = self._fn(*self._args)
         if st != SV_OK:
@@ -457,7 +536,7 @@ class PreparedTreeCall:
     """``sv_verify_tree_greedy`` with every argument checked and marshalled once
     (the tree counterpart of :class:`PreparedChainCall`)."""
 
-    def __init__(self, target, node_tokens, parents, *, stream=None):
+    def _init(self, target, node_tokens, parents, *, stream=None):
         B, N1, V = target.shape
         N = N1 - 1
         dev = target.device
@@ -480,6 +559,14 @@ class PreparedTreeCall:
             _ptr(o["accept_len"]), _ptr(o["path_nodes"]), _ptr(o["next_token"]), _ptr(o["err_flags"]),
             _ptr(self._ws), self._ws.numel(), _stream_handle(dev, stream))
 
+    def __init__(self, *args, stream=None, **kw):
+        # outputs and the workspace are allocated and zero-filled on the
+        # stream the calls will run on (the caller's current one by default)
+        first = args[0]
+        with _on_call_stream(first.device, stream) as (s, outer):
+            self._init(*args, stream=s, **kw)
+            _used_on(s, outer, list(args))
+
     def __call__(self):
         st = self._fn(*self._args)
         if st != SV_OK:
@@ -491,7 +578,7 @@ class PreparedTreeSamplingCall:
     """``sv_verify_tree_sampling`` with every argument checked and marshalled
     once (calling the object only enqueues the kernels)."""
 
-    def __init__(self, target, draft, node_tokens, parents, temperature, uniforms, *, stream=None):
+    def _init(self, target, draft, node_tokens, parents, temperature, uniforms, *, stream=None):
         B, N1, V = target.shape
         N = N1 - 1
         dev = target.device
@@ -514,6 +601,14 @@ class PreparedTreeSamplingCall:
             _ptr(target), _ptr(draft), code, _ptr(node_tokens), _ptr(parents), _ptr(temperature), _ptr(uniforms),
             B, N, V, _ptr(o["accept_len"]), _ptr(o["path_nodes"]), _ptr(o["next_token"]), _ptr(o["err_flags"]),
             _ptr(self._ws), self._ws.numel(), _stream_handle(dev, stream))
+
+    def __init__(self, *args, stream=None, **kw):
+        # outputs and the workspace are allocated and zero-filled on the
+        # stream the calls will run on (the caller's current one by default)
+        first = args[0]
+        with _on_call_stream(first.device, stream) as (s, outer):
+            self._init(*args, stream=s, **kw)
+            _used_on(s, outer, list(args))
 
     def __call__(self):
         st = self._fn(*self._args)

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from parity import REL_TOL, to_np64, to_np_i
+from parity import REL_TOL, record_parity, to_np64, to_np_i
 from workloads import CHAIN_CONFIGS, sample_inputs
 
 pytestmark = pytest.mark.gpu
@@ -40,10 +40,20 @@ def _expected_flagged(logits, temperature):
     return total
 
 
-def _compare(out, logits, temperature, uniforms):
+def _oracle_rows(logits, temperature, uniforms, per=256):
+    """The oracle's draft-side sampling, `per` rows at a time."""
+    parts = []
+    for r0 in range(0, logits.shape[0], per):
+        r1 = min(logits.shape[0], r0 + per)
+        parts.append(oracle.sample_rows(to_np64(logits[r0:r1]),
+                                        None if temperature is None else to_np64(temperature[r0:r1]),
+                                        to_np64(uniforms[r0:r1])))
+    return tuple(np.concatenate([p[i] for p in parts]) for i in range(4))
+
+
+def _compare(out, logits, temperature, uniforms, record=None):
     """Tokens exact outside the flag window, q(token) to REL_TOL; returns (rows, flagged)."""
-    t_ref, p_ref, lo, hi = oracle.sample_rows(to_np64(logits), None if temperature is None else to_np64(temperature),
-                                              to_np64(uniforms))
+    t_ref, p_ref, lo, hi = _oracle_rows(logits, temperature, uniforms)
     u = to_np64(uniforms)
     flagged = (np.abs(u - lo) < oracle.FLAG_WINDOW) | (np.abs(hi - u) < oracle.FLAG_WINDOW)
     tok = to_np_i(out["tokens"])
@@ -54,6 +64,12 @@ def _compare(out, logits, temperature, uniforms):
     rel = np.abs(prob[same] - p_ref[same]) / np.maximum(p_ref[same], 1e-30)
     assert rel.max(initial=0.0) <= REL_TOL, f"max relative error of q(token) {rel.max()}"
     expected = _expected_flagged(logits, temperature)
+    if record is not None:
+        margin = np.minimum(u - lo, hi - u)
+        record_parity(record, call="sv_sample_rows", rows=len(u), flagged=int(flagged.sum()),
+                      expected_flagged=expected, mismatched_unflagged=int(bad.sum()),
+                      mismatched_flagged=int((~same & flagged).sum()), max_rel_prob=float(rel.max(initial=0.0)),
+                      min_margin=float(margin.min()))
     assert flagged.sum() <= 3 * expected + 3, f"{flagged.sum()} flagged rows, about {expected:.1f} expected"
     assert np.all((tok >= 0) & (tok < logits.shape[1]))
     return len(u), int(flagged.sum())
@@ -72,21 +88,22 @@ def test_draft_rows_of_the_chain_workloads(sv, name):
     inp = sample_inputs(cfg, device="cuda")
     out = _run(sv, inp)
     assert int(out["err_flags"].item()) == 0
-    rows, flagged = _compare(out, inp["logits"], inp["temperature"], inp["uniforms"])
+    rows, flagged = _compare(out, inp["logits"], inp["temperature"], inp["uniforms"],
+                             record=f"sample_rows_of_{cfg.name}")
     print(name, "rows", rows, "flagged", flagged, flush=True)
 
 
-def test_c3_draft_rows_sampled(sv):
-    # 2048 rows of V = 152064 with per-row temperatures U[0.3, 1.3]; the oracle
-    # checks a sample of 256 rows
+def test_c3_draft_rows_full(sv):
+    # all 2048 rows of V = 152064 with per-row temperatures U[0.3, 1.3]
     cfg = CHAIN_CONFIGS["c3_s1.0"]
     _say("sample rows of", cfg.name, "B*K =", cfg.B * cfg.K, "V =", cfg.V)
     inp = sample_inputs(cfg, device="cuda")
     out = _run(sv, inp)
     assert int(out["err_flags"].item()) == 0
-    rows = torch.from_numpy(np.random.Generator(np.random.Philox(5)).choice(cfg.B * cfg.K, 256, replace=False))
-    sub = {"tokens": out["tokens"][rows.cuda()], "prob": out["prob"][rows.cuda()]}
-    _compare(sub, inp["logits"][rows.cuda()], inp["temperature"][rows.cuda()], inp["uniforms"][rows.cuda()])
+    rows, flagged = _compare(out, inp["logits"], inp["temperature"], inp["uniforms"],
+                             record=f"sample_rows_of_{cfg.name}")
+    assert rows == cfg.B * cfg.K
+    print(cfg.name, "rows", rows, "flagged", flagged, flush=True)
 
 
 def test_law_of_the_drawn_token(sv):

@@ -4,6 +4,7 @@ import pytest
 import torch
 
 import oracle
+from parity import record_parity
 from workloads import TREE_CONFIGS, tree_inputs, tree_parents_ranked
 
 pytestmark = pytest.mark.gpu
@@ -49,6 +50,16 @@ def test_c4_full(sv):
     t = _np(inp["target"].float())
     ties = sum(int((t[b, n] == t[b, n, g[b, n]]).sum() > 1) for b in range(cfg.B) for n in range(cfg.N + 1))
     print(cfg.name, "positions with a tied maximum:", ties, flush=True)
+    mask = sv.sv_build_tree_mask(inp["parents"])
+    torch.cuda.synchronize()
+    mask_same = bool(np.array_equal(_np(mask["mask"]), oracle.tree_mask(_np(inp["parents"]))))
+    assert mask_same
+    record_parity(cfg.name, call="sv_verify_tree_greedy + sv_build_tree_mask", rows=cfg.B,
+                  mismatched=int((_np(out["accept_len"]) != ref["accept_len"]).sum()
+                                 + (_np(out["path_nodes"]) != ref["path_nodes"]).any(axis=1).sum()
+                                 + (_np(out["next_token"]) != ref["next_token"]).sum()),
+                  positions_with_tied_maximum=ties, mask_bit_exact=mask_same,
+                  mask_bytes=int(cfg.N * cfg.N), mean_accept_len=float(mean_len))
 
 
 def _random_tree(rng, N, p_root=0.15):

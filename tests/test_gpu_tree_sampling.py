@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle
+from parity import record_parity
 from workloads import SAMPLE_TREE_CONFIGS, sample_draft_tokens_gumbel, sample_tree_inputs, seed_stream
 
 pytestmark = pytest.mark.gpu
@@ -103,8 +104,13 @@ def test_c4s_full(sv):
     assert int(out["err_flags"].item()) == 0
     ref = _oracle(inp)
     assert ref["valid"].all()
-    _compare(out, ref, cfg.name)
+    same = _compare(out, ref, cfg.name)
     _structure(out, _np(inp["parents"]), cfg.N, cfg.V)
+    record_parity(cfg.name, call="sv_verify_tree_sampling", rows=cfg.B, flagged=int(ref["flagged"].sum()),
+                  mismatched_unflagged=int((~same & ~ref["flagged"]).sum()),
+                  mismatched_flagged=int((~same & ref["flagged"]).sum()),
+                  min_margin=float(ref["margin"].min()), mean_accept_len=float(ref["accept_len"].mean()),
+                  children_tested=int(ref["tests"].sum()))
     assert 0.5 < ref["accept_len"].mean() < 5.0
 
 
@@ -377,7 +383,7 @@ def test_split_walks_on_concurrent_streams(sv):
             assert torch.equal(ob[k], ref_b[k]), k
 
 
-def _chi2_ok(counts, probs, label, min_expected=5.0):
+def _chi2_ok(counts, probs, label, level, pvals, min_expected=5.0):
     from scipy import stats
     n = counts.sum()
     exp = probs * n
@@ -391,15 +397,19 @@ def _chi2_ok(counts, probs, label, min_expected=5.0):
     obs, ex = obs[keep], ex[keep]
     ex = ex * obs.sum() / ex.sum()
     p = stats.chisquare(obs, ex).pvalue
-    print(f"{label}: n {int(n)}, categories {len(obs)}, chi-square p-value {p:.3g}", flush=True)
-    return p > 1e-6
+    print(f"{label}: n {int(n)}, categories {len(obs)}, chi-square p-value {p:.3g} (bar {level:.3g})", flush=True)
+    pvals.append(float(p))
+    return p > level
 
 
 @pytest.mark.slow
 def test_monte_carlo_losslessness(sv):
     # one tree and one pair of logit tensors shared by every sequence; the
-    # sequences differ in their drafted node tokens and uniforms
-    B = 1 << 16
+    # sequences differ in their drafted node tokens and uniforms. Four
+    # chi-square tests at an overall level of 0.01 (Bonferroni: each p-value
+    # must exceed 0.0025).
+    B = 1 << 20
+    level = 0.01 / 4
     parents = np.array([-1, -1, -1, 0, 0, 1], dtype=np.int32)
     N, V = len(parents), 64
     cfg = SAMPLE_TREE_CONFIGS["c4s"].with_(name="tree_sampling_mc", B=1, N=N, V=V, dtype="bf16", target_sigma=1.2,
@@ -424,10 +434,13 @@ def test_monte_carlo_losslessness(sv):
     first = np.where(acc >= 1, tok[rows, np.maximum(path[:, 0], 0)], nxt)
     t64 = _np(one["target"][0].double())
     p_root = oracle.temperature_softmax(t64[0], 1.0)
-    assert _chi2_ok(np.bincount(first, minlength=V), p_root, "first emitted token")
+    pvals = []
+    assert _chi2_ok(np.bincount(first, minlength=V), p_root, "first emitted token", level, pvals)
     # given that child v of the root was accepted first, the next emitted token follows p at v's position
     for v in (0, 1, 2):
         sel = (acc >= 1) & (path[:, 0] == v)
         nxt_tok = np.where(acc[sel] >= 2, tok[rows[sel], np.maximum(path[sel, 1], 0)], nxt[sel])
         assert _chi2_ok(np.bincount(nxt_tok, minlength=V), oracle.temperature_softmax(t64[v + 1], 1.0),
-                        f"token after accepted child {v}")
+                        f"token after accepted child {v}", level, pvals)
+    record_parity("tree_sampling_mc", call="sv_verify_tree_sampling", trials=B, chi2_pvalues=pvals,
+                  bonferroni_bar_each=level)

@@ -58,7 +58,7 @@ def test_workspace_returns_to_zero(sv):
             if bad is None:
                 assert flags == 0
                 rep = compare_chain(out, oracle_chain(inp))
-                assert_chain_parity(rep, 0.05)
+                assert_chain_parity(rep)
             else:
                 assert flags & sv.SV_ERRF_TOKEN
                 acc = out["accept_len"].cpu().numpy()
@@ -99,8 +99,10 @@ def test_sampling_leaves_the_workspace_zero(sv):
         tok = out["tokens"].cpu().numpy()
         if bad is None:
             assert int(out["err_flags"].item()) == 0
-            ref, _, _, _ = oracle.sample_rows(logits.float().cpu().numpy(), T.cpu().numpy(), u.cpu().numpy())
-            assert (tok == ref).mean() > 0.97
+            ref, _, lo, hi = oracle.sample_rows(logits.float().cpu().numpy(), T.cpu().numpy(), u.cpu().numpy())
+            uu = u.double().cpu().numpy()
+            near = (np.abs(uu - lo) < oracle.FLAG_WINDOW) | (np.abs(hi - uu) < oracle.FLAG_WINDOW)
+            assert np.array_equal(tok[~near], ref[~near]), np.nonzero((tok != ref) & ~near)[0]
         else:
             assert int(out["err_flags"].item()) & sv.SV_ERRF_TEMPERATURE
             assert tok[bad] == -1 and np.all(np.delete(tok, bad) >= 0)

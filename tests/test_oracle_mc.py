@@ -174,3 +174,36 @@ def test_negative_control_reused_uniform_fails(mc_inputs):
 
 def test_oracle_module_exports():
     assert oracle.FLAG_WINDOW == 1e-6
+
+
+def test_flag_rate_predicts_the_flagged_count():
+    """The oracle's flag_rate diagnostic (the chance that fresh uniforms land
+    within the 1e-6 window of a decision threshold) predicts how many rows
+    are flagged: over 2 x 10^6 seeded trials of the V = 16, K = 3 workload
+    (fresh uniforms for each million) the flagged count is a Poisson count
+    with mean sum(flag_rate). With V = 16 about 3e-5 of the rows flag, so the
+    count is large enough to test; a rate off by a factor of two (one side
+    of each window only, say) fails by more than 5 sigma."""
+    from workloads.synth import seed_stream
+
+    x = mc_chain_inputs(MC_CONFIG, TRIALS)
+    tr = x["target_row"].double().numpy()
+    dr = x["draft_row"].double().numpy()
+    tokens = x["draft_tokens"].numpy().astype(np.int64)
+    T = x["temperature"].double().numpy()
+    K1, V = tr.shape
+    flagged = rate = 0.0
+    for it in (1, 2):
+        u = seed_stream(MC_CONFIG.config_id, MC_CONFIG.variant, 3, 100 + it).random((TRIALS, K1), dtype=np.float32)
+        u = u.astype(np.float64)
+        for s in range(0, TRIALS, CHUNK):
+            e = min(TRIALS, s + CHUNK)
+            m = e - s
+            r = verify_chain(np.broadcast_to(tr, (m, K1, V)), np.broadcast_to(dr, (m, K1 - 1, V)), tokens[s:e],
+                             T[s:e], u[s:e])
+            flagged += float(r["flagged"].sum())
+            rate += float(r["flag_rate"].sum())
+    assert rate > 40, rate
+    z = (flagged - rate) / np.sqrt(rate)
+    print("flagged", flagged, "expected", rate, "z", z)
+    assert abs(z) < 5, (flagged, rate)
