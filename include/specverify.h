@@ -159,6 +159,22 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
                           int32_t* err_flags, void* workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/*
+ * How many kernel launches sv_verify_chain makes for a call of this shape on
+ * the current device: 1 when the statistics pass and the sampling pass run
+ * as one launch, 2 when they run as two; 0 for invalid sizes or dtype. The
+ * one-launch form is taken when the call's grid (statistics chunks and
+ * sampling workgroups) is larger than the device holds at once, the rows
+ * start on 16-byte boundaries (rows_aligned != 0: V * element size a
+ * multiple of 16 and both logit tensors 16-byte aligned), K >= 1, no entropy
+ * is requested (with_entropy == 0) and the statistics of a sequence fit the
+ * decision's single round of loads. The outputs are bit-identical either
+ * way; only the timing differs (see the launch-events hook below, which
+ * times the first launch). Host-only query; nothing is enqueued.
+ */
+int32_t sv_chain_launches(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32_t rows_aligned,
+                          int32_t with_entropy);
+
 /* ------------------------------------------------------------------------
  * Draft-side sampling.
  *

@@ -22,6 +22,7 @@ from .specverify import (  # noqa: F401
     library,
     reset_workspaces,
     sv_build_tree_mask,
+    sv_chain_launches,
     sv_chain_workspace_bytes,
     sv_sample_rows,
     sv_sample_workspace_bytes,

@@ -84,9 +84,45 @@ int64_t piece_slots(int64_t B, int32_t rows, int32_t V, sv_dtype d, int64_t chun
   return ch > seg ? ch : seg;
 }
 
+// Compute units of the current device (0 if the runtime cannot say).
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return 0;
+  return cus;
+}
+
+// The one-launch chain call (statistics and sampling in one grid) serves
+// the calls whose grid is larger than the device holds at once, where the
+// sampling of the first sequences can overlap the streaming of the last
+// ones: on MI355X B=64 K=5 V=128256 bf16 took 50.8 us against 52.8 us in two
+// launches, B=256 K=8 V=152064 239 us against 250 us, B=1024 K=6 V=256000
+// 1173 us against 1190 us. A smaller grid starts all at once, so all the
+// workgroups of a sequence take their tickets together and queue on one
+// counter: B=4 K=4 V=32000 fp32 took 26.1 us against 20.1 us. It also needs
+// rows on 16-byte boundaries (the chunked layout), at least one drafted
+// token, no entropy or drawn probability requested, and statistics that the
+// decision reads in one round: every piece of each of the 2K+1 rows among
+// G lanes of one wave with at most 4 pieces per lane (G as the decision
+// takes it), chunk indices within 32 bits. Other calls keep the statistics
+// pass and the sampling pass as two launches.
+bool one_launch_ok(const sv::PieceLayout& L, int32_t B, int32_t K, int32_t nblk_b, bool extra_outputs) {
+  if (!SV_ONE_LAUNCH || L.cps <= 0 || K <= 0 || extra_outputs) return false;
+  const int64_t grid = static_cast<int64_t>(B) * (L.cps + nblk_b);
+  const int cus = device_cus();
+  if (cus < 1 || grid <= static_cast<int64_t>(cus) * sv::kOneLaunchWGsPerCU) return false;
+  const int64_t R = 2LL * K + 1;
+  if (R * L.nvec > static_cast<int64_t>(UINT32_MAX)) return false;
+  const int64_t pmax = (L.nvec + L.per - 2) / L.per + 1;  // pieces of a row, at most
+  int64_t G = 1;
+  while (G < pmax && R * 2 * G <= 64) G <<= 1;
+  return R * G <= 64 && pmax <= 4 * G;
+}
+
 struct ChainLayout {
   int32_t ntiles, tiles_per_block, nblk_b;
-  size_t off_part_m, off_part_s, off_part_a, off_cnt, off_tiles, off_gat, off_abort, total;
+  size_t off_part_m, off_part_s, off_part_a, off_cnt, off_tiles, off_gat, off_abort, off_tk, off_done, total;
 };
 
 ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
@@ -110,13 +146,17 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   L.off_part_a = off;
   off = align_up(off + sizeof(uint64_t) * parts);
   L.off_cnt = off;
-  off = align_up(off + sizeof(uint32_t) * B);
+  off = align_up(off + sizeof(uint32_t) * B * sv::kCtrStride);
   L.off_tiles = off;
   off = align_up(off + sizeof(uint64_t) * static_cast<int64_t>(B) * L.ntiles);
   L.off_gat = off;
   off = align_up(off + sizeof(uint64_t) * static_cast<int64_t>(B) * R);
   L.off_abort = off;
   off = align_up(off + sizeof(uint64_t));
+  L.off_tk = off;
+  off = align_up(off + sizeof(uint32_t) * B * sv::kCtrStride);
+  L.off_done = off;
+  off = align_up(off + sizeof(uint32_t) * B * sv::kCtrStride);
   L.total = off;
   return L;
 }
@@ -197,10 +237,8 @@ TreeSamplingLayout tree_sampling_layout(int32_t B, int32_t N, int32_t V, sv_dtyp
 // compute units (B G about the number of compute units), each with at least
 // one run per wave, at most kMaxWalkGroups.
 int32_t walk_groups(int32_t B, int32_t nrun) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    return 1;
+  const int cus = device_cus();
+  if (cus < 1) return 1;
   const int64_t by_cus = cus / (B > 0 ? B : 1);
   const int64_t by_runs = ceil_div(nrun, 16);
   int64_t g = by_cus < by_runs ? by_cus : by_runs;
@@ -293,8 +331,11 @@ sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dty
   p.tile_sum = reinterpret_cast<uint64_t*>(ws + L.off_tiles);
   p.gat = reinterpret_cast<uint64_t*>(ws + L.off_gat);
   p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
+  p.tk = reinterpret_cast<uint32_t*>(ws + L.off_tk);
+  p.done = reinterpret_cast<uint32_t*>(ws + L.off_done);
+  p.one_launch = one_launch_ok(p.L, B, K, p.nblk_b, entropy != nullptr || drawn_prob != nullptr) ? 1 : 0;
 
-  if (static_cast<int64_t>(B) * sv::items_per_seq(p.L) > INT32_MAX || static_cast<int64_t>(B) * p.nblk_b > INT32_MAX)
+  if (static_cast<int64_t>(B) * (sv::items_per_seq(p.L) + p.nblk_b) > INT32_MAX)
     return SV_ERR_UNSUPPORTED;
   return from_hip(sv::launch_chain(p, dtype, ev, stream));
 }
@@ -302,6 +343,16 @@ sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dty
 }  // namespace
 
 extern "C" {
+
+int32_t sv_chain_launches(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32_t rows_aligned,
+                          int32_t with_entropy) {
+  if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return 0;
+  if (B == 0) return 0;
+  const bool chunked = rows_aligned != 0 && whole_vector_rows(V, dtype);
+  const sv::PieceLayout L =
+      piece_layout(2 * K + 1, V, dtype, chunked, row_chunk_vecs(B, 2 * K + 1, V, dtype, sv::kChunksChain));
+  return one_launch_ok(L, B, K, chain_layout(B, K, V, dtype).nblk_b, with_entropy != 0) ? 1 : 2;
+}
 
 sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,
                           const int32_t* draft_tokens, const float* temperature, const float* uniforms,

@@ -237,6 +237,85 @@ __device__ __forceinline__ uint32_t wave_or_err(uint32_t v) {
   return r;
 }
 
+// The decision of sequence b once its rows' log-normalisers are in s_L
+// (wave 0; lane k < K holds drafted token k, its uniform and the two
+// gathered logits): p_k(x_k), q_k(x_k) in fp64, alpha_k = min(1, p/q),
+// acceptance while u_k < alpha_k, j = the first rejection (ballot). Leaves
+// the sampling plan in *s_plan; the `writer` also writes accept_len, the
+// accepted prefix of out_tokens, p_draft / q_draft and the error bits.
+template <class T>
+__device__ __forceinline__ void decide_tail(const ChainParams& P, int b, SeqPlan* s_plan, bool writer,
+                                            const double* s_L, int x, float u, uint64_t vt, uint64_t vd,
+                                            uint32_t err, float Tv) {
+  const int K = P.K;
+  const int lane = lane_id();
+  // s_L is written by the group leaders and read by other lanes of this wave.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  float lt = 0.0f, ld = 0.0f;
+  if (lane < K) {
+    if (x < 0 || x >= P.V) {
+      err |= SV_ERRF_TOKEN;
+    } else {
+      if (vt == 0ull || vd == 0ull) err |= kErrInternal;
+      lt = untag_float(vt);
+      ld = untag_float(vd);
+    }
+  }
+  const Scale c = exponent_scale(Tv);
+  if (!(Tv > 0.0f) || !isfinite(Tv)) err |= SV_ERRF_TEMPERATURE;
+  const double c64 = static_cast<double>(c.hi) + static_cast<double>(c.lo);
+  bool reject = false;
+  if (lane < K) {
+    float pf = NAN, qf = NAN;
+    if (x >= 0 && x < P.V) {
+      // p = 2^ap, q = 2^aq; alpha = min(1, p / q) = 2^min(0, ap - aq)
+      const double ap = static_cast<double>(lt) * c64 - s_L[lane];
+      const double aq = static_cast<double>(ld) * c64 - s_L[K + 1 + lane];
+      const double p = exp2_split(ap);
+      const double q = exp2_split(aq);
+      const double alpha = (p > 0.0) ? ((q > 0.0) ? ((ap >= aq) ? 1.0 : exp2_split(ap - aq)) : 1.0) : 0.0;
+      reject = !(static_cast<double>(u) < alpha);
+      pf = static_cast<float>(p);
+      qf = static_cast<float>(q);
+    }
+    if (writer && P.p_draft != nullptr) P.p_draft[static_cast<int64_t>(b) * K + lane] = pf;
+    if (writer && P.q_draft != nullptr) P.q_draft[static_cast<int64_t>(b) * K + lane] = qf;
+  }
+  const uint64_t rej = __ballot(reject);
+  const int j = (rej != 0ull) ? (__ffsll(static_cast<unsigned long long>(rej)) - 1) : K;
+  err = wave_or_err(err);
+  const bool bad = err != 0u;
+
+  // Lane i writes out_tokens[i] (K + 1 <= 64): its own token up to j, -1 after;
+  // the drawn token at j is written by the sampling pass.
+  if (writer && lane <= K && !(lane == j && !bad))
+    P.out_tokens[static_cast<int64_t>(b) * (K + 1) + lane] = (bad || lane > j) ? -1 : x;
+  if (lane == 0) {
+    if (writer) {
+      if (P.accept_len != nullptr) P.accept_len[b] = bad ? -1 : j;
+      if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
+      if (bad && P.drawn_prob != nullptr) P.drawn_prob[b] = NAN;
+      raise_error(P.err_flags, err);
+    }
+    SeqPlan pl;
+    pl.j = bad ? -1 : j;
+    pl.c_hi = c.hi;
+    pl.c_lo = c.lo;
+    split(s_L[j], pl.lt_hi, pl.lt_lo);
+    if (j < K) {
+      split(s_L[K + 1 + j] - s_L[j], pl.d_hi, pl.d_lo);
+    } else {
+      pl.d_hi = 0.0f;
+      pl.d_lo = 0.0f;
+    }
+    pl.pad = 0u;
+    *s_plan = pl;
+  }
+}
+
 template <class T, bool kEnt>
 __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
@@ -338,71 +417,138 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
             (fin && Tv > 0.0f && isfinite(Tv)) ? static_cast<float>(0.6931471805599453 * (lz - al / zl)) : NAN;
     }
   }
-  // s_L is written by the group leaders and read by other lanes of this wave.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  decide_tail<T>(P, b, s_plan, writer, s_L, x, u, vt, vd, err, Tv);
+}
 
-  float lt = 0.0f, ld = 0.0f;
-  if (lane < K) {
-    if (x < 0 || x >= P.V) {
-      err |= SV_ERRF_TOKEN;
-    } else {
-      if (vt == 0ull || vd == 0ull) err |= kErrInternal;
-      lt = untag_float(vt);
-      ld = untag_float(vd);
-    }
-  }
-  const Scale c = exponent_scale(Tv);
-  if (!(Tv > 0.0f) || !isfinite(Tv)) err |= SV_ERRF_TEMPERATURE;
-  const double c64 = static_cast<double>(c.hi) + static_cast<double>(c.lo);
-  bool reject = false;
-  if (lane < K) {
-    float pf = NAN, qf = NAN;
-    if (x >= 0 && x < P.V) {
-      // p = 2^ap, q = 2^aq; alpha = min(1, p / q) = 2^min(0, ap - aq)
-      const double ap = static_cast<double>(lt) * c64 - s_L[lane];
-      const double aq = static_cast<double>(ld) * c64 - s_L[K + 1 + lane];
-      const double p = exp2_split(ap);
-      const double q = exp2_split(aq);
-      const double alpha = (p > 0.0) ? ((q > 0.0) ? ((ap >= aq) ? 1.0 : exp2_split(ap - aq)) : 1.0) : 0.0;
-      reject = !(static_cast<double>(u) < alpha);
-      pf = static_cast<float>(p);
-      qf = static_cast<float>(q);
-    }
-    if (writer && P.p_draft != nullptr) P.p_draft[static_cast<int64_t>(b) * K + lane] = pf;
-    if (writer && P.q_draft != nullptr) P.q_draft[static_cast<int64_t>(b) * K + lane] = qf;
-  }
-  const uint64_t rej = __ballot(reject);
-  const int j = (rej != 0ull) ? (__ffsll(static_cast<unsigned long long>(rej)) - 1) : K;
-  err = wave_or_err(err);
-  const bool bad = err != 0u;
+// Lanes per row of the decision's statistics combine: the largest power of
+// two G (at most one past the row's piece count) with 2K+1 rows of 2G lanes
+// fitting a wave, as decide_wave takes it.
+__device__ __forceinline__ int decision_lanes(int R, int pmax) {
+  int G = 1;
+  while (G < pmax && R * 2 * G <= kWave) G <<= 1;
+  return G;
+}
 
-  // Lane i writes out_tokens[i] (K + 1 <= 64): its own token up to j, -1 after;
-  // the drawn token at j is written by the sampling pass.
-  if (writer && lane <= K && !(lane == j && !bad))
-    P.out_tokens[static_cast<int64_t>(b) * (K + 1) + lane] = (bad || lane > j) ? -1 : x;
-  if (lane == 0) {
-    if (writer) {
-      if (P.accept_len != nullptr) P.accept_len[b] = bad ? -1 : j;
-      if (bad && P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
-      if (bad && P.drawn_prob != nullptr) P.drawn_prob[b] = NAN;
-      raise_error(P.err_flags, err);
-    }
-    SeqPlan pl;
-    pl.j = bad ? -1 : j;
-    pl.c_hi = c.hi;
-    pl.c_lo = c.lo;
-    split(s_L[j], pl.lt_hi, pl.lt_lo);
-    if (j < K) {
-      split(s_L[K + 1 + j] - s_L[j], pl.d_hi, pl.d_lo);
-    } else {
-      pl.d_hi = 0.0f;
-      pl.d_lo = 0.0f;
-    }
-    pl.pad = 0u;
-    *s_plan = pl;
+// One-launch call: the decision of sequence b (wave 0) from statistics
+// written by running workgroups of the same launch. The host takes the
+// one-launch call only when every piece of every row is in the first round
+// of decide_wave (at most 4 pieces per lane, 2K+1 rows of G lanes in one
+// wave, chunk indices within 32 bits), and this function makes exactly
+// decide_wave's operations in the same order on that round, so the
+// normalisers, and every output, are bit-identical to the two-launch call.
+// Every slot is read with an agent-scope load, all issued together; a slot
+// still zero (its store not visible yet) makes the wave return false before
+// anything is written, for the caller to read again.
+template <class T>
+__device__ bool decide_live_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
+  __shared__ double s_L[2 * SV_MAX_K + 1];
+  const int K = P.K;
+  const int R = 2 * K + 1;
+  const int lane = lane_id();
+  const PieceLayout& L = P.L;
+  const int G = decision_lanes(R, max_pieces(L));
+  const int r = lane / G;
+  const int gl = lane % G;
+  const bool row_ok = r < R;
+  uint32_t err = 0u;
+
+  // this lane's pieces gl + i G of row r: chunks ch0 + gl + i G up to chl
+  const uint32_t nv = static_cast<uint32_t>(L.nvec), pr = static_cast<uint32_t>(L.per);
+  const uint32_t rr = row_ok ? static_cast<uint32_t>(r) : 0u;
+  const uint32_t ch0 = rr * nv / pr;
+  const uint32_t chl = ((rr + 1u) * nv - 1u) / pr;
+  const uint32_t first_row0 = ch0 * pr / nv;
+  const int64_t base = static_cast<int64_t>(b) * L.cps;
+  const int64_t any_slot = base * L.kmax;  // a valid address
+  uint64_t rm[4], rs[4];
+  bool has[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t p = static_cast<uint32_t>(gl + i * G);
+    const uint32_t ch = ch0 + p;
+    has[i] = row_ok && ch <= chl;
+    const int64_t sl = has[i] ? (base + ch) * L.kmax + (p == 0u ? rr - first_row0 : 0u) : any_slot;
+    rm[i] = peek(&P.part_m[sl]);
+    rs[i] = peek(&P.part_s[sl]);
   }
+  const float Tv = temperature_of(P.temperature, b);
+  int x = -1;
+  float u = 0.0f;
+  uint64_t vt = 0ull, vd = 0ull;
+  if (K > 0) {  // every lane loads (lanes past K repeat lane K - 1's values and drop them)
+    const int k = min(lane, K - 1);
+    x = P.tokens[static_cast<int64_t>(b) * K + k];
+    u = P.uniforms[static_cast<int64_t>(b) * (K + 1) + k];
+    vt = peek(&P.gat[static_cast<int64_t>(b) * R + k]);
+    vd = peek(&P.gat[static_cast<int64_t>(b) * R + K + 1 + k]);
+    if (lane >= K) x = -1;
+  }
+  bool missing = lane < K && x >= 0 && x < P.V && (vt == 0ull || vd == 0ull);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) missing |= has[i] && (rm[i] == 0ull || rs[i] == 0ull);
+  if (__ballot(missing) != 0ull) return false;
+
+  // decide_wave's combine of one round: running reference mf, fp64 sum zf
+  float mf = -INFINITY;
+  double zf = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (!has[i]) continue;
+    const float mm = untag_float(rm[i]);
+    const double sv = untag_nonneg_double(rs[i]);
+    if (mm == -INFINITY) continue;
+    if (mm > mf) {
+      const double f = (mf == -INFINITY) ? 0.0 : ref_factor(mf, mm);
+      zf = zf * f + sv;
+      mf = mm;
+    } else {
+      zf += sv * ref_factor(mm, mf);
+    }
+  }
+  float M = mf;
+  for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  const double fl = (mf == -INFINITY) ? 0.0 : ref_factor(mf, M);
+  double zl = zf * fl;
+  for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
+  if (row_ok && gl == 0) {
+    const bool fin = (zl > 0.0) && isfinite(zl) && isfinite(M);
+    if (!fin) err |= SV_ERRF_NONFINITE;
+    const double lz = fin ? log2_fast(zl) : log2(zl);
+    s_L[r] = static_cast<double>(M) + lz;
+  }
+  decide_tail<T>(P, b, s_plan, writer, s_L, x, u, vt, vd, err, Tv);
+  return true;
+}
+
+// One-launch call: wave 0 of a sampling workgroup of sequence b waits until
+// every statistics chunk of b has been counted (P.done[b] reaches the chunks
+// per sequence), then makes the decision, reading the slots again while a
+// store is not yet visible. Every chunk it waits for was handed out by the
+// sequence's ticket queue before this sampling role, to a workgroup that is
+// running and waits for nothing, so the wait ends; it is still bounded
+// like await_slot. Returns false on expiry or on an abort raised elsewhere.
+template <class T>
+__device__ bool decide_live(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
+  const uint32_t need = static_cast<uint32_t>(P.L.cps);
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  uint32_t* done = P.done + static_cast<int64_t>(b) * kCtrStride;
+  while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+    if (peek(P.abort) != 0ull) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      publish(P.abort, 1ull);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(SV_POLL_SLEEP);
+  }
+  while (!decide_live_wave<T>(P, b, s_plan, writer)) {
+    if (peek(P.abort) != 0ull) return false;
+    if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      publish(P.abort, 1ull);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  return true;
 }
 
 template <class T>
@@ -688,13 +834,30 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
 // pair, TPB at a time, and publishes their totals; the last workgroup of the sequence to finish draws the token
 // and returns the sequence's workspace (statistics pieces, gathered logits,
 // tile totals, arrival counter) to zero.
-template <class T, int TPB, bool kDraft, bool kEnt>
+// kLive: the one-launch call (statistics of the same launch, see
+// decide_live); a decision that never completes reports the sequence as an
+// invalid row with SV_ERRF_INTERNAL.
+template <class T, int TPB, bool kDraft, bool kEnt, bool kLive = false>
 __device__ void sample_seq(const ChainParams& P, int b, int blk) {
   constexpr int NV = kEptVecs<T>;
   __shared__ double s_red[TPB][kWaves];
   __shared__ int s_flag;
   __shared__ SeqPlan s_plan;
-  if (wave_id() == 0) decide_wave<T, kEnt>(P, b, &s_plan, blk == 0);
+  if (wave_id() == 0) {
+    if constexpr (kLive) {
+      if (!decide_live<T>(P, b, &s_plan, blk == 0) && lane_id() == 0) {
+        if (blk == 0) {
+          P.accept_len[b] = -1;
+          for (int i = 0; i <= P.K; ++i) P.out_tokens[static_cast<int64_t>(b) * (P.K + 1) + i] = -1;
+          if (P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
+        }
+        raise_error(P.err_flags, kErrInternal);
+        s_plan.j = -1;
+      }
+    } else {
+      decide_wave<T, kEnt>(P, b, &s_plan, blk == 0);
+    }
+  }
   __syncthreads();
   const SeqPlan pl = s_plan;
 
@@ -733,7 +896,8 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
     }
   }
 
-  if (!arrive_and_check_last(&P.cnt[b], static_cast<uint32_t>(P.nblk_b), &s_flag)) return;
+  uint32_t* cnt = P.cnt + static_cast<int64_t>(b) * (kLive ? kCtrStride : 1);
+  if (!arrive_and_check_last(cnt, static_cast<uint32_t>(P.nblk_b), &s_flag)) return;
   if (pl.j >= 0) chain_draw<T>(P, b, pl);
   // Every workgroup of the sequence has read the statistics pieces and
   // published its totals: leave the sequence's workspace all zero.
@@ -749,7 +913,8 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
   }
   const int R = 2 * P.K + 1;
   for (int r = threadIdx.x; r < R; r += kThreads) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
-  reset_counter(&P.cnt[b]);
+  reset_counter(cnt);
+  if constexpr (kLive) reset_counter(P.done + static_cast<int64_t>(b) * kCtrStride);
 }
 
 }  // namespace
@@ -804,6 +969,78 @@ __global__ __launch_bounds__(kThreads) void chain_sample_one_row_kernel(ChainPar
                                                                                 static_cast<int>(blockIdx.x / B));
 }
 
+// The sequence whose ticket queue block `blk` of the one-launch grid serves.
+// Grid order: the statistics blocks of sequences 0 .. lag-1 (cps each); then
+// for s = lag .. B-1 the statistics blocks of s followed by the sampling
+// blocks of s - lag (nblk each); then the sampling blocks of the last lag
+// sequences. Every sequence owns cps + nblk blocks.
+__device__ __forceinline__ uint32_t one_launch_sequence(uint32_t blk, uint32_t B, uint32_t cps, uint32_t nblk) {
+  const uint32_t lag = min(static_cast<uint32_t>(kSampleLag), B);
+  if (blk < lag * cps) return blk / cps;
+  const uint32_t i = blk - lag * cps;
+  const uint32_t seg = cps + nblk;
+  const uint32_t nmid = B - lag;
+  if (i < nmid * seg) {
+    const uint32_t s = lag + i / seg;
+    return (i % seg < cps) ? s : s - lag;
+  }
+  return nmid + (i - nmid * seg) / nblk;
+}
+
+// One-launch call (rows on 16-byte boundaries, no entropy requested): the
+// statistics chunks and the sampling workgroups of every sequence in one
+// grid, so that the sampling of the sequences streamed first overlaps the
+// streaming of the later ones instead of waiting for the whole pass.
+//
+// Roles come from one ticket queue per sequence. Sequence b owns cps
+// statistics blocks (blocks b cps .. b cps + cps - 1) and nblk_b sampling
+// blocks (after every sequence's statistics blocks); a workgroup of b's
+// blocks takes the next ticket of b's queue when it starts. Tickets
+// 0 .. cps-1 stream b's chunks, tickets cps .. cps+nblk_b-1 sample b. A
+// sampling role therefore waits only for chunks whose tickets were taken
+// earlier, by workgroups that are running and wait for nothing: every wait
+// ends, whatever order the hardware dispatches workgroups in and whatever
+// else runs beside the launch. With the usual in-order dispatch the block
+// order (statistics first, sequence by sequence) starts the sampling of the
+// first sequences while the last ones stream. The workgroup that takes the
+// last ticket of a queue returns its counter to zero; a statistics role
+// counts its chunk in P.done[b] once its slot stores have completed.
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_ONE_LAUNCH_WAVES, SV_ONE_LAUNCH_WAVES))) void chain_one_launch_kernel(ChainParams P) {
+  __shared__ uint32_t s_ticket;
+  const uint32_t cps = static_cast<uint32_t>(P.L.cps);
+  const uint32_t nblk = static_cast<uint32_t>(P.nblk_b);
+  const uint32_t b = one_launch_sequence(blockIdx.x, static_cast<uint32_t>(P.B), cps, nblk);
+  if (threadIdx.x == 0) {
+    uint32_t* tk = P.tk + static_cast<int64_t>(b) * kCtrStride;
+    const uint32_t t = __hip_atomic_fetch_add(tk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t + 1u == cps + nblk) __hip_atomic_store(tk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_ticket = t;
+  }
+  __syncthreads();
+  const uint32_t t = s_ticket;
+  if (t >= cps + nblk) {  // a ticket counter not left at zero: the workspace was not re-zeroed
+    if (threadIdx.x == 0) {
+      raise_error(P.err_flags, kErrInternal);
+      publish(P.abort, 1ull);
+    }
+    return;
+  }
+  if (t < cps) {
+    stats_chunk<T, kStatsTPB, false>(P, static_cast<int>(b), static_cast<int>(t));
+    if (threadIdx.x == 0) {
+      // count the chunk once this thread's slot stores have completed (the
+      // readers still check every slot's tag and read again if it is zero)
+      __builtin_amdgcn_s_waitcnt(0);
+      __hip_atomic_fetch_add(P.done + static_cast<int64_t>(b) * kCtrStride, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+  } else {
+    if (SV_SAMPLE_PRIO > 0) __builtin_amdgcn_s_setprio(SV_SAMPLE_PRIO);
+    sample_seq<T, kLiveTiles, true, false, true>(P, static_cast<int>(b), static_cast<int>(t - cps));
+  }
+}
+
 // ---------------------------------------------------------------- launcher
 
 template <class T>
@@ -811,8 +1048,15 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
   const int64_t grid_a = static_cast<int64_t>(p.B) * items_per_seq(p.L);
   const int64_t grid_c = static_cast<int64_t>(p.B) * p.nblk_b;
   if (grid_a > INT32_MAX || grid_c > INT32_MAX) return hipErrorInvalidConfiguration;
-  // Armed events take the statistics kernel's own start and end timestamps.
+  // Armed events take the statistics kernel's own start and end timestamps
+  // (the whole call's, for the one-launch kernel).
   const bool ent = p.entropy != nullptr;
+  if (p.one_launch) {
+    const int64_t grid = static_cast<int64_t>(p.B) * (p.L.cps + p.nblk_b);
+    if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
+    launch_stream_pass(chain_one_launch_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), stream, ev, p);
+    return hipGetLastError();
+  }
   if (p.L.cps > 0)
     launch_stream_pass(ent ? chain_stats_chunk_entropy_kernel<T> : chain_stats_chunk_kernel<T>,
                        dim3(static_cast<uint32_t>(grid_a)), dim3(kStatsTPB), stream, ev, p);

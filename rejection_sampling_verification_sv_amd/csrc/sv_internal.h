@@ -107,6 +107,12 @@ struct ChainParams {
                       // token (rows 0..K-1 and K+1..2K; set by the pass that
                       // streams the piece holding it)
   uint64_t* abort;    // [1] set when a bounded wait expires (drains the launch)
+  // One-launch call (statistics and sampling in one grid, see
+  // chain_one_launch_kernel): per sequence, the ticket counter of its queue
+  // and the number of statistics chunks counted.
+  int32_t one_launch;
+  uint32_t* tk;       // [B]
+  uint32_t* done;     // [B]
 };
 
 // Sampling verification of a candidate tree: the run records of the target
@@ -247,6 +253,55 @@ constexpr int kStreamUEnt = SV_STREAM_U_ENT;
 #define SV_STATS_TPB 256
 #endif
 constexpr int kStatsTPB = SV_STATS_TPB;
+// The one-launch chain call: on (1) for the calls it serves (see
+// one_launch_ok on the host), or off (0: always two launches). Waves per
+// SIMD its kernel (statistics and sampling roles) is compiled for, and the
+// sampling tiles whose loads a workgroup keeps in flight together: 69 VGPRs
+// with four tiles (7 waves/SIMD), 62 with one or two (8 waves; measured
+// 52.1 us per B=64 K=5 V=128256 bf16 call with two, 50.8-51.4 us with four
+// at 7 waves).
+#ifndef SV_ONE_LAUNCH
+#define SV_ONE_LAUNCH 1
+#endif
+#ifndef SV_ONE_LAUNCH_WAVES
+#define SV_ONE_LAUNCH_WAVES 7
+#endif
+constexpr int kOneLaunchWGsPerCU = SV_ONE_LAUNCH_WAVES;  // 4-wave workgroups on 4 SIMDs
+#ifndef SV_LIVE_TILES
+#define SV_LIVE_TILES 4
+#endif
+constexpr int kLiveTiles = SV_LIVE_TILES;
+// Per-sequence counters of the one-launch call (ticket, chunks counted,
+// sampling arrivals) lie this many 32-bit words apart. Packed counters put
+// the polls of the waiting sampling workgroups and the contended ticket
+// atomics on one memory channel, and the streaming workgroups, which have
+// loads queued on every channel, stall behind them: on B=64 K=5 V=128256
+// bf16 the call took 109-116 us with packed counters, 50.8 us with counters
+// 256 bytes apart, 51.4 us 4 KB apart and 53.3 us 64 bytes apart.
+#ifndef SV_CTR_STRIDE
+#define SV_CTR_STRIDE 64
+#endif
+constexpr int kCtrStride = SV_CTR_STRIDE;
+// Pause between two polls of a waiting sampling workgroup (s_sleep units
+// of 64 cycles), and the wave priority (0-3) of the sampling roles (3
+// measured 52.3 us per B=64 K=5 call against 51.4 us at 0, polls 8 or 32
+// the same).
+#ifndef SV_POLL_SLEEP
+#define SV_POLL_SLEEP 8
+#endif
+#ifndef SV_SAMPLE_PRIO
+#define SV_SAMPLE_PRIO 0
+#endif
+// Block order of the one-launch grid: the sampling blocks of sequence b
+// follow the statistics blocks of sequence b + lag (the last lag sequences'
+// sampling blocks close the grid), so that with in-order dispatch they start
+// about when b's statistics are done. lag >= B puts every sampling block
+// after every statistics block (a lag of 16 or 32 sequences measured 56.7
+// and 52.8 us per B=64 K=5 call against 51.4 us).
+#ifndef SV_SAMPLE_LAG
+#define SV_SAMPLE_LAG 1000000
+#endif
+constexpr int kSampleLag = SV_SAMPLE_LAG;
 // Waves per SIMD the chunked statistics stream is compiled for (8: at most 64
 // VGPRs; 4: at most 128).
 #ifndef SV_STATS_WAVES

@@ -90,6 +90,8 @@ def _load():
             _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
         ]
         lib.sv_sample_rows.restype = ctypes.c_int
+        lib.sv_chain_launches.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int, _c_i32, _c_i32]
+        lib.sv_chain_launches.restype = _c_i32
         lib.sv_time_next_stream_pass.argtypes = [_c_ptr, _c_ptr]
         lib.sv_time_next_stream_pass.restype = ctypes.c_int
         _lib = lib
@@ -242,6 +244,13 @@ def workspace(device, nbytes: int, stream=None) -> torch.Tensor:
 
 def sv_chain_workspace_bytes(B: int, K: int, V: int, dtype: torch.dtype) -> int:
     return int(_load().sv_chain_workspace_bytes(B, K, V, _DTYPES[dtype]))
+
+
+def sv_chain_launches(B: int, K: int, V: int, dtype: torch.dtype, rows_aligned: bool = True,
+                      with_entropy: bool = False) -> int:
+    """Kernel launches ``sv_verify_chain`` makes for this shape on the current
+    device: 1 (statistics and sampling in one launch) or 2; 0 if invalid."""
+    return int(_load().sv_chain_launches(B, K, V, _DTYPES[dtype], int(rows_aligned), int(with_entropy)))
 
 
 def sv_tree_workspace_bytes(B: int, N: int, V: int, dtype: torch.dtype) -> int:

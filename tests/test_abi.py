@@ -180,3 +180,18 @@ def test_stream_pass_hook_arguments(lib):
     assert f(FAKE, FAKE + 64) == 0
     assert _chain(lib, t=None) == INV
     assert f(None, None) == 0
+
+
+def test_chain_launches_query(lib):
+    # host-only query of the launch form; without a device (this container)
+    # the library cannot size the grid against the device and answers 2
+    f = lib.sv_chain_launches
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int32, ctypes.c_int32]
+    f.restype = ctypes.c_int32
+    assert f(-1, 5, 10, 1, 1, 0) == 0 and f(4, 64, 10, 1, 1, 0) == 0 and f(4, 2, 0, 1, 1, 0) == 0
+    assert f(4, 2, 10, 7, 1, 0) == 0      # bad dtype
+    assert f(0, 5, 128256, 1, 1, 0) == 0  # nothing to launch
+    assert f(64, 5, 128256, 1, 1, 1) == 2  # entropy: always two launches
+    assert f(64, 5, 128255, 1, 1, 0) == 2  # rows off 16-byte boundaries
+    assert f(64, 0, 128256, 1, 1, 0) == 2  # K = 0
+    assert f(64, 5, 128256, 1, 1, 0) in (1, 2)

@@ -316,6 +316,33 @@ def test_repeat_is_bit_identical(sv):
             assert torch.equal(first[k], again[k]), k
 
 
+def test_concurrent_one_launch_calls(sv):
+    # two calls large enough for the one-launch kernel, on two streams at
+    # once (each with its own workspace): together they hold more workgroups
+    # than the device, and both must match their single-stream outputs
+    cfg = CHAIN_CONFIGS["c2"]
+    inp_a = chain_inputs(cfg, device="cuda")
+    inp_b = chain_inputs(cfg.with_(variant=cfg.variant + 20, B=96), device="cuda")
+    _say("two one-launch calls on two streams", cfg.name, "and B=96 variant", cfg.variant + 20)
+    ref_a = _run(sv, inp_a)
+    ref_b = _run(sv, inp_b)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(5):
+        oa = sv.sv_verify_chain(inp_a["target"], inp_a["draft"], inp_a["draft_tokens"], inp_a["temperature"],
+                                inp_a["uniforms"], stream=s1)
+        ob = sv.sv_verify_chain(inp_b["target"], inp_b["draft"], inp_b["draft_tokens"], inp_b["temperature"],
+                                inp_b["uniforms"], stream=s2)
+        outs.append((oa, ob))
+    torch.cuda.synchronize()
+    for oa, ob in outs:
+        assert int(oa["err_flags"].item()) == 0 and int(ob["err_flags"].item()) == 0
+        for k in ("accept_len", "out_tokens", "p_draft", "q_draft", "residual_mass"):
+            assert torch.equal(oa[k], ref_a[k]), k
+            assert torch.equal(ob[k], ref_b[k]), k
+    assert_chain_parity(compare_chain(ref_b, oracle_chain(inp_b)))
+
+
 def test_concurrent_streams(sv):
     inp_a = _to(_rand_case(32, 5, 50000, torch.bfloat16, seed=85), "cuda")
     inp_b = _to(_rand_case(48, 4, 30000, torch.float32, seed=86), "cuda")

@@ -106,3 +106,26 @@ def test_sampling_leaves_the_workspace_zero(sv):
         else:
             assert int(out["err_flags"].item()) & sv.SV_ERRF_TEMPERATURE
             assert tok[bad] == -1 and np.all(np.delete(tok, bad) >= 0)
+
+
+def test_one_launch_call_leaves_the_workspace_zero(sv):
+    # calls whose grid is larger than the device holds at once take the
+    # one-launch kernel (ticket queues, chunk counters and arrival counters
+    # per sequence): one zero-filled workspace serves them back to back, is
+    # all zero after each, and a two-launch call on it in between still works
+    big = CHAIN_CONFIGS["c2"]
+    small = dict(B=8, K=5, V=4096, dtype="bf16", seed=408)
+    nbytes = max(sv.sv_chain_workspace_bytes(big.B, big.K, big.V, torch.bfloat16),
+                 sv.sv_chain_workspace_bytes(small["B"], small["K"], small["V"], torch.bfloat16))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    for i, (label, inp) in enumerate([("one-launch c2", chain_inputs(big, device="cuda")),
+                                      ("two-launch B8", _chain_case(**small)),
+                                      ("one-launch c2, second input set",
+                                       chain_inputs(big.with_(variant=big.variant + 10), device="cuda"))]):
+        _say("workspace:", label)
+        out = sv.sv_verify_chain(inp["target"], inp["draft"], inp["draft_tokens"], inp["temperature"],
+                                 inp["uniforms"], workspace_tensor=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero().item()) == 0, f"workspace dirty after {label}"
+        assert int(out["err_flags"].item()) == 0
+        assert_chain_parity(compare_chain(out, oracle_chain(inp)))
