@@ -160,6 +160,32 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
                           hipStream_t stream);
 
 /*
+ * sv_verify_chain for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same arguments without the workspace: the call uses a static array of
+ * SV_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs
+ * on until the process ends (8 MiB covers, for instance, B=1024 K=6
+ * V=256000 bf16, which needs 6.7 MiB). It allocates nothing: no hipMalloc,
+ * no hipFree. Each call first clears the part of the array it uses (one
+ * small fill kernel on `stream`, then the kernels of sv_verify_chain), so
+ * it does not depend on what an earlier call left there. Every call on one
+ * GPU shares that GPU's array: two calls that overlap in time on one GPU
+ * (different streams or host threads) race and give undefined results.
+ * Outputs and error bits are those of sv_verify_chain on the same inputs.
+ * Returns SV_ERR_UNSUPPORTED when sv_chain_workspace_bytes(B, K, V, dtype)
+ * exceeds SV_NOALLOC_SCRATCH_BYTES, and otherwise what sv_verify_chain
+ * returns (SV_ERR_HIP also if the array's address cannot be obtained); on an
+ * error return nothing is enqueued. The launch counts of sv_chain_launches
+ * hold, plus the fill kernel.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (8u << 20)
+sv_status sv_verify_chain_noalloc(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                                  const int32_t* draft_tokens, const float* temperature, const float* uniforms,
+                                  int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
+                                  float* p_draft, float* q_draft, float* residual_mass, float* entropy,
+                                  int32_t* err_flags, hipStream_t stream);
+
+/*
  * How many kernel launches sv_verify_chain makes for a call of this shape on
  * the current device: 1 when the statistics pass and the sampling pass run
  * as one launch, 2 when they run as two; 0 for invalid sizes or dtype. The

@@ -31,6 +31,7 @@ from .specverify import (  # noqa: F401
     sv_tree_sampling_workspace_bytes,
     sv_tree_workspace_bytes,
     sv_verify_chain,
+    sv_verify_chain_noalloc,
     sv_verify_tree_greedy,
     sv_verify_tree_sampling,
 )

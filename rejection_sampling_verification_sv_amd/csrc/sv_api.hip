@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "sv_internal.h"
 
 namespace {
@@ -283,13 +285,61 @@ size_t sv_chain_workspace_bytes(int32_t B, int32_t K, int32_t V, sv_dtype dtype)
 
 namespace {
 
+// ---------------------------------------------------------------- the chain call that allocates nothing
+//
+// sv_verify_chain_noalloc uses this array as its workspace: one copy per
+// GPU, held until the process ends, shared by every such call on that GPU.
+// Host code never uses the array's name as an address (on the host it is a
+// stand-in, not device memory): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of the array (SV_ERR_HIP if the runtime cannot
+// give its address).
+sv_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SV_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SV_OK;
+}
+
+// Zero n16 16-byte words at p (a kernel, not a memset node, so a caller may
+// capture it in a graph).
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, uint64_t n16) {
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256u + threadIdx.x; i < n16;
+       i += static_cast<uint64_t>(gridDim.x) * 256u)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Zero the first `bytes` bytes (a multiple of 256, as every workspace
+// layout's total is) of a 256-byte-aligned buffer on `stream`.
+hipError_t zero_fill(void* buf, size_t bytes, hipStream_t stream) {
+  const uint64_t n16 = bytes / 16;
+  if (n16 == 0) return hipSuccess;
+  const uint64_t blocks = (n16 + 255) / 256;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<uint32_t>(blocks < 1024 ? blocks : 1024)), dim3(256), 0,
+                     stream, static_cast<uint4*>(buf), n16);
+  return hipGetLastError();
+}
+
 // A chain verification call; draft-side sampling is the K = 0 case with the
 // drawn token's probability requested.
 sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dtype dtype, const int32_t* draft_tokens,
                      const float* temperature, const float* uniforms, int32_t B, int32_t K, int32_t V,
                      int32_t* accept_len, int32_t* out_tokens, float* p_draft, float* q_draft, float* residual_mass,
                      float* entropy, float* drawn_prob, int32_t* err_flags, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream, const sv::PassEvents& ev) {
+                     hipStream_t stream, const sv::PassEvents& ev, bool zero_first = false) {
   if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return SV_ERR_INVALID_ARGUMENT;
   if (B == 0) return SV_OK;
   if (target_logits == nullptr || uniforms == nullptr || out_tokens == nullptr) return SV_ERR_INVALID_ARGUMENT;
@@ -337,6 +387,10 @@ sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dty
 
   if (static_cast<int64_t>(B) * (sv::items_per_seq(p.L) + p.nblk_b) > INT32_MAX)
     return SV_ERR_UNSUPPORTED;
+  if (zero_first) {  // the part of the workspace this call uses, cleared on its stream first
+    const hipError_t e = zero_fill(workspace, L.total, stream);
+    if (e != hipSuccess) return SV_ERR_HIP;
+  }
   return from_hip(sv::launch_chain(p, dtype, ev, stream));
 }
 
@@ -365,6 +419,25 @@ sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, s
   return chain_call(target_logits, draft_logits, dtype, draft_tokens, temperature, uniforms, B, K, V, accept_len,
                     out_tokens, p_draft, q_draft, residual_mass, entropy, nullptr, err_flags, workspace,
                     workspace_bytes, stream, ev);
+}
+
+sv_status sv_verify_chain_noalloc(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                                  const int32_t* draft_tokens, const float* temperature, const float* uniforms,
+                                  int32_t B, int32_t K, int32_t V, int32_t* accept_len, int32_t* out_tokens,
+                                  float* p_draft, float* q_draft, float* residual_mass, float* entropy,
+                                  int32_t* err_flags, hipStream_t stream) {
+  const sv::PassEvents ev = sv::take_pass_events();
+  if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return SV_ERR_INVALID_ARGUMENT;
+  if (B > 0 && accept_len == nullptr) return SV_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SV_OK;
+  const size_t need = chain_layout(B, K, V, dtype).total;
+  if (need > static_cast<size_t>(SV_NOALLOC_SCRATCH_BYTES)) return SV_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  const sv_status st = scratch_of_current_device(&ws);
+  if (st != SV_OK) return st;
+  return chain_call(target_logits, draft_logits, dtype, draft_tokens, temperature, uniforms, B, K, V, accept_len,
+                    out_tokens, p_draft, q_draft, residual_mass, entropy, nullptr, err_flags, ws, need, stream, ev,
+                    /*zero_first=*/true);
 }
 
 size_t sv_sample_workspace_bytes(int32_t R, int32_t V, sv_dtype dtype) {

@@ -90,6 +90,11 @@ def _load():
             _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
         ]
         lib.sv_sample_rows.restype = ctypes.c_int
+        lib.sv_verify_chain_noalloc.argtypes = [
+            _c_ptr, _c_ptr, ctypes.c_int, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+        ]
+        lib.sv_verify_chain_noalloc.restype = ctypes.c_int
         lib.sv_chain_launches.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int, _c_i32, _c_i32]
         lib.sv_chain_launches.restype = _c_i32
         lib.sv_time_next_stream_pass.argtypes = [_c_ptr, _c_ptr]
@@ -257,21 +262,11 @@ def sv_tree_workspace_bytes(B: int, N: int, V: int, dtype: torch.dtype) -> int:
     return int(_load().sv_tree_workspace_bytes(B, N, V, _DTYPES[dtype]))
 
 
-@_stream_ordered
-def sv_verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
-                    temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
-                    accept_len=None, out_tokens=None, p_draft=None, q_draft=None, residual_mass=None,
-                    entropy=None, err_flags=None, workspace_tensor=None, stream=None, want_probs: bool = True,
-                    want_entropy: bool = False) -> dict:
-    """Chain verification (``sv_verify_chain``). Shapes as in include/specverify.h.
-
-    Returns a dict with ``accept_len [B]``, ``out_tokens [B,K+1]``, and when
-    ``want_probs`` ``p_draft``, ``q_draft [B,K]``, ``residual_mass [B]``, when
-    ``want_entropy`` (or an ``entropy`` tensor is passed) ``entropy [B,2K+1]``,
-    plus ``err_flags [1]``. Outputs are ready once the stream has been
-    synchronised.
-    """
-    lib = _load()
+def _chain_prepare(target, draft, draft_tokens, temperature, uniforms, accept_len, out_tokens, p_draft, q_draft,
+                   residual_mass, entropy, err_flags, want_probs, want_entropy):
+    """Check a chain call's tensors and allocate the outputs the caller did
+    not pass (on the current stream, which the public calls make the call's
+    stream). Returns (B, K, V, dtype code, output dict)."""
     if target.dim() != 3:
         raise ValueError("target must be [B, K+1, V]")
     B, K1, V = target.shape
@@ -287,30 +282,78 @@ def sv_verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_t
     _dev(uniforms, "uniforms", dtype=torch.float32, shape=(B, K1), device=dev)
     i32 = dict(dtype=torch.int32, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
-    accept_len = torch.empty((B,), **i32) if accept_len is None else _dev(accept_len, "accept_len", torch.int32, (B,), dev)
-    out_tokens = torch.empty((B, K1), **i32) if out_tokens is None else _dev(out_tokens, "out_tokens", torch.int32, (B, K1), dev)
+    out = {
+        "accept_len": torch.empty((B,), **i32) if accept_len is None
+        else _dev(accept_len, "accept_len", torch.int32, (B,), dev),
+        "out_tokens": torch.empty((B, K1), **i32) if out_tokens is None
+        else _dev(out_tokens, "out_tokens", torch.int32, (B, K1), dev),
+        "err_flags": torch.zeros((1,), **i32) if err_flags is None
+        else _dev(err_flags, "err_flags", torch.int32, (1,), dev),
+    }
     if want_probs:
-        p_draft = torch.empty((B, K), **f32) if p_draft is None else _dev(p_draft, "p_draft", torch.float32, (B, K), dev)
-        q_draft = torch.empty((B, K), **f32) if q_draft is None else _dev(q_draft, "q_draft", torch.float32, (B, K), dev)
-        residual_mass = torch.empty((B,), **f32) if residual_mass is None else _dev(residual_mass, "residual_mass", torch.float32, (B,), dev)
+        out["p_draft"] = torch.empty((B, K), **f32) if p_draft is None else _dev(p_draft, "p_draft", torch.float32, (B, K), dev)
+        out["q_draft"] = torch.empty((B, K), **f32) if q_draft is None else _dev(q_draft, "q_draft", torch.float32, (B, K), dev)
+        out["residual_mass"] = (torch.empty((B,), **f32) if residual_mass is None
+                                else _dev(residual_mass, "residual_mass", torch.float32, (B,), dev))
     if entropy is not None:
-        _dev(entropy, "entropy", torch.float32, (B, 2 * K + 1), dev)
+        out["entropy"] = _dev(entropy, "entropy", torch.float32, (B, 2 * K + 1), dev)
     elif want_entropy:
-        entropy = torch.empty((B, 2 * K + 1), **f32)
-    err_flags = torch.zeros((1,), **i32) if err_flags is None else _dev(err_flags, "err_flags", torch.int32, (1,), dev)
+        out["entropy"] = torch.empty((B, 2 * K + 1), **f32)
+    return B, K, V, code, out
+
+
+def _chain_pointers(target, draft, draft_tokens, temperature, uniforms, B, K, V, code, o):
+    return (_ptr(target), _ptr(draft) if K > 0 else None, code, _ptr(draft_tokens) if K > 0 else None,
+            _ptr(temperature), _ptr(uniforms), B, K, V,
+            _ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o.get("p_draft")), _ptr(o.get("q_draft")),
+            _ptr(o.get("residual_mass")), _ptr(o.get("entropy")), _ptr(o["err_flags"]))
+
+
+@_stream_ordered
+def sv_verify_chain(target: torch.Tensor, draft: Optional[torch.Tensor], draft_tokens: Optional[torch.Tensor],
+                    temperature: Optional[torch.Tensor], uniforms: torch.Tensor, *,
+                    accept_len=None, out_tokens=None, p_draft=None, q_draft=None, residual_mass=None,
+                    entropy=None, err_flags=None, workspace_tensor=None, stream=None, want_probs: bool = True,
+                    want_entropy: bool = False) -> dict:
+    """Chain verification (``sv_verify_chain``). Shapes as in include/specverify.h.
+
+    Returns a dict with ``accept_len [B]``, ``out_tokens [B,K+1]``, and when
+    ``want_probs`` ``p_draft``, ``q_draft [B,K]``, ``residual_mass [B]``, when
+    ``want_entropy`` (or an ``entropy`` tensor is passed) ``entropy [B,2K+1]``,
+    plus ``err_flags [1]``. Outputs are ready once the stream has been
+    synchronised.
+    """
+    lib = _load()
+    B, K, V, code, out = _chain_prepare(target, draft, draft_tokens, temperature, uniforms, accept_len, out_tokens,
+                                        p_draft, q_draft, residual_mass, entropy, err_flags, want_probs,
+                                        want_entropy)
+    dev = target.device
     nbytes = int(lib.sv_chain_workspace_bytes(B, K, V, code))
     ws = workspace(dev, nbytes, stream) if workspace_tensor is None else workspace_tensor
-    st = lib.sv_verify_chain(
-        _ptr(target), _ptr(draft) if K > 0 else None, code, _ptr(draft_tokens) if K > 0 else None,
-        _ptr(temperature), _ptr(uniforms), B, K, V,
-        _ptr(accept_len), _ptr(out_tokens), _ptr(p_draft), _ptr(q_draft), _ptr(residual_mass), _ptr(entropy),
-        _ptr(err_flags), _ptr(ws), ws.numel(), _stream_handle(dev, stream))
+    st = lib.sv_verify_chain(*_chain_pointers(target, draft, draft_tokens, temperature, uniforms, B, K, V, code, out),
+                             _ptr(ws), ws.numel(), _stream_handle(dev, stream))
     _check(st, "sv_verify_chain")
-    out = {"accept_len": accept_len, "out_tokens": out_tokens, "err_flags": err_flags}
-    if want_probs:
-        out.update(p_draft=p_draft, q_draft=q_draft, residual_mass=residual_mass)
-    if entropy is not None:
-        out["entropy"] = entropy
+    return out
+
+
+@_stream_ordered
+def sv_verify_chain_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor],
+                            draft_tokens: Optional[torch.Tensor], temperature: Optional[torch.Tensor],
+                            uniforms: torch.Tensor, *, accept_len=None, out_tokens=None, p_draft=None, q_draft=None,
+                            residual_mass=None, entropy=None, err_flags=None, stream=None, want_probs: bool = True,
+                            want_entropy: bool = False) -> dict:
+    """``sv_verify_chain_noalloc``: chain verification on the library's static
+    per-GPU scratch array, no workspace. The library allocates nothing; to
+    allocate nothing here either, pass every output tensor (and err_flags).
+    Calls that overlap in time on one GPU race (they share the array)."""
+    lib = _load()
+    B, K, V, code, out = _chain_prepare(target, draft, draft_tokens, temperature, uniforms, accept_len, out_tokens,
+                                        p_draft, q_draft, residual_mass, entropy, err_flags, want_probs,
+                                        want_entropy)
+    st = lib.sv_verify_chain_noalloc(
+        *_chain_pointers(target, draft, draft_tokens, temperature, uniforms, B, K, V, code, out),
+        _stream_handle(target.device, stream))
+    _check(st, "sv_verify_chain_noalloc")
     return out
 
 

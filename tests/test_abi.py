@@ -195,3 +195,20 @@ def test_chain_launches_query(lib):
     assert f(64, 5, 128255, 1, 1, 0) == 2  # rows off 16-byte boundaries
     assert f(64, 0, 128256, 1, 1, 0) == 2  # K = 0
     assert f(64, 5, 128256, 1, 1, 0) in (1, 2)
+
+
+def test_noalloc_rejects_oversize_before_touching_the_device(lib):
+    # B=256 K=63 V=256000 bf16 needs more workspace than the static array
+    # holds: rejected from the sizes alone (no pointer is dereferenced)
+    f = lib.sv_verify_chain_noalloc
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + [ctypes.c_void_p] * 8
+    ws = lib.sv_chain_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int]
+    assert ws(256, 63, 256000, 1) > 8 << 20 >= ws(1024, 6, 256000, 1)
+    fake = ctypes.c_void_p(16)  # never dereferenced on these paths
+    assert f(None, None, 1, None, None, None, 256, 63, 256000, fake, None, None, None, None, None, None, None) == 2
+    assert f(None, None, 1, None, None, None, 4, 64, 100, fake, None, None, None, None, None, None, None) == 1
+    assert f(None, None, 1, None, None, None, 0, 5, 100, fake, None, None, None, None, None, None, None) == 0
