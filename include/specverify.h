@@ -202,6 +202,64 @@ int32_t sv_chain_launches(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32
                           int32_t with_entropy);
 
 /* ------------------------------------------------------------------------
+ * Chain verification with the target's LM head in the call.
+ *
+ * The target model scores every verified position in one forward pass, and
+ * its last layer maps each position's final hidden state to one logit per
+ * vocabulary entry ([Topologies] section 2 timeline figure, step 2;
+ * [Draft-and-Verify] "Why autoregressive decoding is slow": the pass is
+ * bound by streaming the weights):
+ *
+ *   logits[m, v] = sum_h hidden[m, h] * head_weight[v, h]
+ *
+ * sv_lm_head_logits computes that layer alone (a bf16 MFMA GEMM, fp32
+ * accumulation, logits rounded to bf16, round to nearest even).
+ * sv_verify_chain_lm_head computes it for the B (K+1) target rows of a
+ * chain verification and takes each row's softmax statistics in the GEMM's
+ * epilogue, from the rounded values it stores, so the target logits are not
+ * read back for them; the draft rows are streamed once as in sv_verify_chain,
+ * and the decision and the residual or bonus draw are sv_verify_chain's (the
+ * draw re-reads the stored target row at the first rejection). The outputs
+ * follow sv_verify_chain exactly, on target logits equal to the returned
+ * `target_logits`.
+ *
+ * Both take bf16 only, H a multiple of 64 (>= 64), V a multiple of 8, and
+ * 16-byte-aligned hidden, head_weight, logits and draft_logits; otherwise
+ * SV_ERR_INVALID_ARGUMENT, and nothing is enqueued.
+ */
+size_t sv_lm_head_chain_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t H);
+
+/*
+ *   hidden         [M, H] bf16 (device, read only)
+ *   head_weight    [V, H] bf16, one row per vocabulary entry (read only)
+ *   M, H, V        host ints: M >= 0
+ *   logits         [M, V] bf16 out
+ *   stream         HIP stream (NULL = default)
+ */
+sv_status sv_lm_head_logits(const void* hidden, const void* head_weight, int32_t M, int32_t H, int32_t V,
+                            void* logits, hipStream_t stream);
+
+/*
+ *   hidden         [B, K+1, H] bf16: the target's final hidden state at each
+ *                  verified position (read only)
+ *   head_weight    [V, H] bf16 (read only)
+ *   H              host int: hidden size
+ *   target_logits  [B, K+1, V] bf16 out: the target's logits (the GEMM's
+ *                  stored output, which the call also reads for its draw)
+ *   draft_logits .. err_flags: as sv_verify_chain (bf16 draft logits;
+ *                  no entropy output)
+ *   workspace      device buffer of at least
+ *                  sv_lm_head_chain_workspace_bytes() bytes, zero-filled
+ *                  before first use; each successful call leaves it zero
+ *   stream         HIP stream (NULL = default)
+ */
+sv_status sv_verify_chain_lm_head(const void* hidden, const void* head_weight, int32_t H, void* target_logits,
+                                  const void* draft_logits, const int32_t* draft_tokens, const float* temperature,
+                                  const float* uniforms, int32_t B, int32_t K, int32_t V, int32_t* accept_len,
+                                  int32_t* out_tokens, float* p_draft, float* q_draft, float* residual_mass,
+                                  int32_t* err_flags, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Draft-side sampling.
  *
  * Bytes of device workspace sv_sample_rows needs; 0 for invalid sizes. Same
@@ -399,9 +457,10 @@ sv_status sv_build_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, i
  * Profiling hook (not part of the verification contract).
  *
  * Arms the calling host thread's NEXT sv_verify_chain, sv_verify_tree_greedy,
- * sv_sample_rows or sv_verify_tree_sampling call to launch its streaming pass
- * (the kernel that reads every logit once: chain statistics, tree argmax, run
- * records) with `before` and `after` as the launch's start and stop events
+ * sv_sample_rows, sv_verify_tree_sampling, sv_verify_chain_lm_head or
+ * sv_lm_head_logits call to launch its first kernel (the kernel that reads
+ * every logit once: chain statistics, the one-launch chain kernel, tree
+ * argmax, run records; the LM-head GEMM) with `before` and `after` as the launch's start and stop events
  * (hipExtLaunchKernel), so that they carry that kernel's own start and end
  * timestamps; the call then disarms the hook. A call that
  * fails its argument checks records nothing and also disarms it.

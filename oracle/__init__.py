@@ -19,4 +19,7 @@ from .specverify_oracle import (  # noqa: F401
     verify_tree_stochastic,
     children_in_order,
     tree_mask,
+    round_to_bf16,
+    lm_head_logits,
+    verify_chain_lm_head,
 )

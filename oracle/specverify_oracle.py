@@ -314,6 +314,52 @@ def verify_chain_distributions(p, q, draft_tokens, uniforms, valid):
     }
 
 
+# ----------------------------------------------------------------------------- the target's LM head
+
+def round_to_bf16(x):
+    """Round to the nearest bfloat16 value, ties to even, returned as float64.
+
+    bfloat16 keeps 8 significant bits (the upper half of a binary32). A
+    finite x = m 2^e with m in [1/2, 1) becomes rint(m 2^8) 2^(e-8), rint
+    rounding half to even. Values beyond the binary32 exponent range are
+    outside this oracle's use (the synthetic logits are small).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+
+
+def lm_head_logits(hidden, weight):
+    """The target's logits at every verified position: logits[m, v] =
+    sum_h hidden[m, h] weight[v, h], in float64.
+
+    [Topologies] section 2 timeline figure, step 2 (the target model scores
+    every drafted position in one forward pass); [Draft-and-Verify] "Why
+    autoregressive decoding is slow" and "The draft-and-verify loop" (each
+    verified position yields a distribution over the vocabulary). The pages
+    do not print the model; the last layer is taken as a plain linear map
+    from the final hidden state to one logit per vocabulary entry.
+    ``hidden [..., H]`` (any leading shape), ``weight [V, H]``.
+    """
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    return h @ w.T
+
+
+def verify_chain_lm_head(hidden, weight, draft_logits, draft_tokens, temperature, uniforms, with_entropy=False):
+    """Chain verification with the target's logits made by its LM head:
+    the logits of ``hidden [B, K+1, H]`` through ``weight [V, H]``
+    (:func:`lm_head_logits`), stored as bfloat16 (:func:`round_to_bf16`,
+    the precision the target hands to verification), then
+    :func:`verify_chain` on them with the draft's logits. Returns
+    verify_chain's dict plus ``target_logits [B, K+1, V]`` (the stored
+    values, float64)."""
+    t = round_to_bf16(lm_head_logits(hidden, weight))
+    res = verify_chain(t, draft_logits, draft_tokens, temperature, uniforms, with_entropy=with_entropy)
+    res["target_logits"] = t
+    return res
+
+
 # ----------------------------------------------------------------------------- tree verification
 
 def _check_parents(parents):

@@ -32,6 +32,9 @@ from .specverify import (  # noqa: F401
     sv_tree_workspace_bytes,
     sv_verify_chain,
     sv_verify_chain_noalloc,
+    sv_verify_chain_lm_head,
+    sv_lm_head_logits,
+    sv_lm_head_chain_workspace_bytes,
     sv_verify_tree_greedy,
     sv_verify_tree_sampling,
 )

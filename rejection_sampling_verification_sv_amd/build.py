@@ -17,7 +17,7 @@ REPO_DIR = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["sv_api.hip", "sv_chain.hip", "sv_sample.hip", "sv_tree.hip", "sv_tree_sample.hip"]
+SOURCES = ["sv_api.hip", "sv_chain.hip", "sv_lm_head.hip", "sv_sample.hip", "sv_tree.hip", "sv_tree_sample.hip"]
 HEADERS = ["sv_device.h", "sv_internal.h", "sv_stream.h"]
 ARCH = "gfx950"
 

@@ -127,7 +127,9 @@ struct ChainLayout {
   size_t off_part_m, off_part_s, off_part_a, off_cnt, off_tiles, off_gat, off_abort, off_tk, off_done, total;
 };
 
-ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
+// min_parts: slots the call's statistics need at least (a layout other than
+// the ones sized here, e.g. the LM-head call's one piece per row).
+ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d, int64_t min_parts = 0) {
   ChainLayout L{};
   const int32_t R = 2 * K + 1;
   L.ntiles = static_cast<int32_t>(ceil_div(V, sv::kSampleTile));
@@ -139,7 +141,8 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d) {
   const int64_t groups = ceil_div(static_cast<int64_t>(B) * ceil_div(L.ntiles, group), sv::kSampleBlocks);
   L.tiles_per_block = static_cast<int32_t>(group * (groups < 1 ? 1 : groups));
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
-  const int64_t parts = piece_slots(B, R, V, d, row_chunk_vecs(B, R, V, d, sv::kChunksChain));
+  int64_t parts = piece_slots(B, R, V, d, row_chunk_vecs(B, R, V, d, sv::kChunksChain));
+  if (parts < min_parts) parts = min_parts;
   size_t off = 0;
   L.off_part_m = off;
   off = align_up(off + sizeof(uint64_t) * parts);
@@ -438,6 +441,138 @@ sv_status sv_verify_chain_noalloc(const void* target_logits, const void* draft_l
   return chain_call(target_logits, draft_logits, dtype, draft_tokens, temperature, uniforms, B, K, V, accept_len,
                     out_tokens, p_draft, q_draft, residual_mass, entropy, nullptr, err_flags, ws, need, stream, ev,
                     /*zero_first=*/true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The LM-head chain call: shapes it serves (bf16 only; H a multiple of 64,
+// V of 8) and its workspace: the chain call's regions (slots for the
+// whole-row layout), then the GEMM's statistics pieces.
+bool lm_head_sizes_ok(int32_t B, int32_t K, int32_t V, int32_t H) {
+  return chain_sizes_ok(B, K, V) && V >= 8 && V % 8 == 0 && H >= 64 && H % 64 == 0 &&
+         static_cast<int64_t>(B) * (K + 1) <= INT32_MAX;
+}
+
+struct LMHeadLayout {
+  ChainLayout chain;
+  int32_t ntn;
+  size_t off_pieces, total;
+};
+
+// One piece per row: every row a chunk of its own.
+sv::PieceLayout lm_head_piece_layout(int32_t K, int32_t V) {
+  return piece_layout(2 * K + 1, V, SV_DTYPE_BF16, true, row_vecs(V, SV_DTYPE_BF16));
+}
+
+LMHeadLayout lm_head_layout(int32_t B, int32_t K, int32_t V) {
+  LMHeadLayout L{};
+  L.chain = chain_layout(B, K, V, SV_DTYPE_BF16, B * sv::slots_per_seq(lm_head_piece_layout(K, V)));
+  L.ntn = static_cast<int32_t>(ceil_div(V, sv::kLMTile));
+  L.off_pieces = L.chain.total;
+  L.total = align_up(L.off_pieces + sizeof(float2) * static_cast<int64_t>(B) * (K + 1) * L.ntn);
+  return L;
+}
+
+sv::LMHeadParams lm_head_params(const void* hidden, const void* weight, void* logits, int32_t M, int32_t N,
+                                int32_t H, int32_t K1, const float* temperature) {
+  sv::LMHeadParams g{};
+  g.hidden = hidden;
+  g.weight = weight;
+  g.logits = logits;
+  g.M = M;
+  g.N = N;
+  g.H = H;
+  g.K1 = K1;
+  g.temperature = temperature;
+  g.mtiles = static_cast<int32_t>(ceil_div(M, sv::kLMTile));
+  g.ntiles_n = static_cast<int32_t>(ceil_div(N, sv::kLMTile));
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_lm_head_chain_workspace_bytes(int32_t B, int32_t K, int32_t V, int32_t H) {
+  if (!lm_head_sizes_ok(B, K, V, H)) return 0;
+  return lm_head_layout(B, K, V).total;
+}
+
+sv_status sv_lm_head_logits(const void* hidden, const void* head_weight, int32_t M, int32_t H, int32_t V,
+                            void* logits, hipStream_t stream) {
+  const sv::PassEvents ev = sv::take_pass_events();
+  if (M < 0 || !lm_head_sizes_ok(1, 0, V, H)) return SV_ERR_INVALID_ARGUMENT;
+  if (M == 0) return SV_OK;
+  if (hidden == nullptr || head_weight == nullptr || logits == nullptr) return SV_ERR_INVALID_ARGUMENT;
+  if (!aligned_to(hidden, 16) || !aligned_to(head_weight, 16) || !aligned_to(logits, 16))
+    return SV_ERR_INVALID_ARGUMENT;
+  const sv::LMHeadParams g = lm_head_params(hidden, head_weight, logits, M, V, H, 1, nullptr);
+  if (sv::lm_head_grid(g) > INT32_MAX) return SV_ERR_UNSUPPORTED;
+  return from_hip(sv::launch_lm_head_gemm(g, false, ev, stream));
+}
+
+sv_status sv_verify_chain_lm_head(const void* hidden, const void* head_weight, int32_t H, void* target_logits,
+                                  const void* draft_logits, const int32_t* draft_tokens, const float* temperature,
+                                  const float* uniforms, int32_t B, int32_t K, int32_t V, int32_t* accept_len,
+                                  int32_t* out_tokens, float* p_draft, float* q_draft, float* residual_mass,
+                                  int32_t* err_flags, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  const sv::PassEvents ev = sv::take_pass_events();
+  if (!lm_head_sizes_ok(B, K, V, H)) return SV_ERR_INVALID_ARGUMENT;
+  if (B == 0) return SV_OK;
+  if (hidden == nullptr || head_weight == nullptr || target_logits == nullptr || uniforms == nullptr ||
+      accept_len == nullptr || out_tokens == nullptr)
+    return SV_ERR_INVALID_ARGUMENT;
+  if (K > 0 && (draft_logits == nullptr || draft_tokens == nullptr)) return SV_ERR_INVALID_ARGUMENT;
+  if (!aligned_to(hidden, 16) || !aligned_to(head_weight, 16) || !aligned_to(target_logits, 16) ||
+      (K > 0 && !aligned_to(draft_logits, 16)))
+    return SV_ERR_INVALID_ARGUMENT;
+  const LMHeadLayout LL = lm_head_layout(B, K, V);
+  if (workspace == nullptr || workspace_bytes < LL.total || !aligned_to(workspace, 8)) return SV_ERR_WORKSPACE;
+  const int32_t M = B * (K + 1);
+  char* ws = static_cast<char*>(workspace);
+  sv::LMHeadParams g = lm_head_params(hidden, head_weight, target_logits, M, V, H, K + 1, temperature);
+  g.pieces = reinterpret_cast<float2*>(ws + LL.off_pieces);  // the epilogue's statistics, [M, ntn]
+  if (sv::lm_head_grid(g) > INT32_MAX) return SV_ERR_UNSUPPORTED;
+
+  const ChainLayout& L = LL.chain;
+  sv::ChainParams p{};
+  p.target = target_logits;  // the GEMM's stored logits feed the gathers and the draw
+  p.draft = draft_logits;
+  p.tokens = draft_tokens;
+  p.temperature = temperature;
+  p.uniforms = uniforms;
+  p.B = B;
+  p.K = K;
+  p.V = V;
+  // one piece per row: the target rows' from the GEMM's pieces, the draft
+  // rows' from one stream over each row
+  p.L = lm_head_piece_layout(K, V);
+  p.ntiles = L.ntiles;
+  p.tiles_per_block = L.tiles_per_block;
+  p.nblk_b = L.nblk_b;
+  p.accept_len = accept_len;
+  p.out_tokens = out_tokens;
+  p.p_draft = p_draft;
+  p.q_draft = q_draft;
+  p.residual_mass = residual_mass;
+  p.err_flags = err_flags;
+  p.part_m = reinterpret_cast<uint64_t*>(ws + L.off_part_m);
+  p.part_s = reinterpret_cast<uint64_t*>(ws + L.off_part_s);
+  p.part_a = reinterpret_cast<uint64_t*>(ws + L.off_part_a);
+  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+  p.tile_sum = reinterpret_cast<uint64_t*>(ws + L.off_tiles);
+  p.gat = reinterpret_cast<uint64_t*>(ws + L.off_gat);
+  p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
+  p.tk = reinterpret_cast<uint32_t*>(ws + L.off_tk);
+  p.done = reinterpret_cast<uint32_t*>(ws + L.off_done);
+  p.lm_pieces = reinterpret_cast<float2*>(ws + LL.off_pieces);
+  p.lm_ntn = LL.ntn;
+  if (static_cast<int64_t>(B) * K + (static_cast<int64_t>(M) + 3) / 4 > INT32_MAX ||
+      static_cast<int64_t>(B) * p.nblk_b > INT32_MAX)
+    return SV_ERR_UNSUPPORTED;
+  return from_hip(sv::launch_chain_lm_head(g, p, ev, stream));
 }
 
 size_t sv_sample_workspace_bytes(int32_t R, int32_t V, sv_dtype dtype) {

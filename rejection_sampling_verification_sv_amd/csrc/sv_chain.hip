@@ -1074,6 +1074,75 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- LM-head chain call
+
+// After the LM-head GEMM: blocks below B K stream one draft row each (the
+// statistics pass over the whole-row layout: rows K+1 .. 2K of each
+// sequence); the others combine the GEMM's pieces of the target rows, one
+// wave per row. A row's pieces are folded in fp64 like the decision folds a
+// row's pieces (a running fp32 reference, sums rescaled by 2^(lower -
+// higher reference)), each lane over every 64th piece, then across the wave;
+// the row's (reference, sum) goes to its slot and, for a drafted position,
+// the stored logit at the drafted token to its gather slot. The pieces are
+// left zero (the workspace contract).
+template <class T>
+__global__ __launch_bounds__(kThreads) void lm_head_stats_kernel(ChainParams P) {
+  const uint32_t K = static_cast<uint32_t>(P.K);
+  const uint32_t ndraft = static_cast<uint32_t>(P.B) * K;
+  if (blockIdx.x < ndraft) {
+    const uint32_t b = blockIdx.x / K;
+    stats_chunk<T, kStatsTPB, false>(P, static_cast<int>(b), static_cast<int>(K + 1 + (blockIdx.x - b * K)));
+    return;
+  }
+  const int64_t M = static_cast<int64_t>(P.B) * (K + 1);
+  const int64_t m = static_cast<int64_t>(blockIdx.x - ndraft) * kWaves + wave_id();
+  if (m >= M) return;
+  const int lane = lane_id();
+  float2* pc = P.lm_pieces + m * P.lm_ntn;
+  float mf = -INFINITY;
+  double zf = 0.0;
+  for (int i = lane; i < P.lm_ntn; i += kWave) {
+    const float2 v = pc[i];
+    pc[i] = make_float2(0.0f, 0.0f);
+    if (v.x == -INFINITY) continue;
+    const double sv = static_cast<double>(v.y);
+    if (v.x > mf) {
+      zf = zf * ((mf == -INFINITY) ? 0.0 : ref_factor(mf, v.x)) + sv;
+      mf = v.x;
+    } else {
+      zf += sv * ref_factor(v.x, mf);
+    }
+  }
+  const float Mx = wave_max(mf);
+  double z = (mf == -INFINITY) ? 0.0 : zf * ref_factor(mf, Mx);
+  z = wave_sum(z);
+  if (lane == 0) {
+    const int b = static_cast<int>(m / (K + 1));
+    const int r = static_cast<int>(m - static_cast<int64_t>(b) * (K + 1));  // target row r of sequence b
+    const int64_t slot = (static_cast<int64_t>(b) * P.L.cps + r) * P.L.kmax;
+    publish(&P.part_m[slot], tag_float(Mx));
+    publish(&P.part_s[slot], tag_nonneg_double(z));
+    const int x = row_token(P, b, r);
+    if (x >= 0 && x < P.V) publish_gather<T>(P, b, r, chain_row<T>(P, b, r), x);
+  }
+}
+
+hipError_t launch_chain_lm_head(const LMHeadParams& g, const ChainParams& p, const PassEvents& ev,
+                                hipStream_t stream) {
+  hipError_t e = launch_lm_head_gemm(g, true, ev, stream);
+  if (e != hipSuccess) return e;
+  const int64_t M = static_cast<int64_t>(p.B) * (p.K + 1);
+  const int64_t grid_s = static_cast<int64_t>(p.B) * p.K + (M + kWaves - 1) / kWaves;
+  const int64_t grid_c = static_cast<int64_t>(p.B) * p.nblk_b;
+  if (grid_s > INT32_MAX || grid_c > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(lm_head_stats_kernel<BF16>, dim3(static_cast<uint32_t>(grid_s)), dim3(kThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  void (*sample)(ChainParams) = p.K == 0 ? chain_sample_one_row_kernel<BF16, false> : chain_sample_kernel<BF16, false>;
+  hipLaunchKernelGGL(sample, dim3(static_cast<uint32_t>(grid_c)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_chain(const ChainParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream) {
   return dtype == SV_DTYPE_BF16 ? launch_chain_t<BF16>(p, ev, stream) : launch_chain_t<F32>(p, ev, stream);
 }

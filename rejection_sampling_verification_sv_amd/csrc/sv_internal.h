@@ -113,7 +113,29 @@ struct ChainParams {
   int32_t one_launch;
   uint32_t* tk;       // [B]
   uint32_t* done;     // [B]
+  // LM-head chain call: the GEMM's statistics pieces of the target rows,
+  // [B (K+1), lm_ntn] (reference, sum), combined into the row slots (and
+  // zeroed) by lm_head_stats_kernel
+  float2* lm_pieces;
+  int32_t lm_ntn;
 };
+
+// The target's LM head as a GEMM: logits [M, N] = hidden [M, H] x weight
+// [N, H]^T, bf16 in and out, fp32 accumulation; with the statistics, one
+// (reference, sum) piece per row and 128-column tile (see sv_lm_head.hip).
+struct LMHeadParams {
+  const void* hidden;        // [M, H] bf16, 16-byte aligned
+  const void* weight;        // [N, H] bf16, 16-byte aligned
+  void* logits;              // [M, N] bf16 out, 16-byte aligned
+  int32_t M, N;              // N a multiple of 8
+  int64_t H;                 // a multiple of 64
+  int32_t K1;                // rows per sequence: row m belongs to sequence m / K1
+  const float* temperature;  // [M / K1] or null (1.0)
+  int32_t mtiles, ntiles_n;  // 128-row and 128-column tiles
+  float2* pieces;            // [M, ntiles_n] out (statistics only)
+};
+constexpr int kLMTile = 128;
+
 
 // Sampling verification of a candidate tree: the run records of the target
 // rows [B, N+1, V] (records rows 0 .. B(N+1)-1) and of the draft rows
@@ -367,5 +389,12 @@ hipError_t launch_tree_sample(const TreeSampleParams& p, sv_dtype dtype,
 hipError_t launch_tree(const TreeParams& p, sv_dtype dtype, const PassEvents& ev, hipStream_t stream);
 hipError_t launch_tree_mask(const int32_t* parents, int32_t N, uint8_t* mask, int32_t* err_flags,
                             hipStream_t stream);
+int64_t lm_head_grid(const LMHeadParams& p);
+hipError_t launch_lm_head_gemm(const LMHeadParams& p, bool stats, const PassEvents& ev, hipStream_t stream);
+// The LM-head chain call: the GEMM with statistics, the statistics of the
+// draft rows and the combine of the target rows' pieces (one launch), then
+// the sampling pass (the chain call's, whole-row layout).
+hipError_t launch_chain_lm_head(const LMHeadParams& g, const ChainParams& p, const PassEvents& ev,
+                                hipStream_t stream);
 
 }  // namespace sv

@@ -95,6 +95,15 @@ def _load():
             _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
         ]
         lib.sv_verify_chain_noalloc.restype = ctypes.c_int
+        lib.sv_lm_head_chain_workspace_bytes.argtypes = [_c_i32, _c_i32, _c_i32, _c_i32]
+        lib.sv_lm_head_chain_workspace_bytes.restype = _c_size
+        lib.sv_lm_head_logits.argtypes = [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_ptr, _c_ptr]
+        lib.sv_lm_head_logits.restype = ctypes.c_int
+        lib.sv_verify_chain_lm_head.argtypes = [
+            _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32,
+            _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr,
+        ]
+        lib.sv_verify_chain_lm_head.restype = ctypes.c_int
         lib.sv_chain_launches.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int, _c_i32, _c_i32]
         lib.sv_chain_launches.restype = _c_i32
         lib.sv_time_next_stream_pass.argtypes = [_c_ptr, _c_ptr]
@@ -354,6 +363,64 @@ def sv_verify_chain_noalloc(target: torch.Tensor, draft: Optional[torch.Tensor],
         *_chain_pointers(target, draft, draft_tokens, temperature, uniforms, B, K, V, code, out),
         _stream_handle(target.device, stream))
     _check(st, "sv_verify_chain_noalloc")
+    return out
+
+
+def sv_lm_head_chain_workspace_bytes(B: int, K: int, V: int, H: int) -> int:
+    return int(_load().sv_lm_head_chain_workspace_bytes(B, K, V, H))
+
+
+@_stream_ordered
+def sv_lm_head_logits(hidden: torch.Tensor, head_weight: torch.Tensor, *, logits=None, stream=None) -> torch.Tensor:
+    """The LM head alone (``sv_lm_head_logits``): ``hidden [..., H]`` bf16
+    through ``head_weight [V, H]`` bf16 -> logits ``[..., V]`` bf16."""
+    lib = _load()
+    H = hidden.shape[-1]
+    V = head_weight.shape[0]
+    dev = hidden.device
+    _dev(hidden, "hidden", torch.bfloat16)
+    _dev(head_weight, "head_weight", torch.bfloat16, (V, H), dev)
+    M = hidden.numel() // H
+    shape = tuple(hidden.shape[:-1]) + (V,)
+    logits = (torch.empty(shape, dtype=torch.bfloat16, device=dev) if logits is None
+              else _dev(logits, "logits", torch.bfloat16, shape, dev))
+    _check(lib.sv_lm_head_logits(_ptr(hidden), _ptr(head_weight), M, H, V, _ptr(logits), _stream_handle(dev, stream)),
+           "sv_lm_head_logits")
+    return logits
+
+
+@_stream_ordered
+def sv_verify_chain_lm_head(hidden: torch.Tensor, head_weight: torch.Tensor, draft: Optional[torch.Tensor],
+                            draft_tokens: Optional[torch.Tensor], temperature: Optional[torch.Tensor],
+                            uniforms: torch.Tensor, *, target_logits=None, accept_len=None, out_tokens=None,
+                            p_draft=None, q_draft=None, residual_mass=None, err_flags=None, workspace_tensor=None,
+                            stream=None, want_probs: bool = True) -> dict:
+    """Chain verification with the target's LM head in the call
+    (``sv_verify_chain_lm_head``): ``hidden [B, K+1, H]`` and ``head_weight
+    [V, H]`` bf16 give the target logits (returned as ``target_logits``), the
+    rest as :func:`sv_verify_chain`."""
+    lib = _load()
+    if hidden.dim() != 3:
+        raise ValueError("hidden must be [B, K+1, H]")
+    B, K1, H = hidden.shape
+    V = head_weight.shape[0]
+    dev = hidden.device
+    _dev(hidden, "hidden", torch.bfloat16)
+    _dev(head_weight, "head_weight", torch.bfloat16, (V, H), dev)
+    target_logits = (torch.empty((B, K1, V), dtype=torch.bfloat16, device=dev) if target_logits is None
+                     else _dev(target_logits, "target_logits", torch.bfloat16, (B, K1, V), dev))
+    _, K, _, code, out = _chain_prepare(target_logits, draft, draft_tokens, temperature, uniforms, accept_len,
+                                        out_tokens, p_draft, q_draft, residual_mass, None, err_flags, want_probs,
+                                        False)
+    nbytes = int(lib.sv_lm_head_chain_workspace_bytes(B, K, V, H))
+    ws = workspace(dev, nbytes, stream) if workspace_tensor is None else workspace_tensor
+    st = lib.sv_verify_chain_lm_head(
+        _ptr(hidden), _ptr(head_weight), H, _ptr(target_logits), _ptr(draft) if K > 0 else None,
+        _ptr(draft_tokens) if K > 0 else None, _ptr(temperature), _ptr(uniforms), B, K, V,
+        _ptr(out["accept_len"]), _ptr(out["out_tokens"]), _ptr(out.get("p_draft")), _ptr(out.get("q_draft")),
+        _ptr(out.get("residual_mass")), _ptr(out["err_flags"]), _ptr(ws), ws.numel(), _stream_handle(dev, stream))
+    _check(st, "sv_verify_chain_lm_head")
+    out["target_logits"] = target_logits
     return out
 
 

@@ -25,4 +25,7 @@ from .synth import (  # noqa: F401
     tree_parents_ranked,
     tree_inputs,
     sample_draft_tokens_gumbel,
+    LMHeadConfig,
+    LM_HEAD_CONFIGS,
+    lm_head_chain_inputs,
 )

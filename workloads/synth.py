@@ -50,6 +50,9 @@ STREAM_UNIFORMS = 3
 STREAM_TEMPERATURE = 4
 STREAM_TREE_REPLACE = 5
 STREAM_SAMPLE_UNIFORMS = 6
+STREAM_HIDDEN = 7
+STREAM_WEIGHT = 8
+STREAM_DRAFT_WEIGHT = 9
 
 _TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -181,6 +184,51 @@ class SampleTreeConfig:
 SAMPLE_TREE_CONFIGS = {
     "c4s": SampleTreeConfig("tree_sampling_b32_n64_v128256_bf16", 6, 32, 64, 128256, "bf16", 3.0, 1.0, 1.0,
                             (4, 3, 2, 2, 1)),
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class LMHeadConfig:
+    """Chain verification whose target logits come out of the target's LM
+    head: hidden states ``[B, K+1, H]`` and head weights ``[V, H]`` (bf16).
+
+    The hidden states are N(0, 1) with a last column of ones; the weights are
+    N(0, target_sigma^2 / (H - 1)) with a last column holding the Zipf
+    log-prior -s ln(v + 1), so the logits look like the chain workload's
+    N(0, target_sigma^2) + prior. The draft's logits come from its own head:
+    the same hidden states through the weights plus N(0, draft_sigma^2 /
+    (H - 1)) noise, so draft - target has about draft_sigma's spread.
+    ``exact``: integer hidden states and weights in [-3, 3] (draft head:
+    each weight moved by +-1 with probability 0.2 each), whose sums a float32
+    accumulation forms exactly; the temperature then scales those integer
+    logits to the same spread.
+    """
+
+    name: str
+    config_id: int
+    B: int
+    K: int
+    V: int
+    H: int
+    target_sigma: float
+    zipf_s: float
+    draft_sigma: float
+    temperature: float
+    exact: bool = False
+    variant: int = 0
+
+    @property
+    def rows(self) -> int:
+        return self.B * (2 * self.K + 1)
+
+    def with_(self, **kw) -> "LMHeadConfig":
+        return dataclasses.replace(self, **kw)
+
+
+LM_HEAD_CONFIGS = {
+    "c2h": LMHeadConfig("lm_head_chain_b64_k5_v128256_h8192_bf16", 7, 64, 5, 128256, 8192, 2.5, 1.1, 0.8, 0.7),
+    "c2h_int": LMHeadConfig("lm_head_chain_b64_k5_v128256_h8192_bf16_integer", 8, 64, 5, 128256, 8192, 2.5, 1.1,
+                            0.8, 0.7, exact=True),
 }
 
 
@@ -528,3 +576,55 @@ def sample_tree_inputs(cfg: SampleTreeConfig, device="cpu", parents=None) -> dic
         tokens[b0:b1] = sample_draft_tokens_gumbel(rows, T[b0:b1], gx)
     return {"target": target, "draft": draft, "node_tokens": tokens,
             "parents": torch.from_numpy(parents).to(target.device), "temperature": T, "uniforms": uniforms}
+
+
+# ----------------------------------------------------------------------------- LM-head chain inputs
+
+def lm_head_chain_inputs(cfg: LMHeadConfig, device="cuda") -> dict:
+    """All inputs of one LM-head chain-verification call on ``device`` (a GPU;
+    the weights of the c2h workload are 2.1 GB).
+
+    Keys: ``hidden [B,K+1,H]``, ``weight [V,H]``, ``draft [B,K,V]`` (bf16),
+    ``draft_tokens [B,K]`` int32 (drawn from the stored draft logits at the
+    temperature), ``temperature [B]`` and ``uniforms [B,K+1]`` float32.
+    """
+    B, K, V, H = cfg.B, cfg.K, cfg.V, cfg.H
+    gh = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_HIDDEN)
+    gw = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_WEIGHT)
+    gd = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_DRAFT_WEIGHT)
+    prior = torch.from_numpy(zipf_log_prior(V, cfg.zipf_s)).to(device=device, dtype=torch.float32)
+    if cfg.exact:
+        hidden = torch.randint(-3, 4, (B, K + 1, H), generator=gh, device=device).float()
+        weight = torch.randint(-3, 4, (V, H), generator=gw, device=device).float()
+        weight[:, H - 1] = torch.round(8.0 * prior)
+        spread = math.sqrt((H - 1) * 4.0 * 4.0)  # sd of a sum of H-1 products of two uniform ints in [-3, 3]
+        temperature = cfg.temperature * spread / cfg.target_sigma
+    else:
+        hidden = torch.randn((B, K + 1, H), generator=gh, device=device)
+        weight = torch.randn((V, H), generator=gw, device=device) * (cfg.target_sigma / math.sqrt(H - 1))
+        weight[:, H - 1] = prior
+        temperature = cfg.temperature
+    hidden[..., H - 1] = 1.0
+    hidden = hidden.to(torch.bfloat16)
+    weight = weight.to(torch.bfloat16)
+    # the draft's head: perturbed weights on the same hidden states
+    draft = torch.empty((B, K, V), dtype=torch.bfloat16, device=device)
+    h_draft = hidden[:, :K].reshape(B * K, H).float()
+    per = max(1, (1 << 28) // (4 * max(1, B * K)))  # vocabulary rows per chunk
+    for v0 in range(0, V, per):
+        v1 = min(V, v0 + per)
+        w = weight[v0:v1].float()
+        if cfg.exact:
+            r = torch.rand(w.shape, generator=gd, device=device)
+            w = w + (r < 0.2).float() - (r > 0.8).float()
+        else:
+            w = w + torch.randn(w.shape, generator=gd, device=device) * (cfg.draft_sigma / math.sqrt(H - 1))
+        draft[:, :, v0:v1] = (h_draft @ w.T).reshape(B, K, v1 - v0).to(torch.bfloat16)
+        del w
+    temp = torch.full((B,), float(temperature), dtype=torch.float32, device=device)
+    gx = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_DRAFT_TOKENS)
+    tokens = sample_draft_tokens_gumbel(draft, temp, gx)
+    gu = _torch_generator(device, cfg.config_id, cfg.variant, STREAM_UNIFORMS)
+    uniforms = torch.rand((B, K + 1), generator=gu, device=device, dtype=torch.float32)
+    return {"hidden": hidden, "weight": weight, "draft": draft, "draft_tokens": tokens, "temperature": temp,
+            "uniforms": uniforms}
