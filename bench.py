@@ -56,8 +56,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2",
-                    help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain), c4 (greedy tree), c4s (sampling tree) "
-                         "or s1, s2, s3 (draft-side sampling)")
+                    help="c1, c2, c3_s0.3, c3_s1.0, c3_s3.0, c5 (chain), c4 (greedy tree), c4s (sampling tree), "
+                         "s1, s2, s3 (draft-side sampling) or c2h (chain with the target's LM head in the call)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of each call captured in a HIP graph (the call's launches without the "
@@ -206,6 +206,127 @@ def cpu_baseline_sample(inp, cfg, budget_s: float) -> dict:
     }
 
 
+def cpu_baseline_lm_head(inp, cfg, budget_s: float) -> dict:
+    """The oracle's LM-head chain verification (fp64 matmul of each sequence's
+    hidden states with the whole head, bf16 rounding, verify_chain), one
+    sequence at a time; the head's conversion to fp64 is not timed."""
+    import numpy as np
+
+    import oracle
+
+    w64 = inp["weight"].double().numpy()
+    jobs = [(lambda b=b: (inp["hidden"][b:b + 1].double().numpy(), w64, inp["draft"][b:b + 1].double().numpy(),
+                          inp["draft_tokens"][b:b + 1].numpy().astype(np.int64),
+                          inp["temperature"][b:b + 1].double().numpy(), inp["uniforms"][b:b + 1].double().numpy()),
+             oracle.verify_chain_lm_head, 1) for b in range(cfg.B)]
+    threads_before = os.environ.get("OMP_NUM_THREADS")
+    done, wall, cpu = _timed_oracle(jobs, budget_s)
+    return {
+        "value": done * (2 * cfg.K + 1) * cfg.V / wall,
+        "unit": "rows·vocab/s",
+        "cores": max(1, round(cpu / wall)),
+        "kind": "oracle",
+        "sample": f"{done} sequences of the same workload (fp64 LM head through numpy's multithreaded matmul, "
+                  f"OMP_NUM_THREADS={threads_before}), {wall:.1f} s in the oracle, {cpu:.1f} s CPU",
+    }
+
+
+def bench_lm_head(args, sv, torch, cfg, dev, stream) -> dict:
+    """Chain verification with the target's LM head in the call, against the
+    LM head alone followed by sv_verify_chain on its logits."""
+    from workloads import lm_head_chain_inputs
+
+    B, K, V, H = cfg.B, cfg.K, cfg.V, cfg.H
+    M = B * (K + 1)
+    sets = [lm_head_chain_inputs(cfg.with_(variant=cfg.variant + 10 * i) if i else cfg, device=dev)
+            for i in range(N_SETS)]
+    fused = [sv.PreparedLMHeadChainCall(x["hidden"], x["weight"], x["draft"], x["draft_tokens"], x["temperature"],
+                                        x["uniforms"], stream=stream) for x in sets]
+    heads = [sv.PreparedLMHeadLogitsCall(x["hidden"], x["weight"], stream=stream) for x in sets]
+    verifies = [sv.PreparedChainCall(h.logits, x["draft"], x["draft_tokens"], x["temperature"], x["uniforms"],
+                                     stream=stream) for h, x in zip(heads, sets)]
+    torch.cuda.synchronize()
+
+    def timed(step, n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        with torch.cuda.stream(stream):
+            for i in range(args.warmup):
+                step(i)
+            ev[0].record(stream)
+            for i in range(n):
+                step(i)
+            ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / n
+
+    def armed(call, n):
+        kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in kev:
+            a.record(stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        for i in range(n):
+            sv.sv_time_next_stream_pass(*kev[i])
+            call(i)
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in kev) / n
+
+    nsets = len(sets)
+    t0 = time.perf_counter()
+    fused_ms = timed(lambda i: fused[i % nsets](), args.steps)
+    t_wall = time.perf_counter() - t0
+    unfused_ms = timed(lambda i: (heads[i % nsets](), verifies[i % nsets]()), args.steps)
+    verify_ms = timed(lambda i: verifies[i % nsets](), args.steps)
+    gemm_stats_ms = armed(lambda i: fused[i % nsets](), args.steps)
+    gemm_plain_ms = armed(lambda i: heads[i % nsets](), args.steps)
+    flags = sum(int(c.out["err_flags"].item()) for c in fused + verifies)
+    assert flags == 0, f"device error flags {flags}"
+
+    flops = 2.0 * M * H * V
+    gemm_bytes = V * H * 2 + M * H * 2 + M * V * 2  # weights and hidden states once, logits written
+    tflops = flops / (gemm_stats_ms * 1e-3) / 1e12
+    elems = B * (2 * K + 1) * V
+    return {
+        "metric": f"lm-head verify throughput: rows·vocab/s, B={B} K={K} V={V} H={H} bf16",
+        "value": elems / (fused_ms * 1e-3),
+        "unit": "rows·vocab/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": fused_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x bf16 -> f32 (GEMM), f32 (verification)",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": B, "K": K, "V": V, "H": H, "logits": "bf16",
+                   "temperature": cfg.temperature, "input_sets_rotated": nsets},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": 2500.0,
+            "unit": "TFLOP/s",
+            "frac": tflops / 2500.0,
+            "traffic": None,
+            "kernel": "lm_head_gemm_kernel<true> (the LM head with the statistics epilogue)",
+            "algorithmic_flops_per_launch": flops,
+            "duration_us_avg": gemm_stats_ms * 1e3,
+            "hbm": {"algorithmic_bytes_per_launch": gemm_bytes,
+                    "achieved_gbs": gemm_bytes / (gemm_stats_ms * 1e-3) / 1e9, "peak_gbs": HBM_PEAK_GBS,
+                    "frac": gemm_bytes / (gemm_stats_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "timing": "launch start/stop events of the GEMM over a separate pass of the same steps",
+        },
+        "fused_call_us": fused_ms * 1e3,
+        "unfused_call_us": unfused_ms * 1e3,
+        "lm_head_alone_us": gemm_plain_ms * 1e3,
+        "lm_head_with_statistics_us": gemm_stats_ms * 1e3,
+        "verify_after_fused_gemm_us": (fused_ms - gemm_stats_ms) * 1e3,
+        "sv_verify_chain_on_the_logits_us": verify_ms * 1e3,
+        "wall_s_timed": t_wall,
+        "_cpu_inp": sets[0],
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -233,6 +354,16 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     wl = args.workload
+    from workloads import LM_HEAD_CONFIGS
+    if wl in LM_HEAD_CONFIGS:
+        cfg = LM_HEAD_CONFIGS[wl]
+        result = bench_lm_head(args, sv, torch, cfg, dev, stream)
+        cpu_inp = result.pop("_cpu_inp")
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline_lm_head({k: v.cpu() for k, v in cpu_inp.items()}, cfg,
+                                                          args.cpu_seconds)
+        print(json.dumps(result), flush=True)
+        return
     kind = ("tree" if wl in TREE_CONFIGS else "treesample" if wl in SAMPLE_TREE_CONFIGS
             else "sample" if wl in SAMPLE_WORKLOADS else "chain")
     if kind == "treesample":

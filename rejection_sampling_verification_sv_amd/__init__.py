@@ -6,6 +6,8 @@ ctypes binding. Build with ``python -m rejection_sampling_verification_sv_amd.bu
 """
 from .specverify import (  # noqa: F401
     PreparedChainCall,
+    PreparedLMHeadChainCall,
+    PreparedLMHeadLogitsCall,
     PreparedSampleCall,
     PreparedTreeCall,
     PreparedTreeSamplingCall,

@@ -734,3 +734,65 @@ class PreparedTreeSamplingCall:
         if st != SV_OK:
             _check(st, "sv_verify_tree_sampling")
         return self.out
+
+
+class PreparedLMHeadChainCall:
+    """``sv_verify_chain_lm_head`` with every argument checked and marshalled
+    once (calling the object only enqueues the kernels)."""
+
+    def _init(self, hidden, head_weight, draft, draft_tokens, temperature, uniforms, *, stream=None):
+        B, K1, H = hidden.shape
+        V = head_weight.shape[0]
+        K = K1 - 1
+        dev = hidden.device
+        self.out = sv_verify_chain_lm_head(hidden, head_weight, draft, draft_tokens, temperature, uniforms,
+                                           stream=stream)
+        lib = _load()
+        self._ws = workspace(dev, int(lib.sv_lm_head_chain_workspace_bytes(B, K, V, H)), stream)
+        self._keep = (hidden, head_weight, draft, draft_tokens, temperature, uniforms)
+        o = self.out
+        self._fn = lib.sv_verify_chain_lm_head
+        self._args = (
+            _ptr(hidden), _ptr(head_weight), H, _ptr(o["target_logits"]), _ptr(draft) if K > 0 else None,
+            _ptr(draft_tokens) if K > 0 else None, _ptr(temperature), _ptr(uniforms), B, K, V,
+            _ptr(o["accept_len"]), _ptr(o["out_tokens"]), _ptr(o.get("p_draft")), _ptr(o.get("q_draft")),
+            _ptr(o.get("residual_mass")), _ptr(o["err_flags"]), _ptr(self._ws), self._ws.numel(),
+            _stream_handle(dev, stream))
+
+    def __init__(self, *args, stream=None, **kw):
+        first = args[0]
+        with _on_call_stream(first.device, stream) as (s, outer):
+            self._init(*args, stream=s, **kw)
+            _used_on(s, outer, list(args))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SV_OK:
+            _check(st, "sv_verify_chain_lm_head")
+        return self.out
+
+
+class PreparedLMHeadLogitsCall:
+    """``sv_lm_head_logits`` marshalled once (the LM head alone)."""
+
+    def _init(self, hidden, head_weight, *, stream=None):
+        H = hidden.shape[-1]
+        V = head_weight.shape[0]
+        dev = hidden.device
+        self.logits = sv_lm_head_logits(hidden, head_weight, stream=stream)
+        self._keep = (hidden, head_weight)
+        self._fn = _load().sv_lm_head_logits
+        self._args = (_ptr(hidden), _ptr(head_weight), hidden.numel() // H, H, V, _ptr(self.logits),
+                      _stream_handle(dev, stream))
+
+    def __init__(self, *args, stream=None, **kw):
+        first = args[0]
+        with _on_call_stream(first.device, stream) as (s, outer):
+            self._init(*args, stream=s, **kw)
+            _used_on(s, outer, list(args))
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != SV_OK:
+            _check(st, "sv_lm_head_logits")
+        return self.logits
