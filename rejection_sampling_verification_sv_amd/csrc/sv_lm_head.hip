@@ -83,28 +83,26 @@ __global__ __launch_bounds__(256, 2) void lm_head_gemm_kernel(LMHeadParams P) {
   const uint16_t* W = static_cast<const uint16_t*>(P.weight);
 
   // this thread's four 16-byte pieces of each operand tile per k-step:
-  // row idx >> 3, k offset (idx & 7) * 8, idx = tid + 256 q
+  // row idx >> 3, k offset (idx & 7) * 8, idx = tid + 256 q. Rows past M
+  // (past N) read the last row instead: the loads stay unconditional 16-byte
+  // loads, and what those rows produce is neither stored nor counted.
   const uint16_t* ga[4];
   const uint16_t* gb[4];
-  bool va[4], vb[4];
   int lds_off[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int idx = tid + 256 * q;
     const int row = idx >> 3, ch = idx & 7;
-    va[q] = m0 + row < P.M;
-    vb[q] = n0 + row < P.N;
-    ga[q] = A + (va[q] ? static_cast<int64_t>(m0 + row) * H : 0) + ch * 8;
-    gb[q] = W + (vb[q] ? static_cast<int64_t>(n0 + row) * H : 0) + ch * 8;
+    ga[q] = A + static_cast<int64_t>(min(m0 + row, P.M - 1)) * H + ch * 8;
+    gb[q] = W + static_cast<int64_t>(min(n0 + row, P.N - 1)) * H + ch * 8;
     lds_off[q] = row * kLdsRow + ch * 8;
   }
-  const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
   uint4 ra[4], rb[4];
   auto fetch = [&](int64_t k0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      ra[q] = va[q] ? load16(ga[q] + k0) : zero;
-      rb[q] = vb[q] ? load16(gb[q] + k0) : zero;
+      ra[q] = load16(ga[q] + k0);
+      rb[q] = load16(gb[q] + k0);
     }
   };
   auto stash = [&](int buf) {
