@@ -469,7 +469,7 @@ sv::PieceLayout lm_head_piece_layout(int32_t K, int32_t V) {
 LMHeadLayout lm_head_layout(int32_t B, int32_t K, int32_t V) {
   LMHeadLayout L{};
   L.chain = chain_layout(B, K, V, SV_DTYPE_BF16, B * sv::slots_per_seq(lm_head_piece_layout(K, V)));
-  L.ntn = static_cast<int32_t>(ceil_div(V, sv::kLMTile));
+  L.ntn = static_cast<int32_t>(ceil_div(V, sv::kLMPiece));
   L.off_pieces = L.chain.total;
   L.total = align_up(L.off_pieces + sizeof(float2) * static_cast<int64_t>(B) * (K + 1) * L.ntn);
   return L;
@@ -486,8 +486,7 @@ sv::LMHeadParams lm_head_params(const void* hidden, const void* weight, void* lo
   g.H = H;
   g.K1 = K1;
   g.temperature = temperature;
-  g.mtiles = static_cast<int32_t>(ceil_div(M, sv::kLMTile));
-  g.ntiles_n = static_cast<int32_t>(ceil_div(N, sv::kLMTile));
+  g.npieces = static_cast<int32_t>(ceil_div(N, sv::kLMPiece));
   return g;
 }
 

@@ -122,7 +122,7 @@ struct ChainParams {
 
 // The target's LM head as a GEMM: logits [M, N] = hidden [M, H] x weight
 // [N, H]^T, bf16 in and out, fp32 accumulation; with the statistics, one
-// (reference, sum) piece per row and 128-column tile (see sv_lm_head.hip).
+// (reference, sum) piece per row and 128-column piece (see sv_lm_head.hip).
 struct LMHeadParams {
   const void* hidden;        // [M, H] bf16, 16-byte aligned
   const void* weight;        // [N, H] bf16, 16-byte aligned
@@ -131,10 +131,11 @@ struct LMHeadParams {
   int64_t H;                 // a multiple of 64
   int32_t K1;                // rows per sequence: row m belongs to sequence m / K1
   const float* temperature;  // [M / K1] or null (1.0)
-  int32_t mtiles, ntiles_n;  // 128-row and 128-column tiles
-  float2* pieces;            // [M, ntiles_n] out (statistics only)
+  int32_t npieces;           // 128-column statistics pieces per row, ceil(N / 128)
+  float2* pieces;            // [M, npieces] out (statistics only)
+  int32_t mt, nt;            // GEMM tiles along M and N (set by launch_lm_head_gemm)
 };
-constexpr int kLMTile = 128;
+constexpr int kLMPiece = 128;
 
 
 // Sampling verification of a candidate tree: the run records of the target
