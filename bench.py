@@ -424,10 +424,13 @@ def main():
                   "input_sets_rotated": len(sets)}
         if args.entropy:
             config["entropy"] = "every position, [B, 2K+1]"
-        one = sv.sv_chain_launches(B, K, V, sets[0]["target"].dtype, True, args.entropy) == 1
-        config["launches_per_call"] = 1 if one else 2
-        kernel_name = ("chain_one_launch_kernel (the whole call in one launch: every logit row once, then the "
-                       "row pair at each sequence's first rejection)" if one else
+        form = sv.sv_chain_form(B, K, V, sets[0]["target"].dtype, True, args.entropy)
+        config["launches_per_call"] = 2 if form == 3 else 1
+        kernel_name = ("chain_small_kernel (the whole call in one launch, the statistics workgroups deciding and "
+                       "drawing: every logit row once, then the row pair at each sequence's first rejection)"
+                       if form == 1 else
+                       "chain_one_launch_kernel (the whole call in one launch: every logit row once, then the "
+                       "row pair at each sequence's first rejection)" if form == 2 else
                        "chain_stats_chunk_entropy_kernel (statistics pass with the entropy: every logit row once)"
                        if args.entropy else "chain_stats_chunk_kernel (statistics pass: every logit row once)")
     else:

@@ -24,6 +24,7 @@ from .specverify import (  # noqa: F401
     library,
     reset_workspaces,
     sv_build_tree_mask,
+    sv_chain_form,
     sv_chain_launches,
     sv_chain_workspace_bytes,
     sv_sample_rows,

@@ -122,9 +122,81 @@ bool one_launch_ok(const sv::PieceLayout& L, int32_t B, int32_t K, int32_t nblk_
   return R * G <= 64 && pmax <= 4 * G;
 }
 
+// The most pieces of a row the decision reads in one round: G lanes per
+// row (G the largest power of two with 2K+1 rows of 2G lanes in one wave)
+// with up to 4 pieces each.
+int64_t one_round_pieces(int32_t K) {
+  const int64_t R = 2LL * K + 1;
+  int64_t G = 1;
+  while (R * 2 * G <= 64) G <<= 1;
+  return 4 * G;
+}
+
+// Chunk size of the small call: every row cut into k pieces, k a divisor
+// of the row's vector count (so no chunk crosses a row end: one piece, one
+// combine and one slot per chunk) closest to a piece of kSmallTargetVecs
+// vectors (about 22 KB: smaller chunks cost more arrivals and a wider
+// decision, larger ones more than one round trip of loads), with no more
+// than kSmallChunks chunks per call nor more pieces than one decision round
+// reads. Measured on MI355X, per call:
+//   B=4 K=4 V=32000 fp32:    9 KB chunks across row ends 16.9 us, 21 KB
+//                            across 15.6 us, 16-31 KB on row ends 14.8-15.0 us;
+//   B=4 K=5 V=128256 bf16:   21 KB on row ends 18.2 us, 23 KB across 19.1 us.
+int64_t small_chunk_vecs(int64_t B, int32_t K, int32_t V, sv_dtype d) {
+  const int32_t R = 2 * K + 1;
+  const int64_t nvec = row_vecs(V, d);
+  const int64_t seq_rows = B * R;
+  const int64_t k0 = ceil_div(nvec, sv::kSmallTargetVecs);
+  int64_t kmax = 2 * k0;
+  const int64_t kcall = seq_rows > 0 ? sv::kSmallChunks / seq_rows : 1;
+  if (kmax > kcall) kmax = kcall;
+  const int64_t kcap = one_round_pieces(K) - 1;
+  if (kmax > kcap) kmax = kcap;
+  int64_t k = 1;  // 1 divides every row
+  for (int64_t c = 2; c <= kmax; ++c) {
+    if (nvec % c != 0) continue;
+    const int64_t dc = c > k0 ? c - k0 : k0 - c, dk = k > k0 ? k - k0 : k0 - k;
+    if (dc <= dk) k = c;
+  }
+  return ceil_div(nvec, k);
+}
+
+// Whether a chain call may take the small form at all: every form of such a
+// call then cuts its rows into the small call's chunks, so that the forms
+// keep giving bit-identical outputs.
+bool small_shape(int32_t B, int32_t K, int32_t V, sv_dtype d) {
+  return SV_SMALL && K >= 1 && whole_vector_rows(V, d) &&
+         static_cast<int64_t>(B) * (2 * K + 1) <= sv::kSmallMaxRows;
+}
+
+// Chunk size of a chain call's statistics pass (chunked layout).
+int64_t chain_chunk_vecs(int32_t B, int32_t K, int32_t V, sv_dtype d) {
+  return small_shape(B, K, V, d) ? small_chunk_vecs(B, K, V, d)
+                                 : row_chunk_vecs(B, 2 * K + 1, V, d, sv::kChunksChain);
+}
+
+// The small chain call (chain_small_kernel: the statistics workgroups also
+// decide and sample) serves calls of at most kSmallMaxRows rows in all whose
+// grid the device holds at once (kSmallWGsPerCU workgroups per compute
+// unit), with rows on 16-byte boundaries, at least one drafted token, no
+// entropy or drawn probability requested, and statistics that the decision
+// reads in one round (as one_launch_ok).
+bool small_ok(const sv::PieceLayout& L, int32_t B, int32_t K, int32_t V, sv_dtype d, bool extra_outputs) {
+  if (!small_shape(B, K, V, d) || L.cps <= 0 || extra_outputs) return false;
+  const int cus = device_cus();
+  if (cus < 1 || static_cast<int64_t>(B) * L.cps > static_cast<int64_t>(cus) * sv::kSmallWGsPerCU) return false;
+  const int64_t R = 2LL * K + 1;
+  if (R * L.nvec > static_cast<int64_t>(UINT32_MAX)) return false;
+  const int64_t pmax = (L.nvec + L.per - 2) / L.per + 1;  // pieces of a row, at most
+  int64_t G = 1;
+  while (G < pmax && R * 2 * G <= 64) G <<= 1;
+  return R * G <= 64 && pmax <= 4 * G;
+}
+
 struct ChainLayout {
   int32_t ntiles, tiles_per_block, nblk_b;
-  size_t off_part_m, off_part_s, off_part_a, off_cnt, off_tiles, off_gat, off_abort, off_tk, off_done, total;
+  size_t off_part_m, off_part_s, off_part_a, off_cnt, off_tiles, off_gat, off_abort, off_tk, off_done, off_plan,
+      total;
 };
 
 // min_parts: slots the call's statistics need at least (a layout other than
@@ -141,7 +213,7 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d, int64_t mi
   const int64_t groups = ceil_div(static_cast<int64_t>(B) * ceil_div(L.ntiles, group), sv::kSampleBlocks);
   L.tiles_per_block = static_cast<int32_t>(group * (groups < 1 ? 1 : groups));
   L.nblk_b = static_cast<int32_t>(ceil_div(L.ntiles, L.tiles_per_block));
-  int64_t parts = piece_slots(B, R, V, d, row_chunk_vecs(B, R, V, d, sv::kChunksChain));
+  int64_t parts = piece_slots(B, R, V, d, chain_chunk_vecs(B, K, V, d));
   if (parts < min_parts) parts = min_parts;
   size_t off = 0;
   L.off_part_m = off;
@@ -162,6 +234,8 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d, int64_t mi
   off = align_up(off + sizeof(uint32_t) * B * sv::kCtrStride);
   L.off_done = off;
   off = align_up(off + sizeof(uint32_t) * B * sv::kCtrStride);
+  L.off_plan = off;
+  off = align_up(off + sizeof(uint64_t) * static_cast<int64_t>(B) * sv::kPlanStride);
   L.total = off;
   return L;
 }
@@ -365,7 +439,7 @@ sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dty
   // The chunked layout needs every row on a 16-byte boundary.
   const bool chunked = whole_vector_rows(V, dtype) && aligned_to(target_logits, 16) &&
                        (K == 0 || aligned_to(draft_logits, 16));
-  p.L = piece_layout(2 * K + 1, V, dtype, chunked, row_chunk_vecs(B, 2 * K + 1, V, dtype, sv::kChunksChain));
+  p.L = piece_layout(2 * K + 1, V, dtype, chunked, chain_chunk_vecs(B, K, V, dtype));
   p.ntiles = L.ntiles;
   p.tiles_per_block = L.tiles_per_block;
   p.nblk_b = L.nblk_b;
@@ -386,7 +460,14 @@ sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dty
   p.abort = reinterpret_cast<uint64_t*>(ws + L.off_abort);
   p.tk = reinterpret_cast<uint32_t*>(ws + L.off_tk);
   p.done = reinterpret_cast<uint32_t*>(ws + L.off_done);
-  p.one_launch = one_launch_ok(p.L, B, K, p.nblk_b, entropy != nullptr || drawn_prob != nullptr) ? 1 : 0;
+  p.plan = reinterpret_cast<uint64_t*>(ws + L.off_plan);
+  const bool extra = entropy != nullptr || drawn_prob != nullptr;
+  p.one_launch = one_launch_ok(p.L, B, K, p.nblk_b, extra) ? 1 : 0;
+  if (chunked && small_ok(p.L, B, K, V, dtype, extra)) {
+    p.one_launch = 2;
+    const int64_t tpb = ceil_div(L.ntiles, p.L.cps);
+    p.tiles_per_block = static_cast<int32_t>(tpb < sv::kSmallTiles ? sv::kSmallTiles : tpb);
+  }
 
   if (static_cast<int64_t>(B) * (sv::items_per_seq(p.L) + p.nblk_b) > INT32_MAX)
     return SV_ERR_UNSUPPORTED;
@@ -397,6 +478,19 @@ sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dty
   return from_hip(sv::launch_chain(p, dtype, ev, stream));
 }
 
+// The form a chain call of this shape takes on the current device: 1 small
+// (chain_small_kernel), 2 one launch with ticket queues
+// (chain_one_launch_kernel), 3 two launches; 0 for invalid sizes or dtype
+// or B = 0.
+int32_t chain_form(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32_t rows_aligned, int32_t with_entropy) {
+  if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return 0;
+  if (B == 0) return 0;
+  const bool chunked = rows_aligned != 0 && whole_vector_rows(V, dtype);
+  const sv::PieceLayout L = piece_layout(2 * K + 1, V, dtype, chunked, chain_chunk_vecs(B, K, V, dtype));
+  if (chunked && small_ok(L, B, K, V, dtype, with_entropy != 0)) return 1;
+  return one_launch_ok(L, B, K, chain_layout(B, K, V, dtype).nblk_b, with_entropy != 0) ? 2 : 3;
+}
+
 }  // namespace
 
 extern "C" {
@@ -405,10 +499,12 @@ int32_t sv_chain_launches(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32
                           int32_t with_entropy) {
   if (!dtype_ok(dtype) || !chain_sizes_ok(B, K, V)) return 0;
   if (B == 0) return 0;
-  const bool chunked = rows_aligned != 0 && whole_vector_rows(V, dtype);
-  const sv::PieceLayout L =
-      piece_layout(2 * K + 1, V, dtype, chunked, row_chunk_vecs(B, 2 * K + 1, V, dtype, sv::kChunksChain));
-  return one_launch_ok(L, B, K, chain_layout(B, K, V, dtype).nblk_b, with_entropy != 0) ? 1 : 2;
+  const int32_t form = chain_form(B, K, V, dtype, rows_aligned, with_entropy);
+  return form == 0 ? 0 : (form == 3 ? 2 : 1);
+}
+
+int32_t sv_chain_form(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32_t rows_aligned, int32_t with_entropy) {
+  return chain_form(B, K, V, dtype, rows_aligned, with_entropy);
 }
 
 sv_status sv_verify_chain(const void* target_logits, const void* draft_logits, sv_dtype dtype,

@@ -169,6 +169,78 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
   }
 }
 
+// The small call's statistics chunk: stats_chunk's row pieces, batches of
+// kStreamU vectors per thread and operations in the same order (so the same
+// slots, bit for bit), with every load of the chunk issued before the first
+// batch is reduced: one round trip instead of one per batch. Plain loads, so
+// the rows stay in L2 for the row pair the sampling reads again. At most two
+// row pieces and kMaxB batches; returns false, with nothing loaded, for a
+// chunk that needs more (the caller streams it with stats_chunk).
+template <class T, int TPB, int kMaxB>
+__device__ bool stats_chunk_prefetched(const ChainParams& P, int b, int ch) {
+  constexpr int NW = TPB / kWave;
+  constexpr int U = kStreamU;
+  constexpr int STEP = TPB * U;
+  __shared__ float s_redf[NW];
+  __shared__ double s_redd[NW];
+  const int R = 2 * P.K + 1;
+  const int64_t nvec = P.L.nvec;
+  const int64_t lo = static_cast<int64_t>(ch) * P.L.per;
+  const int64_t hi = min(static_cast<int64_t>(R) * nvec, lo + P.L.per);
+  const int r_lo = static_cast<int>(div_nonneg(lo, nvec));
+  const int r_hi = static_cast<int>(div_nonneg(hi - 1, nvec));
+  if (r_hi - r_lo > 1) return false;
+  // piece 0: row r_lo, vectors [a0, a1); piece 1 (r_hi > r_lo): row r_hi, [0, b1)
+  const int64_t a0 = lo - r_lo * nvec;
+  const int64_t a1 = min(hi, (r_lo + 1) * nvec) - r_lo * nvec;
+  const int64_t b1 = (r_hi > r_lo) ? hi - r_hi * nvec : 0;
+  const int nb0 = static_cast<int>((a1 - a0 + STEP - 1) / STEP);
+  const int nb1 = static_cast<int>((b1 + STEP - 1) / STEP);
+  if (nb0 + nb1 > kMaxB) return false;
+  const uint4* body0 = static_cast<const uint4*>(chain_row<T>(P, b, r_lo));
+  const uint4* body1 = static_cast<const uint4*>(chain_row<T>(P, b, r_hi));
+  const int x0 = row_token(P, b, r_lo);
+  const int x1 = row_token(P, b, r_hi);
+  uint4 raw[kMaxB][U];
+#pragma unroll
+  for (int q = 0; q < kMaxB; ++q) {
+    const bool second = q >= nb0;
+    const int64_t start = second ? 0 : a0;
+    const int64_t end = second ? b1 : a1;
+    const uint4* body = second ? body1 : body0;
+    const int64_t k0 = static_cast<int64_t>(second ? q - nb0 : q) * STEP + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u * TPB;
+      raw[q][u] = (q < nb0 + nb1 && start + k < end) ? body[start + k] : neg_inf_vec<T>();
+    }
+  }
+  const Scale c = exponent_scale(temperature_of(P.temperature, b));
+#pragma unroll
+  for (int piece = 0; piece < 2; ++piece) {
+    if (piece == 1 && r_hi == r_lo) break;
+    Running st{-INFINITY, 0.0f, 0.0f};
+#pragma unroll
+    for (int q = 0; q < kMaxB; ++q)
+      if ((piece == 0 && q < nb0) || (piece == 1 && q >= nb0 && q < nb0 + nb1)) add_batch<T, U, false>(st, raw[q], c);
+    float MC;
+    double S;
+    block_combine<NW, false>(st, c, s_redf, s_redd, &MC, &S);
+    if (threadIdx.x == 0) {
+      const int r = piece == 0 ? r_lo : r_hi;
+      const int64_t p0 = piece == 0 ? a0 : 0;
+      const int64_t p1 = piece == 0 ? a1 : b1;
+      const int x = piece == 0 ? x0 : x1;
+      const int64_t slot = (static_cast<int64_t>(b) * P.L.cps + ch) * P.L.kmax + (r - r_lo);
+      publish(&P.part_m[slot], tag_float(MC));
+      publish(&P.part_s[slot], tag_nonneg_double(S));
+      if (x >= 0 && x < P.V && x / T::kVec >= p0 && x / T::kVec < p1)
+        publish_gather<T>(P, b, r, piece == 0 ? body0 : body1, x);
+    }
+  }
+  return true;
+}
+
 // ---------------------------------------------------------------- pass 2
 
 // The decision of sequence b, made by wave 0 of every sampling workgroup of
@@ -440,7 +512,7 @@ __device__ __forceinline__ int decision_lanes(int R, int pmax) {
 // still zero (its store not visible yet) makes the wave return false before
 // anything is written, for the caller to read again.
 template <class T>
-__device__ bool decide_live_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
+__device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
   const int K = P.K;
   const int R = 2 * K + 1;
@@ -669,10 +741,20 @@ __device__ __forceinline__ float tile_weights(const SampleRows& S, int64_t tile,
 // Rescan tile `tile` of the sampling row: the first token (ascending id) with
 // a positive weight whose cumulative weight within the tile exceeds
 // `target`; if rounding leaves none, the last token with a positive weight.
+__device__ int draw_in_weights(int tile, const float (&w)[kSampleEPT], float x, double target, double* s_scan,
+                               int* s_redi);
+
 template <class T>
 __device__ int draw_in_tile(const SampleRows& Sr, int tile, double target, int V, double* s_scan, int* s_redi) {
   float w[kSampleEPT];
   const float x = tile_weights<T>(Sr, tile, V, w);
+  return draw_in_weights(tile, w, x, target, s_scan, s_redi);
+}
+
+// The rescan of draw_in_tile on weights already formed (w, and x their
+// running sum, as tile_compute returns them).
+__device__ int draw_in_weights(int tile, const float (&w)[kSampleEPT], float x, double target, double* s_scan,
+                               int* s_redi) {
   double tot;
   const double excl = block_exclusive_scan(static_cast<double>(x), s_scan, &tot);
   int first = INT_MAX;
@@ -694,25 +776,19 @@ __device__ int draw_in_tile(const SampleRows& Sr, int tile, double target, int V
   return (e >= 0) ? static_cast<int>(static_cast<int64_t>(tile) * kSampleTile + e) : -1;
 }
 
-// Draw the token: called by the last resolving workgroup of sequence b, once
-// every workgroup of the sequence has published its tile totals.
-template <class T>
-__device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
-  __shared__ double s_scan[kWaves];
-  __shared__ int s_redi[kWaves];
-  __shared__ double s_S, s_target;
-  __shared__ int s_tile;
-  __shared__ uint32_t s_err;
+// Step one of the draw, by wave 0 once every tile total of sequence b is
+// published (read with await_slot): the total weight S (fp64, tile order)
+// and the tile holding u_K * S, with the target left inside it, into the
+// caller's shared variables. Up to 64 tiles (the usual case) take one
+// inclusive scan; more tiles are scanned in rounds of 64, twice (total
+// first, then the search). No tile crossing the target (rounding at the top
+// end): the last tile with weight, target +inf; none with weight: tile -1.
+__device__ void locate_tile(const ChainParams& P, int b, double* s_S, int* s_tile, double* s_target,
+                            uint32_t* s_err) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   uint64_t* ts = P.tile_sum + static_cast<int64_t>(b) * P.ntiles;
   const double u = static_cast<double>(P.uniforms[static_cast<int64_t>(b) * (P.K + 1) + P.K]);
-  if (tid == 0) s_err = 0u;
-  __syncthreads();
-
-  // (1) total weight and the tile holding u * total (wave 0, fp64, tile order).
-  //     Up to 64 tiles (the usual case) take one inclusive scan; more tiles
-  //     are scanned in rounds of 64, twice (total first, then the search).
   if (tid < kWave) {
     uint32_t err = 0u;
     double total, target, prefix = 0.0;
@@ -759,18 +835,35 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
         carry += __shfl(inc, kWave - 1, kWave);
       }
     }
-    if (err != 0u) atomicOr(&s_err, err);
+    if (err != 0u) atomicOr(s_err, err);
     if (tid == 0) {
-      s_S = total;
+      *s_S = total;
       if (found >= 0) {
-        s_tile = found;
-        s_target = target - prefix;
+        *s_tile = found;
+        *s_target = target - prefix;
       } else {  // rounding at the top end: the last tile with weight
-        s_tile = last_pos;
-        s_target = INFINITY;
+        *s_tile = last_pos;
+        *s_target = INFINITY;
       }
     }
   }
+}
+
+// Draw the token: called by the last resolving workgroup of sequence b, once
+// every workgroup of the sequence has published its tile totals.
+template <class T>
+__device__ __forceinline__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
+  __shared__ double s_scan[kWaves];
+  __shared__ int s_redi[kWaves];
+  __shared__ double s_S, s_target;
+  __shared__ int s_tile;
+  __shared__ uint32_t s_err;
+  const int tid = threadIdx.x;
+  const double u = static_cast<double>(P.uniforms[static_cast<int64_t>(b) * (P.K + 1) + P.K]);
+  if (tid == 0) s_err = 0u;
+  __syncthreads();
+
+  locate_tile(P, b, &s_S, &s_tile, &s_target, &s_err);
   __syncthreads();
   const double S_res = s_S;
   bool p_only = false;
@@ -828,20 +921,96 @@ __device__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
   }
 }
 
+// Tiles [t_begin, t_end) of sequence b's sampling row pair (plan pl): the
+// weights of each tile, TPB tiles with their loads in flight together, and
+// each tile's total published to its slot.
+// kKeep: the caller's tiles fit one group (t_end - t_begin <= TPB), and the
+// weights of tile t_begin + i and their running sum stay in keep[i],
+// keepx[i] (for the draw of the small call).
+template <class T, int TPB, bool kDraft, bool kKeep = false>
+__device__ __forceinline__ void tile_totals(const ChainParams& P, int b, const SeqPlan& pl, int t_begin, int t_end,
+                            float (*keep)[kSampleEPT] = nullptr, float* keepx = nullptr) {
+  constexpr int NV = kEptVecs<T>;
+  __shared__ double s_red[TPB][kWaves];
+  const SampleRows S = sample_rows<T>(P, b, pl, false);
+#pragma unroll 1
+  for (int t0 = t_begin; t0 < t_end; t0 += TPB) {
+    uint4 rt[TPB][NV], rd[kDraft ? TPB : 1][NV] = {};
+#pragma unroll
+    for (int i = 0; i < TPB; ++i) {
+      if (t0 + i < t_end) {
+        const int64_t e0 =
+            static_cast<int64_t>(t0 + i) * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
+        load_raw<T>(S.t, e0, P.V, rt[i]);
+        if (kDraft && S.d != nullptr) load_raw<T>(S.d, e0, P.V, rd[kDraft ? i : 0]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < TPB; ++i) {
+      float w[kSampleEPT];
+      float x = 0.0f;
+      if (t0 + i < t_end) x = tile_compute<T>(S, rt[i], rd[kDraft ? i : 0], w);
+      const double part = (t0 + i < t_end) ? wave_sum(static_cast<double>(x)) : 0.0;
+      if (lane_id() == 0) s_red[i][wave_id()] = part;
+      if constexpr (kKeep) {
+#pragma unroll
+        for (int e = 0; e < kSampleEPT; ++e) keep[i][e] = w[e];
+        keepx[i] = x;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < TPB && t0 + static_cast<int>(threadIdx.x) < t_end) {
+      double tot = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) tot += s_red[threadIdx.x][w];
+      publish(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t0 + threadIdx.x], tag_nonneg_double(tot));
+    }
+    __syncthreads();  // s_red is reused by the next group
+  }
+}
+
+// The end of a sequence's sampling, by each of its `total` sampling
+// workgroups once its tile totals are published: the last to arrive at
+// *cnt draws the token and returns the sequence's workspace (statistics
+// pieces, gathered logits, tile totals, and with `small` its plan words)
+// to zero, and the counters `cnt` and `also` (if any) to zero.
+template <class T, bool kEnt, bool kSmall = false>
+__device__ void sample_finish(const ChainParams& P, int b, const SeqPlan& pl, uint32_t* cnt, uint32_t total,
+                              uint32_t* also, bool draw = true) {
+  __shared__ int s_flag;
+  if (!arrive_and_check_last(cnt, total, &s_flag)) return;
+  if (draw && pl.j >= 0) chain_draw<T>(P, b, pl);
+  // Every workgroup of the sequence has read the statistics pieces and
+  // published its totals: leave the sequence's workspace all zero.
+  __syncthreads();
+  if (kSmall || pl.j >= 0)  // (a small call's last workgroup may not have read the plan)
+    for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
+  const int64_t per_seq = slots_per_seq(P.L);
+  for (int64_t sl = static_cast<int64_t>(b) * per_seq + threadIdx.x; sl < (static_cast<int64_t>(b) + 1) * per_seq;
+       sl += kThreads) {
+    P.part_m[sl] = 0ull;
+    P.part_s[sl] = 0ull;
+    if constexpr (kEnt) P.part_a[sl] = 0ull;
+  }
+  const int R = 2 * P.K + 1;
+  for (int r = threadIdx.x; r < R; r += kThreads) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
+  if constexpr (kSmall)
+    for (int w = threadIdx.x; w < kPlanWords; w += kThreads) clear_slot(&P.plan[static_cast<int64_t>(b) * kPlanStride + w]);
+  reset_counter(cnt);
+  if (also != nullptr) reset_counter(also);
+}
+
 // Sampling workgroup g of sequence b: its wave 0 makes the sequence's
 // decision (group 0 writes it out), then the workgroup forms the weights of
 // tiles [g * tiles_per_block, (g + 1) * tiles_per_block) of the sampling row
-// pair, TPB at a time, and publishes their totals; the last workgroup of the sequence to finish draws the token
-// and returns the sequence's workspace (statistics pieces, gathered logits,
-// tile totals, arrival counter) to zero.
+// pair, TPB at a time, and publishes their totals; the last workgroup of the
+// sequence to finish draws the token and returns the sequence's workspace
+// (statistics pieces, gathered logits, tile totals, arrival counter) to zero.
 // kLive: the one-launch call (statistics of the same launch, see
 // decide_live); a decision that never completes reports the sequence as an
 // invalid row with SV_ERRF_INTERNAL.
 template <class T, int TPB, bool kDraft, bool kEnt, bool kLive = false>
 __device__ void sample_seq(const ChainParams& P, int b, int blk) {
-  constexpr int NV = kEptVecs<T>;
-  __shared__ double s_red[TPB][kWaves];
-  __shared__ int s_flag;
   __shared__ SeqPlan s_plan;
   if (wave_id() == 0) {
     if constexpr (kLive) {
@@ -860,61 +1029,145 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
   }
   __syncthreads();
   const SeqPlan pl = s_plan;
-
   if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
-    const SampleRows S = sample_rows<T>(P, b, pl, false);
-    // this workgroup's tiles, in groups of TPB whose loads are all in flight at once
     const int t_begin = blk * P.tiles_per_block;
-    const int t_end = min(t_begin + P.tiles_per_block, P.ntiles);
-#pragma unroll 1
-    for (int t0 = t_begin; t0 < t_end; t0 += TPB) {
-      uint4 rt[TPB][NV], rd[kDraft ? TPB : 1][NV] = {};
-#pragma unroll
-      for (int i = 0; i < TPB; ++i) {
-        if (t0 + i < t_end) {
-          const int64_t e0 =
-              static_cast<int64_t>(t0 + i) * kSampleTile + static_cast<int64_t>(threadIdx.x) * kSampleEPT;
-          load_raw<T>(S.t, e0, P.V, rt[i]);
-          if (kDraft && S.d != nullptr) load_raw<T>(S.d, e0, P.V, rd[kDraft ? i : 0]);
-        }
+    tile_totals<T, TPB, kDraft>(P, b, pl, t_begin, min(t_begin + P.tiles_per_block, P.ntiles));
+  }
+  uint32_t* cnt = P.cnt + static_cast<int64_t>(b) * (kLive ? kCtrStride : 1);
+  sample_finish<T, kEnt>(P, b, pl, cnt, static_cast<uint32_t>(P.nblk_b),
+                         kLive ? P.done + static_cast<int64_t>(b) * kCtrStride : nullptr);
+}
+
+// ---------------------------------------------------------------- small calls
+
+// The plan of sequence b as tagged words (never zero once written).
+__device__ __forceinline__ void publish_plan(const ChainParams& P, int b, const SeqPlan& pl) {
+  uint64_t* w = P.plan + static_cast<int64_t>(b) * kPlanStride;
+  publish(&w[1], tag_float(pl.c_hi));
+  publish(&w[2], tag_float(pl.c_lo));
+  publish(&w[3], tag_float(pl.lt_hi));
+  publish(&w[4], tag_float(pl.lt_lo));
+  publish(&w[5], tag_float(pl.d_hi));
+  publish(&w[6], tag_float(pl.d_lo));
+  publish(&w[0], (1ull << 63) | static_cast<uint64_t>(static_cast<uint32_t>(pl.j + 1)));
+}
+
+// Read sequence b's plan (wave 0, one round of loads); false while a word
+// is not visible yet.
+__device__ __forceinline__ bool read_plan(const ChainParams& P, int b, SeqPlan* s_plan) {
+  const uint64_t* w = P.plan + static_cast<int64_t>(b) * kPlanStride;
+  const int lane = lane_id();
+  const uint64_t v = peek(&w[lane < 7 ? lane : 0]);
+  if (__ballot(v == 0ull) != 0ull) return false;
+  const uint64_t w0 = __shfl(v, 0, kWave);
+  if (lane == 0) {
+    s_plan->j = static_cast<int32_t>(static_cast<uint32_t>(w0)) - 1;
+    s_plan->pad = 0u;
+  }
+  const float f = untag_float(v);
+  switch (lane) {
+    case 1: s_plan->c_hi = f; break;
+    case 2: s_plan->c_lo = f; break;
+    case 3: s_plan->lt_hi = f; break;
+    case 4: s_plan->lt_lo = f; break;
+    case 5: s_plan->d_hi = f; break;
+    case 6: s_plan->d_lo = f; break;
+    default: break;
+  }
+  return true;
+}
+
+// Wave 0 of the decider: the decision from the published statistics (read
+// again while a slot is not visible yet), written out, and the plan
+// published for the sequence's other workgroups. Every slot it reads was
+// stored by a workgroup that counted its chunk after its stores completed,
+// so the loop ends; bounded like await_slot all the same. On expiry the
+// sequence is reported as an invalid row (plan j = -1, SV_ERRF_INTERNAL).
+template <class T>
+__device__ void small_decide(const ChainParams& P, int b, SeqPlan* s_plan) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  bool ok = true;
+  while (!decide_live_wave<T>(P, b, s_plan, true)) {
+    if (peek(P.abort) != 0ull || __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      if (peek(P.abort) == 0ull) publish(P.abort, 1ull);
+      ok = false;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (!ok && lane_id() == 0) {
+    P.accept_len[b] = -1;
+    for (int i = 0; i <= P.K; ++i) P.out_tokens[static_cast<int64_t>(b) * (P.K + 1) + i] = -1;
+    if (P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
+    raise_error(P.err_flags, kErrInternal);
+    s_plan->j = -1;
+  }
+  if (lane_id() == 0) publish_plan(P, b, *s_plan);
+}
+
+// Wave 0 of any other workgroup: wait for the decider's plan. The decider
+// counted its chunk after every other chunk of the sequence, so it is
+// running and waits for nothing but visible stores: the wait ends (bounded
+// all the same; on expiry the sequence draws nothing here, SV_ERRF_INTERNAL).
+__device__ void small_await_plan(const ChainParams& P, int b, SeqPlan* s_plan) {
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  while (!read_plan(P, b, s_plan)) {
+    if (peek(P.abort) != 0ull || __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+      if (peek(P.abort) == 0ull) publish(P.abort, 1ull);
+      if (lane_id() == 0) {
+        raise_error(P.err_flags, kErrInternal);
+        s_plan->j = -1;
       }
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// The small call's draw, by every workgroup that holds tiles (their
+// weights in keep, tiles [t_begin, t_end)) once it has published their
+// totals: wave 0 reads every tile total of the sequence (they come from
+// workgroups that have all started, since each counted its chunk before the
+// plan existed, and that wait for nothing more) and finds the tile holding
+// the target, as chain_draw does; the workgroup that holds that tile draws
+// from its weights, with chain_draw's operations, so the same token. A
+// residual that vanished in fp32, or no tile with weight, leaves the draw
+// to the workgroup holding tile 0, which runs chain_draw itself.
+template <class T, int TPB>
+__device__ __forceinline__ void small_owner_draw(const ChainParams& P, int b, const SeqPlan& pl, int t_begin, int t_end,
+                                 const float (&keep)[TPB][kSampleEPT], const float (&keepx)[TPB]) {
+  __shared__ double s_scan[kWaves];
+  __shared__ int s_redi[kWaves];
+  __shared__ double s_S, s_target;
+  __shared__ int s_tile;
+  __shared__ uint32_t s_err;
+  if (threadIdx.x == 0) s_err = 0u;
+  __syncthreads();
+  locate_tile(P, b, &s_S, &s_tile, &s_target, &s_err);
+  __syncthreads();
+  const double S_res = s_S;
+  const int tile = s_tile;
+  if ((!(S_res > 0.0) && pl.j < P.K) || tile < 0) {
+    if (t_begin == 0) chain_draw<T>(P, b, pl);
+    return;
+  }
+  if (tile < t_begin || tile >= t_end) return;
+  float w[kSampleEPT];
+  float x = 0.0f;
 #pragma unroll
-      for (int i = 0; i < TPB; ++i) {
-        float w[kSampleEPT];
-        const double part =
-            (t0 + i < t_end) ? wave_sum(static_cast<double>(tile_compute<T>(S, rt[i], rd[kDraft ? i : 0], w))) : 0.0;
-        if (lane_id() == 0) s_red[i][wave_id()] = part;
-      }
-      __syncthreads();
-      if (threadIdx.x < TPB && t0 + static_cast<int>(threadIdx.x) < t_end) {
-        double tot = 0.0;
+  for (int i = 0; i < TPB; ++i) {
+    if (t_begin + i == tile) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) tot += s_red[threadIdx.x][w];
-        publish(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t0 + threadIdx.x], tag_nonneg_double(tot));
-      }
-      __syncthreads();  // s_red is reused by the next group
+      for (int e = 0; e < kSampleEPT; ++e) w[e] = keep[i][e];
+      x = keepx[i];
     }
   }
-
-  uint32_t* cnt = P.cnt + static_cast<int64_t>(b) * (kLive ? kCtrStride : 1);
-  if (!arrive_and_check_last(cnt, static_cast<uint32_t>(P.nblk_b), &s_flag)) return;
-  if (pl.j >= 0) chain_draw<T>(P, b, pl);
-  // Every workgroup of the sequence has read the statistics pieces and
-  // published its totals: leave the sequence's workspace all zero.
-  __syncthreads();
-  if (pl.j >= 0)
-    for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
-  const int64_t per_seq = slots_per_seq(P.L);
-  for (int64_t sl = static_cast<int64_t>(b) * per_seq + threadIdx.x; sl < (static_cast<int64_t>(b) + 1) * per_seq;
-       sl += kThreads) {
-    P.part_m[sl] = 0ull;
-    P.part_s[sl] = 0ull;
-    if constexpr (kEnt) P.part_a[sl] = 0ull;
+  const int token = draw_in_weights(tile, w, x, s_target, s_scan, s_redi);
+  if (threadIdx.x == 0) {
+    P.out_tokens[static_cast<int64_t>(b) * (P.K + 1) + pl.j] = token;
+    if (P.residual_mass != nullptr) P.residual_mass[b] = (pl.j < P.K) ? static_cast<float>(S_res) : -1.0f;
+    raise_error(P.err_flags, s_err);
   }
-  const int R = 2 * P.K + 1;
-  for (int r = threadIdx.x; r < R; r += kThreads) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
-  reset_counter(cnt);
-  if constexpr (kLive) reset_counter(P.done + static_cast<int64_t>(b) * kCtrStride);
 }
 
 }  // namespace
@@ -1041,6 +1294,74 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_ONE
   }
 }
 
+// Small call (at most a few hundred rows in all, the grid resident at once):
+// one launch of B cps workgroups, one per statistics chunk, which also
+// decide and sample. Workgroup (b, ch) streams chunk ch of sequence b and
+// counts it in done[b] once its slot stores have completed. The last of
+// b's chunks to be counted makes b's decision (wave 0, writing the outputs
+// it fixes) and publishes the plan; the other workgroups of b wait for the
+// plan. Every workgroup then forms the weights of its share of the
+// sampling row pair's tiles and publishes their totals, and the last of b's
+// workgroups to arrive draws the token and clears b's workspace.
+//
+// Why the waits end in any dispatch order, whatever else runs: a workgroup
+// waits only for the plan of its own sequence, which comes from the
+// workgroup that counted the last chunk; that workgroup has started, and its
+// decision reads only slots stored by workgroups that counted their chunks
+// after their stores completed. No workgroup waits for one that has not
+// started. The waits are bounded all the same (await_slot's limit).
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((flatten)) void chain_small_kernel(ChainParams P) {
+  static_assert(kStatsTPB == kThreads, "the statistics chunk runs on the whole workgroup");
+  __shared__ SeqPlan s_plan;
+  __shared__ int s_last;
+  const uint32_t cps = static_cast<uint32_t>(P.L.cps);
+  const uint32_t bu = blockIdx.x / cps;
+  const int b = static_cast<int>(bu);
+  const int ch = static_cast<int>(blockIdx.x - bu * cps);
+  if (!stats_chunk_prefetched<T, kStatsTPB, kSmallMaxBatches>(P, b, ch)) stats_chunk<T, kStatsTPB, false>(P, b, ch);
+  uint32_t* done = P.done + static_cast<int64_t>(b) * kCtrStride;
+  if (threadIdx.x == 0) {
+    // count the chunk once this thread's slot stores have completed (the
+    // decider still checks every slot's tag and reads again if it is zero)
+    __builtin_amdgcn_s_waitcnt(0);
+    const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = (prev + 1u == cps) ? 1 : 0;
+    if (prev >= cps) {  // a counter not left at zero: the workspace was not re-zeroed
+      raise_error(P.err_flags, kErrInternal);
+      publish(P.abort, 1ull);
+    }
+  }
+  __syncthreads();
+  // the draw by the workgroup holding the target's tile when every
+  // workgroup's tiles fit one group, else by the last to arrive (which
+  // then needs the plan); a workgroup without tiles otherwise does not
+  const bool owners = P.tiles_per_block <= kSmallTiles;
+  const int t_begin = ch * P.tiles_per_block;
+  const int t_end = min(t_begin + P.tiles_per_block, P.ntiles);
+  if (wave_id() == 0) {
+    if (s_last)
+      small_decide<T>(P, b, &s_plan);
+    else if (!owners || t_begin < t_end)
+      small_await_plan(P, b, &s_plan);
+    else if (lane_id() == 0)
+      s_plan.j = -1;
+  }
+  __syncthreads();
+  const SeqPlan pl = s_plan;
+  if (pl.j >= 0) {
+    if (owners) {
+      float keep[kSmallTiles][kSampleEPT];
+      float keepx[kSmallTiles];
+      tile_totals<T, kSmallTiles, true, true>(P, b, pl, t_begin, t_end, keep, keepx);
+      if (t_begin < t_end) small_owner_draw<T, kSmallTiles>(P, b, pl, t_begin, t_end, keep, keepx);
+    } else {
+      tile_totals<T, kLiveTiles, true>(P, b, pl, t_begin, t_end);
+    }
+  }
+  sample_finish<T, false, true>(P, b, pl, P.cnt + static_cast<int64_t>(b) * kCtrStride, cps, done, !owners);
+}
+
 // ---------------------------------------------------------------- launcher
 
 template <class T>
@@ -1051,6 +1372,12 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
   // Armed events take the statistics kernel's own start and end timestamps
   // (the whole call's, for the one-launch kernel).
   const bool ent = p.entropy != nullptr;
+  if (p.one_launch == 2) {
+    const int64_t grid = static_cast<int64_t>(p.B) * p.L.cps;
+    if (grid > INT32_MAX || p.plan == nullptr) return hipErrorInvalidConfiguration;
+    launch_stream_pass(chain_small_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), stream, ev, p);
+    return hipGetLastError();
+  }
   if (p.one_launch) {
     const int64_t grid = static_cast<int64_t>(p.B) * (p.L.cps + p.nblk_b);
     if (grid > INT32_MAX) return hipErrorInvalidConfiguration;

@@ -113,6 +113,12 @@ struct ChainParams {
   int32_t one_launch;
   uint32_t* tk;       // [B]
   uint32_t* done;     // [B]
+  // Small call (chain_small_kernel, one_launch == 2): the statistics
+  // workgroups also sample. The last of a sequence's chunks to be counted in
+  // done[b] makes the decision and publishes its plan here, kPlanStride
+  // words per sequence, the first 8 of them tagged (j + 1, c_hi, c_lo,
+  // lt_hi, lt_lo, d_hi, d_lo; one unused).
+  uint64_t* plan;
   // LM-head chain call: the GEMM's statistics pieces of the target rows,
   // [B (K+1), lm_ntn] (reference, sum), combined into the row slots (and
   // zeroed) by lm_head_stats_kernel
@@ -356,6 +362,43 @@ constexpr int kChunksTree = SV_CHUNKS_TREE;
 #ifndef SV_CHUNK_MIN_VECS
 #define SV_CHUNK_MIN_VECS 2048
 #endif
+// Small calls (at most kSmallMaxRows logit rows in all, B (2K+1)): one
+// launch whose statistics workgroups also decide and sample. Chunk size
+// aimed at (16-byte vectors), the most chunks per call, and the workgroups
+// per compute unit the whole grid must fit in to take the path.
+#ifndef SV_SMALL
+#define SV_SMALL 1
+#endif
+#ifndef SV_SMALL_MAX_ROWS
+#define SV_SMALL_MAX_ROWS 256
+#endif
+#ifndef SV_SMALL_TARGET_VECS
+#define SV_SMALL_TARGET_VECS 1400
+#endif
+#ifndef SV_SMALL_CHUNKS
+#define SV_SMALL_CHUNKS 768
+#endif
+#ifndef SV_SMALL_WGS_PER_CU
+#define SV_SMALL_WGS_PER_CU 6
+#endif
+constexpr int kSmallMaxRows = SV_SMALL_MAX_ROWS;
+constexpr int kSmallTargetVecs = SV_SMALL_TARGET_VECS;
+constexpr int kSmallChunks = SV_SMALL_CHUNKS;
+constexpr int kSmallWGsPerCU = SV_SMALL_WGS_PER_CU;
+constexpr int kPlanWords = 8;     // plan words per sequence
+constexpr int kPlanStride = 32;   // words between two sequences' plans (256 bytes: the plans of
+                                  // different sequences, polled by their workgroups, on different channels)
+// Batches of kStreamU vectors per thread the small call's statistics chunk
+// keeps in registers (all its loads in flight together).
+constexpr int kSmallMaxBatches = 6;
+// Tiles per workgroup of the small call's sampling (at least, and the most
+// for which its workgroups keep their tile weights and the one holding the
+// target's tile draws): few workgroups hold tiles, so few wait for the plan
+// and read the tile totals.
+#ifndef SV_SMALL_TILES
+#define SV_SMALL_TILES 1
+#endif
+constexpr int kSmallTiles = SV_SMALL_TILES;
 constexpr int kChunkMinVecs = SV_CHUNK_MIN_VECS;
 
 static_assert(kErrInternal == SV_ERRF_INTERNAL, "error bit mismatch");

@@ -106,6 +106,8 @@ def _load():
         lib.sv_verify_chain_lm_head.restype = ctypes.c_int
         lib.sv_chain_launches.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int, _c_i32, _c_i32]
         lib.sv_chain_launches.restype = _c_i32
+        lib.sv_chain_form.argtypes = [_c_i32, _c_i32, _c_i32, ctypes.c_int, _c_i32, _c_i32]
+        lib.sv_chain_form.restype = _c_i32
         lib.sv_time_next_stream_pass.argtypes = [_c_ptr, _c_ptr]
         lib.sv_time_next_stream_pass.restype = ctypes.c_int
         _lib = lib
@@ -265,6 +267,13 @@ def sv_chain_launches(B: int, K: int, V: int, dtype: torch.dtype, rows_aligned: 
     """Kernel launches ``sv_verify_chain`` makes for this shape on the current
     device: 1 (statistics and sampling in one launch) or 2; 0 if invalid."""
     return int(_load().sv_chain_launches(B, K, V, _DTYPES[dtype], int(rows_aligned), int(with_entropy)))
+
+
+def sv_chain_form(B: int, K: int, V: int, dtype: torch.dtype, rows_aligned: bool = True,
+                  with_entropy: bool = False) -> int:
+    """``sv_chain_form``: 1 small call, 2 one launch with ticket queues, 3 two
+    launches (0: invalid sizes or B = 0), on the current device."""
+    return int(_load().sv_chain_form(B, K, V, _DTYPES[dtype], int(rows_aligned), int(with_entropy)))
 
 
 def sv_tree_workspace_bytes(B: int, N: int, V: int, dtype: torch.dtype) -> int:

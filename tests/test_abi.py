@@ -197,6 +197,19 @@ def test_chain_launches_query(lib):
     assert f(64, 5, 128256, 1, 1, 0) in (1, 2)
 
 
+def test_chain_form_query(lib):
+    # host-only; without a device the call cannot be sized against one, so
+    # only the two-launch form (3) is reported for valid shapes
+    f = lib.sv_chain_form
+    f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int32, ctypes.c_int32]
+    f.restype = ctypes.c_int32
+    assert f(-1, 5, 10, 1, 1, 0) == 0 and f(4, 2, 10, 7, 1, 0) == 0 and f(0, 5, 128256, 1, 1, 0) == 0
+    assert f(4, 4, 32000, 0, 1, 1) == 3      # entropy requested: never the small or one-launch form
+    assert f(4, 4, 32000, 0, 0, 0) == 3      # rows off 16-byte boundaries
+    assert f(4, 0, 32000, 0, 1, 0) == 3      # K = 0
+    assert f(4, 4, 32000, 0, 1, 0) in (1, 3)
+
+
 def test_noalloc_rejects_oversize_before_touching_the_device(lib):
     # B=256 K=63 V=256000 bf16 needs more workspace than the static array
     # holds: rejected from the sizes alone (no pointer is dereferenced)

@@ -73,6 +73,18 @@ def test_c1_recipe_more_sequences(sv):
     _parity_full(sv, _to(chain_inputs(cfg), "cuda"), cfg.name + "_b128")
 
 
+@pytest.mark.parametrize("B,K", [(1, 5), (4, 5), (16, 5), (2, 8), (23, 5)])
+def test_small_calls_at_the_c2_row_shape(sv, B, K):
+    # the pages' batch sizes (1 to 16 sequences) at V = 128256 bf16: calls of
+    # at most 256 rows in all take the small form (one launch whose
+    # statistics workgroups decide and draw), compared in full
+    cfg = CHAIN_CONFIGS["c2"].with_(B=B, K=K, variant=40 + B + K)
+    assert sv.sv_chain_form(B, K, cfg.V, torch.bfloat16) == 1
+    inp = chain_inputs(cfg, device="cuda")
+    _, _, rep = _parity_full(sv, inp, f"{cfg.name} small call B={B} K={K}")
+    record_parity(f"{cfg.name}_small_b{B}_k{K}", call="sv_verify_chain (small form)", **rep.record())
+
+
 def test_c2_full(sv):
     cfg = CHAIN_CONFIGS["c2"]
     inp = chain_inputs(cfg, device="cuda")
