@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "tree": ["sv_tree.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
     # the counted kernel is the statistics stream of sv_tree_sample.hip (the walk shares the file)
     "treesample": ["sv_tree_sample.hip", "sv_stream.h", "sv_device.h", "sv_internal.h", "sv_api.hip"],
+    "lmhead": ["sv_lm_head.hip", "sv_device.h", "sv_internal.h", "sv_api.hip"],
 }
 
 
@@ -279,6 +280,9 @@ def bench_lm_head(args, sv, torch, cfg, dev, stream) -> dict:
     verify_ms = timed(lambda i: verifies[i % nsets](), args.steps)
     gemm_stats_ms = armed(lambda i: fused[i % nsets](), args.steps)
     gemm_plain_ms = armed(lambda i: heads[i % nsets](), args.steps)
+    # the library GEMM beside it: torch's bf16 linear layer (hipBLASLt) on the same operands
+    lib_ms = timed(lambda i: torch.nn.functional.linear(sets[i % nsets]["hidden"].reshape(M, H),
+                                                        sets[i % nsets]["weight"]), args.steps)
     flags = sum(int(c.out["err_flags"].item()) for c in fused + verifies)
     assert flags == 0, f"device error flags {flags}"
 
@@ -307,7 +311,7 @@ def bench_lm_head(args, sv, torch, cfg, dev, stream) -> dict:
             "peak": 2500.0,
             "unit": "TFLOP/s",
             "frac": tflops / 2500.0,
-            "traffic": None,
+            "traffic": counted_traffic(args.workload, "lmhead"),
             "kernel": "lm_head_gemm_kernel<true> (the LM head with the statistics epilogue)",
             "algorithmic_flops_per_launch": flops,
             "duration_us_avg": gemm_stats_ms * 1e3,
@@ -320,11 +324,40 @@ def bench_lm_head(args, sv, torch, cfg, dev, stream) -> dict:
         "unfused_call_us": unfused_ms * 1e3,
         "lm_head_alone_us": gemm_plain_ms * 1e3,
         "lm_head_with_statistics_us": gemm_stats_ms * 1e3,
+        "torch_linear_bf16_us": lib_ms * 1e3,
         "verify_after_fused_gemm_us": (fused_ms - gemm_stats_ms) * 1e3,
         "sv_verify_chain_on_the_logits_us": verify_ms * 1e3,
         "wall_s_timed": t_wall,
         "_cpu_inp": sets[0],
     }
+
+
+def small_batch_latencies(sv, torch, cfg, dev, stream, batches=(1, 4, 16), n=200) -> dict:
+    """Per-call time of the same chain recipe at the pages' batch sizes (one
+    to sixteen sequences), three rotating input sets, n calls back to back
+    between two events; with the form each call takes (sv_chain_form)."""
+    from workloads import chain_inputs
+    out = {}
+    for B in batches:
+        c = cfg.with_(B=B, variant=cfg.variant + 300 + B)
+        sets = [chain_inputs(c.with_(variant=c.variant + 10 * i), device=dev) for i in range(N_SETS)]
+        calls = [sv.PreparedChainCall(s["target"], s["draft"], s["draft_tokens"], s["temperature"], s["uniforms"],
+                                      stream=stream) for s in sets]
+        for i in range(20):
+            calls[i % N_SETS]()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            calls[i % N_SETS]()
+        b.record(stream)
+        torch.cuda.synchronize()
+        assert sum(int(x.out["err_flags"].item()) for x in calls) == 0
+        out[f"B={B}"] = {"call_us": a.elapsed_time(b) / n * 1e3,
+                         "form": {1: "small", 2: "one launch", 3: "two launches"}[
+                             sv.sv_chain_form(B, c.K, c.V, sets[0]["target"].dtype)],
+                         "K": c.K, "V": c.V, "logits": c.dtype}
+    return out
 
 
 def main():
@@ -467,19 +500,31 @@ def main():
             steps[i % nsets]()
     torch.cuda.synchronize()
 
-    # Timed region: K steps, events around each call on the library's stream.
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # Timed region: K steps back to back on the library's stream, between one
+    # start and one stop event.
+    e_start, e_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        e_start.record(stream)
+        for i in range(args.steps):
+            steps[i % nsets]()
+        e_stop.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    total_ms = e_start.elapsed_time(e_stop)
+    ms_per_step = total_ms / args.steps
+
+    # Per-call times: the same K steps again with an event after every call
+    # (the events add a little to each call, so they are kept out of the
+    # timed region).
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with torch.cuda.stream(stream):
         ev[0].record(stream)
         for i in range(args.steps):
             steps[i % nsets]()
             ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall0
-    total_ms = ev[0].elapsed_time(ev[-1])
-    ms_per_step = total_ms / args.steps
     per_call_ms = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
 
     # Kernel region: the same K steps again, each call's streaming kernel
@@ -552,6 +597,8 @@ def main():
         "warm_same_inputs_us": warm_ms * 1e3,
         "wall_s_timed": t_wall,
     }
+    if kind == "chain" and wl == "c2" and not args.entropy and not args.graph:
+        result["small_batch"] = small_batch_latencies(sv, torch, cfg, dev, stream)
     if not args.no_cpu_baseline:
         cpu_inp = {k: v.cpu() for k, v in sets[0].items()}
         if kind == "chain":
