@@ -61,7 +61,16 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 typedef struct ihipEvent_t* hipEvent_t;
 
-typedef enum sv_status {
+/* In C++ both enums have int as their fixed underlying type, so every int a
+ * C caller passes (an unknown status code, a bad dtype) is a valid value of
+ * the type; the size and calling convention are those of int either way. */
+#ifdef __cplusplus
+#define SV_ENUM_INT : int
+#else
+#define SV_ENUM_INT
+#endif
+
+typedef enum sv_status SV_ENUM_INT {
   SV_OK = 0,
   SV_ERR_INVALID_ARGUMENT = 1, /* a size, pointer or alignment is invalid      */
   SV_ERR_UNSUPPORTED = 2,      /* valid but beyond this build's limits         */
@@ -69,7 +78,7 @@ typedef enum sv_status {
   SV_ERR_HIP = 4               /* the HIP runtime refused the launch           */
 } sv_status;
 
-typedef enum sv_dtype {
+typedef enum sv_dtype SV_ENUM_INT {
   SV_DTYPE_F32 = 0, /* IEEE binary32 logits                                 */
   SV_DTYPE_BF16 = 1 /* bfloat16 logits (16 high bits of a binary32)          */
 } sv_dtype;
