@@ -462,7 +462,8 @@ def main():
         kernel_name = ("chain_small_kernel (the whole call in one launch, the statistics workgroups deciding and "
                        "drawing: every logit row once, then the row pair at each sequence's first rejection)"
                        if form == 1 else
-                       "chain_one_launch_kernel (the whole call in one launch: every logit row once, then the "
+                       ("chain_one_launch_entropy_kernel" if args.entropy else "chain_one_launch_kernel") +
+                       " (the whole call in one launch: every logit row once, then the "
                        "row pair at each sequence's first rejection)" if form == 2 else
                        "chain_stats_chunk_entropy_kernel (statistics pass with the entropy: every logit row once)"
                        if args.entropy else "chain_stats_chunk_kernel (statistics pass: every logit row once)")
@@ -559,7 +560,7 @@ def main():
     assert flags == 0, f"device error flags {flags}"
 
     achieved = stream_bytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = counted_traffic(wl, kind)
+    traffic = counted_traffic(wl + ("_entropy" if args.entropy else ""), kind)
     result = {
         "metric": (METRIC if wl == "c2" and not args.entropy and not args.graph else
                    f"sampling throughput: rows·vocab/s + HBM GB/s vs peak, {config['workload']}" if kind == "sample"

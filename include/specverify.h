@@ -201,10 +201,11 @@ sv_status sv_verify_chain_noalloc(const void* target_logits, const void* draft_l
  * one-launch form is taken when the call's grid (statistics chunks and
  * sampling workgroups) is larger than the device holds at once, the rows
  * start on 16-byte boundaries (rows_aligned != 0: V * element size a
- * multiple of 16 and both logit tensors 16-byte aligned), K >= 1, no entropy
- * is requested (with_entropy == 0) and the statistics of a sequence fit the
- * decision's single round of loads. Small calls (B (2K+1) <= 256 rows in
- * all, rows on 16-byte boundaries, K >= 1, no entropy) whose grid the
+ * multiple of 16 and both logit tensors 16-byte aligned), K >= 1 and the
+ * statistics of a sequence fit the decision's single round of loads, with or
+ * without the entropy (with_entropy != 0 when it is requested). Small calls
+ * (B (2K+1) <= 256 rows in all, rows on 16-byte boundaries, K >= 1, no
+ * entropy) whose grid the
  * device holds at once also run as one launch, in which the statistics
  * workgroups decide and sample (sv_chain_form tells the two apart). The
  * outputs are bit-identical whichever form a call takes; only the timing
@@ -219,7 +220,8 @@ int32_t sv_chain_launches(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32
  * device (arguments as sv_chain_launches): 1 the small call (one launch,
  * chain_small_kernel: the statistics workgroups of each sequence also make
  * its decision and draw), 2 one launch with ticket queues
- * (chain_one_launch_kernel), 3 two launches (statistics pass, then sampling
+ * (chain_one_launch_kernel, or chain_one_launch_entropy_kernel with the
+ * entropy requested), 3 two launches (statistics pass, then sampling
  * pass); 0 for invalid sizes or dtype, or B = 0. Host-only query.
  */
 int32_t sv_chain_form(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32_t rows_aligned, int32_t with_entropy);

@@ -104,13 +104,13 @@ int device_cus() {
 // workgroups of a sequence take their tickets together and queue on one
 // counter: B=4 K=4 V=32000 fp32 took 26.1 us against 20.1 us. It also needs
 // rows on 16-byte boundaries (the chunked layout), at least one drafted
-// token, no entropy or drawn probability requested, and statistics that the
-// decision reads in one round: every piece of each of the 2K+1 rows among
+// token, no drawn probability requested (the entropy takes a kernel variant
+// of its own), and statistics that the decision reads in one round: every piece of each of the 2K+1 rows among
 // G lanes of one wave with at most 4 pieces per lane (G as the decision
 // takes it), chunk indices within 32 bits. Other calls keep the statistics
 // pass and the sampling pass as two launches.
-bool one_launch_ok(const sv::PieceLayout& L, int32_t B, int32_t K, int32_t nblk_b, bool extra_outputs) {
-  if (!SV_ONE_LAUNCH || L.cps <= 0 || K <= 0 || extra_outputs) return false;
+bool one_launch_ok(const sv::PieceLayout& L, int32_t B, int32_t K, int32_t nblk_b, bool drawn_prob) {
+  if (!SV_ONE_LAUNCH || L.cps <= 0 || K <= 0 || drawn_prob) return false;
   const int64_t grid = static_cast<int64_t>(B) * (L.cps + nblk_b);
   const int cus = device_cus();
   if (cus < 1 || grid <= static_cast<int64_t>(cus) * sv::kOneLaunchWGsPerCU) return false;
@@ -462,7 +462,7 @@ sv_status chain_call(const void* target_logits, const void* draft_logits, sv_dty
   p.done = reinterpret_cast<uint32_t*>(ws + L.off_done);
   p.plan = reinterpret_cast<uint64_t*>(ws + L.off_plan);
   const bool extra = entropy != nullptr || drawn_prob != nullptr;
-  p.one_launch = one_launch_ok(p.L, B, K, p.nblk_b, extra) ? 1 : 0;
+  p.one_launch = one_launch_ok(p.L, B, K, p.nblk_b, drawn_prob != nullptr) ? 1 : 0;
   if (chunked && small_ok(p.L, B, K, V, dtype, extra)) {
     p.one_launch = 2;
     const int64_t tpb = ceil_div(L.ntiles, p.L.cps);
@@ -488,7 +488,7 @@ int32_t chain_form(int32_t B, int32_t K, int32_t V, sv_dtype dtype, int32_t rows
   const bool chunked = rows_aligned != 0 && whole_vector_rows(V, dtype);
   const sv::PieceLayout L = piece_layout(2 * K + 1, V, dtype, chunked, chain_chunk_vecs(B, K, V, dtype));
   if (chunked && small_ok(L, B, K, V, dtype, with_entropy != 0)) return 1;
-  return one_launch_ok(L, B, K, chain_layout(B, K, V, dtype).nblk_b, with_entropy != 0) ? 2 : 3;
+  return one_launch_ok(L, B, K, chain_layout(B, K, V, dtype).nblk_b, false) ? 2 : 3;
 }
 
 }  // namespace

@@ -127,7 +127,7 @@ __device__ void stats_segment(const ChainParams& P, int b, int r, int seg) {
     const int64_t slot = (static_cast<int64_t>(b) * R + r) * P.L.nseg + seg;
     publish(&P.part_m[slot], tag_float(MC));
     publish(&P.part_s[slot], tag_nonneg_double(S));
-    if constexpr (kEnt) publish(&P.part_a[slot], static_cast<uint64_t>(__double_as_longlong(A)));
+    if constexpr (kEnt) publish(&P.part_a[slot], tag_any_double(A));
     if (x >= 0 && x < P.V) publish_gather<T>(P, b, r, row, x);
   }
 }
@@ -162,7 +162,7 @@ __device__ void stats_chunk(const ChainParams& P, int b, int ch) {
       const int64_t slot = (static_cast<int64_t>(b) * P.L.cps + ch) * P.L.kmax + (r - r_lo);
       publish(&P.part_m[slot], tag_float(MC));
       publish(&P.part_s[slot], tag_nonneg_double(S));
-      if constexpr (kEnt) publish(&P.part_a[slot], static_cast<uint64_t>(__double_as_longlong(A)));
+      if constexpr (kEnt) publish(&P.part_a[slot], tag_any_double(A));
       // the piece holding the drafted token publishes its logit
       if (x >= 0 && x < P.V && x / T::kVec >= p0 && x / T::kVec < p1) publish_gather<T>(P, b, r, body, x);
     }
@@ -448,10 +448,10 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
       }
       more = (n == 4);
       for (int i = 0; i < n; ++i) {
-        if (rm[i] == 0ull || rs[i] == 0ull) err |= kErrInternal;
+        if (rm[i] == 0ull || rs[i] == 0ull || (ent && ra[i] == 0ull)) err |= kErrInternal;
         const float mm = untag_float(rm[i]);
         const double sv = untag_nonneg_double(rs[i]);
-        const double av = __longlong_as_double(static_cast<long long>(ra[i]));
+        const double av = untag_any_double(ra[i]);
         if (mm == -INFINITY) continue;
         if (mm > mf) {
           const double d = static_cast<double>(mm) - static_cast<double>(mf);
@@ -511,7 +511,7 @@ __device__ __forceinline__ int decision_lanes(int R, int pmax) {
 // Every slot is read with an agent-scope load, all issued together; a slot
 // still zero (its store not visible yet) makes the wave return false before
 // anything is written, for the caller to read again.
-template <class T>
+template <class T, bool kEnt = false>
 __device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
   const int K = P.K;
@@ -532,7 +532,7 @@ __device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, Se
   const uint32_t first_row0 = ch0 * pr / nv;
   const int64_t base = static_cast<int64_t>(b) * L.cps;
   const int64_t any_slot = base * L.kmax;  // a valid address
-  uint64_t rm[4], rs[4];
+  uint64_t rm[4], rs[4], ra[4];
   bool has[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -542,6 +542,7 @@ __device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, Se
     const int64_t sl = has[i] ? (base + ch) * L.kmax + (p == 0u ? rr - first_row0 : 0u) : any_slot;
     rm[i] = peek(&P.part_m[sl]);
     rs[i] = peek(&P.part_s[sl]);
+    ra[i] = kEnt ? peek(&P.part_a[sl]) : 0ull;
   }
   const float Tv = temperature_of(P.temperature, b);
   int x = -1;
@@ -557,36 +558,53 @@ __device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, Se
   }
   bool missing = lane < K && x >= 0 && x < P.V && (vt == 0ull || vd == 0ull);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) missing |= has[i] && (rm[i] == 0ull || rs[i] == 0ull);
+  for (int i = 0; i < 4; ++i) missing |= has[i] && (rm[i] == 0ull || rs[i] == 0ull || (kEnt && ra[i] == 0ull));
   if (__ballot(missing) != 0ull) return false;
 
   // decide_wave's combine of one round: running reference mf, fp64 sum zf
+  // (and af, the fp64 sum of 2^a * a at the reference mf)
   float mf = -INFINITY;
-  double zf = 0.0;
+  double zf = 0.0, af = 0.0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (!has[i]) continue;
     const float mm = untag_float(rm[i]);
     const double sv = untag_nonneg_double(rs[i]);
+    const double av = untag_any_double(ra[i]);
     if (mm == -INFINITY) continue;
     if (mm > mf) {
+      const double d = static_cast<double>(mm) - static_cast<double>(mf);
       const double f = (mf == -INFINITY) ? 0.0 : ref_factor(mf, mm);
+      if constexpr (kEnt) af = (mf == -INFINITY ? 0.0 : f * (af - d * zf)) + av;
       zf = zf * f + sv;
       mf = mm;
     } else {
-      zf += sv * ref_factor(mm, mf);
+      const double d = static_cast<double>(mf) - static_cast<double>(mm);
+      const double f = ref_factor(mm, mf);
+      zf += sv * f;
+      if constexpr (kEnt) af += f * (av - d * sv);
     }
   }
   float M = mf;
   for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  const double dl = static_cast<double>(M) - static_cast<double>(mf);
   const double fl = (mf == -INFINITY) ? 0.0 : ref_factor(mf, M);
   double zl = zf * fl;
   for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
+  double al = 0.0;
+  if constexpr (kEnt) {
+    al = (mf == -INFINITY) ? 0.0 : fl * (af - dl * zf);
+    for (int o = 1; o < G; o <<= 1) al += __shfl_xor(al, o, kWave);
+  }
   if (row_ok && gl == 0) {
     const bool fin = (zl > 0.0) && isfinite(zl) && isfinite(M);
     if (!fin) err |= SV_ERRF_NONFINITE;
     const double lz = fin ? log2_fast(zl) : log2(zl);
     s_L[r] = static_cast<double>(M) + lz;
+    // H = ln 2 * (log2 Z - A / Z), as decide_wave
+    if (kEnt && writer)
+      P.entropy[static_cast<int64_t>(b) * R + r] =
+          (fin && Tv > 0.0f && isfinite(Tv)) ? static_cast<float>(0.6931471805599453 * (lz - al / zl)) : NAN;
   }
   decide_tail<T>(P, b, s_plan, writer, s_L, x, u, vt, vd, err, Tv);
   return true;
@@ -599,7 +617,7 @@ __device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, Se
 // sequence's ticket queue before this sampling role, to a workgroup that is
 // running and waits for nothing, so the wait ends; it is still bounded
 // like await_slot. Returns false on expiry or on an abort raised elsewhere.
-template <class T>
+template <class T, bool kEnt = false>
 __device__ bool decide_live(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
   const uint32_t need = static_cast<uint32_t>(P.L.cps);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -612,7 +630,7 @@ __device__ bool decide_live(const ChainParams& P, int b, SeqPlan* s_plan, bool w
     }
     __builtin_amdgcn_s_sleep(SV_POLL_SLEEP);
   }
-  while (!decide_live_wave<T>(P, b, s_plan, writer)) {
+  while (!decide_live_wave<T, kEnt>(P, b, s_plan, writer)) {
     if (peek(P.abort) != 0ull) return false;
     if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
       publish(P.abort, 1ull);
@@ -1014,11 +1032,13 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
   __shared__ SeqPlan s_plan;
   if (wave_id() == 0) {
     if constexpr (kLive) {
-      if (!decide_live<T>(P, b, &s_plan, blk == 0) && lane_id() == 0) {
+      if (!decide_live<T, kEnt>(P, b, &s_plan, blk == 0) && lane_id() == 0) {
         if (blk == 0) {
           P.accept_len[b] = -1;
           for (int i = 0; i <= P.K; ++i) P.out_tokens[static_cast<int64_t>(b) * (P.K + 1) + i] = -1;
           if (P.residual_mass != nullptr) P.residual_mass[b] = -1.0f;
+          if (kEnt)
+            for (int r = 0; r <= 2 * P.K; ++r) P.entropy[static_cast<int64_t>(b) * (2 * P.K + 1) + r] = NAN;
         }
         raise_error(P.err_flags, kErrInternal);
         s_plan.j = -1;
@@ -1240,7 +1260,7 @@ __device__ __forceinline__ uint32_t one_launch_sequence(uint32_t blk, uint32_t B
   return nmid + (i - nmid * seg) / nblk;
 }
 
-// One-launch call (rows on 16-byte boundaries, no entropy requested): the
+// One-launch call (rows on 16-byte boundaries, K >= 1): the
 // statistics chunks and the sampling workgroups of every sequence in one
 // grid, so that the sampling of the sequences streamed first overlaps the
 // streaming of the later ones instead of waiting for the whole pass.
@@ -1258,8 +1278,8 @@ __device__ __forceinline__ uint32_t one_launch_sequence(uint32_t blk, uint32_t B
 // first sequences while the last ones stream. The workgroup that takes the
 // last ticket of a queue returns its counter to zero; a statistics role
 // counts its chunk in P.done[b] once its slot stores have completed.
-template <class T>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_ONE_LAUNCH_WAVES, SV_ONE_LAUNCH_WAVES))) void chain_one_launch_kernel(ChainParams P) {
+template <class T, bool kEnt>
+__device__ __forceinline__ void one_launch_item(const ChainParams& P) {
   __shared__ uint32_t s_ticket;
   const uint32_t cps = static_cast<uint32_t>(P.L.cps);
   const uint32_t nblk = static_cast<uint32_t>(P.nblk_b);
@@ -1280,7 +1300,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_ONE
     return;
   }
   if (t < cps) {
-    stats_chunk<T, kStatsTPB, false>(P, static_cast<int>(b), static_cast<int>(t));
+    stats_chunk<T, kStatsTPB, kEnt>(P, static_cast<int>(b), static_cast<int>(t));
     if (threadIdx.x == 0) {
       // count the chunk once this thread's slot stores have completed (the
       // readers still check every slot's tag and read again if it is zero)
@@ -1290,8 +1310,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_ONE
     }
   } else {
     if (SV_SAMPLE_PRIO > 0) __builtin_amdgcn_s_setprio(SV_SAMPLE_PRIO);
-    sample_seq<T, kLiveTiles, true, false, true>(P, static_cast<int>(b), static_cast<int>(t - cps));
+    sample_seq<T, live_tiles<T>(), true, kEnt, true>(P, static_cast<int>(b), static_cast<int>(t - cps));
   }
+}
+
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_ONE_LAUNCH_WAVES, SV_ONE_LAUNCH_WAVES))) void chain_one_launch_kernel(ChainParams P) {
+  one_launch_item<T, false>(P);
+}
+
+// The same call with the entropy of every row requested: the statistics
+// roles also publish A per piece, the deciding workgroup writes the entropy.
+template <class T>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_ONE_LAUNCH_WAVES, SV_ONE_LAUNCH_WAVES))) void chain_one_launch_entropy_kernel(ChainParams P) {
+  one_launch_item<T, true>(P);
 }
 
 // Small call (at most a few hundred rows in all, the grid resident at once):
@@ -1356,7 +1388,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((flatten)) void chain_small
       tile_totals<T, kSmallTiles, true, true>(P, b, pl, t_begin, t_end, keep, keepx);
       if (t_begin < t_end) small_owner_draw<T, kSmallTiles>(P, b, pl, t_begin, t_end, keep, keepx);
     } else {
-      tile_totals<T, kLiveTiles, true>(P, b, pl, t_begin, t_end);
+      tile_totals<T, live_tiles<T>(), true>(P, b, pl, t_begin, t_end);
     }
   }
   sample_finish<T, false, true>(P, b, pl, P.cnt + static_cast<int64_t>(b) * kCtrStride, cps, done, !owners);
@@ -1381,7 +1413,8 @@ static hipError_t launch_chain_t(const ChainParams& p, const PassEvents& ev, hip
   if (p.one_launch) {
     const int64_t grid = static_cast<int64_t>(p.B) * (p.L.cps + p.nblk_b);
     if (grid > INT32_MAX) return hipErrorInvalidConfiguration;
-    launch_stream_pass(chain_one_launch_kernel<T>, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), stream, ev, p);
+    launch_stream_pass(ent ? chain_one_launch_entropy_kernel<T> : chain_one_launch_kernel<T>,
+                       dim3(static_cast<uint32_t>(grid)), dim3(kThreads), stream, ev, p);
     return hipGetLastError();
   }
   if (p.L.cps > 0)

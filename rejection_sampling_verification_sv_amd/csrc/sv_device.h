@@ -356,6 +356,13 @@ __device__ __forceinline__ uint64_t tag_nonneg_double(double d) {
 __device__ __forceinline__ double untag_nonneg_double(uint64_t v) {
   return __longlong_as_double(static_cast<long long>(v & ~(1ull << 63)));
 }
+// any double, stored as the complement of its bits: zero only for the
+// all-ones pattern, a NaN that no arithmetic here produces (a NaN it makes
+// or passes on from fp32 inputs has zero low mantissa bits)
+__device__ __forceinline__ uint64_t tag_any_double(double d) {
+  return ~static_cast<uint64_t>(__double_as_longlong(d));
+}
+__device__ __forceinline__ double untag_any_double(uint64_t v) { return __longlong_as_double(static_cast<long long>(~v)); }
 
 // Every thread of the block calls this after thread 0 has published the
 // block's slots. Returns true in exactly one block per counter round (the

@@ -99,8 +99,8 @@ struct ChainParams {
   // workspace (all zero between calls)
   uint64_t* part_m;   // per row piece: tagged fp32 reference fl(max * c_hi)
   uint64_t* part_s;   // per row piece: tagged fp64 sum of 2^(x c - reference)
-  uint64_t* part_a;   // per row piece, entropy only: fp64 bits of the sum of
-                      // 2^a * a, a = x c - reference (untagged)
+  uint64_t* part_a;   // per row piece, entropy only: tagged (complemented)
+                      // fp64 sum of 2^a * a, a = x c - reference
   uint32_t* cnt;      // [B] sampling workgroups finished
   uint64_t* tile_sum; // [B, ntiles] tagged fp64 sampling weight per tile
   uint64_t* gat;      // [B, 2K+1] tagged fp32 logit of row r at its drafted
@@ -300,6 +300,13 @@ constexpr int kOneLaunchWGsPerCU = SV_ONE_LAUNCH_WAVES;  // 4-wave workgroups on
 #define SV_LIVE_TILES 4
 #endif
 constexpr int kLiveTiles = SV_LIVE_TILES;
+// The same in tiles of a dtype: fp32 tiles are twice the bytes of bf16 ones,
+// so half as many keep the same loads in flight (with four, the fp32 kernel
+// spilled 30 VGPRs to scratch at 7 waves/SIMD).
+template <class T>
+constexpr int live_tiles() {
+  return T::kBytes == 2 ? kLiveTiles : (kLiveTiles + 1) / 2;
+}
 // Per-sequence counters of the one-launch call (ticket, chunks counted,
 // sampling arrivals) lie this many 32-bit words apart. Packed counters put
 // the polls of the waiting sampling workgroups and the contended ticket
@@ -336,13 +343,10 @@ constexpr int kSampleLag = SV_SAMPLE_LAG;
 #ifndef SV_STATS_WAVES
 #define SV_STATS_WAVES 8
 #endif
-// The same for the entropy variant of the stream: its extra accumulator does
-// not fit 64 VGPRs with two batches of two vectors in flight (82 VGPRs, 5
-// waves/SIMD at run time). Measured on c2: 41.7 us; one vector per batch at
-// 8 waves/SIMD 39.1 us but with other rounding of p and q; 8 waves with
-// spills 61 us.
+// The same for the entropy variant of the stream (66 VGPRs with bf16: its
+// extra accumulator and the two forms of a batch's sum of A).
 #ifndef SV_STATS_WAVES_ENT
-#define SV_STATS_WAVES_ENT 4
+#define SV_STATS_WAVES_ENT 7
 #endif
 
 // Chunked layouts: each row is cut into k equal chunks (one workgroup each),

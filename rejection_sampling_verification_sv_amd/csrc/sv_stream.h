@@ -104,39 +104,60 @@ template <class T, int U = kStatsUnroll, bool kEnt = false>
 __device__ __forceinline__ void add_batch(Running& st, const uint4 (&raw)[U], Scale c) {
   if constexpr (kEnt && T::kVec == 8) {
     // bf16 with the entropy: the same operations in the same order as
-    // running_add (one group of 8 per vector), with the values widened twice
-    // from the raw vectors (for the maximum, then behind an empty asm for
-    // the exponentials) so that 16 floats do not stay live across both
-    float bm = -INFINITY;
+    // running_add (one group of 8 per vector), so the same (reference, sum);
+    // A as one fma chain
+    float t[U][8];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float t[8];
-      unpack<T>(raw[u], t);
+    for (int u = 0; u < U; ++u) unpack<T>(raw[u], t[u]);
+    float bm = -INFINITY, bl = INFINITY;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bm = fmaxf(bm, t[i]);
-    }
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        bm = fmaxf(bm, t[u][i]);
+        bl = fminf(bl, t[u][i]);
+      }
     const float m_new = fmaxf(st.mx, bm);
     const float scale = (st.mx == -INFINITY) ? 0.0f : fast_exp2(st.mx * c.hi - m_new * c.hi);
     st.a = (st.mx == -INFINITY) ? 0.0f : scale * (st.a - (m_new * c.hi - st.mx * c.hi) * st.s);
     st.mx = m_new;
     const float neg_m = neg_reference(m_new, c);
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float acca = st.a;  // A feeds only the entropy: one fma chain
+    float acca = st.a;
+    // Arguments below kArgFloor have 2^a = 0, so the clamp changes nothing
+    // but the product 0 * -inf of a masked logit: a batch without -inf
+    // (the usual case) sums A unclamped
+    if (bl != -INFINITY) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint4 r = raw[u];
-      asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w));
-      float t[8], e[8];
-      unpack<T>(r, t);
+      for (int u = 0; u < U; ++u) {
+        float e[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float arg = scaled_arg(t[i], c, neg_m);
-        e[i] = fast_exp2(arg);
-        acca = fmaf(e[i], fmaxf(arg, kArgFloor), acca);
+        for (int i = 0; i < 8; ++i) {
+          const float arg = scaled_arg(t[u][i], c, neg_m);
+          e[i] = fast_exp2(arg);
+          acca = fmaf(e[i], arg, acca);
+        }
+        acc[u & 3] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       }
-      acc[u & 3] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float e[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float arg = scaled_arg(t[u][i], c, neg_m);
+          e[i] = fast_exp2(arg);
+          acca = fmaf(e[i], fmaxf(arg, kArgFloor), acca);
+        }
+        acc[u & 3] += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      }
     }
     st.s = st.s * scale + ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    // A is made here, batch by batch: otherwise the compiler sinks the fma
+    // chain into the next batch's rescale, which drops A when no finite
+    // logit has been seen, and keeps this batch's 16 arguments and
+    // exponentials live across the next batch's loads (82 VGPRs, not 57)
+    asm volatile("" : "+v"(acca));
     st.a = acca;
   } else {
     float x[U * T::kVec];

@@ -71,7 +71,11 @@ def _check(sv, inp, rows=None, label="", record=False):
 def test_entropy_of_the_chain_workloads(sv, name):
     cfg = CHAIN_CONFIGS[name]
     _say("entropy", cfg.name)
-    _check(sv, chain_inputs(cfg, device="cuda"), label=cfg.name, record=True)
+    inp = chain_inputs(cfg, device="cuda")
+    if name == "c2":  # the one-launch form, with its entropy variant
+        B, _, V = inp["target"].shape
+        assert sv.sv_chain_form(B, inp["draft"].shape[1], V, inp["target"].dtype, True, True) == 2
+    _check(sv, inp, label=cfg.name, record=True)
 
 
 def test_entropy_c3_per_row_temperature_full(sv):
