@@ -240,20 +240,39 @@ ChainLayout chain_layout(int32_t B, int32_t K, int32_t V, sv_dtype d, int64_t mi
   return L;
 }
 
-// One-pass draft-side sampling: runs of kRunVecs vectors per row, split
-// evenly into cps chunks per row (about kChunksSample chunks per call, each of
-// at least kChunkMinVecs vectors), one record per run.
-struct RunLayout {
-  int32_t nrun, cps;
-  size_t total;
+// Draft-side sampling (rows on 16-byte boundaries): units of kUnitVecs vectors (upr per row),
+// records of kSegVecs vectors (nrec per row); a grid of about one round of
+// resident blocks on MI355X (256 compute units x kSampleWGsPerCU), fewer
+// for small calls (about kSampleUnitsPerWave units per wave), in ngroups
+// groups of wpg blocks. The layout depends on the call's shape only (not on
+// the device), so the workspace size does too.
+struct SampleLayout {
+  int32_t upr, nrec, ngroups, wpg;
+  size_t off_m, off_s, off_take, total;
 };
 
-RunLayout run_layout(int32_t R, int32_t V, sv_dtype d) {
-  RunLayout L{};
-  L.nrun = static_cast<int32_t>(ceil_div(row_vecs(V, d), sv::kRunVecs));
-  const int64_t runs = ceil_div(chunk_vecs(R, 1, V, d, sv::kChunksSample), sv::kRunVecs);
-  L.cps = static_cast<int32_t>(ceil_div(L.nrun, runs));
-  L.total = align_up(sizeof(uint64_t) * static_cast<int64_t>(R) * L.nrun);
+SampleLayout sample_layout(int32_t R, int32_t V, sv_dtype d) {
+  SampleLayout L{};
+  const int64_t nvec = row_vecs(V, d);
+  const int64_t upr = nvec > 0 ? ceil_div(nvec, sv::kUnitVecs) : 1;
+  const int64_t units = static_cast<int64_t>(R) * upr;
+  int64_t blocks = ceil_div(units, static_cast<int64_t>(sv::kWaves) * sv::kSampleUnitsPerWave);
+  const int64_t most = 256LL * sv::kSampleWGsPerCU;
+  blocks = blocks < 1 ? 1 : (blocks > most ? most : blocks);
+  const int64_t groups = blocks < sv::kSampleGroups ? blocks : sv::kSampleGroups;
+  L.upr = static_cast<int32_t>(upr);
+  L.nrec = static_cast<int32_t>(upr * sv::kSegsPerUnit);
+  L.ngroups = static_cast<int32_t>(groups);
+  L.wpg = static_cast<int32_t>(ceil_div(blocks, groups));
+  const int64_t nrec = static_cast<int64_t>(R) * L.nrec;
+  size_t off = 0;
+  L.off_m = off;
+  off = align_up(off + sizeof(uint64_t) * nrec);
+  L.off_s = off;
+  off = align_up(off + sizeof(uint64_t) * nrec);
+  L.off_take = off;
+  off = align_up(off + sizeof(uint32_t) * static_cast<int64_t>(sv::kSampleGroups) * sv::kCtrStride);
+  L.total = off;
   return L;
 }
 
@@ -672,11 +691,11 @@ sv_status sv_verify_chain_lm_head(const void* hidden, const void* head_weight, i
 
 size_t sv_sample_workspace_bytes(int32_t R, int32_t V, sv_dtype dtype) {
   if (!chain_sizes_ok(R, 0, V) || !dtype_ok(dtype)) return 0;
-  // rows on 16-byte boundaries use the run records, others the chain
+  // rows on 16-byte boundaries use the segment records, others the chain
   // workspace of R sequences with K = 0; both start at offset 0
   const size_t chain = chain_layout(R, 0, V, dtype).total;
-  const size_t runs = whole_vector_rows(V, dtype) ? run_layout(R, V, dtype).total : 0;
-  return chain > runs ? chain : runs;
+  const size_t segs = whole_vector_rows(V, dtype) ? sample_layout(R, V, dtype).total : 0;
+  return chain > segs ? chain : segs;
 }
 
 sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temperature, const float* uniforms,
@@ -692,8 +711,10 @@ sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temper
   if (!whole_vector_rows(V, dtype) || !aligned_to(logits, 16))  // rows off 16-byte boundaries: two passes
     return chain_call(logits, nullptr, dtype, nullptr, temperature, uniforms, R, 0, V, nullptr, out_tokens, nullptr,
                       nullptr, nullptr, nullptr, out_prob, err_flags, workspace, workspace_bytes, stream, ev);
-  const RunLayout L = run_layout(R, V, dtype);
-  if (static_cast<int64_t>(R) * L.cps > INT32_MAX) return SV_ERR_UNSUPPORTED;
+  const SampleLayout L = sample_layout(R, V, dtype);
+  if (static_cast<int64_t>(R) * L.upr > INT32_MAX || static_cast<int64_t>(R) * L.nrec > INT32_MAX)
+    return SV_ERR_UNSUPPORTED;
+  char* ws = static_cast<char*>(workspace);
   sv::SampleParams p{};
   p.logits = logits;
   p.temperature = temperature;
@@ -701,12 +722,16 @@ sv_status sv_sample_rows(const void* logits, sv_dtype dtype, const float* temper
   p.R = R;
   p.V = V;
   p.nvec = row_vecs(V, dtype);
-  p.nrun = L.nrun;
-  p.cps = L.cps;
+  p.upr = L.upr;
+  p.nrec = L.nrec;
+  p.ngroups = L.ngroups;
+  p.wpg = L.wpg;
   p.out_tokens = out_tokens;
   p.out_prob = out_prob;
   p.err_flags = err_flags;
-  p.rec = static_cast<uint64_t*>(workspace);
+  p.rec_m = reinterpret_cast<uint64_t*>(ws + L.off_m);
+  p.rec_s = reinterpret_cast<uint64_t*>(ws + L.off_s);
+  p.take = reinterpret_cast<uint32_t*>(ws + L.off_take);
   return from_hip(sv::launch_sample(p, dtype, ev, stream));
 }
 

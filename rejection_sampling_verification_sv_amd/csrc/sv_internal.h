@@ -195,23 +195,54 @@ struct TreeParams {
   uint64_t* part;     // per row piece: (max value bits << 32) | (lowest index + 1)
 };
 
-// One-pass draft-side sampling (rows on 16-byte boundaries): each row is cut
-// into runs of kRunVecs 16-byte vectors (the last run of a row may be
-// short); the streaming pass reduces every run to one tagged record
-// (reference, sum) and the draw re-reads one run per row. The runs of a row
-// are split evenly into cps chunks (one workgroup each), about
-// kChunksSample chunks per call. Runs of 128 vectors (1024 bf16 tokens) and
-// about 4096 chunks measured best on 320 and 2048 rows of V = 128256 and
-// 152064 (256-vector runs and 2048 chunks: up to 20 % slower).
+// Runs of kRunVecs 16-byte vectors (the last run of a row may be short):
+// the unit of the sampling-tree walk's passes over a row pair.
 #ifndef SV_RUN_VECS
 #define SV_RUN_VECS 128
 #endif
 constexpr int kRunVecs = SV_RUN_VECS;
 constexpr int kRunLaneVecs = kRunVecs / kWave;  // vectors per lane per run
-#ifndef SV_CHUNKS_SAMPLE
-#define SV_CHUNKS_SAMPLE 4096
+
+// One-launch draft-side sampling (rows on 16-byte boundaries). Each row is
+// cut into units of kUnitVecs 16-byte vectors (upr per row, the last may be
+// short), and every unit into segments of kSegVecs vectors, one record per
+// segment (nrec = upr * kSegsPerUnit per row, in token order; segments past
+// the row's end are empty records). The call's R * upr units are split into
+// ngroups contiguous ranges; group k's range is streamed by the waves of
+// blocks k, k + ngroups, k + 2 ngroups, ... (wpg blocks: one of every
+// round in which the hardware hands blocks out), which take its units in
+// order from the group's counter, one unit per wave at a time. A second
+// launch draws each row's token from its records and one segment.
+#ifndef SV_SEG_VECS
+#define SV_SEG_VECS 256
 #endif
-constexpr int kChunksSample = SV_CHUNKS_SAMPLE;
+constexpr int kSegVecs = SV_SEG_VECS;
+#ifndef SV_SEGS_PER_UNIT
+#define SV_SEGS_PER_UNIT 4
+#endif
+constexpr int kSegsPerUnit = SV_SEGS_PER_UNIT;
+constexpr int kUnitVecs = kSegVecs * kSegsPerUnit;
+#ifndef SV_SAMPLE_WGS_PER_CU
+#define SV_SAMPLE_WGS_PER_CU 8
+#endif
+constexpr int kSampleWGsPerCU = SV_SAMPLE_WGS_PER_CU;
+#ifndef SV_SAMPLE_GROUPS
+#define SV_SAMPLE_GROUPS 256
+#endif
+constexpr int kSampleGroups = SV_SAMPLE_GROUPS;
+// Units per wave the grid is sized for, at least (small calls launch fewer
+// blocks). Measured on MI355X, s2 = 320 rows of V = 128256 bf16 and
+// s3 = 2048 rows of V = 152064 bf16, stream kernel by its launch events:
+// 1024-vector units, one unit per wave 19.4 / 108.3 us; two units per wave
+// 23.1 / 107.0 us; 512-vector units 19.7-20.5 / 109.1-109.2 us; 256-vector
+// units 21.8 / 114.2 us. A static split (one piece per wave, no counter)
+// measured 18.4 / 110.7 us.
+#ifndef SV_SAMPLE_UNITS_PER_WAVE
+#define SV_SAMPLE_UNITS_PER_WAVE 1
+#endif
+constexpr int kSampleUnitsPerWave = SV_SAMPLE_UNITS_PER_WAVE;
+constexpr int kSegLaneVecs = kSegVecs / kWave;  // vectors per lane of the draw's rescan
+static_assert(kSegVecs % (kWave * 2) == 0, "segments are whole batches of the stream");
 
 struct SampleParams {
   const void* logits;      // [R, V] rows; row r uses temperature[r]
@@ -219,16 +250,21 @@ struct SampleParams {
   const float* uniforms;
   int32_t R, V;
   int64_t nvec;        // 16-byte vectors per row
-  int32_t nrun;        // runs per row
-  int32_t cps;         // chunks per row (<= nrun)
+  int32_t upr;         // units per row
+  int32_t nrec;        // records per row (upr * kSegsPerUnit)
+  int32_t ngroups;     // unit groups (and counters)
+  int32_t wpg;         // blocks per group
   int32_t* out_tokens;
   float* out_prob;
   int32_t* err_flags;
-  uint64_t* rec;       // workspace [R, nrun]: record of run g of row r
+  uint64_t* rec_m;     // workspace [R, nrec]: tagged fp32 reference of a segment
+  uint64_t* rec_s;     // workspace [R, nrec]: tagged fp64 sum of 2^(x c - reference)
+  uint32_t* take;      // workspace [ngroups * kCtrStride]: units of the group handed out (+ failed takes)
 };
 
-// A run record: the fp32 reference in the upper half, the fp32 sum with its
-// sign bit set in the lower half (so a written record is never zero).
+// A run record of the sampling-tree walk: the fp32 reference in the upper
+// half, the fp32 sum with its sign bit set in the lower half (so a written
+// record is never zero).
 __device__ __forceinline__ uint64_t tag_run(float ref, float sum) {
   return (static_cast<uint64_t>(__float_as_uint(ref)) << 32) |
          static_cast<uint64_t>(__float_as_uint(sum) | 0x80000000u);

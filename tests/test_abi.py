@@ -183,15 +183,15 @@ def test_stream_pass_hook_arguments(lib):
 
 
 def test_chain_launches_query(lib):
-    # host-only query of the launch form; without a device (this container)
-    # the library cannot size the grid against the device and answers 2
+    # host-only query of the launch form; without a device the library
+    # cannot size the grid against one and answers 2 where one launch needs it
     f = lib.sv_chain_launches
     f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int32, ctypes.c_int32]
     f.restype = ctypes.c_int32
     assert f(-1, 5, 10, 1, 1, 0) == 0 and f(4, 64, 10, 1, 1, 0) == 0 and f(4, 2, 0, 1, 1, 0) == 0
     assert f(4, 2, 10, 7, 1, 0) == 0      # bad dtype
     assert f(0, 5, 128256, 1, 1, 0) == 0  # nothing to launch
-    assert f(64, 5, 128256, 1, 1, 1) == 2  # entropy: always two launches
+    assert f(64, 5, 128256, 1, 1, 1) in (1, 2)  # entropy: its own one-launch kernel
     assert f(64, 5, 128255, 1, 1, 0) == 2  # rows off 16-byte boundaries
     assert f(64, 0, 128256, 1, 1, 0) == 2  # K = 0
     assert f(64, 5, 128256, 1, 1, 0) in (1, 2)
@@ -204,7 +204,7 @@ def test_chain_form_query(lib):
     f.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.c_int32, ctypes.c_int32]
     f.restype = ctypes.c_int32
     assert f(-1, 5, 10, 1, 1, 0) == 0 and f(4, 2, 10, 7, 1, 0) == 0 and f(0, 5, 128256, 1, 1, 0) == 0
-    assert f(4, 4, 32000, 0, 1, 1) == 3      # entropy requested: never the small or one-launch form
+    assert f(4, 4, 32000, 0, 1, 1) == 3      # entropy requested: never the small form (and too small for one launch)
     assert f(4, 4, 32000, 0, 0, 0) == 3      # rows off 16-byte boundaries
     assert f(4, 0, 32000, 0, 1, 0) == 3      # K = 0
     assert f(4, 4, 32000, 0, 1, 0) in (1, 3)
