@@ -25,10 +25,11 @@
 // Pass 2 — tree_sample_walk_kernel, one 1024-thread workgroup per sequence,
 // all threads following the same walk (every decision is computed by every
 // thread from the same shared values):
+//   up front, one round trip: every node's token, uniform and two logits at
+//   its parent's position, and every position's target and draft
+//   log-normalisers from their records (fp64), into LDS;
 //   at each node: its children by one ballot per wave over the parent array
-//   (one node per thread), their tokens, uniforms and logits at the node's
-//   position prefetched into LDS; the log-normalisers of the node's target
-//   and draft rows from their run records (fp64);
+//   (one node per thread);
 //   each child's test in fp64: P_r(x) = max(0, P_{r-1}(x) - q(x)) / Z_r
 //   applied r times to p(x), alpha = min(1, P_r(x) / q(x));
 //   each rejection: one block-wide pass over the row pair forming
@@ -206,29 +207,6 @@ __device__ void walk_exchange(const TreeSampleParams& P, int b, uint32_t pass, i
   if (err != 0u) atomicOr(s_err, err);
 }
 
-// One wave: (M, Z) of a row from its run records, M = the largest reference,
-// Z = sum of sum * 2^(ref - M) in fp64 (fixed order).
-__device__ void row_norm_wave(const uint64_t* rec, int nrun, float* M, double* Z, uint32_t* err) {
-  const int lane = lane_id();
-  float m = -INFINITY;
-  for (int g = lane; g < nrun; g += kWave) {
-    const uint64_t v = rec[g];
-    if (v == 0ull) *err |= kErrInternal;
-    m = fmaxf(m, run_ref(v));
-  }
-  m = wave_max_dpp(m);
-  double z = 0.0;
-  for (int g = lane; g < nrun; g += kWave) {
-    const uint64_t v = rec[g];
-    const float ref = run_ref(v);
-    const float s = run_sum(v);
-    if (s != s) z += static_cast<double>(s);
-    else if (ref != -INFINITY && s > 0.0f) z += static_cast<double>(s) * ref_factor(ref, m);
-  }
-  *M = m;
-  *Z = wave_sum(z);
-}
-
 // The final draw by one wave: the run whose inclusive total first exceeds
 // u * (sum of the run totals) (the last run with weight if rounding leaves
 // none), then that run rescanned in ascending token order (lane l holds its
@@ -343,16 +321,15 @@ template <class T>
 __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSampleParams P) {
   __shared__ int s_par[SV_MAX_TREE_NODES];
   __shared__ int s_kids[SV_MAX_TREE_NODES];
-  __shared__ float s_klt[SV_MAX_TREE_NODES];
-  __shared__ float s_kld[SV_MAX_TREE_NODES];
-  __shared__ float s_ku[SV_MAX_TREE_NODES];
+  __shared__ float s_lt[SV_MAX_TREE_NODES];  // node v's target and draft logits at its parent's position
+  __shared__ float s_ld[SV_MAX_TREE_NODES];
+  __shared__ float s_u[SV_MAX_TREE_NODES];   // node v's uniform
   __shared__ int s_path[SV_MAX_TREE_NODES];
   __shared__ double s_run[kMaxWalkRuns];
   __shared__ double s_Z[SV_MAX_TREE_NODES];
   __shared__ float s_invZ[SV_MAX_TREE_NODES];
+  __shared__ double s_L[2 * (SV_MAX_TREE_NODES + 1)];  // log-normalisers: target rows, then draft rows, by position
   __shared__ uint64_t s_mask[kWalkWaves];
-  __shared__ float s_M[2];
-  __shared__ double s_Zr[2];
   __shared__ double s_sum;
   __shared__ int s_token;
   __shared__ uint32_t s_err;
@@ -403,16 +380,53 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
     s_token = -1;
   }
   __syncthreads();
-  // thread v owns node v (N <= kWalkThreads): its parent, token and uniform
-  int my_x = 0;
-  float my_u = 0.0f;
+  // thread v owns node v (N <= kWalkThreads): its parent, token and uniform,
+  // and its two logits at its parent's position (the position its test is
+  // taken at), all loaded once, up front
   if (tid < N) {
     const int par = P.parents[tid];
+    const int x = P.tokens[static_cast<int64_t>(b) * N + tid];
     s_par[tid] = par;
-    if (!(par == -1 || (par >= 0 && par < tid))) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_PARENT));
-    my_x = P.tokens[static_cast<int64_t>(b) * N + tid];
-    my_u = P.uniforms[static_cast<int64_t>(b) * N1 + tid];
-    if (my_x < 0 || my_x >= P.V) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_TOKEN));
+    s_u[tid] = P.uniforms[static_cast<int64_t>(b) * N1 + tid];
+    const bool par_ok = par == -1 || (par >= 0 && par < tid);
+    const bool x_ok = x >= 0 && x < P.V;
+    if (!par_ok) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_PARENT));
+    if (!x_ok) atomicOr(&s_err, static_cast<uint32_t>(SV_ERRF_TOKEN));
+    float lt = 0.0f, ld = 0.0f;
+    if (par_ok && x_ok) {
+      const int64_t row = static_cast<int64_t>(b) * N1 + (par + 1);
+      lt = load_elem<T>(tbase + row * row_bytes, x);
+      ld = load_elem<T>(dbase + row * row_bytes, x);
+    }
+    s_lt[tid] = lt;
+    s_ld[tid] = ld;
+  }
+  // every position's log-normalisers L = M + log2 Z of its target and draft
+  // rows from their records (M the largest reference, Z the fp64 sum of
+  // sum * 2^(ref - M) in record order; NaN for a row without finite
+  // statistics), one row per thread
+  for (int q = tid; q < 2 * static_cast<int>(N1); q += kWalkThreads) {
+    const int64_t pos = q < N1 ? q : q - N1;
+    const int64_t rec_row = (q < N1 ? 0 : static_cast<int64_t>(P.B) * N1) + static_cast<int64_t>(b) * N1 + pos;
+    const uint64_t* rec = P.rec + rec_row * P.nrec;
+    uint32_t e = 0u;
+    float m = -INFINITY;
+    for (int g = 0; g < P.nrec; ++g) {
+      const uint64_t v = rec[g];
+      if (v == 0ull) e |= kErrInternal;
+      m = fmaxf(m, run_ref(v));
+    }
+    double z = 0.0;
+    for (int g = 0; g < P.nrec; ++g) {
+      const uint64_t v = rec[g];
+      const float ref = run_ref(v);
+      const float sm = run_sum(v);
+      if (sm != sm) z += static_cast<double>(sm);
+      else if (ref != -INFINITY && sm > 0.0f) z += static_cast<double>(sm) * ref_factor(ref, m);
+    }
+    if (e != 0u) atomicOr(&s_err, e);
+    const bool fin = (z > 0.0) && isfinite(z) && isfinite(m);
+    s_L[q] = fin ? static_cast<double>(m) + log2_fast(z) : NAN;
   }
   __syncthreads();
 
@@ -425,26 +439,8 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
       const uint64_t m = __ballot(mine);
       if (lane == 0) s_mask[wv] = m;
       const int64_t rowt = static_cast<int64_t>(b) * N1 + pos;
-      const int64_t rowd = static_cast<int64_t>(P.B) * N1 + rowt;
       const uint4* rt = reinterpret_cast<const uint4*>(tbase + rowt * row_bytes);
       const uint4* rd = reinterpret_cast<const uint4*>(dbase + (rowt)*row_bytes);
-      // a child's two logits at this position, loading while the normalisers are formed
-      float klt = 0.0f, kld = 0.0f;
-      if (mine) {
-        klt = load_elem<T>(rt, my_x);
-        kld = load_elem<T>(rd, my_x);
-      }
-      if (wv < 2) {
-        uint32_t e = 0u;
-        float M;
-        double Z;
-        row_norm_wave(P.rec + (wv == 0 ? rowt : rowd) * P.nrec, P.nrec, &M, &Z, &e);
-        if (lane == 0) {
-          s_M[wv] = M;
-          s_Zr[wv] = Z;
-        }
-        if (e != 0u) atomicOr(&s_err, e);
-      }
       __syncthreads();
       int nkids = 0, before = 0;
 #pragma unroll
@@ -453,23 +449,13 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
         if (w2 < wv) before += pc;
         nkids += pc;
       }
-      if (mine) {
-        const int i = before + __popcll(m & ((1ull << lane) - 1ull));
-        s_kids[i] = tid;
-        s_klt[i] = klt;
-        s_kld[i] = kld;
-        s_ku[i] = my_u;
-      }
+      if (mine) s_kids[before + __popcll(m & ((1ull << lane) - 1ull))] = tid;
       __syncthreads();
-      const float Mt = s_M[0], Md = s_M[1];
-      const double Zt = s_Zr[0], Zd = s_Zr[1];
-      if (s_err != 0u || !(Zt > 0.0) || !(Zd > 0.0) || !isfinite(Zt) || !isfinite(Zd) || !isfinite(Mt) ||
-          !isfinite(Md)) {
+      const double Lt = s_L[pos], Ld = s_L[N1 + pos];
+      if (s_err != 0u || !isfinite(Lt) || !isfinite(Ld)) {
         if (tid == 0) s_err |= SV_ERRF_NONFINITE;
         break;
       }
-      const double Lt = static_cast<double>(Mt) + log2_fast(Zt);
-      const double Ld = static_cast<double>(Md) + log2_fast(Zd);
       WalkRows w;
       w.c = c;
       split_neg(Lt, w.nlt_hi, w.nlt_lo);
@@ -477,15 +463,16 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
       int r = 0;
       bool taken = false, resid_totals = false;
       for (int i = 0; i < nkids; ++i) {
-        const double ap = static_cast<double>(s_klt[i]) * c64 - Lt;
-        const double aq = static_cast<double>(s_kld[i]) * c64 - Ld;
+        const int kid = s_kids[i];
+        const double ap = static_cast<double>(s_lt[kid]) * c64 - Lt;
+        const double aq = static_cast<double>(s_ld[kid]) * c64 - Ld;
         const double p = exp2_split(ap);
         const double q = exp2_split(aq);
         double val = p;
         for (int k = 0; k < r; ++k) val = fmax(val - q, 0.0) / s_Z[k];
         const double alpha = (val > 0.0) ? ((q > 0.0) ? fmin(1.0, val / q) : 1.0) : 0.0;
-        if (static_cast<double>(s_ku[i]) < alpha) {
-          node = s_kids[i];
+        if (static_cast<double>(s_u[kid]) < alpha) {
+          node = kid;
           pos = node + 1;
           if (tid == 0) s_path[depth] = node;
           ++depth;
@@ -520,7 +507,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
         __syncthreads();
       }
       if (taken) {
-        __syncthreads();  // s_kids, s_klt, ... are rewritten for the next node
+        __syncthreads();  // s_kids and s_mask are rewritten for the next node
         continue;
       }
       // no child accepted (or a leaf): draw from P_r at this position
