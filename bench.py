@@ -429,8 +429,8 @@ def main():
         config = {"workload": f"sample_r{R}_v{V}_{cfg.dtype}" + ("_graph" if args.graph else ""), "rows": R, "V": V,
                   "logits": cfg.dtype,
                   "from": cfg.name, "input_sets_rotated": len(sets)}
-        kernel_name = ("sample_rows_kernel (the whole call in one launch: every row once, a record per segment of "
-                       "up to 1024 vectors of a wave piece, then one segment per row again for the draw)")
+        kernel_name = ("sample_stream_kernel (one pass over the rows: a record per 256-vector segment; the draw "
+                       "is a second launch)")
     elif kind == "chain":
         cfg = CHAIN_CONFIGS[wl]
         B, K, V = cfg.B, cfg.K, cfg.V
