@@ -192,9 +192,25 @@ def test_repeat_is_bit_identical(sv):
     assert torch.equal(a["tokens"], b["tokens"]) and torch.equal(a["prob"], b["prob"])
 
 
+@pytest.mark.parametrize("dtype,V,R", [(torch.bfloat16, 8, 5000), (torch.bfloat16, 2048, 2049),
+                                       (torch.float32, 4, 3000), (torch.bfloat16, 12288, 700)])
+def test_many_short_rows(sv, dtype, V, R):
+    # units of the stream much shorter than a wave's share: waves cross rows
+    # (each row its own scale), take several units each, or none at all
+    # (more waves than units), and every group's counter still closes
+    _say("many short rows: R =", R, "V =", V, dtype, "Philox seed", 50 + V)
+    rng = np.random.Generator(np.random.Philox(50 + V))
+    logits = torch.from_numpy(rng.normal(0, 2.5, (R, V)).astype(np.float32)).to(dtype).cuda()
+    T = torch.from_numpy(rng.uniform(0.3, 1.5, R).astype(np.float32)).cuda()
+    u = torch.from_numpy(rng.random(R, dtype=np.float32)).cuda()
+    out = _run(sv, {"logits": logits, "temperature": T, "uniforms": u})
+    assert int(out["err_flags"].item()) == 0
+    _compare(out, logits, T, u)
+
+
 @pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 600000), (torch.float32, 300000)])
 def test_long_rows_reread_records(sv, dtype, V):
-    # more than 256 runs of 256 vectors per row: the draw re-reads its records
+    # more than 128 records (256-vector segments) per row: the draw re-reads its records
     _say("long rows: R = 5, V =", V, dtype, "Philox seed 34")
     rng = np.random.Generator(np.random.Philox(34))
     R = 5

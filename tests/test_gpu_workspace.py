@@ -108,6 +108,30 @@ def test_sampling_leaves_the_workspace_zero(sv):
             assert tok[bad] == -1 and np.all(np.delete(tok, bad) >= 0)
 
 
+def test_sampling_workspace_across_shapes(sv):
+    # one workspace, sized for the largest, serves draft-side sampling calls
+    # of very different unit counts back to back (the groups' counters and
+    # the records are all zero after each call)
+    shapes = [(5000, 8), (320, 12800), (3, 128256), (5000, 8)]
+    nbytes = max(sv.sv_sample_workspace_bytes(R, V, torch.bfloat16) for R, V in shapes)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    rng = np.random.Generator(np.random.Philox(409))
+    for R, V in shapes:
+        _say("sampling workspace across shapes: R =", R, "V =", V)
+        logits = torch.from_numpy(rng.normal(0, 2, (R, V)).astype(np.float32)).to(torch.bfloat16).cuda()
+        T = torch.full((R,), 0.8, device="cuda")
+        u = torch.from_numpy(rng.random(R, dtype=np.float32)).cuda()
+        out = sv.sv_sample_rows(logits, T, u, workspace_tensor=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero().item()) == 0, f"workspace dirty after R={R} V={V}"
+        assert int(out["err_flags"].item()) == 0
+        ref, _, lo, hi = oracle.sample_rows(logits.float().cpu().numpy(), T.cpu().numpy(), u.cpu().numpy())
+        uu = u.double().cpu().numpy()
+        near = (np.abs(uu - lo) < oracle.FLAG_WINDOW) | (np.abs(hi - uu) < oracle.FLAG_WINDOW)
+        tok = out["tokens"].cpu().numpy()
+        assert np.array_equal(tok[~near], ref[~near]), np.nonzero((tok != ref) & ~near)[0]
+
+
 def test_one_launch_call_leaves_the_workspace_zero(sv):
     # calls whose grid is larger than the device holds at once take the
     # one-launch kernel (ticket queues, chunk counters and arrival counters
