@@ -1,7 +1,7 @@
 """Throughput of speculative-sampling verification on one MI355X.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload c2]
-                    [--no-cpu-baseline] [--cpu-seconds 12]
+                    [--no-cpu-baseline] [--cpu-seconds 12] [--cpu-procs 16]
 
 Default workload (the headline line): one step = one sv_verify_chain call over
 one batch of B=64 sequences, K=5 drafted tokens, V=128256, bf16 logits,
@@ -22,7 +22,10 @@ whole call, the roofline of the dominant kernel (the streaming pass, timed
 with HIP events the library records around that one kernel) against MI355X's
 8 TB/s HBM peak, its HBM traffic from committed rocprofv3 counter runs (when
 the kernel sources still match the ones counted), and the CPU oracle timed on
-a bounded sample of the same workload.
+a bounded sample of the same workload: on one core (cpu_baseline), and for the
+chain workloads also in --cpu-procs worker processes at once (child processes
+of this script with the GPU hidden, each running the unchanged oracle on its
+own share of the sequences: cpu_baseline_multicore).
 """
 from __future__ import annotations
 
@@ -66,6 +69,11 @@ def parse():
     ap.add_argument("--entropy", action="store_true",
                     help="chain workloads: also request every position's entropy (the stream's entropy variant)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bound on the oracle sample's wall time")
+    ap.add_argument("--cpu-procs", type=int, default=16,
+                    help="chain workloads: worker processes for the multi-core oracle figure (0: none)")
+    # a worker of the multi-core oracle figure (started by this script itself)
+    ap.add_argument("--oracle-worker", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--worker-index", type=int, default=0, help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run three plain device-to-device copies of MIB MiB (untimed), the known-size "
                          "kernel that scales hardware traffic counters")
@@ -120,9 +128,8 @@ def _timed_oracle(jobs, budget_s: float):
     return int(done), wall, cpu
 
 
-def cpu_baseline_chain(inp, cfg, budget_s: float) -> dict:
-    """The float64 numpy oracle on the same workload: sequences four at a time,
-    in order, wrapping around the batch, for about `budget_s` seconds."""
+def _chain_oracle_jobs(inp, cfg, first: int = 0):
+    """Oracle jobs over the batch, four sequences each, starting at group `first`."""
     import oracle
 
     jobs = []
@@ -132,7 +139,14 @@ def cpu_baseline_chain(inp, cfg, budget_s: float) -> dict:
                                   inp["draft_tokens"][s].numpy().astype("int64"),
                                   inp["temperature"][s].double().numpy(), inp["uniforms"][s].double().numpy()),
                      oracle.verify_chain, s.stop - s.start))
-    done, wall, cpu = _timed_oracle(jobs, budget_s)
+    first %= len(jobs)
+    return jobs[first:] + jobs[:first]
+
+
+def cpu_baseline_chain(inp, cfg, budget_s: float) -> dict:
+    """The float64 numpy oracle on the same workload: sequences four at a time,
+    in order, wrapping around the batch, for about `budget_s` seconds."""
+    done, wall, cpu = _timed_oracle(_chain_oracle_jobs(inp, cfg), budget_s)
     return {
         "value": done * (2 * cfg.K + 1) * cfg.V / wall,
         "unit": "rows·vocab/s",
@@ -140,6 +154,48 @@ def cpu_baseline_chain(inp, cfg, budget_s: float) -> dict:
         "kind": "oracle",
         "sample": f"{done} sequences ({done / cfg.B:.2f} passes over the {cfg.B}-sequence batch) of the same "
                   f"workload, float64 numpy, {wall:.1f} s in the oracle, {cpu:.1f} s CPU",
+    }
+
+
+def oracle_worker(args) -> None:
+    """One process of the multi-core oracle figure: the workload's first input
+    set generated on the CPU, the oracle timed as in cpu_baseline_chain from
+    its own starting group of sequences; prints (sequences, wall, cpu)."""
+    from workloads import CHAIN_CONFIGS, chain_inputs
+
+    cfg = CHAIN_CONFIGS[args.workload]
+    inp = chain_inputs(cfg, device="cpu")
+    done, wall, cpu = _timed_oracle(_chain_oracle_jobs(inp, cfg, first=args.worker_index), args.cpu_seconds)
+    print(json.dumps({"done": done, "wall": wall, "cpu": cpu}), flush=True)
+
+
+def cpu_baseline_chain_procs(wl: str, cfg, budget_s: float, procs: int) -> dict:
+    """The oracle in `procs` worker processes at once (this script with
+    --oracle-worker, the GPU hidden from them), each for about `budget_s`
+    seconds of oracle time: the sum of their rates."""
+    import subprocess
+
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="", CUDA_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="",
+               OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    cmd = [sys.executable, os.path.abspath(__file__), "--oracle-worker", "--workload", wl,
+           "--cpu-seconds", str(budget_s)]
+    ps = [subprocess.Popen(cmd + ["--worker-index", str(i)], stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                           env=env, text=True) for i in range(procs)]
+    recs = []
+    for p in ps:
+        out, err = p.communicate(timeout=budget_s + 600)
+        if p.returncode != 0:
+            raise RuntimeError(f"oracle worker failed ({p.returncode}): {err[-2000:]}")
+        recs.append(json.loads(out.strip().splitlines()[-1]))
+    per_seq = (2 * cfg.K + 1) * cfg.V
+    done = sum(r["done"] for r in recs)
+    return {
+        "value": sum(r["done"] * per_seq / r["wall"] for r in recs),
+        "unit": "rows·vocab/s",
+        "cores": procs,
+        "kind": "oracle",
+        "sample": f"{procs} processes at once, each running the oracle on its own share of the same workload's "
+                  f"sequences for about {budget_s:.0f} s ({done} sequences in all, float64 numpy, one thread each)",
     }
 
 
@@ -362,6 +418,9 @@ def small_batch_latencies(sv, torch, cfg, dev, stream, batches=(1, 4, 16), n=200
 
 def main():
     args = parse()
+    if args.oracle_worker:  # a child of the multi-core oracle figure: CPU only
+        oracle_worker(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); specverify runs on one GPU and has no multi-GPU path.",
               file=sys.stderr)
@@ -605,6 +664,9 @@ def main():
         cpu_inp = {k: v.cpu() for k, v in sets[0].items()}
         if kind == "chain":
             result["cpu_baseline"] = cpu_baseline_chain(cpu_inp, cfg, args.cpu_seconds)
+            if args.cpu_procs > 0:
+                result["cpu_baseline_multicore"] = cpu_baseline_chain_procs(wl, cfg, args.cpu_seconds,
+                                                                            args.cpu_procs)
         elif kind == "sample":
             result["cpu_baseline"] = cpu_baseline_sample(cpu_inp, cfg, args.cpu_seconds)
         elif kind == "treesample":
