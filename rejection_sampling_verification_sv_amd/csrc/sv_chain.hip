@@ -309,6 +309,29 @@ __device__ __forceinline__ uint32_t wave_or_err(uint32_t v) {
   return r;
 }
 
+// One step of a reduction over aligned groups of 2o lanes (o a power of
+// two), after which every lane of each half of a group holds the same value:
+// the value of a lane in the other half. DPP moves within a row of 16 lanes
+// (quad permutes, then the half-row and row mirrors), an LDS permute beyond.
+__device__ __forceinline__ float other_half(float v, int o) {
+  switch (o) {
+    case 1: return dpp_move<0xb1>(v);
+    case 2: return dpp_move<0x4e>(v);
+    case 4: return dpp_move<0x141>(v);
+    case 8: return dpp_move<0x140>(v);
+    default: return __shfl_xor(v, o, kWave);
+  }
+}
+__device__ __forceinline__ double other_half(double v, int o) {
+  switch (o) {
+    case 1: return dpp_f64<0xb1>(v);
+    case 2: return dpp_f64<0x4e>(v);
+    case 4: return dpp_f64<0x141>(v);
+    case 8: return dpp_f64<0x140>(v);
+    default: return __shfl_xor(v, o, kWave);
+  }
+}
+
 // The decision of sequence b once its rows' log-normalisers are in s_L
 // (wave 0; lane k < K holds drafted token k, its uniform and the two
 // gathered logits): p_k(x_k), q_k(x_k) in fp64, alpha_k = min(1, p/q),
@@ -318,7 +341,7 @@ __device__ __forceinline__ uint32_t wave_or_err(uint32_t v) {
 template <class T>
 __device__ __forceinline__ void decide_tail(const ChainParams& P, int b, SeqPlan* s_plan, bool writer,
                                             const double* s_L, int x, float u, uint64_t vt, uint64_t vd,
-                                            uint32_t err, float Tv) {
+                                            uint32_t err, float Tv, Scale c) {
   const int K = P.K;
   const int lane = lane_id();
   // s_L is written by the group leaders and read by other lanes of this wave.
@@ -336,7 +359,6 @@ __device__ __forceinline__ void decide_tail(const ChainParams& P, int b, SeqPlan
       ld = untag_float(vd);
     }
   }
-  const Scale c = exponent_scale(Tv);
   if (!(Tv > 0.0f) || !isfinite(Tv)) err |= SV_ERRF_TEMPERATURE;
   const double c64 = static_cast<double>(c.hi) + static_cast<double>(c.lo);
   bool reject = false;
@@ -468,15 +490,15 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
       }
     }
     float M = mf;
-    for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+    for (int o = 1; o < G; o <<= 1) M = fmaxf(M, other_half(M, o));
     const double dl = static_cast<double>(M) - static_cast<double>(mf);
     const double fl = (mf == -INFINITY) ? 0.0 : ref_factor(mf, M);
     double zl = zf * fl;
-    for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
+    for (int o = 1; o < G; o <<= 1) zl += other_half(zl, o);
     double al = 0.0;
     if constexpr (ent) {
       al = (mf == -INFINITY) ? 0.0 : fl * (af - dl * zf);
-      for (int o = 1; o < G; o <<= 1) al += __shfl_xor(al, o, kWave);
+      for (int o = 1; o < G; o <<= 1) al += other_half(al, o);
     }
     if (row_ok && gl == 0) {
       const bool fin = (zl > 0.0) && isfinite(zl) && isfinite(M);
@@ -489,7 +511,7 @@ __device__ void decide_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool w
             (fin && Tv > 0.0f && isfinite(Tv)) ? static_cast<float>(0.6931471805599453 * (lz - al / zl)) : NAN;
     }
   }
-  decide_tail<T>(P, b, s_plan, writer, s_L, x, u, vt, vd, err, Tv);
+  decide_tail<T>(P, b, s_plan, writer, s_L, x, u, vt, vd, err, Tv, exponent_scale(Tv));
 }
 
 // Lanes per row of the decision's statistics combine: the largest power of
@@ -511,8 +533,36 @@ __device__ __forceinline__ int decision_lanes(int R, int pmax) {
 // Every slot is read with an agent-scope load, all issued together; a slot
 // still zero (its store not visible yet) makes the wave return false before
 // anything is written, for the caller to read again.
+// The inputs of sequence b's decision that do not come from the statistics
+// (wave 0; lane k < K gets drafted token k and its uniform): loaded, and the
+// temperature's scale formed, once before the statistics are polled.
+struct DecideIn {
+  int x;
+  float u;
+  float Tv;
+  Scale c;
+};
+
+__device__ __forceinline__ DecideIn decide_inputs(const ChainParams& P, int b) {
+  DecideIn in;
+  in.Tv = temperature_of(P.temperature, b);
+  in.x = -1;
+  in.u = 0.0f;
+  const int K = P.K;
+  if (K > 0) {  // every lane loads (lanes past K repeat lane K - 1's values and drop them)
+    const int lane = lane_id();
+    const int k = min(lane, K - 1);
+    in.x = P.tokens[static_cast<int64_t>(b) * K + k];
+    in.u = P.uniforms[static_cast<int64_t>(b) * (K + 1) + k];
+    if (lane >= K) in.x = -1;
+  }
+  in.c = exponent_scale(in.Tv);
+  return in;
+}
+
 template <class T, bool kEnt = false>
-__device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
+__device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, SeqPlan* s_plan, bool writer,
+                                                 const DecideIn& in) {
   __shared__ double s_L[2 * SV_MAX_K + 1];
   const int K = P.K;
   const int R = 2 * K + 1;
@@ -544,17 +594,13 @@ __device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, Se
     rs[i] = peek(&P.part_s[sl]);
     ra[i] = kEnt ? peek(&P.part_a[sl]) : 0ull;
   }
-  const float Tv = temperature_of(P.temperature, b);
-  int x = -1;
-  float u = 0.0f;
+  const float Tv = in.Tv;
+  const int x = in.x;
   uint64_t vt = 0ull, vd = 0ull;
-  if (K > 0) {  // every lane loads (lanes past K repeat lane K - 1's values and drop them)
+  if (K > 0) {
     const int k = min(lane, K - 1);
-    x = P.tokens[static_cast<int64_t>(b) * K + k];
-    u = P.uniforms[static_cast<int64_t>(b) * (K + 1) + k];
     vt = peek(&P.gat[static_cast<int64_t>(b) * R + k]);
     vd = peek(&P.gat[static_cast<int64_t>(b) * R + K + 1 + k]);
-    if (lane >= K) x = -1;
   }
   bool missing = lane < K && x >= 0 && x < P.V && (vt == 0ull || vd == 0ull);
 #pragma unroll
@@ -586,15 +632,15 @@ __device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, Se
     }
   }
   float M = mf;
-  for (int o = 1; o < G; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
+  for (int o = 1; o < G; o <<= 1) M = fmaxf(M, other_half(M, o));
   const double dl = static_cast<double>(M) - static_cast<double>(mf);
   const double fl = (mf == -INFINITY) ? 0.0 : ref_factor(mf, M);
   double zl = zf * fl;
-  for (int o = 1; o < G; o <<= 1) zl += __shfl_xor(zl, o, kWave);
+  for (int o = 1; o < G; o <<= 1) zl += other_half(zl, o);
   double al = 0.0;
   if constexpr (kEnt) {
     al = (mf == -INFINITY) ? 0.0 : fl * (af - dl * zf);
-    for (int o = 1; o < G; o <<= 1) al += __shfl_xor(al, o, kWave);
+    for (int o = 1; o < G; o <<= 1) al += other_half(al, o);
   }
   if (row_ok && gl == 0) {
     const bool fin = (zl > 0.0) && isfinite(zl) && isfinite(M);
@@ -606,7 +652,7 @@ __device__ __forceinline__ bool decide_live_wave(const ChainParams& P, int b, Se
       P.entropy[static_cast<int64_t>(b) * R + r] =
           (fin && Tv > 0.0f && isfinite(Tv)) ? static_cast<float>(0.6931471805599453 * (lz - al / zl)) : NAN;
   }
-  decide_tail<T>(P, b, s_plan, writer, s_L, x, u, vt, vd, err, Tv);
+  decide_tail<T>(P, b, s_plan, writer, s_L, x, in.u, vt, vd, err, Tv, in.c);
   return true;
 }
 
@@ -621,6 +667,7 @@ template <class T, bool kEnt = false>
 __device__ bool decide_live(const ChainParams& P, int b, SeqPlan* s_plan, bool writer) {
   const uint32_t need = static_cast<uint32_t>(P.L.cps);
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  const DecideIn in = decide_inputs(P, b);
   uint32_t* done = P.done + static_cast<int64_t>(b) * kCtrStride;
   while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
     if (peek(P.abort) != 0ull) return false;
@@ -630,7 +677,7 @@ __device__ bool decide_live(const ChainParams& P, int b, SeqPlan* s_plan, bool w
     }
     __builtin_amdgcn_s_sleep(SV_POLL_SLEEP);
   }
-  while (!decide_live_wave<T, kEnt>(P, b, s_plan, writer)) {
+  while (!decide_live_wave<T, kEnt>(P, b, s_plan, writer, in)) {
     if (peek(P.abort) != 0ull) return false;
     if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
       publish(P.abort, 1ull);
@@ -770,11 +817,23 @@ __device__ int draw_in_tile(const SampleRows& Sr, int tile, double target, int V
 }
 
 // The rescan of draw_in_tile on weights already formed (w, and x their
-// running sum, as tile_compute returns them).
+// running sum, as tile_compute returns them). Each thread's exclusive prefix
+// within the tile is the fp64 DPP scan of its wave plus the totals of the
+// waves before it (one barrier); each wave's first crossing and last
+// positive weight come from two ballots, and a second barrier lets every
+// thread take the block's: the lowest crossing index, else the last
+// positive weight. s_scan holds kWaves values and s_redi 2 kWaves; a caller
+// that uses them again afterwards needs a barrier first.
 __device__ int draw_in_weights(int tile, const float (&w)[kSampleEPT], float x, double target, double* s_scan,
                                int* s_redi) {
-  double tot;
-  const double excl = block_exclusive_scan(static_cast<double>(x), s_scan, &tot);
+  const int lane = lane_id();
+  const int wv = wave_id();
+  const double inc = wave_scan_dpp(static_cast<double>(x));
+  if (lane == kWave - 1) s_scan[wv] = inc;
+  __syncthreads();
+  double wave_prefix = 0.0;
+  for (int k = 0; k < wv; ++k) wave_prefix += s_scan[k];
+  const double excl = wave_prefix + wave_exclusive_from(inc);
   int first = INT_MAX;
   int lastpos = -1;
   float run = 0.0f;
@@ -787,9 +846,24 @@ __device__ int draw_in_weights(int tile, const float (&w)[kSampleEPT], float x, 
       lastpos = idx;
     }
   }
-  // lowest crossing index in the tile, else the last positive weight
-  const int first_all = -block_max_int(first == INT_MAX ? INT_MIN + 1 : -first, s_redi);
-  const int last_all = block_max_int(lastpos, s_redi);
+  // indices grow with the lane and the wave: the wave's lowest crossing is
+  // its lowest lane's, its last positive weight its highest lane's
+  const uint64_t fb = __ballot(first != INT_MAX);
+  const uint64_t lb = __ballot(lastpos >= 0);
+  const int wf = (fb != 0ull) ? __builtin_amdgcn_readlane(first, __ffsll(static_cast<unsigned long long>(fb)) - 1)
+                              : INT_MAX;
+  const int wl = (lb != 0ull) ? __builtin_amdgcn_readlane(lastpos, 63 - __clzll(static_cast<long long>(lb))) : -1;
+  if (lane == 0) {
+    s_redi[wv] = wf;
+    s_redi[kWaves + wv] = wl;
+  }
+  __syncthreads();
+  int first_all = INT_MAX, last_all = -1;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    first_all = min(first_all, s_redi[k]);
+    last_all = max(last_all, s_redi[kWaves + k]);
+  }
   const int e = (first_all >= 0 && first_all < kSampleTile) ? first_all : last_all;
   return (e >= 0) ? static_cast<int>(static_cast<int64_t>(tile) * kSampleTile + e) : -1;
 }
@@ -801,8 +875,10 @@ __device__ int draw_in_weights(int tile, const float (&w)[kSampleEPT], float x, 
 // inclusive scan; more tiles are scanned in rounds of 64, twice (total
 // first, then the search). No tile crossing the target (rounding at the top
 // end): the last tile with weight, target +inf; none with weight: tile -1.
+// pre: with up to 64 tiles, lane t's slot as the caller already read it
+// (0: not read, or not visible then; read again here).
 __device__ void locate_tile(const ChainParams& P, int b, double* s_S, int* s_tile, double* s_target,
-                            uint32_t* s_err) {
+                            uint32_t* s_err, uint64_t pre = 0ull) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   uint64_t* ts = P.tile_sum + static_cast<int64_t>(b) * P.ntiles;
@@ -812,28 +888,28 @@ __device__ void locate_tile(const ChainParams& P, int b, double* s_S, int* s_til
     double total, target, prefix = 0.0;
     int found = -1, last_pos = -1;
     if (P.ntiles <= kWave) {
-      const double v = (lane < P.ntiles) ? untag_nonneg_double(await_slot(&ts[lane], &err, P.abort)) : 0.0;
-      const double inc = wave_inclusive_scan(v);
-      double excl = __shfl_up(inc, 1, kWave);
-      if (lane == 0) excl = 0.0;
+      const double v =
+          (lane < P.ntiles) ? untag_nonneg_double(pre != 0ull ? pre : await_slot(&ts[lane], &err, P.abort)) : 0.0;
+      const double inc = wave_scan_dpp(v);
+      const double excl = wave_exclusive_from(inc);
       const uint64_t pos = __ballot(lane < P.ntiles && v > 0.0);
       if (pos != 0ull) last_pos = 63 - __clzll(static_cast<long long>(pos));
-      total = __shfl(inc, kWave - 1, kWave);
+      total = readlane_f64(inc, kWave - 1);
       target = u * total;
       const uint64_t hit = __ballot(lane < P.ntiles && v > 0.0 && inc > target);
       if (hit != 0ull) {
         found = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-        prefix = __shfl(excl, found, kWave);
+        prefix = readlane_f64(excl, found);
       }
     } else {
       double carry = 0.0;
       for (int base = 0; base < P.ntiles; base += kWave) {
         const int t = base + lane;
         const double v = (t < P.ntiles) ? untag_nonneg_double(await_slot(&ts[t], &err, P.abort)) : 0.0;
-        const double inc = wave_inclusive_scan(v);
+        const double inc = wave_scan_dpp(v);
         const uint64_t pos = __ballot(t < P.ntiles && v > 0.0);
         if (pos != 0ull) last_pos = base + 63 - __clzll(static_cast<long long>(pos));
-        carry += __shfl(inc, kWave - 1, kWave);
+        carry += readlane_f64(inc, kWave - 1);
       }
       total = carry;
       target = u * total;
@@ -841,16 +917,15 @@ __device__ void locate_tile(const ChainParams& P, int b, double* s_S, int* s_til
       for (int base = 0; base < P.ntiles && found < 0; base += kWave) {
         const int t = base + lane;
         const double v = (t < P.ntiles) ? untag_nonneg_double(peek(&ts[t])) : 0.0;  // seen above
-        const double inc = wave_inclusive_scan(v);
-        double excl = __shfl_up(inc, 1, kWave);
-        if (lane == 0) excl = 0.0;
+        const double inc = wave_scan_dpp(v);
+        const double excl = wave_exclusive_from(inc);
         const uint64_t hit = __ballot(t < P.ntiles && v > 0.0 && carry + inc > target);
         if (hit != 0ull) {
           const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
           found = base + l;
-          prefix = carry + __shfl(excl, l, kWave);
+          prefix = carry + readlane_f64(excl, l);
         }
-        carry += __shfl(inc, kWave - 1, kWave);
+        carry += readlane_f64(inc, kWave - 1);
       }
     }
     if (err != 0u) atomicOr(s_err, err);
@@ -868,11 +943,12 @@ __device__ void locate_tile(const ChainParams& P, int b, double* s_S, int* s_til
 }
 
 // Draw the token: called by the last resolving workgroup of sequence b, once
-// every workgroup of the sequence has published its tile totals.
+// every workgroup of the sequence has published its tile totals (pre: as
+// locate_tile takes it).
 template <class T>
-__device__ __forceinline__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl) {
+__device__ __forceinline__ void chain_draw(const ChainParams& P, int b, const SeqPlan& pl, uint64_t pre = 0ull) {
   __shared__ double s_scan[kWaves];
-  __shared__ int s_redi[kWaves];
+  __shared__ int s_redi[2 * kWaves];
   __shared__ double s_S, s_target;
   __shared__ int s_tile;
   __shared__ uint32_t s_err;
@@ -881,7 +957,7 @@ __device__ __forceinline__ void chain_draw(const ChainParams& P, int b, const Se
   if (tid == 0) s_err = 0u;
   __syncthreads();
 
-  locate_tile(P, b, &s_S, &s_tile, &s_target, &s_err);
+  locate_tile(P, b, &s_S, &s_tile, &s_target, &s_err, pre);
   __syncthreads();
   const double S_res = s_S;
   bool p_only = false;
@@ -968,7 +1044,7 @@ __device__ __forceinline__ void tile_totals(const ChainParams& P, int b, const S
       float w[kSampleEPT];
       float x = 0.0f;
       if (t0 + i < t_end) x = tile_compute<T>(S, rt[i], rd[kDraft ? i : 0], w);
-      const double part = (t0 + i < t_end) ? wave_sum(static_cast<double>(x)) : 0.0;
+      const double part = (t0 + i < t_end) ? wave_sum_f64_dpp(static_cast<double>(x)) : 0.0;
       if (lane_id() == 0) s_red[i][wave_id()] = part;
       if constexpr (kKeep) {
 #pragma unroll
@@ -996,8 +1072,14 @@ template <class T, bool kEnt, bool kSmall = false>
 __device__ void sample_finish(const ChainParams& P, int b, const SeqPlan& pl, uint32_t* cnt, uint32_t total,
                               uint32_t* also, bool draw = true) {
   __shared__ int s_flag;
+  // Wave 0 reads the sequence's tile totals beside the arrival count, so
+  // that the last to arrive starts its draw without another round trip
+  // (a slot read as zero here is read again by locate_tile).
+  uint64_t pre = 0ull;
+  if (draw && pl.j >= 0 && P.ntiles <= kWave && wave_id() == 0)
+    pre = peek(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + (lane_id() < P.ntiles ? lane_id() : 0)]);
   if (!arrive_and_check_last(cnt, total, &s_flag)) return;
-  if (draw && pl.j >= 0) chain_draw<T>(P, b, pl);
+  if (draw && pl.j >= 0) chain_draw<T>(P, b, pl, pre);
   // Every workgroup of the sequence has read the statistics pieces and
   // published its totals: leave the sequence's workspace all zero.
   __syncthreads();
@@ -1106,8 +1188,9 @@ __device__ __forceinline__ bool read_plan(const ChainParams& P, int b, SeqPlan* 
 template <class T>
 __device__ void small_decide(const ChainParams& P, int b, SeqPlan* s_plan) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  const DecideIn in = decide_inputs(P, b);
   bool ok = true;
-  while (!decide_live_wave<T>(P, b, s_plan, true)) {
+  while (!decide_live_wave<T>(P, b, s_plan, true, in)) {
     if (peek(P.abort) != 0ull || __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
       if (peek(P.abort) == 0ull) publish(P.abort, 1ull);
       ok = false;
@@ -1157,7 +1240,7 @@ template <class T, int TPB>
 __device__ __forceinline__ void small_owner_draw(const ChainParams& P, int b, const SeqPlan& pl, int t_begin, int t_end,
                                  const float (&keep)[TPB][kSampleEPT], const float (&keepx)[TPB]) {
   __shared__ double s_scan[kWaves];
-  __shared__ int s_redi[kWaves];
+  __shared__ int s_redi[2 * kWaves];
   __shared__ double s_S, s_target;
   __shared__ int s_tile;
   __shared__ uint32_t s_err;

@@ -79,37 +79,6 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
   return v;
 }
 
-// fp64 lane moves through DPP (both 32-bit halves with the same control;
-// lanes the control leaves without a source read 0).
-template <int kCtrl, int kRowMask = 0xf>
-__device__ __forceinline__ double dpp_f64(double v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), kCtrl, kRowMask, 0xf, true);
-  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), kCtrl, kRowMask, 0xf, true);
-  return __hiloint2double(hi, lo);
-}
-__device__ __forceinline__ double readlane_f64(double v, int lane) {
-  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
-                          __builtin_amdgcn_readlane(__double2loint(v), lane));
-}
-__device__ __forceinline__ float readlane_f32(float v, int lane) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-// Inclusive fp64 prefix sum over the wave in lane order: steps of 1, 2, 4
-// and 8 lanes within each row of 16, then each row adds the totals of the
-// rows before it (row_bcast 15 and 31). DPP moves instead of LDS permutes.
-__device__ __forceinline__ double wave_scan_dpp(double v) {
-  v += dpp_f64<0x111>(v);        // row_shr:1
-  v += dpp_f64<0x112>(v);        // row_shr:2
-  v += dpp_f64<0x114>(v);        // row_shr:4
-  v += dpp_f64<0x118>(v);        // row_shr:8
-  v += dpp_f64<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
-  v += dpp_f64<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
-  return v;
-}
-// The exclusive prefix from the inclusive one: the previous lane's value
-// (wave_shr:1; lane 0 reads 0).
-__device__ __forceinline__ double wave_exclusive_from(double inc) { return dpp_f64<0x138>(inc); }
 
 // Pass 2 for row r (one wave). The records were stored by the previous
 // launch on the same stream: plain loads; a record still zero was never
