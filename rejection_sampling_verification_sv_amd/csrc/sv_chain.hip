@@ -669,14 +669,21 @@ __device__ bool decide_live(const ChainParams& P, int b, SeqPlan* s_plan, bool w
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   const DecideIn in = decide_inputs(P, b);
   uint32_t* done = P.done + static_cast<int64_t>(b) * kCtrStride;
-  while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+  // Once at most SV_EAGER_CHUNKS chunks are uncounted, the slots themselves
+  // are read on every poll: the decision goes ahead as soon as every slot is
+  // visible, whether or not the last counts have landed (the workgroup that
+  // returns the counter to zero waits for them, see sample_finish).
+  uint32_t d = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (d + static_cast<uint32_t>(SV_EAGER_CHUNKS) < need) {
     if (peek(P.abort) != 0ull) return false;
     if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
       publish(P.abort, 1ull);
       return false;
     }
     __builtin_amdgcn_s_sleep(SV_POLL_SLEEP);
+    d = __hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  if (SV_TAIL_PRIO > 0) __builtin_amdgcn_s_setprio(SV_TAIL_PRIO);
   while (!decide_live_wave<T, kEnt>(P, b, s_plan, writer, in)) {
     if (peek(P.abort) != 0ull) return false;
     if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
@@ -1070,7 +1077,7 @@ __device__ __forceinline__ void tile_totals(const ChainParams& P, int b, const S
 // to zero, and the counters `cnt` and `also` (if any) to zero.
 template <class T, bool kEnt, bool kSmall = false>
 __device__ void sample_finish(const ChainParams& P, int b, const SeqPlan& pl, uint32_t* cnt, uint32_t total,
-                              uint32_t* also, bool draw = true) {
+                              uint32_t* also, bool draw = true, uint32_t also_total = 0u) {
   __shared__ int s_flag;
   // Wave 0 reads the sequence's tile totals beside the arrival count, so
   // that the last to arrive starts its draw without another round trip
@@ -1097,7 +1104,23 @@ __device__ void sample_finish(const ChainParams& P, int b, const SeqPlan& pl, ui
   if constexpr (kSmall)
     for (int w = threadIdx.x; w < kPlanWords; w += kThreads) clear_slot(&P.plan[static_cast<int64_t>(b) * kPlanStride + w]);
   reset_counter(cnt);
-  if (also != nullptr) reset_counter(also);
+  if (also != nullptr) {
+    // every count into `also` is issued by a running workgroup whose slots
+    // were all read: wait for the last ones to land before the reset
+    // (bounded; on expiry the reset is skipped and SV_ERRF_INTERNAL raised)
+    if (threadIdx.x == 0 && also_total > 0u) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(also, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < also_total) {
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+          raise_error(P.err_flags, kErrInternal);
+          publish(P.abort, 1ull);
+          return;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    reset_counter(also);
+  }
 }
 
 // Sampling workgroup g of sequence b: its wave 0 makes the sequence's
@@ -1130,6 +1153,8 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
     }
   }
   __syncthreads();
+  if (kLive && SV_TAIL_PRIO > 0 && (SV_TAIL_PRIO_ALL || b >= P.B - SV_LATE_PRIO_SEQS))
+    __builtin_amdgcn_s_setprio(SV_TAIL_PRIO);
   const SeqPlan pl = s_plan;
   if (pl.j >= 0) {  // an invalid row has nothing to draw: its outputs are -1
     const int t_begin = blk * P.tiles_per_block;
@@ -1137,7 +1162,8 @@ __device__ void sample_seq(const ChainParams& P, int b, int blk) {
   }
   uint32_t* cnt = P.cnt + static_cast<int64_t>(b) * (kLive ? kCtrStride : 1);
   sample_finish<T, kEnt>(P, b, pl, cnt, static_cast<uint32_t>(P.nblk_b),
-                         kLive ? P.done + static_cast<int64_t>(b) * kCtrStride : nullptr);
+                         kLive ? P.done + static_cast<int64_t>(b) * kCtrStride : nullptr, true,
+                         kLive ? static_cast<uint32_t>(P.L.cps) : 0u);
 }
 
 // ---------------------------------------------------------------- small calls
@@ -1385,14 +1411,14 @@ __device__ __forceinline__ void one_launch_item(const ChainParams& P) {
   if (t < cps) {
     stats_chunk<T, kStatsTPB, kEnt>(P, static_cast<int>(b), static_cast<int>(t));
     if (threadIdx.x == 0) {
-      // count the chunk once this thread's slot stores have completed (the
-      // readers still check every slot's tag and read again if it is zero)
-      __builtin_amdgcn_s_waitcnt(0);
+      // count the chunk; its slot stores may still be on their way (the
+      // readers check every slot's tag and read again while one is zero)
+      if (SV_COUNT_WAIT) __builtin_amdgcn_s_waitcnt(0);
       __hip_atomic_fetch_add(P.done + static_cast<int64_t>(b) * kCtrStride, 1u, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
-    if (SV_SAMPLE_PRIO > 0) __builtin_amdgcn_s_setprio(SV_SAMPLE_PRIO);
+    if (SV_SAMPLE_PRIO > 0) __builtin_amdgcn_s_setprio(SV_SAMPLE_PRIO);  // (not used: 0)
     sample_seq<T, live_tiles<T>(), true, kEnt, true>(P, static_cast<int>(b), static_cast<int>(t - cps));
   }
 }

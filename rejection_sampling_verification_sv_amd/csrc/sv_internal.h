@@ -364,6 +364,37 @@ constexpr int kCtrStride = SV_CTR_STRIDE;
 #ifndef SV_SAMPLE_PRIO
 #define SV_SAMPLE_PRIO 0
 #endif
+// Wave priority (0-3) of wave 0 of a one-launch sampling role once its
+// sequence's statistics are all counted (the decision, then the rest of the
+// role; SV_TAIL_PRIO_ALL raises the role's other waves too), and whether a
+// statistics role waits for its slot stores before counting its chunk (1)
+// or counts at once (0; the readers retry while a slot is zero). On B=64
+// K=5 V=128256 bf16, priority 1 or 3 took the call from 48.6-48.8 us to
+// 47.4-47.6 us; raising all four waves, or 8 waves/SIMD, was slower
+// (48.6-49.1 us), and so was the large call B=256 K=8 V=152064 with all four
+// raised (240 us against 234 us).
+#ifndef SV_TAIL_PRIO
+#define SV_TAIL_PRIO 3
+#endif
+#ifndef SV_COUNT_WAIT
+#define SV_COUNT_WAIT 0
+#endif
+#ifndef SV_TAIL_PRIO_ALL
+#define SV_TAIL_PRIO_ALL 0
+#endif
+// The last SV_LATE_PRIO_SEQS sequences (the last streamed) raise all the
+// waves of their sampling roles, and a sampling role reads the statistics
+// slots directly once at most SV_EAGER_CHUNKS chunks of its sequence are
+// uncounted. On B=64 K=5 V=128256 bf16: 47.8-48.0 us per call with neither,
+// 47.2-47.6 us with 2 eager chunks (1, 3 and 4 within 0.3 us of it), kernel
+// 43.9 us against 44.2-44.3 us with the last 8 sequences raised as well (16:
+// 44.5-45.0 us).
+#ifndef SV_LATE_PRIO_SEQS
+#define SV_LATE_PRIO_SEQS 8
+#endif
+#ifndef SV_EAGER_CHUNKS
+#define SV_EAGER_CHUNKS 2
+#endif
 // Block order of the one-launch grid: the sampling blocks of sequence b
 // follow the statistics blocks of sequence b + lag (the last lag sequences'
 // sampling blocks close the grid), so that with in-order dispatch they start
