@@ -1086,12 +1086,10 @@ __device__ void sample_finish(const ChainParams& P, int b, const SeqPlan& pl, ui
   if (draw && pl.j >= 0 && P.ntiles <= kWave && wave_id() == 0)
     pre = peek(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + (lane_id() < P.ntiles ? lane_id() : 0)]);
   if (!arrive_and_check_last(cnt, total, &s_flag)) return;
-  if (draw && pl.j >= 0) chain_draw<T>(P, b, pl, pre);
   // Every workgroup of the sequence has read the statistics pieces and
-  // published its totals: leave the sequence's workspace all zero.
-  __syncthreads();
-  if (kSmall || pl.j >= 0)  // (a small call's last workgroup may not have read the plan)
-    for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
+  // published its totals: leave the sequence's workspace all zero, the
+  // pieces and gathered logits at once (the draw reads neither), the tile
+  // totals once the draw has read them.
   const int64_t per_seq = slots_per_seq(P.L);
   for (int64_t sl = static_cast<int64_t>(b) * per_seq + threadIdx.x; sl < (static_cast<int64_t>(b) + 1) * per_seq;
        sl += kThreads) {
@@ -1101,6 +1099,10 @@ __device__ void sample_finish(const ChainParams& P, int b, const SeqPlan& pl, ui
   }
   const int R = 2 * P.K + 1;
   for (int r = threadIdx.x; r < R; r += kThreads) P.gat[static_cast<int64_t>(b) * R + r] = 0ull;
+  if (draw && pl.j >= 0) chain_draw<T>(P, b, pl, pre);
+  __syncthreads();
+  if (kSmall || pl.j >= 0)  // (a small call's last workgroup may not have read the plan)
+    for (int t = threadIdx.x; t < P.ntiles; t += kThreads) clear_slot(&P.tile_sum[static_cast<int64_t>(b) * P.ntiles + t]);
   if constexpr (kSmall)
     for (int w = threadIdx.x; w < kPlanWords; w += kThreads) clear_slot(&P.plan[static_cast<int64_t>(b) * kPlanStride + w]);
   reset_counter(cnt);

@@ -117,10 +117,16 @@ __device__ __forceinline__ float walk_run_sum(const uint4 (&at)[kRunLaneVecs], c
 // One pass of the workgroup over runs [lo, hi) of the row pair: s_run[g] =
 // the fp32 total of the weights of run g (wave w takes runs lo + w,
 // lo + w + 16, ..., the next run's loads in flight while the current one is
-// reduced). No barrier.
+// reduced), and with pub, the same total published for the sequence's other
+// workgroups as walk_exchange reads it (tagged with the pass number). No
+// barrier.
+__device__ __forceinline__ uint64_t pass_word(uint32_t pass, float s) {
+  return (static_cast<uint64_t>(pass) << 32) | static_cast<uint64_t>(__float_as_uint(s));
+}
+
 template <class T, bool kResid, int R>
 __device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int lo, int hi, const WalkRows& w, int r,
-                            const float* invZ, double* s_run) {
+                            const float* invZ, double* s_run, uint64_t* pub, uint32_t pass) {
   const int g0 = lo + wave_id();
   if (g0 >= hi) return;
   float iz[kWalkHoist];
@@ -138,7 +144,10 @@ __device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int 
       walk_load<T>(rd, gn, nvec, bd);
     }
     const float s = wave_sum_dpp(walk_run_sum<T, kResid, R>(at, ad, w, r, invZ, iz));
-    if (lane_id() == 0) s_run[g] = static_cast<double>(s);
+    if (lane_id() == 0) {
+      s_run[g] = static_cast<double>(s);
+      if (pub != nullptr) publish(&pub[g], pass_word(pass, s));
+    }
     if (gn >= hi) break;
     g = gn;
 #pragma unroll
@@ -153,14 +162,14 @@ __device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int 
 // factors in registers, more with the factors read from LDS.
 template <class T, bool kResid>
 __device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int lo, int hi, const WalkRows& w, int r,
-                          const float* invZ, double* s_run) {
+                          const float* invZ, double* s_run, uint64_t* pub, uint32_t pass) {
   static_assert(kWalkHoist == 3, "one case per hoisted count");
   switch (r) {
-    case 0: walk_pass_r<T, kResid, 0>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
-    case 1: walk_pass_r<T, kResid, 1>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
-    case 2: walk_pass_r<T, kResid, 2>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
-    case 3: walk_pass_r<T, kResid, 3>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
-    default: walk_pass_r<T, kResid, -1>(rt, rd, nvec, lo, hi, w, r, invZ, s_run); break;
+    case 0: walk_pass_r<T, kResid, 0>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
+    case 1: walk_pass_r<T, kResid, 1>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
+    case 2: walk_pass_r<T, kResid, 2>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
+    case 3: walk_pass_r<T, kResid, 3>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
+    default: walk_pass_r<T, kResid, -1>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
   }
 }
 
@@ -184,20 +193,23 @@ __device__ __forceinline__ uint64_t await_pass(uint64_t* slot, uint32_t pass, ui
   return 0ull;
 }
 
-// Exchange of one pass among the G workgroups of a sequence (after a
-// barrier of the workgroup): this workgroup's run totals [lo, hi) go out
-// tagged with the pass number (never 0), and the others' are read back
-// into s_run, so every workgroup then holds the totals of all runs, the
-// same values as one workgroup computing them all. Pass k uses buffer k % 2:
-// a workgroup publishes pass k + 2 only after it has read every
-// workgroup's pass k + 1, which each wrote after reading pass k.
+// The exchange slots of pass `pass` of sequence b (pass k uses buffer
+// k % 2).
+__device__ __forceinline__ uint64_t* pass_slots(const TreeSampleParams& P, int b, uint32_t pass) {
+  return P.slots + (static_cast<int64_t>(b) * 2 + (pass & 1u)) * P.nrun;
+}
+
+// Exchange of one pass among the G workgroups of a sequence: each
+// workgroup's run totals [lo, hi) went out tagged with the pass number
+// (never 0) as its pass formed them; the others' are read back into s_run,
+// so every workgroup then holds the totals of all runs, the same values as
+// one workgroup computing them all. A workgroup publishes pass k + 2 (into
+// the buffer of pass k) only after it has read every workgroup's pass
+// k + 1, which each published after reading pass k.
 __device__ void walk_exchange(const TreeSampleParams& P, int b, uint32_t pass, int lo, int hi, double* s_run,
                               uint32_t* s_err) {
-  uint64_t* slots = P.slots + (static_cast<int64_t>(b) * 2 + (pass & 1u)) * P.nrun;
+  uint64_t* slots = pass_slots(P, b, pass);
   const int tid = static_cast<int>(threadIdx.x);
-  for (int g = lo + tid; g < hi; g += kWalkThreads)
-    publish(&slots[g], (static_cast<uint64_t>(pass) << 32) |
-                           static_cast<uint64_t>(__float_as_uint(static_cast<float>(s_run[g]))));
   uint32_t err = 0u;
   for (int g = tid; g < P.nrun; g += kWalkThreads) {
     if (g >= lo && g < hi) continue;
@@ -205,6 +217,18 @@ __device__ void walk_exchange(const TreeSampleParams& P, int b, uint32_t pass, i
     s_run[g] = static_cast<double>(__uint_as_float(static_cast<uint32_t>(v)));
   }
   if (err != 0u) atomicOr(s_err, err);
+}
+
+// The lowest child of `node` above node `after` (children follow their
+// parent, so next_child(node, node) is the first), or -1: 64 nodes per
+// ballot. Every wave gets the same answer.
+__device__ __forceinline__ int next_child(const int* s_par, int N, int node, int after) {
+  for (int base = after + 1; base < N; base += kWave) {
+    const int u = base + lane_id();
+    const uint64_t m = __ballot(u < N && s_par[u] == node);
+    if (m != 0ull) return base + __ffsll(static_cast<unsigned long long>(m)) - 1;
+  }
+  return -1;
 }
 
 // The final draw by one wave: the run whose inclusive total first exceeds
@@ -217,8 +241,10 @@ template <class T, bool kResid>
 __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
                          const float* invZ, const double* s_run, double u) {
   const int lane = lane_id();
+  // rounds of 64 runs: fp64 DPP scans, the round's total from its last lane
   double carry = 0.0;
-  for (int base = 0; base < nrun; base += kWave) carry += __shfl(wave_inclusive_scan(base + lane < nrun ? s_run[base + lane] : 0.0), kWave - 1, kWave);
+  for (int base = 0; base < nrun; base += kWave)
+    carry += readlane_f64(wave_scan_dpp(base + lane < nrun ? s_run[base + lane] : 0.0), kWave - 1);
   const double total = carry;
   const double target = u * total;
   int found = -1, last_pos = -1;
@@ -226,18 +252,16 @@ __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nru
   carry = 0.0;
   for (int base = 0; base < nrun && found < 0; base += kWave) {
     const double v = base + lane < nrun ? s_run[base + lane] : 0.0;
-    const double inc = wave_inclusive_scan(v);
+    const double inc = wave_scan_dpp(v);
     const uint64_t pos = __ballot(v > 0.0);
     if (pos != 0ull) last_pos = base + 63 - __clzll(static_cast<long long>(pos));
     const uint64_t hit = __ballot(v > 0.0 && carry + inc > target);
     if (hit != 0ull) {
       const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      double excl = __shfl_up(inc, 1, kWave);
-      if (lane == 0) excl = 0.0;
       found = base + l;
-      prefix = carry + __shfl(excl, l, kWave);
+      prefix = carry + readlane_f64(wave_exclusive_from(inc), l);
     }
-    carry += __shfl(inc, kWave - 1, kWave);
+    carry += readlane_f64(inc, kWave - 1);
   }
   const int g = found >= 0 ? found : last_pos;
   if (g < 0) return -1;
@@ -261,9 +285,7 @@ __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nru
       lane_tot += wv[i * T::kVec + e];
     }
   }
-  const double inc = wave_inclusive_scan(static_cast<double>(lane_tot));
-  double excl = __shfl_up(inc, 1, kWave);
-  if (lane == 0) excl = 0.0;
+  const double excl = wave_exclusive_from(wave_scan_dpp(static_cast<double>(lane_tot)));
   int first = -1, last = -1;
   float run = 0.0f;
 #pragma unroll
@@ -279,10 +301,10 @@ __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nru
   int sel = -1, e = 0;
   if (hit != 0ull) {
     sel = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-    e = __shfl(first, sel, kWave);
+    e = __builtin_amdgcn_readlane(first, sel);
   } else if (any != 0ull) {
     sel = 63 - __clzll(static_cast<long long>(any));
-    e = __shfl(last, sel, kWave);
+    e = __builtin_amdgcn_readlane(last, sel);
   }
   if (sel < 0) return -1;
   return static_cast<int>((static_cast<int64_t>(g) * kRunVecs + kRunLaneVecs * sel) * T::kVec + e);
@@ -320,17 +342,14 @@ __global__ __launch_bounds__(kStatsTPB) __attribute__((amdgpu_waves_per_eu(SV_ST
 template <class T>
 __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSampleParams P) {
   __shared__ int s_par[SV_MAX_TREE_NODES];
-  __shared__ int s_kids[SV_MAX_TREE_NODES];
   __shared__ float s_lt[SV_MAX_TREE_NODES];  // node v's target and draft logits at its parent's position
   __shared__ float s_ld[SV_MAX_TREE_NODES];
   __shared__ float s_u[SV_MAX_TREE_NODES];   // node v's uniform
   __shared__ int s_path[SV_MAX_TREE_NODES];
-  __shared__ double s_run[kMaxWalkRuns];
+  __shared__ double s_run2[2][kMaxWalkRuns];  // run totals, passes alternating between the two
   __shared__ double s_Z[SV_MAX_TREE_NODES];
   __shared__ float s_invZ[SV_MAX_TREE_NODES];
   __shared__ double s_L[2 * (SV_MAX_TREE_NODES + 1)];  // log-normalisers: target rows, then draft rows, by position
-  __shared__ uint64_t s_mask[kWalkWaves];
-  __shared__ double s_sum;
   __shared__ int s_token;
   __shared__ uint32_t s_err;
   __shared__ int s_role;
@@ -433,26 +452,13 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
   int depth = 0;
   if (s_err == 0u) {  // block-uniform from here: every thread takes the same decisions
     int node = -1, pos = 0;
+    int buf = 0;  // s_run2 buffer of the next pass
     for (;;) {
-      // the children of `node`, ascending (thread v owns node v; N <= kWalkThreads)
-      const bool mine = tid < N && s_par[tid] == node;
-      const uint64_t m = __ballot(mine);
-      if (lane == 0) s_mask[wv] = m;
       const int64_t rowt = static_cast<int64_t>(b) * N1 + pos;
       const uint4* rt = reinterpret_cast<const uint4*>(tbase + rowt * row_bytes);
       const uint4* rd = reinterpret_cast<const uint4*>(dbase + (rowt)*row_bytes);
-      __syncthreads();
-      int nkids = 0, before = 0;
-#pragma unroll
-      for (int w2 = 0; w2 < kWalkWaves; ++w2) {
-        const int pc = __popcll(s_mask[w2]);
-        if (w2 < wv) before += pc;
-        nkids += pc;
-      }
-      if (mine) s_kids[before + __popcll(m & ((1ull << lane) - 1ull))] = tid;
-      __syncthreads();
       const double Lt = s_L[pos], Ld = s_L[N1 + pos];
-      if (s_err != 0u || !isfinite(Lt) || !isfinite(Ld)) {
+      if (!isfinite(Lt) || !isfinite(Ld)) {
         if (tid == 0) s_err |= SV_ERRF_NONFINITE;
         break;
       }
@@ -462,8 +468,8 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
       split_neg(Ld, w.nld_hi, w.nld_lo);
       int r = 0;
       bool taken = false, resid_totals = false;
-      for (int i = 0; i < nkids; ++i) {
-        const int kid = s_kids[i];
+      double* run = s_run2[buf];
+      for (int kid = next_child(s_par, N, node, node); kid >= 0; kid = next_child(s_par, N, node, kid)) {
         const double ap = static_cast<double>(s_lt[kid]) * c64 - Lt;
         const double aq = static_cast<double>(s_ld[kid]) * c64 - Ld;
         const double p = exp2_split(ap);
@@ -479,23 +485,25 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
           taken = true;
           break;
         }
-        // rejected: the residual max(0, P_r - q), per run and in total
-        walk_pass<T, true>(rt, rd, P.nvec, lo, hi, w, r, s_invZ, s_run);
+        // rejected: the residual max(0, P_r - q), per run and in total. A
+        // pass writes the buffer the previous pass did not, so a wave may
+        // start it while others still sum the previous one.
+        run = s_run2[buf];
+        buf ^= 1;
+        ++pass;
+        walk_pass<T, true>(rt, rd, P.nvec, lo, hi, w, r, s_invZ, run, G > 1 ? pass_slots(P, b, pass) : nullptr, pass);
         __syncthreads();
         if (G > 1) {
-          walk_exchange(P, b, ++pass, lo, hi, s_run, &s_err);
+          walk_exchange(P, b, pass, lo, hi, run, &s_err);
           __syncthreads();
         }
-        if (wv == 0) {
-          double z = 0.0;
-          for (int g = lane; g < P.nrun; g += kWave) z += s_run[g];
-          z = wave_sum(z);
-          if (lane == 0) s_sum = z;
-        }
-        __syncthreads();
-        const double Zr = s_sum;
+        // every wave sums the run totals itself, in the same order, and
+        // keeps Z_r (and its inverse) where its own lanes read them
+        double z = 0.0;
+        for (int g = lane; g < P.nrun; g += kWave) z += run[g];
+        const double Zr = wave_sum_f64_dpp(z);
         if (Zr >= static_cast<double>(FLT_MIN)) {  // 1 / Zr stays a finite fp32 factor
-          if (tid == 0) {
+          if (lane == 0) {
             s_Z[r] = Zr;
             s_invZ[r] = static_cast<float>(1.0 / Zr);
           }
@@ -504,28 +512,27 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
         } else {
           resid_totals = false;  // a residual of no (representable) mass: P unchanged
         }
-        __syncthreads();
       }
-      if (taken) {
-        __syncthreads();  // s_kids and s_mask are rewritten for the next node
-        continue;
-      }
+      if (taken) continue;
+      if (s_err != 0u) break;  // an expired exchange wait
       // no child accepted (or a leaf): draw from P_r at this position
       const double u = static_cast<double>(P.uniforms[static_cast<int64_t>(b) * N1 + N]);
-      if (resid_totals) {  // s_run holds the totals of max(0, P_{r-1} - q), proportional to P_r
+      if (resid_totals) {  // run holds the totals of max(0, P_{r-1} - q), proportional to P_r
         if (wv == 0 && gi == 0) {
-          const int t = walk_draw<T, true>(rt, rd, P.nvec, P.nrun, w, r - 1, s_invZ, s_run, u);
+          const int t = walk_draw<T, true>(rt, rd, P.nvec, P.nrun, w, r - 1, s_invZ, run, u);
           if (lane == 0) s_token = t;
         }
       } else {
-        walk_pass<T, false>(rt, rd, P.nvec, lo, hi, w, r, s_invZ, s_run);
+        run = s_run2[buf];
+        ++pass;
+        walk_pass<T, false>(rt, rd, P.nvec, lo, hi, w, r, s_invZ, run, G > 1 ? pass_slots(P, b, pass) : nullptr, pass);
         __syncthreads();
         if (G > 1) {
-          walk_exchange(P, b, ++pass, lo, hi, s_run, &s_err);
+          walk_exchange(P, b, pass, lo, hi, run, &s_err);
           __syncthreads();
         }
         if (wv == 0 && gi == 0) {
-          const int t = walk_draw<T, false>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, s_run, u);
+          const int t = walk_draw<T, false>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, run, u);
           if (lane == 0) s_token = t;
         }
       }
