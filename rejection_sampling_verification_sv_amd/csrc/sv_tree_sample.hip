@@ -50,15 +50,21 @@ namespace {
 
 constexpr int kWalkThreads = 1024;
 constexpr int kWalkWaves = kWalkThreads / kWave;
-// Rejections at one node whose factors a pass keeps in registers (more fall
-// back to reading them from LDS per token).
-constexpr int kWalkHoist = 3;
 
-// The exponent scale and the two rows' log-normalisers split for fp32 use:
-// p(v) = 2^(x_t c - L_t), q(v) = 2^(x_d c - L_d).
+// The distributions of the walk at one position. With p = 2^(x_t c - L_t)
+// and q = 2^(x_d c - L_d) the target and draft distributions there, the
+// distribution after r rejections is P_r = max(0, p - T_r q) / C_r, where
+// T_0 = 0, C_0 = 1, T_{k+1} = T_k + C_k and C_{k+1} = C_k Z_{k+1}, Z_{k+1}
+// the total of the residual max(0, P_k - q): by induction, max(0, P_k - q)
+// = max(0, p - (T_k + C_k) q) / C_k. So every level is one difference of two
+// exponentials, p / C_r and U q with U = T_r / C_r (U_{k+1} = (U_k + 1) /
+// Z_{k+1}), the constants folded into the exponent offsets:
+//   P_r(v)              = max(0, 2^(x_t c - L_t - log2 C_r) - 2^(x_d c - L_d + log2 U_r))
+//   max(0, P_r - q)(v)  = the same with U_r + 1 in place of U_r.
+// WalkRows holds those offsets (negated, as hi + lo fp32 pairs).
 struct WalkRows {
   Scale c;
-  float nlt_hi, nlt_lo, nld_hi, nld_lo;  // -L_t, -L_d as hi + lo
+  float nlt_hi, nlt_lo, nld_hi, nld_lo;
 };
 
 __device__ __forceinline__ void split_neg(double v, float& hi, float& lo) {
@@ -66,24 +72,31 @@ __device__ __forceinline__ void split_neg(double v, float& hi, float& lo) {
   lo = static_cast<float>(-v - static_cast<double>(hi));
 }
 
-// Weight of one token in fp32: the current distribution P_r (kResid false)
-// or its residual max(0, P_r - q) (kResid true), P_0 = p, each earlier
-// rejection k applying max(0, . - q) * invZ[k]. R >= 0: r = R, with the
-// factors in registers (iz); R < 0: any r, the factors read from invZ in LDS.
-// Both forms take the same operations in the same order.
-template <bool kResid, int R>
-__device__ __forceinline__ float walk_weight(float xt, float xd, const WalkRows& w, int r, const float* invZ,
-                                             const float (&iz)[kWalkHoist]) {
-  const float p = fast_exp2(scaled_arg(xt, w.c, w.nlt_hi) + w.nlt_lo);
-  const float q = fast_exp2(scaled_arg(xd, w.c, w.nld_hi) + w.nld_lo);
-  float val = p;
-  if constexpr (R >= 0) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) val = fmaxf(val - q, 0.0f) * iz[k];
+// Offsets for target log-normaliser Lt, draft Ld, the factor C and the
+// draft factor Uq (U, or U + 1 for a residual); Uq = 0 leaves the draft term
+// out. The logarithms of the factors are taken as log2_fast (about 1e-7
+// absolute, the order of the fp32 weights' own rounding).
+__device__ __forceinline__ WalkRows walk_rows(Scale c, double Lt, double Ld, double C, double Uq) {
+  WalkRows w;
+  w.c = c;
+  split_neg(C == 1.0 ? Lt : Lt + log2_fast(C), w.nlt_hi, w.nlt_lo);
+  if (Uq > 0.0) {
+    split_neg(Uq == 1.0 ? Ld : Ld - log2_fast(Uq), w.nld_hi, w.nld_lo);
   } else {
-    for (int k = 0; k < r; ++k) val = fmaxf(val - q, 0.0f) * invZ[k];
+    w.nld_hi = -INFINITY;
+    w.nld_lo = 0.0f;
   }
-  return kResid ? fmaxf(val - q, 0.0f) : val;
+  return w;
+}
+
+// Weight of one token in fp32: max(0, p' - q') with the offsets of w, or p'
+// alone when there is no draft term (kQ false).
+template <bool kQ>
+__device__ __forceinline__ float walk_weight(float xt, float xd, const WalkRows& w) {
+  const float p = fast_exp2(scaled_arg(xt, w.c, w.nlt_hi) + w.nlt_lo);
+  if constexpr (!kQ) return p;
+  const float q = fast_exp2(scaled_arg(xd, w.c, w.nld_hi) + w.nld_lo);
+  return fmaxf(p - q, 0.0f);
 }
 
 // This lane's vectors of run g of a row (vectors g * kRunVecs + lane + 64 i),
@@ -98,18 +111,17 @@ __device__ __forceinline__ void walk_load(const uint4* row, int64_t g, int64_t n
   }
 }
 
-template <class T, bool kResid, int R>
+template <class T, bool kQ>
 __device__ __forceinline__ float walk_run_sum(const uint4 (&at)[kRunLaneVecs], const uint4 (&ad)[kRunLaneVecs],
-                                              const WalkRows& w, int r, const float* invZ,
-                                              const float (&iz)[kWalkHoist]) {
+                                              const WalkRows& w) {
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < kRunLaneVecs; ++i) {
-    float xt[T::kVec], xd[T::kVec];
+    float xt[T::kVec], xd[T::kVec] = {};
     unpack<T>(at[i], xt);
-    unpack<T>(ad[i], xd);
+    if constexpr (kQ) unpack<T>(ad[i], xd);
 #pragma unroll
-    for (int e = 0; e < T::kVec; ++e) s += walk_weight<kResid, R>(xt[e], xd[e], w, r, invZ, iz);
+    for (int e = 0; e < T::kVec; ++e) s += walk_weight<kQ>(xt[e], xd[e], w);
   }
   return s;
 }
@@ -124,26 +136,23 @@ __device__ __forceinline__ uint64_t pass_word(uint32_t pass, float s) {
   return (static_cast<uint64_t>(pass) << 32) | static_cast<uint64_t>(__float_as_uint(s));
 }
 
-template <class T, bool kResid, int R>
-__device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int lo, int hi, const WalkRows& w, int r,
-                            const float* invZ, double* s_run, uint64_t* pub, uint32_t pass) {
+template <class T, bool kQ>
+__device__ void walk_pass_q(const uint4* rt, const uint4* rd, int64_t nvec, int lo, int hi, const WalkRows& w,
+                            double* s_run, uint64_t* pub, uint32_t pass) {
   const int g0 = lo + wave_id();
   if (g0 >= hi) return;
-  float iz[kWalkHoist];
-#pragma unroll
-  for (int k = 0; k < kWalkHoist; ++k) iz[k] = (k < R) ? invZ[k] : 0.0f;
   int g = g0;
-  uint4 at[kRunLaneVecs], ad[kRunLaneVecs];
+  uint4 at[kRunLaneVecs], ad[kRunLaneVecs] = {};
   walk_load<T>(rt, g, nvec, at);
-  walk_load<T>(rd, g, nvec, ad);
+  if constexpr (kQ) walk_load<T>(rd, g, nvec, ad);
   for (;;) {
     const int gn = g + kWalkWaves;
-    uint4 bt[kRunLaneVecs], bd[kRunLaneVecs];
+    uint4 bt[kRunLaneVecs], bd[kRunLaneVecs] = {};
     if (gn < hi) {
       walk_load<T>(rt, gn, nvec, bt);
-      walk_load<T>(rd, gn, nvec, bd);
+      if constexpr (kQ) walk_load<T>(rd, gn, nvec, bd);
     }
-    const float s = wave_sum_dpp(walk_run_sum<T, kResid, R>(at, ad, w, r, invZ, iz));
+    const float s = wave_sum_dpp(walk_run_sum<T, kQ>(at, ad, w));
     if (lane_id() == 0) {
       s_run[g] = static_cast<double>(s);
       if (pub != nullptr) publish(&pub[g], pass_word(pass, s));
@@ -158,19 +167,15 @@ __device__ void walk_pass_r(const uint4* rt, const uint4* rd, int64_t nvec, int 
   }
 }
 
-// walk_pass_r for the r at hand: 0 .. kWalkHoist rejections with their
-// factors in registers, more with the factors read from LDS.
-template <class T, bool kResid>
-__device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int lo, int hi, const WalkRows& w, int r,
-                          const float* invZ, double* s_run, uint64_t* pub, uint32_t pass) {
-  static_assert(kWalkHoist == 3, "one case per hoisted count");
-  switch (r) {
-    case 0: walk_pass_r<T, kResid, 0>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
-    case 1: walk_pass_r<T, kResid, 1>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
-    case 2: walk_pass_r<T, kResid, 2>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
-    case 3: walk_pass_r<T, kResid, 3>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
-    default: walk_pass_r<T, kResid, -1>(rt, rd, nvec, lo, hi, w, r, invZ, s_run, pub, pass); break;
-  }
+// One pass over the workgroup's runs of the distribution or residual that w
+// describes (with the draft term when q is set).
+template <class T>
+__device__ void walk_pass(const uint4* rt, const uint4* rd, int64_t nvec, int lo, int hi, const WalkRows& w, bool q,
+                          double* s_run, uint64_t* pub, uint32_t pass) {
+  if (q)
+    walk_pass_q<T, true>(rt, rd, nvec, lo, hi, w, s_run, pub, pass);
+  else
+    walk_pass_q<T, false>(rt, rd, nvec, lo, hi, w, s_run, pub, pass);
 }
 
 // Wait until *slot holds the totals of pass `pass` (its upper half) and
@@ -231,24 +236,55 @@ __device__ __forceinline__ int next_child(const int* s_par, int N, int node, int
   return -1;
 }
 
-// The final draw by one wave: the run whose inclusive total first exceeds
-// u * (sum of the run totals) (the last run with weight if rounding leaves
-// none), then that run rescanned in ascending token order (lane l holds its
-// vectors kRunLaneVecs * l ..) with the first token whose cumulative weight
-// exceeds the remainder (the last token with weight if none). -1 if no run
-// has weight.
-template <class T, bool kResid>
-__device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nrun, const WalkRows& w, int r,
-                         const float* invZ, const double* s_run, double u) {
+// Step one of the final draw, by any wave (every wave gets the same
+// answer): the run whose inclusive total first exceeds u * (sum of the run
+// totals), with the remainder inside it, or the last run with weight and an
+// infinite remainder if rounding leaves none; run -1 if no run has weight.
+// Rounds of 64 runs, fp64 DPP scans; up to kLocRounds rounds keep their
+// scans in registers for the search, more scan again.
+constexpr int kLocRounds = 4;
+
+struct RunPick {
+  int g;
+  double tk;
+};
+
+__device__ RunPick walk_locate(int nrun, const double* s_run, double u) {
   const int lane = lane_id();
-  // rounds of 64 runs: fp64 DPP scans, the round's total from its last lane
+  int found = -1, last_pos = -1;
+  double prefix = 0.0;
+  if (nrun <= kLocRounds * kWave) {
+    double v[kLocRounds], inc[kLocRounds], rsum[kLocRounds];
+    double carry = 0.0;
+#pragma unroll
+    for (int k = 0; k < kLocRounds; ++k) {
+      const int t = k * kWave + lane;
+      v[k] = (t < nrun) ? s_run[t] : 0.0;
+      inc[k] = wave_scan_dpp(v[k]);
+      rsum[k] = readlane_f64(inc[k], kWave - 1);
+      carry += rsum[k];
+    }
+    const double target = u * carry;
+    carry = 0.0;
+#pragma unroll
+    for (int k = 0; k < kLocRounds; ++k) {
+      const uint64_t pos = __ballot(v[k] > 0.0);
+      if (pos != 0ull) last_pos = k * kWave + 63 - __clzll(static_cast<long long>(pos));
+      const uint64_t hit = __ballot(v[k] > 0.0 && carry + inc[k] > target);
+      if (found < 0 && hit != 0ull) {
+        const int l = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+        found = k * kWave + l;
+        prefix = carry + readlane_f64(wave_exclusive_from(inc[k]), l);
+      }
+      carry += rsum[k];
+    }
+    const int g = found >= 0 ? found : last_pos;
+    return RunPick{g, found >= 0 ? target - prefix : INFINITY};
+  }
   double carry = 0.0;
   for (int base = 0; base < nrun; base += kWave)
     carry += readlane_f64(wave_scan_dpp(base + lane < nrun ? s_run[base + lane] : 0.0), kWave - 1);
-  const double total = carry;
-  const double target = u * total;
-  int found = -1, last_pos = -1;
-  double prefix = 0.0;
+  const double target = u * carry;
   carry = 0.0;
   for (int base = 0; base < nrun && found < 0; base += kWave) {
     const double v = base + lane < nrun ? s_run[base + lane] : 0.0;
@@ -264,24 +300,31 @@ __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nru
     carry += readlane_f64(inc, kWave - 1);
   }
   const int g = found >= 0 ? found : last_pos;
-  if (g < 0) return -1;
-  const double tk = found >= 0 ? target - prefix : INFINITY;
+  return RunPick{g, found >= 0 ? target - prefix : INFINITY};
+}
+
+// Step two, by one wave (of the workgroup whose runs include g, which read
+// them in its last pass): run g rescanned in ascending token order (lane l
+// holds its vectors kRunLaneVecs * l ..) with the first token whose
+// cumulative weight exceeds the remainder tk (the last token with weight if
+// none).
+template <class T, bool kQ>
+__device__ int walk_rescan_q(const uint4* rt, const uint4* rd, int64_t nvec, int g, double tk, const WalkRows& w) {
+  const int lane = lane_id();
   // lane l: vectors g * kRunVecs + kRunLaneVecs * l + i, its tokens in ascending order
   const int64_t vb = static_cast<int64_t>(g) * kRunVecs + kRunLaneVecs * lane;
-  constexpr float kNoFactors[kWalkHoist] = {};
   constexpr int NE = kRunLaneVecs * T::kVec;
   float wv[NE];
   float lane_tot = 0.0f;
 #pragma unroll
   for (int i = 0; i < kRunLaneVecs; ++i) {
     const uint4 qt = (vb + i < nvec) ? rt[vb + i] : neg_inf_vec<T>();
-    const uint4 qd = (vb + i < nvec) ? rd[vb + i] : neg_inf_vec<T>();
-    float xt[T::kVec], xd[T::kVec];
+    float xt[T::kVec], xd[T::kVec] = {};
     unpack<T>(qt, xt);
-    unpack<T>(qd, xd);
+    if constexpr (kQ) unpack<T>((vb + i < nvec) ? rd[vb + i] : neg_inf_vec<T>(), xd);
 #pragma unroll
     for (int e = 0; e < T::kVec; ++e) {
-      wv[i * T::kVec + e] = walk_weight<kResid, -1>(xt[e], xd[e], w, r, invZ, kNoFactors);
+      wv[i * T::kVec + e] = walk_weight<kQ>(xt[e], xd[e], w);
       lane_tot += wv[i * T::kVec + e];
     }
   }
@@ -308,6 +351,12 @@ __device__ int walk_draw(const uint4* rt, const uint4* rd, int64_t nvec, int nru
   }
   if (sel < 0) return -1;
   return static_cast<int>((static_cast<int64_t>(g) * kRunVecs + kRunLaneVecs * sel) * T::kVec + e);
+}
+
+template <class T>
+__device__ int walk_rescan(const uint4* rt, const uint4* rd, int64_t nvec, int g, double tk, const WalkRows& w,
+                           bool q) {
+  return q ? walk_rescan_q<T, true>(rt, rd, nvec, g, tk, w) : walk_rescan_q<T, false>(rt, rd, nvec, g, tk, w);
 }
 
 }  // namespace
@@ -347,10 +396,9 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
   __shared__ float s_u[SV_MAX_TREE_NODES];   // node v's uniform
   __shared__ int s_path[SV_MAX_TREE_NODES];
   __shared__ double s_run2[2][kMaxWalkRuns];  // run totals, passes alternating between the two
-  __shared__ double s_Z[SV_MAX_TREE_NODES];
-  __shared__ float s_invZ[SV_MAX_TREE_NODES];
   __shared__ double s_L[2 * (SV_MAX_TREE_NODES + 1)];  // log-normalisers: target rows, then draft rows, by position
   __shared__ int s_token;
+  __shared__ int s_drawn;
   __shared__ uint32_t s_err;
   __shared__ int s_role;
 
@@ -397,6 +445,7 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
   if (tid == 0) {
     s_err = (!(Tv > 0.0f) || !isfinite(Tv)) ? static_cast<uint32_t>(SV_ERRF_TEMPERATURE) : 0u;
     s_token = -1;
+    s_drawn = -1;
   }
   __syncthreads();
   // thread v owns node v (N <= kWalkThreads): its parent, token and uniform,
@@ -462,22 +511,23 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
         if (tid == 0) s_err |= SV_ERRF_NONFINITE;
         break;
       }
-      WalkRows w;
-      w.c = c;
-      split_neg(Lt, w.nlt_hi, w.nlt_lo);
-      split_neg(Ld, w.nld_hi, w.nld_lo);
-      int r = 0;
+      // P_r at this position as (C_r, U_r), P_0 = p (see WalkRows), with
+      // iC = 1 / C_r
+      double C = 1.0, iC = 1.0, U = 0.0;
       bool taken = false, resid_totals = false;
+      WalkRows wl{};  // the offsets of the last pass (its residual)
       double* run = s_run2[buf];
       for (int kid = next_child(s_par, N, node, node); kid >= 0; kid = next_child(s_par, N, node, kid)) {
         const double ap = static_cast<double>(s_lt[kid]) * c64 - Lt;
         const double aq = static_cast<double>(s_ld[kid]) * c64 - Ld;
-        const double p = exp2_split(ap);
         const double q = exp2_split(aq);
-        double val = p;
-        for (int k = 0; k < r; ++k) val = fmax(val - q, 0.0) / s_Z[k];
-        const double alpha = (val > 0.0) ? ((q > 0.0) ? fmin(1.0, val / q) : 1.0) : 0.0;
-        if (static_cast<double>(s_u[kid]) < alpha) {
+        // P_r(x) = max(0, p(x) / C_r - U_r q(x))
+        const double pc = exp2_split(ap) * iC;
+        const double val = (U > 0.0) ? fmax(pc - U * q, 0.0) : pc;
+        // u < alpha = min(1, P_r(x) / q(x)) (1 where q vanishes, 0 where P_r
+        // does), tested as u q < P_r(x): no division
+        const double uk = static_cast<double>(s_u[kid]);
+        if (val > 0.0 && uk < 1.0 && (q > 0.0 ? uk * q < val : true)) {
           node = kid;
           pos = node + 1;
           if (tid == 0) s_path[depth] = node;
@@ -491,23 +541,23 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
         run = s_run2[buf];
         buf ^= 1;
         ++pass;
-        walk_pass<T, true>(rt, rd, P.nvec, lo, hi, w, r, s_invZ, run, G > 1 ? pass_slots(P, b, pass) : nullptr, pass);
+        wl = walk_rows(c, Lt, Ld, C, U + 1.0);
+        walk_pass<T>(rt, rd, P.nvec, lo, hi, wl, true, run, G > 1 ? pass_slots(P, b, pass) : nullptr, pass);
         __syncthreads();
         if (G > 1) {
           walk_exchange(P, b, pass, lo, hi, run, &s_err);
           __syncthreads();
         }
         // every wave sums the run totals itself, in the same order, and
-        // keeps Z_r (and its inverse) where its own lanes read them
+        // moves on to P_{r+1} = max(0, P_r - q) / Z
         double z = 0.0;
         for (int g = lane; g < P.nrun; g += kWave) z += run[g];
         const double Zr = wave_sum_f64_dpp(z);
-        if (Zr >= static_cast<double>(FLT_MIN)) {  // 1 / Zr stays a finite fp32 factor
-          if (lane == 0) {
-            s_Z[r] = Zr;
-            s_invZ[r] = static_cast<float>(1.0 / Zr);
-          }
-          ++r;
+        if (Zr >= static_cast<double>(FLT_MIN)) {
+          const double iZ = 1.0 / Zr;
+          U = (U + 1.0) * iZ;
+          C *= Zr;
+          iC *= iZ;
           resid_totals = true;
         } else {
           resid_totals = false;  // a residual of no (representable) mass: P unchanged
@@ -517,37 +567,53 @@ __global__ __launch_bounds__(kWalkThreads) void tree_sample_walk_kernel(TreeSamp
       if (s_err != 0u) break;  // an expired exchange wait
       // no child accepted (or a leaf): draw from P_r at this position
       const double u = static_cast<double>(P.uniforms[static_cast<int64_t>(b) * N1 + N]);
-      if (resid_totals) {  // run holds the totals of max(0, P_{r-1} - q), proportional to P_r
-        if (wv == 0 && gi == 0) {
-          const int t = walk_draw<T, true>(rt, rd, P.nvec, P.nrun, w, r - 1, s_invZ, run, u);
-          if (lane == 0) s_token = t;
+      // The run is located by every wave (the same answer everywhere); the
+      // workgroup whose runs include it (it read them in its last pass) draws.
+      if (resid_totals) {  // run holds the totals of the last residual, proportional to P_r
+        if (wv == 0) {
+          const RunPick pick = walk_locate(P.nrun, run, u);
+          if (lane == 0) s_drawn = pick.g;
+          if (pick.g >= lo && pick.g < hi) {
+            const int t = walk_rescan<T>(rt, rd, P.nvec, pick.g, pick.tk, wl, true);
+            if (lane == 0) s_token = t;
+          }
         }
       } else {
         run = s_run2[buf];
         ++pass;
-        walk_pass<T, false>(rt, rd, P.nvec, lo, hi, w, r, s_invZ, run, G > 1 ? pass_slots(P, b, pass) : nullptr, pass);
+        const WalkRows w = walk_rows(c, Lt, Ld, C, U);
+        walk_pass<T>(rt, rd, P.nvec, lo, hi, w, U > 0.0, run, G > 1 ? pass_slots(P, b, pass) : nullptr, pass);
         __syncthreads();
         if (G > 1) {
           walk_exchange(P, b, pass, lo, hi, run, &s_err);
           __syncthreads();
         }
-        if (wv == 0 && gi == 0) {
-          const int t = walk_draw<T, false>(rt, rd, P.nvec, P.nrun, w, r, s_invZ, run, u);
-          if (lane == 0) s_token = t;
+        if (wv == 0) {
+          const RunPick pick = walk_locate(P.nrun, run, u);
+          if (lane == 0) s_drawn = pick.g;
+          if (pick.g >= lo && pick.g < hi) {
+            const int t = walk_rescan<T>(rt, rd, P.nvec, pick.g, pick.tk, w, U > 0.0);
+            if (lane == 0) s_token = t;
+          }
         }
       }
       break;
     }
   }
   __syncthreads();
+  const int drawn_run = s_drawn;  // the run the token is drawn from (-1: none, or the walk ended early)
   // no token with weight in a distribution that passed the normaliser checks
   // would take every weight underflowing: reported as a zero normaliser
-  if (gi == 0) {  // the sequence's outputs
-    const uint32_t err = s_err | ((s_err == 0u && s_token < 0) ? static_cast<uint32_t>(SV_ERRF_NONFINITE) : 0u);
-    const bool bad = err != 0u;
+  const uint32_t err =
+      s_err | ((s_err == 0u && drawn_run < 0) ? static_cast<uint32_t>(SV_ERRF_NONFINITE) : 0u);
+  const bool bad = err != 0u;
+  // the drawn token by the workgroup that drew it (by workgroup 0 when there
+  // is none), the rest of the sequence's outputs by workgroup 0
+  const bool draws = drawn_run >= 0 ? (drawn_run >= lo && drawn_run < hi) : (gi == 0);
+  if (draws && tid == 0) P.next_token[b] = bad ? -1 : s_token;
+  if (gi == 0) {
     if (tid == 0) {
       P.accept_len[b] = bad ? -1 : depth;
-      P.next_token[b] = bad ? -1 : s_token;
       raise_error(P.err_flags, err);
     }
     for (int i = tid; i < N; i += kWalkThreads)
