@@ -1464,15 +1464,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((flatten)) void chain_small
   const int ch = static_cast<int>(blockIdx.x - bu * cps);
   if (!stats_chunk_prefetched<T, kStatsTPB, kSmallMaxBatches>(P, b, ch)) stats_chunk<T, kStatsTPB, false>(P, b, ch);
   uint32_t* done = P.done + static_cast<int64_t>(b) * kCtrStride;
-  if (threadIdx.x == 0) {
-    // count the chunk once this thread's slot stores have completed (the
-    // decider still checks every slot's tag and reads again if it is zero)
-    __builtin_amdgcn_s_waitcnt(0);
-    const uint32_t prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev + 1u == cps) ? 1 : 0;
-    if (prev >= cps) {  // a counter not left at zero: the workspace was not re-zeroed
-      raise_error(P.err_flags, kErrInternal);
-      publish(P.abort, 1ull);
+  __shared__ int s_seen;
+  if (wave_id() == 0) {
+    if (SV_SMALL_PRIO > 0) __builtin_amdgcn_s_setprio(SV_SMALL_PRIO);
+    uint32_t prev = 0u;
+    if (threadIdx.x == 0) {
+      // count the chunk (with SV_SMALL_COUNT_WAIT once this thread's slot
+      // stores have completed; the decider checks every slot's tag and
+      // reads again while one is zero)
+      if (SV_SMALL_COUNT_WAIT) __builtin_amdgcn_s_waitcnt(0);
+      prev = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Beside the count, every workgroup reads the sequence's slots once and
+    // decides if all are visible (the same decision, and the same outputs,
+    // as the one the last to count makes): the last one then usually has
+    // its plan one round trip sooner, and others need not wait for it.
+    const DecideIn in = decide_inputs(P, b);
+    const bool seen = SV_SMALL_SPEC ? decide_live_wave<T>(P, b, &s_plan, true, in) : false;
+    if (lane_id() == 0) {
+      s_last = (prev + 1u == cps) ? 1 : 0;
+      s_seen = seen ? 1 : 0;
+      if (prev >= cps) {  // a counter not left at zero: the workspace was not re-zeroed
+        raise_error(P.err_flags, kErrInternal);
+        publish(P.abort, 1ull);
+      }
     }
   }
   __syncthreads();
@@ -1483,12 +1498,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((flatten)) void chain_small
   const int t_begin = ch * P.tiles_per_block;
   const int t_end = min(t_begin + P.tiles_per_block, P.ntiles);
   if (wave_id() == 0) {
-    if (s_last)
-      small_decide<T>(P, b, &s_plan);
-    else if (!owners || t_begin < t_end)
+    if (s_last) {
+      if (s_seen) {
+        if (lane_id() == 0) publish_plan(P, b, s_plan);
+      } else {
+        small_decide<T>(P, b, &s_plan);
+      }
+    } else if (s_seen) {
+      // the plan is already here
+    } else if (!owners || t_begin < t_end) {
       small_await_plan(P, b, &s_plan);
-    else if (lane_id() == 0)
+    } else if (lane_id() == 0) {
       s_plan.j = -1;
+    }
   }
   __syncthreads();
   const SeqPlan pl = s_plan;
