@@ -1213,7 +1213,7 @@ __device__ __forceinline__ bool read_plan(const ChainParams& P, int b, SeqPlan* 
 // stored by a workgroup that counted its chunk after its stores completed,
 // so the loop ends; bounded like await_slot all the same. On expiry the
 // sequence is reported as an invalid row (plan j = -1, SV_ERRF_INTERNAL).
-template <class T>
+template <class T, bool kPublish = true>
 __device__ void small_decide(const ChainParams& P, int b, SeqPlan* s_plan) {
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   const DecideIn in = decide_inputs(P, b);
@@ -1233,7 +1233,7 @@ __device__ void small_decide(const ChainParams& P, int b, SeqPlan* s_plan) {
     raise_error(P.err_flags, kErrInternal);
     s_plan->j = -1;
   }
-  if (lane_id() == 0) publish_plan(P, b, *s_plan);
+  if (kPublish && lane_id() == 0) publish_plan(P, b, *s_plan);
 }
 
 // Wave 0 of any other workgroup: wait for the decider's plan. The decider
@@ -1498,7 +1498,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((flatten)) void chain_small
   const int t_begin = ch * P.tiles_per_block;
   const int t_end = min(t_begin + P.tiles_per_block, P.ntiles);
   if (wave_id() == 0) {
-    if (s_last) {
+    if (SV_SMALL_POLL_SLOTS) {
+      // Every workgroup that needs the plan reads the slots again until all
+      // are visible and decides itself: no hand-off of the plan. Every slot
+      // comes from a workgroup of this grid, which the device holds at once
+      // (checked on the host), so each is written: the wait ends (bounded
+      // as small_decide's).
+      if (s_seen) {
+        // decided from the first read
+      } else if (s_last || !owners || t_begin < t_end) {
+        small_decide<T, false>(P, b, &s_plan);
+      } else if (lane_id() == 0) {
+        s_plan.j = -1;
+      }
+    } else if (s_last) {
       if (s_seen) {
         if (lane_id() == 0) publish_plan(P, b, s_plan);
       } else {

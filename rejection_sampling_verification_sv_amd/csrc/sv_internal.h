@@ -409,6 +409,9 @@ constexpr int kCtrStride = SV_CTR_STRIDE;
 #ifndef SV_SMALL_SPEC
 #define SV_SMALL_SPEC 1
 #endif
+#ifndef SV_SMALL_POLL_SLOTS
+#define SV_SMALL_POLL_SLOTS 1
+#endif
 // Block order of the one-launch grid: the sampling blocks of sequence b
 // follow the statistics blocks of sequence b + lag (the last lag sequences'
 // sampling blocks close the grid), so that with in-order dispatch they start
