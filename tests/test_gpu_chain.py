@@ -377,6 +377,37 @@ def test_concurrent_streams(sv):
         assert torch.equal(ob["out_tokens"], ref_b["out_tokens"])
 
 
+def test_small_calls_beside_other_launches(sv):
+    # Small-form calls (every workgroup of a sequence waits for the sequence's
+    # slots) on two streams at once, beside a one-launch call on a third
+    # stream that holds more workgroups than the device: every output must
+    # equal the same call's on one stream, with no error flag.
+    c1 = CHAIN_CONFIGS["c1"]
+    inp_a = chain_inputs(c1, device="cuda")
+    inp_b = chain_inputs(CHAIN_CONFIGS["c2"].with_(B=16, variant=CHAIN_CONFIGS["c2"].variant + 30), device="cuda")
+    inp_c = chain_inputs(CHAIN_CONFIGS["c2"], device="cuda")
+    assert sv.sv_chain_form(c1.B, c1.K, c1.V, inp_a["target"].dtype) == 1
+    assert sv.sv_chain_form(16, CHAIN_CONFIGS["c2"].K, CHAIN_CONFIGS["c2"].V, torch.bfloat16) == 1
+    _say("two small calls and a one-launch call on three streams", c1.name, "B=16 c2 recipe", CHAIN_CONFIGS["c2"].name)
+    refs = [_run(sv, inp) for inp in (inp_a, inp_b, inp_c)]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    outs = []
+    for _ in range(8):
+        row = []
+        for inp, st in zip((inp_c, inp_a, inp_b), (streams[2], streams[0], streams[1])):
+            with torch.cuda.stream(st):
+                row.append(sv.sv_verify_chain(inp["target"], inp["draft"], inp["draft_tokens"], inp["temperature"],
+                                              inp["uniforms"], stream=st))
+        outs.append((row[1], row[2], row[0]))
+    torch.cuda.synchronize()
+    for got in outs:
+        for o, ref in zip(got, refs):
+            assert int(o["err_flags"].item()) == 0
+            for k in ("accept_len", "out_tokens", "p_draft", "q_draft", "residual_mass"):
+                assert torch.equal(o[k], ref[k]), k
+    assert_chain_parity(compare_chain(refs[0], oracle_chain(inp_a)))
+
+
 def test_vanished_residual_draws_from_p(sv):
     """A rejected position whose residual max(0, p - q) sums to zero (the
     rule for that case: draw from p at that position). At position 0 of
